@@ -1,0 +1,96 @@
+"""Planted mistakes in the oracle (on the CPU only): each plausible slip —
+a wrong index, a dropped term, a transposed operand, an off-by-one mask, the
+wrong tie rule — must make at least one pin fail.  This is evidence that the
+pins constrain the oracle rather than restate it."""
+import numpy as np
+import pytest
+
+import test_oracle_attention as att
+import test_oracle_codecs as cod
+import test_oracle_paging as pag
+from oracle import codecs, paged
+
+_orig_attend = paged.attend
+_orig_gather = paged.gather
+
+
+def _attend_no_scale(q, K, V, scale, visible=None):
+    return _orig_attend(q, K, V, 1.0, visible)
+
+
+def _attend_transposed(q, K, V, scale, visible=None):
+    # Weights applied to K instead of V.
+    return _orig_attend(q, K, K, scale, visible)
+
+
+def _attend_no_max_shift(q, K, V, scale, visible=None):
+    q, K, V = (np.asarray(a, np.float64) for a in (q, K, V))
+    if visible is not None:
+        K, V = K[visible], V[visible]
+    if K.shape[0] == 0:
+        return np.zeros(V.shape[1])
+    with np.errstate(over="ignore", invalid="ignore"):
+        p = np.exp((K @ q) * float(np.float32(scale)))
+        return (p @ V) / p.sum()
+
+
+def _attend_causal_off_by_one(q, K, V, scale, visible=None):
+    if visible is not None:
+        visible = np.roll(visible, -1)
+        visible[-1] = False
+    return _orig_attend(q, K, V, scale, visible)
+
+
+def _gather_wrong_offset(pool, table_row, length):
+    out = _orig_gather(pool, table_row, length + 1)
+    return out[1:]
+
+
+def _kv_head_modulo(h, num_heads, num_kv_heads):
+    return h % num_kv_heads
+
+
+def _merge_without_rescale(states):
+    w = np.array([l for _, l, _ in states])
+    o = np.stack([o for _, _, o in states])
+    return (w[:, None] * o).sum(0) / w.sum()
+
+
+def _encode_ties_away(x):
+    x = np.asarray(x, np.float32)
+    out = codecs._orig_f32_to_e4m3fn(x)
+    pos = codecs.e4m3fn_to_f64(np.arange(0x7F, dtype=np.uint8))
+    mids = (pos[:-1] + pos[1:]) / 2
+    a = np.abs(x.astype(np.float64))
+    tie = np.isin(a, mids)
+    up = np.searchsorted(pos, a)
+    return np.where(tie, (up | (out & 0x80)).astype(np.uint8), out)
+
+
+MUTATIONS = [
+    ("attend", _attend_no_scale, [att.test_decode_matches_torch_sdpa_tiny]),
+    ("attend", _attend_transposed, [att.test_decode_matches_torch_sdpa_tiny]),
+    ("attend", _attend_no_max_shift, [att.test_decode_closed_forms]),
+    ("attend", _attend_causal_off_by_one, [att.test_prefill_matches_sdpa_with_offset_causal_mask]),
+    ("gather", _gather_wrong_offset, [pag.test_lib_worked_example_slots_and_gather]),
+    ("_kv_head", _kv_head_modulo, [att.test_decode_matches_torch_sdpa_tiny]),
+    ("lse_merge", _merge_without_rescale, [att.test_split_merge_equals_unsplit]),
+]
+
+
+@pytest.mark.parametrize("name,fn,pins", MUTATIONS, ids=[f"{m[0]}:{m[1].__name__}" for m in MUTATIONS])
+def test_planted_mistake_is_caught(monkeypatch, name, fn, pins):
+    monkeypatch.setattr(paged, name, fn)
+    for pin in pins:
+        with pytest.raises((AssertionError, ValueError, IndexError)):
+            if pin is att.test_split_merge_equals_unsplit:
+                pin(48)
+            else:
+                pin()
+
+
+def test_planted_tie_rule_is_caught(monkeypatch):
+    monkeypatch.setattr(codecs, "_orig_f32_to_e4m3fn", codecs.f32_to_e4m3fn, raising=False)
+    monkeypatch.setattr(codecs, "f32_to_e4m3fn", _encode_ties_away)
+    with pytest.raises(AssertionError):
+        cod.test_e4m3fn_encode_ties_go_to_even_code()
