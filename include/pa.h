@@ -1,0 +1,235 @@
+/*
+ * pa.h — paged K/V cache attention for AMD Instinct MI355X (gfx950), C ABI.
+ *
+ * The library implements the data-parallel path of PagedAttention as the
+ * pages describe it:
+ *   [LIB]  "vLLM：大语言模型推理与服务库", §4 "vLLM核心——PagedAttention"
+ *          (§4.2 physical blocks, block table, block pool; §4.3 writing a
+ *          new token's K/V; §4.4 the attention kernel's inputs and per-block
+ *          computation);
+ *   [EVAL] "vLLM 高性能大语言模型推理引擎深度技术评估与分布式架构展望"
+ *          (logical-to-physical block mapping, step 4: the kernel gathers
+ *          K/V in place through the block table; the fork/append/free
+ *          primitives and copy-on-write; chunked prefill);
+ *   [ESSAY] the openeuler.csdn.net vLLM essay, "PagedAttention：把操作系统
+ *          的分页搬上 GPU" (kernel grid over heads, sequences and partitions);
+ *   [DEEP] "vLLM 深度解析：从 PagedAttention 到生产部署", §3.1 (block table,
+ *          prefix sharing, copy-on-write).
+ *
+ * ---------------------------------------------------------------------------
+ * Conventions shared by every call
+ * ---------------------------------------------------------------------------
+ * Pointers.  Every array argument is a DEVICE pointer owned by the caller.
+ *   The library allocates no memory, keeps no per-call state and never
+ *   synchronises: work is enqueued on `stream` (a hipStream_t; NULL = the
+ *   default stream) and is complete only when the caller synchronises.
+ *   Scalars (sizes, max lengths, scales) are host values, so no call reads
+ *   device memory on the host.
+ *
+ * Element types (pa_dtype).  PA_F32 = IEEE binary32; PA_BF16 = bfloat16;
+ *   PA_FP8_E4M3 = OCP FP8 E4M3FN (bias 7, no infinities, 0x7F/0xFF NaN,
+ *   largest finite 448) holding value * scale with a per-tensor fp32 scale.
+ *
+ * K/V pool layout.  The K cache and the V cache are two separate pools with
+ *   the same shape
+ *       [num_blocks][num_kv_heads][block_size][head_size]
+ *   head dimension fastest.  A (block, kv_head) tile of block_size tokens is
+ *   contiguous (4 KiB for bf16 16x128, fp8 32x128 and f32 16x64), and one
+ *   token row of one head is head_size contiguous elements.  Slot s of the
+ *   pool is offset s % block_size of physical block s / block_size.
+ *   Bytes of one pool: num_blocks * num_kv_heads * block_size * head_size *
+ *   element size (pa_pool_bytes).
+ *
+ * Block tables.  block_tables is int32 [num_seqs][max_blocks_per_seq],
+ *   row-major: entry j of row s is the physical block holding tokens
+ *   j*block_size .. j*block_size+block_size-1 of sequence s ([LIB] §4.2
+ *   item 2).  Entries at or past ceil(seq_len / block_size) are never read
+ *   (callers usually fill them with -1).  Tables may share blocks (prefix
+ *   sharing, [DEEP] §3.1).
+ *
+ * GQA.  num_heads query heads read num_kv_heads K/V heads in contiguous
+ *   groups: query head h reads KV head h / (num_heads / num_kv_heads).
+ *
+ * Errors.  Every call validates its host arguments before enqueuing work
+ *   and returns one of the PA_* codes below; on error nothing is enqueued.
+ *   pa_strerror(code) names the code; pa_last_error() returns a message
+ *   about the most recent failure on the calling thread.  Device-side
+ *   data errors (a block id >= num_blocks, a slot past the pool) cannot be
+ *   seen on the host and are undefined behaviour, like a bad page-table
+ *   entry.
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PA_F32 = 0,
+  PA_BF16 = 1,
+  PA_FP8_E4M3 = 2
+} pa_dtype;
+
+enum {
+  PA_OK = 0,
+  PA_ERR_INVALID = -1,     /* null pointer, bad size, inconsistent arguments   */
+  PA_ERR_UNSUPPORTED = -2, /* dtype / head_size / block_size / group not built */
+  PA_ERR_WORKSPACE = -3,   /* workspace missing or too small                   */
+  PA_ERR_HIP = -4          /* the HIP runtime refused a launch                 */
+};
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int32_t pa_version(void);
+
+/* Name of an error code. Never NULL. */
+const char* pa_strerror(int32_t code);
+
+/* Detail of the most recent error on the calling thread ("" if none). */
+const char* pa_last_error(void);
+
+/* Bytes of ONE pool (K or V) in the layout above; 0 for invalid input. */
+size_t pa_pool_bytes(int32_t num_blocks, int32_t num_kv_heads, int32_t block_size,
+                     int32_t head_size, int32_t cache_dtype);
+
+/*
+ * pa_cache_write — the slot-mapped cache write ("reshape and cache").
+ *
+ * [LIB] §4.3 item 2: each generated token's K/V is written into its
+ * sequence's current block (a new block is taken from the pool when the
+ * last one is full — that allocation is the caller's; it arrives here as
+ * the slot).  For each token t with slot = slot_mapping[t] >= 0 and each KV
+ * head h:
+ *     k_cache[slot / block_size][h][slot % block_size][:] = enc(key[t][h][:])
+ *     v_cache[...same...]                                  = enc(value[t][h][:])
+ * A negative slot marks a padding token and is skipped.  Two tokens must not
+ * share a slot.
+ *
+ *   key, value     [num_tokens][num_kv_heads][head_size] of src_dtype, contiguous
+ *   src_dtype      PA_F32 or PA_BF16 (or PA_FP8_E4M3 into an fp8 cache)
+ *   k_cache,v_cache  pools of cache_dtype, layout above
+ *   slot_mapping   int64 [num_tokens]
+ *   k_scale, v_scale  per-tensor scales, used only when cache_dtype is fp8
+ *                  and src_dtype is not: enc(x) = E4M3FN(clamp(fp32(x) /
+ *                  scale, -448, 448)) rounded to nearest, ties to even; NaN
+ *                  stays NaN (0x7F with its sign).  Otherwise enc is a bit
+ *                  copy (src_dtype must equal cache_dtype).
+ * Supported: head_size * sizeof(cache element) a multiple of 16 bytes.
+ * num_tokens == 0 is a valid no-op.
+ */
+int32_t pa_cache_write(const void* key, const void* value, int32_t src_dtype,
+                       int32_t num_tokens,
+                       void* k_cache, void* v_cache, int32_t cache_dtype,
+                       int32_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                       int32_t head_size,
+                       const int64_t* slot_mapping, float k_scale, float v_scale,
+                       void* stream);
+
+/*
+ * pa_copy_blocks — the block copy behind copy-on-write.
+ *
+ * [EVAL] "束搜索与并行采样的三大调度原语": fork makes a child table point at
+ * the parent's physical blocks; when a shared block is about to change, only
+ * that block is copied into a fresh one ([DEEP] §3.1 copy-on-write).  For
+ * each pair i, every K and V element of physical block block_mapping[2i]
+ * (all heads, all offsets) is copied bit-exactly into block
+ * block_mapping[2i+1].
+ *
+ *   block_mapping  int64 [num_pairs][2] = (src, dst), device memory
+ * Destinations must be distinct and must not be the source of any pair
+ * (all copies run concurrently).  num_pairs == 0 is a valid no-op.
+ */
+int32_t pa_copy_blocks(void* k_cache, void* v_cache, int32_t cache_dtype,
+                       int32_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                       int32_t head_size,
+                       const int64_t* block_mapping, int32_t num_pairs, void* stream);
+
+/*
+ * Workspace bytes pa_decode needs for split-K partials; 0 when
+ * partition_size == 0 or one partition covers max_seq_len.
+ */
+size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t head_size,
+                                int32_t max_seq_len, int32_t partition_size);
+
+/*
+ * pa_decode — one query token per sequence against its paged context.
+ *
+ * [LIB] §4.4 items 1 and 3: with q, the K/V block pools, the block tables
+ * and each sequence's context length, every query walks its sequence's
+ * physical blocks, scores q·k, takes the softmax and weights V:
+ *     out[s][h][:] = sum_t softmax_t(scale * q[s][h]·K_s[t][g]) * V_s[t][g]
+ * over t < seq_lens[s], g = h / (num_heads / num_kv_heads), with K_s[t] read
+ * from block block_tables[s][t / block_size], offset t % block_size, in place
+ * ([EVAL] mapping step 4).  fp8 caches are dequantised as code * k_scale and
+ * code * v_scale.  seq_lens[s] == 0 yields zeros.  The softmax runs in fp32
+ * with a running maximum.
+ *
+ * Split-K ([ESSAY]: a grid axis over partitions of the context): with
+ * partition_size > 0 (a multiple of block_size) each sequence's context is
+ * cut into ceil(seq_len / partition_size) partitions processed in parallel;
+ * each writes its (max score, exp-sum, normalised output) into `workspace`
+ * and a second kernel merges them with log-sum-exp weights.  Sequences with
+ * a single partition are finished by the first kernel.  partition_size == 0
+ * processes each sequence in one partition and needs no workspace.
+ *
+ *   out            [num_seqs][num_heads][head_size] of q_dtype
+ *   query          [num_seqs][num_heads][head_size] of q_dtype
+ *   q_dtype/cache_dtype  (PA_F32, PA_F32), (PA_BF16, PA_BF16), (PA_BF16, PA_FP8_E4M3)
+ *   block_tables   int32 [num_seqs][max_blocks_per_seq]
+ *   seq_lens       int32 [num_seqs], each in [0, max_seq_len] and
+ *                  ceil(seq_len / block_size) <= max_blocks_per_seq
+ *   max_seq_len    host upper bound of seq_lens (sizes the grid)
+ *   workspace      device buffer of >= pa_decode_workspace_size(...) bytes
+ * Supported: head_size 64 or 128, block_size 16 or 32, num_heads /
+ * num_kv_heads in {1, 2, 4, 8}, except f32 with head_size 128.
+ */
+int32_t pa_decode(void* out, const void* query, int32_t q_dtype,
+                  int32_t num_seqs, int32_t num_heads, int32_t head_size,
+                  const void* k_cache, const void* v_cache, int32_t cache_dtype,
+                  int32_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                  const int32_t* block_tables, int32_t max_blocks_per_seq,
+                  const int32_t* seq_lens, int32_t max_seq_len,
+                  float scale, float k_scale, float v_scale,
+                  int32_t partition_size, void* workspace, size_t workspace_bytes,
+                  void* stream);
+
+/*
+ * pa_prefill_chunk — causal attention for chunks of prompt tokens whose K/V
+ * are already in the paged cache.
+ *
+ * [EVAL] "分块预填充克服队头阻塞": a long prompt is processed in chunks so it
+ * can share a step with decode.  Chunk c has query rows
+ * query_start_loc[c] .. query_start_loc[c+1]-1 and seq_lens[c] keys in the
+ * cache (earlier chunks and itself, written beforehand with
+ * pa_cache_write).  Query i of a chunk of n queries sits at position
+ * seq_lens[c] - n + i and attends keys 0..that position:
+ *     out[r][h][:] = sum_{j <= pos} softmax_j(scale * q[r][h]·K_c[j][g]) * V_c[j][g]
+ * QK^T and PV run on the matrix cores (bf16 operands, fp32 accumulation;
+ * fp8 K/V widen exactly to bf16 and their scales are applied in fp32).
+ *
+ *   out, query     [num_tokens][num_heads][head_size] of q_dtype
+ *   q_dtype/cache_dtype  (PA_BF16, PA_BF16) or (PA_BF16, PA_FP8_E4M3)
+ *   query_start_loc int32 [num_chunks + 1], query_start_loc[num_chunks] == num_tokens
+ *   max_query_len  host upper bound of the chunks' query counts
+ *   block_tables   int32 [num_chunks][max_blocks_per_seq]
+ *   seq_lens       int32 [num_chunks]; each >= its chunk's query count
+ * Supported: head_size 128, block_size 16 or 32, group size in {1, 2, 4, 8}.
+ */
+int32_t pa_prefill_chunk(void* out, const void* query, int32_t q_dtype,
+                         int32_t num_tokens, int32_t num_heads, int32_t head_size,
+                         const int32_t* query_start_loc, int32_t num_chunks,
+                         int32_t max_query_len,
+                         const void* k_cache, const void* v_cache, int32_t cache_dtype,
+                         int32_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                         const int32_t* block_tables, int32_t max_blocks_per_seq,
+                         const int32_t* seq_lens,
+                         float scale, float k_scale, float v_scale, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

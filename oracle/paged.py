@@ -102,47 +102,66 @@ def attend(q, K, V, scale: float, visible=None):
     return (p @ V) / p.sum()
 
 
-def paged_decode(q, k_pool, v_pool, block_tables, seq_lens, scale: float):
+def _seq_kv(k_pool, v_pool, table_row, L, kv_dtype, k_scale, v_scale):
+    """Gathered K and V of one sequence as float64 [L, Hkv, D].  With
+    ``kv_dtype`` the pools hold raw storage words, decoded after the gather."""
+    K = gather(k_pool, table_row, L)
+    V = gather(v_pool, table_row, L)
+    if kv_dtype is not None:
+        K = pool_values(K, kv_dtype, k_scale)
+        V = pool_values(V, kv_dtype, v_scale)
+    return K, V
+
+
+def paged_decode(q, k_pool, v_pool, block_tables, seq_lens, scale: float, kv_dtype=None,
+                 k_scale: float = 1.0, v_scale: float = 1.0, seqs=None):
     """One query token per sequence against its whole paged context.
 
-    q: [S, Hq, D] float64; k_pool, v_pool: float64 pools
-    ``[num_blocks, Hkv, block_size, D]``; block_tables: [S, MB]; seq_lens: [S]
-    (the context includes the token just written).  Returns [S, Hq, D]."""
+    q: [S, Hq, D]; k_pool, v_pool: pools ``[num_blocks, Hkv, block_size, D]``
+    of float64 values, or of raw storage words of ``kv_dtype`` (fp8 scaled by
+    k_scale / v_scale); block_tables: [S, MB]; seq_lens: [S] (the context
+    includes the token just written).  ``seqs`` restricts the work to some
+    sequences (other rows stay zero).  Returns float64 [S, Hq, D]."""
     q = np.asarray(q, dtype=np.float64)
     S, Hq, D = q.shape
     Hkv = k_pool.shape[1]
     out = np.zeros((S, Hq, D), dtype=np.float64)
-    for s in range(S):
+    for s in (range(S) if seqs is None else seqs):
         L = int(seq_lens[s])
-        K = gather(k_pool, block_tables[s], L)
-        V = gather(v_pool, block_tables[s], L)
+        K, V = _seq_kv(k_pool, v_pool, block_tables[s], L, kv_dtype, k_scale, v_scale)
         for h in range(Hq):
             g = _kv_head(h, Hq, Hkv)
             out[s, h] = attend(q[s, h], K[:, g, :], V[:, g, :], scale)
     return out
 
 
-def paged_prefill(q, query_start, k_pool, v_pool, block_tables, seq_lens, scale: float):
+def paged_prefill(q, query_start, k_pool, v_pool, block_tables, seq_lens, scale: float,
+                  kv_dtype=None, k_scale: float = 1.0, v_scale: float = 1.0, rows=None):
     """Causal attention for chunks of queries appended to paged sequences.
 
     Chunk c owns query rows query_start[c]:query_start[c+1]; it has
     n_c = query_start[c+1] - query_start[c] queries and seq_lens[c] keys in
     the cache, its own included.  Query i of the chunk sits at position
-    seq_lens[c] - n_c + i and sees keys 0..that position."""
+    seq_lens[c] - n_c + i and sees keys 0..that position.  Pools as in
+    ``paged_decode``; ``rows`` restricts the work to some query rows."""
     q = np.asarray(q, dtype=np.float64)
     T, Hq, D = q.shape
     Hkv = k_pool.shape[1]
     out = np.zeros((T, Hq, D), dtype=np.float64)
+    want = None if rows is None else set(int(r) for r in rows)
     for c in range(len(seq_lens)):
         a, b = int(query_start[c]), int(query_start[c + 1])
         L = int(seq_lens[c])
         n = b - a
         if n > L:
             raise ValueError("a chunk cannot hold more queries than keys")
-        K = gather(k_pool, block_tables[c], L)
-        V = gather(v_pool, block_tables[c], L)
+        if want is not None and not any(a <= r < b for r in want):
+            continue
+        K, V = _seq_kv(k_pool, v_pool, block_tables[c], L, kv_dtype, k_scale, v_scale)
         keys = np.arange(L)
         for i in range(n):
+            if want is not None and a + i not in want:
+                continue
             pos = L - n + i
             for h in range(Hq):
                 g = _kv_head(h, Hq, Hkv)

@@ -1,0 +1,188 @@
+"""ctypes binding of ``libpa.so`` (the C ABI in include/pa.h).
+
+Argument marshalling only: each function takes torch tensors that already
+live on the GPU, reads their data pointers and shapes, and calls the C entry
+point of the same name on the current HIP stream.  Every step of the path
+runs in the library's kernels; there is no fallback.  If the library is not
+built, loading it raises ``PagedAttentionError``.
+
+Tensor conventions (all contiguous, on the same device):
+  K/V pools      [num_blocks, num_kv_heads, block_size, head_size];
+                 float32, bfloat16, or uint8 / float8_e4m3fn for fp8 E4M3FN
+  queries, out   [num_tokens, num_heads, head_size]
+  block_tables   int32 [num_seqs, max_blocks_per_seq]
+  seq_lens       int32 [num_seqs]
+  slot_mapping   int64 [num_tokens]
+  block_mapping  int64 [num_pairs, 2]
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+PA_F32, PA_BF16, PA_FP8_E4M3 = 0, 1, 2
+PA_OK, PA_ERR_INVALID, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = 0, -1, -2, -3, -4
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
+
+_c_int, _c_f, _c_p, _c_sz = ctypes.c_int32, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+
+_SIGNATURES = {
+    "pa_version": ([], _c_int),
+    "pa_strerror": ([_c_int], ctypes.c_char_p),
+    "pa_last_error": ([], ctypes.c_char_p),
+    "pa_pool_bytes": ([_c_int, _c_int, _c_int, _c_int, _c_int], _c_sz),
+    "pa_cache_write": ([_c_p, _c_p, _c_int, _c_int, _c_p, _c_p, _c_int, _c_int, _c_int, _c_int,
+                        _c_int, _c_p, _c_f, _c_f, _c_p], _c_int),
+    "pa_copy_blocks": ([_c_p, _c_p, _c_int, _c_int, _c_int, _c_int, _c_int, _c_p, _c_int, _c_p],
+                       _c_int),
+    "pa_decode_workspace_size": ([_c_int, _c_int, _c_int, _c_int, _c_int], _c_sz),
+    "pa_decode": ([_c_p, _c_p, _c_int, _c_int, _c_int, _c_int, _c_p, _c_p, _c_int, _c_int, _c_int,
+                   _c_int, _c_p, _c_int, _c_p, _c_int, _c_f, _c_f, _c_f, _c_int, _c_p, _c_sz,
+                   _c_p], _c_int),
+    "pa_prefill_chunk": ([_c_p, _c_p, _c_int, _c_int, _c_int, _c_int, _c_p, _c_int, _c_int, _c_p,
+                          _c_p, _c_int, _c_int, _c_int, _c_int, _c_p, _c_int, _c_p, _c_f, _c_f,
+                          _c_f, _c_p], _c_int),
+}
+
+
+class PagedAttentionError(RuntimeError):
+    """A library call returned an error code (message from pa_last_error)."""
+
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{msg} [{code}]")
+        self.code = code
+
+
+_lib = None
+
+
+def load(path: Optional[str] = None):
+    """Load the HIP library (once) and declare its C signatures."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise PagedAttentionError(PA_ERR_HIP, f"HIP library not built: {p} is missing "
+                                  "(run __graft_entry__.build() or paged_kv_cache_11_amd/build.py)")
+    lib = ctypes.CDLL(p)
+    for name, (args, res) in _SIGNATURES.items():
+        f = getattr(lib, name)
+        f.argtypes, f.restype = args, res
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def exported_symbols():
+    return sorted(_SIGNATURES)
+
+
+def _check(code: int):
+    if code != PA_OK:
+        raise PagedAttentionError(code, load().pa_last_error().decode() or
+                                  load().pa_strerror(code).decode())
+
+
+def dtype_code(t) -> int:
+    import torch
+
+    if t.dtype == torch.float32:
+        return PA_F32
+    if t.dtype == torch.bfloat16:
+        return PA_BF16
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return PA_FP8_E4M3
+    raise PagedAttentionError(PA_ERR_UNSUPPORTED, f"no pa dtype for {t.dtype}")
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise PagedAttentionError(PA_ERR_INVALID, "tensors passed to the library must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _pool_dims(k_cache, v_cache):
+    if k_cache.dim() != 4 or tuple(k_cache.shape) != tuple(v_cache.shape) or k_cache.dtype != v_cache.dtype:
+        raise PagedAttentionError(PA_ERR_INVALID, "k_cache and v_cache must be equal 4-D pools "
+                                  "[num_blocks, num_kv_heads, block_size, head_size]")
+    nb, hkv, bs, d = (int(x) for x in k_cache.shape)
+    return nb, hkv, bs, d
+
+
+def pa_version() -> int:
+    return int(load().pa_version())
+
+
+def pa_pool_bytes(num_blocks, num_kv_heads, block_size, head_size, cache_dtype) -> int:
+    return int(load().pa_pool_bytes(num_blocks, num_kv_heads, block_size, head_size, cache_dtype))
+
+
+def pa_cache_write(key, value, k_cache, v_cache, slot_mapping, k_scale: float = 1.0,
+                   v_scale: float = 1.0, stream=None) -> None:
+    """Write key/value [num_tokens, num_kv_heads, head_size] into their slots."""
+    nb, hkv, bs, d = _pool_dims(k_cache, v_cache)
+    _check(load().pa_cache_write(_ptr(key), _ptr(value), dtype_code(key), int(key.shape[0]),
+                                 _ptr(k_cache), _ptr(v_cache), dtype_code(k_cache), nb, bs, hkv, d,
+                                 _ptr(slot_mapping), float(k_scale), float(v_scale), _stream(stream)))
+
+
+def pa_copy_blocks(k_cache, v_cache, block_mapping, stream=None) -> None:
+    """Copy whole physical blocks (src, dst) in both pools."""
+    nb, hkv, bs, d = _pool_dims(k_cache, v_cache)
+    n = int(block_mapping.shape[0]) if block_mapping is not None else 0
+    _check(load().pa_copy_blocks(_ptr(k_cache), _ptr(v_cache), dtype_code(k_cache), nb, bs, hkv, d,
+                                 _ptr(block_mapping) if n else None, n, _stream(stream)))
+
+
+def pa_decode_workspace_size(num_seqs, num_heads, head_size, max_seq_len, partition_size) -> int:
+    return int(load().pa_decode_workspace_size(num_seqs, num_heads, head_size, max_seq_len,
+                                               partition_size))
+
+
+def pa_decode(out, query, k_cache, v_cache, block_tables, seq_lens, max_seq_len: int,
+              scale: float, k_scale: float = 1.0, v_scale: float = 1.0,
+              partition_size: int = 0, workspace=None, stream=None) -> None:
+    """Decode attention of query [num_seqs, num_heads, head_size] into out.
+
+    With ``workspace=None`` and a split that needs one, a workspace tensor
+    is taken from torch's allocator."""
+    import torch
+
+    nb, hkv, bs, d = _pool_dims(k_cache, v_cache)
+    S, H = int(query.shape[0]), int(query.shape[1])
+    need = pa_decode_workspace_size(S, H, d, max_seq_len, partition_size)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=query.device)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(load().pa_decode(_ptr(out), _ptr(query), dtype_code(query), S, H, d, _ptr(k_cache),
+                            _ptr(v_cache), dtype_code(k_cache), nb, bs, hkv, _ptr(block_tables),
+                            int(block_tables.shape[1]), _ptr(seq_lens), int(max_seq_len),
+                            float(scale), float(k_scale), float(v_scale), int(partition_size),
+                            _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def pa_prefill_chunk(out, query, query_start_loc, max_query_len: int, k_cache, v_cache,
+                     block_tables, seq_lens, scale: float, k_scale: float = 1.0,
+                     v_scale: float = 1.0, stream=None) -> None:
+    """Causal attention of chunk queries [num_tokens, num_heads, head_size]."""
+    nb, hkv, bs, d = _pool_dims(k_cache, v_cache)
+    T, H = int(query.shape[0]), int(query.shape[1])
+    _check(load().pa_prefill_chunk(_ptr(out), _ptr(query), dtype_code(query), T, H, d,
+                                   _ptr(query_start_loc), int(seq_lens.shape[0]),
+                                   int(max_query_len), _ptr(k_cache), _ptr(v_cache),
+                                   dtype_code(k_cache), nb, bs, hkv, _ptr(block_tables),
+                                   int(block_tables.shape[1]), _ptr(seq_lens), float(scale),
+                                   float(k_scale), float(v_scale), _stream(stream)))

@@ -1,0 +1,120 @@
+// cache_kernels.hip — the slot-mapped cache write and the block copy.
+//
+// Cache write: "vLLM：大语言模型推理与服务库" §4.3 item 2 — each new token's
+// K/V goes into its sequence's current block; the block (and so the slot)
+// was chosen by the caller's allocator.  Block copy: the copy-on-write step
+// of the fork/append/free primitives in "vLLM 高性能大语言模型推理引擎深度
+// 技术评估与分布式架构展望" and "vLLM 深度解析" §3.1.
+//
+// Both are HBM-bound scatters/copies of 16-byte chunks: every thread moves
+// one 16-byte chunk of the destination, so each wavefront writes 1 KiB of
+// contiguous pool (one token row of a head is head_size contiguous elements
+// and one block of all heads is contiguous).
+#include "pa_internal.h"
+
+namespace pa {
+
+// One thread per 16-byte destination chunk; chunk c of row (t, h).
+template <typename SRC, typename DST>
+__global__ __launch_bounds__(256) void cache_write_kernel(
+    const uint8_t* __restrict__ key, const uint8_t* __restrict__ value,
+    uint8_t* __restrict__ k_cache, uint8_t* __restrict__ v_cache,
+    const int64_t* __restrict__ slot_mapping, int64_t total_chunks,
+    int chunks_per_row, int num_kv_heads, int block_size, int head_size,
+    float k_scale, float v_scale) {
+  constexpr int SB = Elem<SRC>::bytes, DB = Elem<DST>::bytes;
+  constexpr int EPC = 16 / DB;  // elements per destination chunk
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= total_chunks) return;
+  const int c = (int)(i % chunks_per_row);
+  const int64_t row = i / chunks_per_row;        // t * Hkv + h
+  const int h = (int)(row % num_kv_heads);
+  const int64_t t = row / num_kv_heads;
+  const int64_t slot = slot_mapping[t];
+  if (slot < 0) return;
+  const int64_t blk = slot / block_size;
+  const int off = (int)(slot % block_size);
+  const int64_t dst_elem =
+      ((blk * num_kv_heads + h) * block_size + off) * (int64_t)head_size + (int64_t)c * EPC;
+  const int64_t src_elem = row * (int64_t)head_size + (int64_t)c * EPC;
+#pragma unroll
+  for (int kv = 0; kv < 2; ++kv) {
+    const uint8_t* src = (kv ? value : key) + src_elem * SB;
+    uint8_t* dst = (kv ? v_cache : k_cache) + dst_elem * DB;
+    if constexpr (std::is_same<SRC, DST>::value) {
+      *(u32x4*)dst = *(const u32x4*)src;
+    } else {
+      static_assert(std::is_same<DST, FP8>::value, "only fp8 caches quantise");
+      const float sc = kv ? v_scale : k_scale;
+      float x[EPC];
+      constexpr int NSRC = EPC * SB / 16;  // 16-byte source vectors per chunk
+#pragma unroll
+      for (int j = 0; j < NSRC; ++j) {
+        const u32x4 w = ((const u32x4*)src)[j];
+        Vec<SRC>::to_f32(w, x + j * Vec<SRC>::n);
+      }
+      uint32_t out[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        uint32_t b = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) b |= f32_to_e4m3fn(x[4 * j + k] / sc) << (8 * k);
+        out[j] = b;
+      }
+      *(u32x4*)dst = u32x4{out[0], out[1], out[2], out[3]};
+    }
+  }
+}
+
+template <typename SRC, typename DST>
+static hipError_t launch_cache_write(const CacheWriteArgs& a) {
+  const int chunks_per_row = a.head_size * Elem<DST>::bytes / 16;
+  const int64_t total = (int64_t)a.num_tokens * a.num_kv_heads * chunks_per_row;
+  const int64_t nblocks = (total + 255) / 256;
+  hipLaunchKernelGGL((cache_write_kernel<SRC, DST>), dim3((unsigned)nblocks), dim3(256), 0,
+                     a.stream, (const uint8_t*)a.key, (const uint8_t*)a.value,
+                     (uint8_t*)a.k_cache, (uint8_t*)a.v_cache, a.slot_mapping, total,
+                     chunks_per_row, a.num_kv_heads, a.block_size, a.head_size, a.k_scale,
+                     a.v_scale);
+  return hipGetLastError();
+}
+
+hipError_t cache_write(const CacheWriteArgs& a) {
+  if (a.src_dtype == a.cache_dtype) {
+    switch (a.cache_dtype) {
+      case PA_F32: return launch_cache_write<F32, F32>(a);
+      case PA_BF16: return launch_cache_write<BF16, BF16>(a);
+      default: return launch_cache_write<FP8, FP8>(a);
+    }
+  }
+  if (a.src_dtype == PA_F32) return launch_cache_write<F32, FP8>(a);
+  return launch_cache_write<BF16, FP8>(a);
+}
+
+// grid: x = chunk group of one block, y = pair, z = 0 (K) / 1 (V).
+__global__ __launch_bounds__(256) void copy_blocks_kernel(
+    uint8_t* __restrict__ k_cache, uint8_t* __restrict__ v_cache,
+    const int64_t* __restrict__ block_mapping, int64_t block_chunks) {
+  const int64_t pair = blockIdx.y;
+  const int64_t src = block_mapping[2 * pair], dst = block_mapping[2 * pair + 1];
+  uint8_t* pool = blockIdx.z ? v_cache : k_cache;
+  const u32x4* s = (const u32x4*)pool + src * block_chunks;
+  u32x4* d = (u32x4*)pool + dst * block_chunks;
+  for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < block_chunks;
+       c += (int64_t)gridDim.x * blockDim.x)
+    d[c] = s[c];
+}
+
+hipError_t copy_blocks(const CopyBlocksArgs& a) {
+  const int64_t block_bytes =
+      (int64_t)a.num_kv_heads * a.block_size * a.head_size * dtype_bytes(a.cache_dtype);
+  const int64_t block_chunks = block_bytes / 16;
+  int64_t gx = (block_chunks + 255) / 256;
+  if (gx > 64) gx = 64;
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)gx, (unsigned)a.num_pairs, 2), dim3(256),
+                     0, a.stream, (uint8_t*)a.k_cache, (uint8_t*)a.v_cache, a.block_mapping,
+                     block_chunks);
+  return hipGetLastError();
+}
+
+}  // namespace pa

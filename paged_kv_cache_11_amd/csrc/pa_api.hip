@@ -1,0 +1,260 @@
+// pa_api.hip — the C ABI of the library (declared in include/pa.h):
+// host-side validation, workspace carving and launch dispatch.  No call
+// allocates memory or synchronises; every error is detected on the host
+// before anything is enqueued.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "pa_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int32_t fail(int32_t code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int32_t ok() {
+  g_last_error.clear();
+  return PA_OK;
+}
+
+bool valid_dtype(int32_t d) { return d == PA_F32 || d == PA_BF16 || d == PA_FP8_E4M3; }
+
+int32_t check_pool(const void* k_cache, const void* v_cache, int32_t cache_dtype,
+                   int32_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                   int32_t head_size) {
+  if (!k_cache || !v_cache) return fail(PA_ERR_INVALID, "k_cache / v_cache is NULL");
+  if (!valid_dtype(cache_dtype)) return fail(PA_ERR_INVALID, "unknown cache dtype %d", cache_dtype);
+  if (num_blocks <= 0 || block_size <= 0 || num_kv_heads <= 0 || head_size <= 0)
+    return fail(PA_ERR_INVALID,
+                "pool sizes must be positive (num_blocks %d, block_size %d, num_kv_heads %d, "
+                "head_size %d)", num_blocks, block_size, num_kv_heads, head_size);
+  if ((head_size * pa::dtype_bytes(cache_dtype)) % 16 != 0)
+    return fail(PA_ERR_UNSUPPORTED, "a head row must be a multiple of 16 bytes (head_size %d)",
+                head_size);
+  return PA_OK;
+}
+
+int32_t hip_result(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  if (e == hipErrorInvalidValue)
+    return fail(PA_ERR_UNSUPPORTED, "%s: shape not instantiated", what);
+  return fail(PA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Partitions of the longest sequence (1 when not split).
+int64_t decode_max_parts(int32_t max_seq_len, int32_t partition_size) {
+  if (partition_size <= 0 || max_seq_len <= partition_size) return 1;
+  return ceil_div(max_seq_len, partition_size);
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+extern "C" {
+
+int32_t pa_version(void) { return 100; }
+
+const char* pa_strerror(int32_t code) {
+  switch (code) {
+    case PA_OK: return "PA_OK";
+    case PA_ERR_INVALID: return "PA_ERR_INVALID: invalid argument";
+    case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED: combination not built";
+    case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: workspace missing or too small";
+    case PA_ERR_HIP: return "PA_ERR_HIP: HIP runtime error";
+    default: return "unknown pa error code";
+  }
+}
+
+const char* pa_last_error(void) { return g_last_error.c_str(); }
+
+size_t pa_pool_bytes(int32_t num_blocks, int32_t num_kv_heads, int32_t block_size,
+                     int32_t head_size, int32_t cache_dtype) {
+  if (num_blocks <= 0 || num_kv_heads <= 0 || block_size <= 0 || head_size <= 0 ||
+      !valid_dtype(cache_dtype))
+    return 0;
+  return (size_t)num_blocks * num_kv_heads * block_size * head_size * pa::dtype_bytes(cache_dtype);
+}
+
+int32_t pa_cache_write(const void* key, const void* value, int32_t src_dtype, int32_t num_tokens,
+                       void* k_cache, void* v_cache, int32_t cache_dtype, int32_t num_blocks,
+                       int32_t block_size, int32_t num_kv_heads, int32_t head_size,
+                       const int64_t* slot_mapping, float k_scale, float v_scale,
+                       void* stream) {
+  if (int32_t r = check_pool(k_cache, v_cache, cache_dtype, num_blocks, block_size, num_kv_heads,
+                             head_size))
+    return r;
+  if (num_tokens < 0) return fail(PA_ERR_INVALID, "num_tokens %d < 0", num_tokens);
+  if (!valid_dtype(src_dtype)) return fail(PA_ERR_INVALID, "unknown src dtype %d", src_dtype);
+  if (src_dtype != cache_dtype && !(cache_dtype == PA_FP8_E4M3 && src_dtype != PA_FP8_E4M3))
+    return fail(PA_ERR_UNSUPPORTED, "no cache write from dtype %d into dtype %d", src_dtype,
+                cache_dtype);
+  if (cache_dtype == PA_FP8_E4M3 && src_dtype != PA_FP8_E4M3 &&
+      !(k_scale > 0.f && v_scale > 0.f && k_scale < INFINITY && v_scale < INFINITY))
+    return fail(PA_ERR_INVALID, "fp8 scales must be finite and positive");
+  if (num_tokens == 0) return ok();
+  if (!key || !value || !slot_mapping)
+    return fail(PA_ERR_INVALID, "key / value / slot_mapping is NULL");
+  pa::CacheWriteArgs a{key, value, src_dtype, num_tokens, k_cache, v_cache, cache_dtype,
+                       num_blocks, block_size, num_kv_heads, head_size, slot_mapping, k_scale,
+                       v_scale, (hipStream_t)stream};
+  return hip_result(pa::cache_write(a), "pa_cache_write");
+}
+
+int32_t pa_copy_blocks(void* k_cache, void* v_cache, int32_t cache_dtype, int32_t num_blocks,
+                       int32_t block_size, int32_t num_kv_heads, int32_t head_size,
+                       const int64_t* block_mapping, int32_t num_pairs, void* stream) {
+  if (int32_t r = check_pool(k_cache, v_cache, cache_dtype, num_blocks, block_size, num_kv_heads,
+                             head_size))
+    return r;
+  if (num_pairs < 0) return fail(PA_ERR_INVALID, "num_pairs %d < 0", num_pairs);
+  if (num_pairs == 0) return ok();
+  if (!block_mapping) return fail(PA_ERR_INVALID, "block_mapping is NULL");
+  pa::CopyBlocksArgs a{k_cache, v_cache, cache_dtype, num_blocks, block_size, num_kv_heads,
+                       head_size, block_mapping, num_pairs, (hipStream_t)stream};
+  return hip_result(pa::copy_blocks(a), "pa_copy_blocks");
+}
+
+size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t head_size,
+                                int32_t max_seq_len, int32_t partition_size) {
+  if (num_seqs <= 0 || num_heads <= 0 || head_size <= 0) return 0;
+  const int64_t mp = decode_max_parts(max_seq_len, partition_size);
+  if (mp <= 1) return 0;
+  const size_t n = (size_t)num_seqs * num_heads * mp;
+  return align256(n * head_size * sizeof(float)) + align256(n * 2 * sizeof(float));
+}
+
+int32_t pa_decode(void* out, const void* query, int32_t q_dtype, int32_t num_seqs,
+                  int32_t num_heads, int32_t head_size, const void* k_cache, const void* v_cache,
+                  int32_t cache_dtype, int32_t num_blocks, int32_t block_size,
+                  int32_t num_kv_heads, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                  const int32_t* seq_lens, int32_t max_seq_len, float scale, float k_scale,
+                  float v_scale, int32_t partition_size, void* workspace, size_t workspace_bytes,
+                  void* stream) {
+  if (int32_t r = check_pool(k_cache, v_cache, cache_dtype, num_blocks, block_size, num_kv_heads,
+                             head_size))
+    return r;
+  if (num_seqs < 0) return fail(PA_ERR_INVALID, "num_seqs %d < 0", num_seqs);
+  if (num_heads <= 0 || num_heads % num_kv_heads != 0)
+    return fail(PA_ERR_INVALID, "num_heads %d must be a positive multiple of num_kv_heads %d",
+                num_heads, num_kv_heads);
+  if (!valid_dtype(q_dtype)) return fail(PA_ERR_INVALID, "unknown query dtype %d", q_dtype);
+  if (max_blocks_per_seq <= 0) return fail(PA_ERR_INVALID, "max_blocks_per_seq must be > 0");
+  if (max_seq_len < 0 || (int64_t)max_seq_len > (int64_t)max_blocks_per_seq * block_size)
+    return fail(PA_ERR_INVALID, "max_seq_len %d does not fit %d blocks of %d tokens", max_seq_len,
+                max_blocks_per_seq, block_size);
+  if (partition_size < 0 || partition_size % block_size != 0)
+    return fail(PA_ERR_INVALID, "partition_size %d must be >= 0 and a multiple of block_size %d",
+                partition_size, block_size);
+  if (!(scale == scale) || !(k_scale == k_scale) || !(v_scale == v_scale))
+    return fail(PA_ERR_INVALID, "scales must not be NaN");
+  const int group = num_heads / num_kv_heads;
+  if (!pa::decode_supported(q_dtype, cache_dtype, head_size, block_size, group))
+    return fail(PA_ERR_UNSUPPORTED,
+                "decode not built for q dtype %d, cache dtype %d, head_size %d, block_size %d, "
+                "group %d", q_dtype, cache_dtype, head_size, block_size, group);
+  if (num_seqs == 0) return ok();
+  if (!out || !query || !block_tables || !seq_lens)
+    return fail(PA_ERR_INVALID, "out / query / block_tables / seq_lens is NULL");
+  const int64_t mp = decode_max_parts(max_seq_len, partition_size);
+  if (mp > 65535) return fail(PA_ERR_INVALID, "too many partitions (%lld)", (long long)mp);
+  float* part_o = nullptr;
+  float* part_ml = nullptr;
+  if (mp > 1) {
+    const size_t need = pa_decode_workspace_size(num_seqs, num_heads, head_size, max_seq_len,
+                                                 partition_size);
+    if (!workspace || workspace_bytes < need)
+      return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                  workspace ? workspace_bytes : (size_t)0);
+    const size_t n = (size_t)num_seqs * num_heads * mp;
+    part_o = (float*)workspace;
+    part_ml = (float*)((char*)workspace + align256(n * head_size * sizeof(float)));
+  }
+  pa::DecodeArgs a{};
+  a.out = out; a.query = query; a.q_dtype = q_dtype;
+  a.num_seqs = num_seqs; a.num_heads = num_heads; a.head_size = head_size;
+  a.k_cache = k_cache; a.v_cache = v_cache; a.cache_dtype = cache_dtype;
+  a.num_blocks = num_blocks; a.block_size = block_size; a.num_kv_heads = num_kv_heads;
+  a.block_tables = block_tables; a.max_blocks_per_seq = max_blocks_per_seq;
+  a.seq_lens = seq_lens; a.max_seq_len = max_seq_len;
+  a.scale = scale; a.k_scale = k_scale; a.v_scale = v_scale;
+  a.partition_blocks = mp > 1 ? partition_size / block_size : 0;
+  a.max_parts = (int32_t)mp;
+  a.part_o = part_o; a.part_ml = part_ml;
+  a.stream = (hipStream_t)stream;
+  hipError_t e;
+  if (cache_dtype == PA_F32) e = pa::decode_f32(a);
+  else if (cache_dtype == PA_BF16) e = pa::decode_bf16(a);
+  else e = pa::decode_fp8(a);
+  return hip_result(e, "pa_decode");
+}
+
+int32_t pa_prefill_chunk(void* out, const void* query, int32_t q_dtype, int32_t num_tokens,
+                         int32_t num_heads, int32_t head_size, const int32_t* query_start_loc,
+                         int32_t num_chunks, int32_t max_query_len, const void* k_cache,
+                         const void* v_cache, int32_t cache_dtype, int32_t num_blocks,
+                         int32_t block_size, int32_t num_kv_heads, const int32_t* block_tables,
+                         int32_t max_blocks_per_seq, const int32_t* seq_lens, float scale,
+                         float k_scale, float v_scale, void* stream) {
+  if (int32_t r = check_pool(k_cache, v_cache, cache_dtype, num_blocks, block_size, num_kv_heads,
+                             head_size))
+    return r;
+  if (num_tokens < 0 || num_chunks < 0 || max_query_len < 0)
+    return fail(PA_ERR_INVALID, "negative size");
+  if (num_heads <= 0 || num_heads % num_kv_heads != 0)
+    return fail(PA_ERR_INVALID, "num_heads %d must be a positive multiple of num_kv_heads %d",
+                num_heads, num_kv_heads);
+  if (!valid_dtype(q_dtype)) return fail(PA_ERR_INVALID, "unknown query dtype %d", q_dtype);
+  if (max_blocks_per_seq <= 0) return fail(PA_ERR_INVALID, "max_blocks_per_seq must be > 0");
+  if (!(scale == scale) || !(k_scale == k_scale) || !(v_scale == v_scale))
+    return fail(PA_ERR_INVALID, "scales must not be NaN");
+  const int group = num_heads / num_kv_heads;
+  if (!pa::prefill_supported(q_dtype, cache_dtype, head_size, block_size, group))
+    return fail(PA_ERR_UNSUPPORTED,
+                "prefill not built for q dtype %d, cache dtype %d, head_size %d, block_size %d, "
+                "group %d", q_dtype, cache_dtype, head_size, block_size, group);
+  if (num_tokens == 0 || num_chunks == 0) return ok();
+  if (!out || !query || !query_start_loc || !block_tables || !seq_lens)
+    return fail(PA_ERR_INVALID, "a device array argument is NULL");
+  pa::PrefillArgs a{};
+  a.out = out; a.query = query; a.q_dtype = q_dtype;
+  a.num_tokens = num_tokens; a.num_heads = num_heads; a.head_size = head_size;
+  a.query_start_loc = query_start_loc; a.num_chunks = num_chunks; a.max_query_len = max_query_len;
+  a.k_cache = k_cache; a.v_cache = v_cache; a.cache_dtype = cache_dtype;
+  a.num_blocks = num_blocks; a.block_size = block_size; a.num_kv_heads = num_kv_heads;
+  a.block_tables = block_tables; a.max_blocks_per_seq = max_blocks_per_seq;
+  a.seq_lens = seq_lens;
+  a.scale = scale; a.k_scale = k_scale; a.v_scale = v_scale;
+  a.stream = (hipStream_t)stream;
+  return hip_result(pa::prefill(a), "pa_prefill_chunk");
+}
+
+}  // extern "C"
+
+namespace pa {
+
+bool decode_supported(int32_t q_dtype, int32_t cache_dtype, int head_size, int block_size,
+                      int group) {
+  const bool g_ok = group == 1 || group == 2 || group == 4 || group == 8;
+  const bool bs_ok = block_size == 16 || block_size == 32;
+  if (!g_ok || !bs_ok) return false;
+  if (q_dtype == PA_F32 && cache_dtype == PA_F32) return head_size == 64;
+  if (q_dtype == PA_BF16 && (cache_dtype == PA_BF16 || cache_dtype == PA_FP8_E4M3))
+    return head_size == 64 || head_size == 128;
+  return false;
+}
+
+}  // namespace pa

@@ -1,0 +1,96 @@
+// pa_internal.h — host-side argument bundles and launcher declarations
+// shared between the C ABI (pa_api.hip) and the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "../../include/pa.h"
+#include "pa_device.h"
+
+namespace pa {
+
+inline int dtype_bytes(int32_t dt) { return dt == PA_F32 ? 4 : dt == PA_BF16 ? 2 : 1; }
+
+struct CacheWriteArgs {
+  const void* key;
+  const void* value;
+  int32_t src_dtype;
+  int32_t num_tokens;
+  void* k_cache;
+  void* v_cache;
+  int32_t cache_dtype;
+  int32_t num_blocks, block_size, num_kv_heads, head_size;
+  const int64_t* slot_mapping;
+  float k_scale, v_scale;
+  hipStream_t stream;
+};
+
+struct CopyBlocksArgs {
+  void* k_cache;
+  void* v_cache;
+  int32_t cache_dtype;
+  int32_t num_blocks, block_size, num_kv_heads, head_size;
+  const int64_t* block_mapping;
+  int32_t num_pairs;
+  hipStream_t stream;
+};
+
+struct DecodeArgs {
+  void* out;
+  const void* query;
+  int32_t q_dtype;
+  int32_t num_seqs, num_heads, head_size;
+  const void* k_cache;
+  const void* v_cache;
+  int32_t cache_dtype;
+  int32_t num_blocks, block_size, num_kv_heads;
+  const int32_t* block_tables;
+  int32_t max_blocks_per_seq;
+  const int32_t* seq_lens;
+  int32_t max_seq_len;
+  float scale, k_scale, v_scale;
+  int32_t partition_blocks;  // blocks per partition; 0 = whole sequence
+  int32_t max_parts;         // grid extent over partitions
+  float* part_o;             // [num_seqs][num_heads][max_parts][head_size]
+  float* part_ml;            // [num_seqs][num_heads][max_parts][2]
+  hipStream_t stream;
+};
+
+struct PrefillArgs {
+  void* out;
+  const void* query;
+  int32_t q_dtype;
+  int32_t num_tokens, num_heads, head_size;
+  const int32_t* query_start_loc;
+  int32_t num_chunks, max_query_len;
+  const void* k_cache;
+  const void* v_cache;
+  int32_t cache_dtype;
+  int32_t num_blocks, block_size, num_kv_heads;
+  const int32_t* block_tables;
+  int32_t max_blocks_per_seq;
+  const int32_t* seq_lens;
+  float scale, k_scale, v_scale;
+  hipStream_t stream;
+};
+
+hipError_t cache_write(const CacheWriteArgs& a);
+hipError_t copy_blocks(const CopyBlocksArgs& a);
+
+// Decode launchers, one per (query, cache) dtype pair; each dispatches on
+// head_size, block_size and group size.  Return hipErrorInvalidValue for a
+// shape that was not instantiated.
+hipError_t decode_f32(const DecodeArgs& a);
+hipError_t decode_bf16(const DecodeArgs& a);
+hipError_t decode_fp8(const DecodeArgs& a);
+bool decode_supported(int32_t q_dtype, int32_t cache_dtype, int head_size, int block_size,
+                      int group);
+
+hipError_t prefill(const PrefillArgs& a);
+bool prefill_supported(int32_t q_dtype, int32_t cache_dtype, int head_size, int block_size,
+                       int group);
+
+}  // namespace pa
