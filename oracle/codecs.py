@@ -20,7 +20,7 @@ import numpy as np
 def bf16_to_f64(bits) -> np.ndarray:
     """Decode bfloat16 bit patterns (uint16) to float64, field by field."""
     u = np.asarray(bits, dtype=np.uint16).astype(np.int64)
-    sign = np.where(u >> 15, -1.0, 1.0)
+    sign = np.where(u >> 15, -1.0, 1.0)  # applied with copysign: NaNs keep their sign
     e = (u >> 7) & 0xFF
     m = (u & 0x7F).astype(np.float64)
     with np.errstate(over="ignore", invalid="ignore"):
@@ -28,7 +28,7 @@ def bf16_to_f64(bits) -> np.ndarray:
         sub = np.ldexp(m / 128.0, -126)
         val = np.where(e == 0, sub, normal)
         val = np.where(e == 255, np.where(m == 0, np.inf, np.nan), val)
-    return sign * val
+    return np.copysign(val, sign)
 
 
 def f32_to_f64(bits) -> np.ndarray:
@@ -39,14 +39,14 @@ def f32_to_f64(bits) -> np.ndarray:
 def e4m3fn_to_f64(bits) -> np.ndarray:
     """Decode OCP E4M3FN bytes (uint8) to float64, field by field."""
     u = np.asarray(bits, dtype=np.uint8).astype(np.int64)
-    sign = np.where(u >> 7, -1.0, 1.0)
+    sign = np.where(u >> 7, -1.0, 1.0)  # applied with copysign: NaNs keep their sign
     e = (u >> 3) & 0xF
     m = (u & 0x7).astype(np.float64)
     normal = np.ldexp(1.0 + m / 8.0, (e - 7).astype(np.int64))
     sub = np.ldexp(m / 8.0, -6)
     val = np.where(e == 0, sub, normal)
     val = np.where((e == 15) & (m == 7), np.nan, val)
-    return sign * val
+    return np.copysign(val, sign)
 
 
 # All non-negative finite E4M3FN magnitudes, indexed by their code 0x00..0x7E.

@@ -54,7 +54,9 @@ def oracle_pool(b: wl.PagedBatch, sel=slice(None)):
     return kp, vp
 
 
-def raw_equal(gpu_t, oracle_raw) -> bool:
+def raw_equal(gpu_t, oracle_raw, report=True) -> bool:
+    """Bitwise equality of a GPU pool with the oracle's raw pool; on a
+    mismatch, print the first differing words."""
     g = gpu_t.contiguous().cpu()
     if g.dtype == torch.bfloat16:
         g = g.view(torch.int16).numpy().view(np.uint16)
@@ -62,7 +64,15 @@ def raw_equal(gpu_t, oracle_raw) -> bool:
         g = g.view(torch.int32).numpy().view(np.uint32)
     else:
         g = g.numpy()
-    return g.shape == oracle_raw.shape and np.array_equal(g, oracle_raw)
+    if g.shape != oracle_raw.shape:
+        say(f"shape {g.shape} != {oracle_raw.shape}")
+        return False
+    diff = np.argwhere(g != oracle_raw)
+    if len(diff) and report:
+        say(f"{len(diff)} words differ; first: " + ", ".join(
+            f"{tuple(i)}: gpu {int(g[tuple(i)]):#x} oracle {int(oracle_raw[tuple(i)]):#x}"
+            for i in diff[:10]))
+    return len(diff) == 0
 
 
 def query_tensor(b: wl.PagedBatch, q=None):

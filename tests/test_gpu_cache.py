@@ -71,7 +71,16 @@ def test_cache_write_fp8_quantise_edges_and_padding(src):
     kp, vp = G.gpu_pool(b)
     G.gpu_fill(b, kp, vp)
     okp, ovp = G.oracle_pool(b)
-    assert G.raw_equal(kp, okp) and G.raw_equal(vp, ovp)
+    ok_k, ok_v = G.raw_equal(kp, okp), G.raw_equal(vp, ovp)
+    if not (ok_k and ok_v):
+        src_vals = wl.storage_tensor(vals, src).float().numpy()
+        for pool, ref, sv in ((kp, okp, src_vals), (vp, ovp, src_vals[::-1])):
+            g = pool.cpu().numpy()
+            for blk, h, off, d in np.argwhere(g != ref)[:10]:
+                t = int(np.nonzero(slots == blk * bs + off)[0][0])
+                G.say(f"token {t} head {h} dim {d}: src {sv[t, h, d]!r} gpu {g[blk, h, off, d]:#x} "
+                      f"oracle {ref[blk, h, off, d]:#x}")
+    assert ok_k and ok_v
 
 
 def test_cache_write_zero_tokens_is_noop():

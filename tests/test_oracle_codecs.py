@@ -14,6 +14,7 @@ def test_bf16_decode_all_codes_match_torch():
     nan = np.isnan(ref)
     assert np.array_equal(np.isnan(ours), nan)
     assert np.array_equal(ours[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(ours), bits >= 0x8000)   # NaNs included
     # Signed zeros and infinities sit where the definition puts them.
     assert ours[0x0000] == 0.0 and np.signbit(ours[0x8000])
     assert ours[0x7F80] == np.inf and ours[0xFF80] == -np.inf
@@ -35,6 +36,7 @@ def test_e4m3fn_decode_all_codes_match_torch():
     # Definition landmarks: only S.1111.111 is NaN, 448 is the largest
     # magnitude, 2^-9 the smallest subnormal, 2^-6 the smallest normal.
     assert set(np.nonzero(nan)[0].tolist()) == {0x7F, 0xFF}
+    assert np.array_equal(np.signbit(ours), bits >= 0x80)     # NaNs included
     assert ours[0x7E] == 448.0 and ours[0xFE] == -448.0
     assert ours[0x01] == 2.0 ** -9 and ours[0x08] == 2.0 ** -6
     assert np.all(np.diff(ours[:0x7F]) > 0)  # monotone over the positive codes
@@ -99,3 +101,11 @@ def test_decode_dispatch_applies_fp8_scale_only():
     assert codecs.decode(np.array([0x3F80], np.uint16), "bf16", 0.5)[0] == 1.0
     with pytest.raises(ValueError):
         codecs.decode(np.array([0], np.uint8), "int8")
+
+
+def test_nan_sign_survives_decode_and_quantise():
+    # A negative NaN stays negative through decode and the fp8 quantiser.
+    for bits, dt in ((np.array([0xFFC0], np.uint16), "bf16"), (np.array([0xFF], np.uint8), "fp8")):
+        x = codecs.decode(bits, dt).astype(np.float32)
+        assert np.isnan(x[0]) and np.signbit(x[0])
+        assert codecs.quantize_e4m3fn(x, 0.5)[0] == 0xFF
