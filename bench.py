@@ -1,0 +1,252 @@
+"""Benchmark of the paged-attention decode step on one MI355X.
+
+One step = the hot path over one batch of the Llama-3-8B-shape decode
+workload (64 sequences, lengths uniform in [512, 4096], 32 query / 8 KV
+heads, head size 128, block 16, bf16): ``pa_cache_write`` of each sequence's
+new token, then ``pa_decode`` (split-K decode kernel + log-sum-exp reduce
+kernel).  Inputs are resident in HBM before timing starts.  Three
+independent copies of the K/V pools are rotated step by step so that each
+step streams its K/V from HBM rather than from the 256 MB last-level cache.
+
+Prints ONE JSON line (rank 0):
+  value       effective decode K/V read rate, GB/s (algorithmic K/V bytes of
+              the step / step time; bytes = sum(seq_lens) x 4096)
+  roofline    the pa_decode call (decode kernel + reduce kernel) timed with
+              HIP events on its stream: algorithmic bytes / average duration
+              against the 8 TB/s HBM3E peak
+  cpu_baseline  the float64 CPU oracle on the same workload (test
+              infrastructure, timed on the host cores)
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "decode KV GB/s (% HBM peak) + tokens/s, Llama-3-8B shape bs=64, 1 GPU"
+DEFAULT_WORKLOAD = "llama3_8b_decode_bf16"
+N_SETS = 3
+
+
+def kernel_source_digest() -> str:
+    """Digest of the decode kernel sources, to tie stored counter data to code."""
+    h = hashlib.sha256()
+    for f in ("decode_impl.h", "pa_device.h"):
+        with open(os.path.join(ROOT, "paged_kv_cache_11_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(workload: str, launches_per_step: float):
+    """HBM bytes per decode launch from committed rocprofv3 counter runs,
+    or None if they were taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"decode_kernel_{workload}_counters.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("source_digest") != kernel_source_digest():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(b, budget_s: float = 12.0):
+    """Time the float64 CPU oracle (test infrastructure) on this workload:
+    build its pool with its cache write, then run its decode over the
+    sequences, repeating whole passes until the time budget is spent."""
+    from oracle import paged as opg
+    from paged_kv_cache_11_amd import workloads as wl
+
+    try:
+        import threadpoolctl
+
+        blas_threads = max((i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()),
+                           default=1)
+    except Exception:  # pragma: no cover
+        blas_threads = 1
+    kp = wl.poisoned_pool(b.num_blocks, b.num_kv_heads, b.block_size, b.head_size, b.kv_dtype)
+    vp = wl.poisoned_pool(b.num_blocks, b.num_kv_heads, b.block_size, b.head_size, b.kv_dtype)
+    ks = wl.storage_bits(wl.storage_tensor(b.k, b.kv_src_dtype))
+    vs = wl.storage_bits(wl.storage_tensor(b.v, b.kv_src_dtype))
+    opg.cache_write(kp, vp, b.kv_dtype, ks, vs, b.kv_src_dtype, b.slot_mapping, b.k_scale,
+                    b.v_scale)
+    q64 = wl.storage_tensor(b.q, b.q_dtype).float().numpy().astype(np.float64)
+    seqs_done, tokens_read, t0 = 0, 0, time.perf_counter()
+    while seqs_done < b.num_seqs or time.perf_counter() - t0 < budget_s:
+        s = seqs_done % b.num_seqs
+        opg.paged_decode(q64, kp, vp, b.block_tables, b.seq_lens, b.scale, kv_dtype=b.kv_dtype,
+                         k_scale=b.k_scale, v_scale=b.v_scale, seqs=[s])
+        seqs_done += 1
+        tokens_read += int(b.seq_lens[s])
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {
+        "value": seqs_done / dt, "unit": "tokens/s", "cores": int(blas_threads), "kind": "oracle",
+        "gbs": tokens_read * b.kv_bytes_per_token() / dt / 1e9,
+        "sample": f"{seqs_done} sequence decodes of the same workload ({tokens_read} cached tokens "
+                  f"read) in {dt:.1f} s; host has {os.cpu_count()} logical cpus",
+    }
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--partition-size", type=int, default=-1,
+                    help="pa_decode partition_size: -1 balanced split (default), 0 none, or tokens")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also run pa_copy_blocks over this many MiB (counter calibration)")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the decode path "
+              "shards by sequence or KV head with no exchange, so it is not run on several "
+              "GPUs here.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from paged_kv_cache_11_amd import binding as pa
+    from paged_kv_cache_11_amd import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    pa.load()
+    dev = torch.device("cuda:0")
+    b = wl.make(args.workload)
+    print(f"[bench] workload {b.name}: {b.num_seqs} seqs, lens {int(b.seq_lens.min())}.."
+          f"{int(b.seq_lens.max())}, pool {b.num_blocks} blocks, {b.kv_dtype}", file=sys.stderr,
+          flush=True)
+
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}[b.kv_dtype]
+    shape = (b.num_blocks, b.num_kv_heads, b.block_size, b.head_size)
+    k0 = torch.zeros(shape, dtype=tdt, device=dev)
+    v0 = torch.zeros(shape, dtype=tdt, device=dev)
+    chunk = 1 << 16
+    for a in range(0, len(b.slot_mapping), chunk):
+        pa.pa_cache_write(wl.storage_tensor(b.k[a:a + chunk], b.kv_src_dtype).to(dev),
+                          wl.storage_tensor(b.v[a:a + chunk], b.kv_src_dtype).to(dev), k0, v0,
+                          torch.from_numpy(b.slot_mapping[a:a + chunk]).to(dev), b.k_scale,
+                          b.v_scale)
+    sets = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(N_SETS - 1)]
+    q = wl.storage_tensor(b.q, b.q_dtype).to(dev)
+    out = torch.empty_like(q)
+    tables = torch.from_numpy(b.block_tables).to(dev)
+    lens = torch.from_numpy(b.seq_lens).to(dev)
+    # The step's new tokens: the last token of every sequence.
+    ends = np.cumsum(b.seq_lens.astype(np.int64))
+    new_idx = ends - 1
+    k_new = wl.storage_tensor(b.k[new_idx], b.kv_src_dtype).to(dev)
+    v_new = wl.storage_tensor(b.v[new_idx], b.kv_src_dtype).to(dev)
+    slots_new = torch.from_numpy(b.slot_mapping[new_idx]).to(dev)
+    ps = args.partition_size
+    ws_bytes = pa.pa_decode_workspace_size(b.num_seqs, b.num_heads, b.num_kv_heads, b.head_size,
+                                           b.max_seq_len, ps)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        kc, vc = sets[i % N_SETS]
+        pa.pa_cache_write(k_new, v_new, kc, vc, slots_new, b.k_scale, b.v_scale, stream=stream)
+        if ev is not None:
+            ev[0].record(stream)
+        pa.pa_decode(out, q, kc, vc, tables, lens, b.max_seq_len, b.scale, b.k_scale, b.v_scale,
+                     ps, ws, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall / args.steps * 1e3
+
+    # Per-call decode durations with HIP events on the launch stream.
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    dec_ms = np.array([a.elapsed_time(c) for a, c in evs])
+    dec_avg_s = float(dec_ms.mean()) / 1e3
+
+    kv_bytes = b.decode_kv_bytes()
+    gbs = kv_bytes / (ms_per_step / 1e3) / 1e9
+    achieved = kv_bytes / dec_avg_s / 1e9
+    print(f"[bench] step {ms_per_step * 1e3:.1f} us, decode call {dec_avg_s * 1e6:.1f} us "
+          f"(p10 {np.percentile(dec_ms, 10) * 1e3:.1f}, p90 {np.percentile(dec_ms, 90) * 1e3:.1f}), "
+          f"{achieved:.0f} GB/s in decode", file=sys.stderr, flush=True)
+
+    calib = None
+    if args.copy_calibration_mib:
+        nbk = args.copy_calibration_mib * (1 << 20) // (2 * k0[0].numel() * k0.element_size())
+        nbk = min(nbk, b.num_blocks // 2)
+        pairs = torch.stack([torch.arange(nbk), torch.arange(nbk) + b.num_blocks // 2], 1)
+        pairs = pairs.to(torch.int64).to(dev).contiguous()
+        pa.pa_copy_blocks(k0, v0, pairs)
+        torch.cuda.synchronize()
+        calib = {"copy_bytes_read": int(2 * nbk * k0[0].numel() * k0.element_size())}
+
+    traffic = stored_traffic(b.name, 1)
+    cpu = cpu_baseline(b, args.cpu_budget)
+    tokens_per_s = b.num_seqs / (ms_per_step / 1e3)
+    res = {
+        "metric": METRIC,
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": b.kv_dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": b.name, "num_seqs": b.num_seqs, "num_heads": b.num_heads,
+            "num_kv_heads": b.num_kv_heads, "head_size": b.head_size,
+            "block_size": b.block_size, "seq_lens": f"uniform [{int(b.seq_lens.min())}, "
+            f"{int(b.seq_lens.max())}] (seeded)", "sum_seq_lens": int(b.seq_lens.sum()),
+            "pool_blocks": b.num_blocks, "partition_size": ps,
+            "kv_bytes_per_step": kv_bytes, "input_sets_rotated": N_SETS,
+            "step": "pa_cache_write(new token per sequence) + pa_decode (split-K + LSE reduce)",
+        },
+        "tokens_per_s": round(tokens_per_s, 1),
+        "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "roofline": {
+            "kernel": "pa_decode (decode_kernel + lse_reduce_kernel)",
+            "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic, "avg_us": round(dec_avg_s * 1e6, 2),
+        },
+        "cpu_baseline": cpu,
+    }
+    if calib:
+        res["copy_calibration"] = calib
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -147,12 +147,17 @@ int32_t pa_copy_blocks(void* k_cache, void* v_cache, int32_t cache_dtype,
                        int32_t head_size,
                        const int64_t* block_mapping, int32_t num_pairs, void* stream);
 
+/* partition_size value selecting the balanced split of pa_decode. */
+#define PA_PARTITION_BALANCED (-1)
+
 /*
- * Workspace bytes pa_decode needs for split-K partials; 0 when
- * partition_size == 0 or one partition covers max_seq_len.
+ * Workspace bytes pa_decode needs for split-K partials: 0 when
+ * partition_size == 0 or one partition covers max_seq_len; for
+ * PA_PARTITION_BALANCED two partial states per wavefront of the largest
+ * balanced grid plus a two-word cut record per (sequence, KV head).
  */
-size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t head_size,
-                                int32_t max_seq_len, int32_t partition_size);
+size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                int32_t head_size, int32_t max_seq_len, int32_t partition_size);
 
 /*
  * pa_decode — one query token per sequence against its paged context.
@@ -174,6 +179,13 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t hea
  * and a second kernel merges them with log-sum-exp weights.  Sequences with
  * a single partition are finished by the first kernel.  partition_size == 0
  * processes each sequence in one partition and needs no workspace.
+ * partition_size == PA_PARTITION_BALANCED cuts, per KV head, the blocks of
+ * all sequences into equal contiguous runs, one per wavefront of a grid
+ * sized to the device (so every wavefront streams the same number of
+ * blocks whatever the length mix).  A wavefront finishes every sequence it
+ * holds whole; a sequence cut between wavefronts leaves one partial state
+ * per piece in `workspace`, and a second kernel merges them with the same
+ * log-sum-exp weights.  The workspace needs no initialisation.
  *
  *   out            [num_seqs][num_heads][head_size] of q_dtype
  *   query          [num_seqs][num_heads][head_size] of q_dtype

@@ -22,6 +22,7 @@ import os
 from typing import Optional
 
 PA_F32, PA_BF16, PA_FP8_E4M3 = 0, 1, 2
+PA_PARTITION_BALANCED = -1
 PA_OK, PA_ERR_INVALID, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = 0, -1, -2, -3, -4
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
@@ -37,7 +38,7 @@ _SIGNATURES = {
                         _c_int, _c_p, _c_f, _c_f, _c_p], _c_int),
     "pa_copy_blocks": ([_c_p, _c_p, _c_int, _c_int, _c_int, _c_int, _c_int, _c_p, _c_int, _c_p],
                        _c_int),
-    "pa_decode_workspace_size": ([_c_int, _c_int, _c_int, _c_int, _c_int], _c_sz),
+    "pa_decode_workspace_size": ([_c_int, _c_int, _c_int, _c_int, _c_int, _c_int], _c_sz),
     "pa_decode": ([_c_p, _c_p, _c_int, _c_int, _c_int, _c_int, _c_p, _c_p, _c_int, _c_int, _c_int,
                    _c_int, _c_p, _c_int, _c_p, _c_int, _c_f, _c_f, _c_f, _c_int, _c_p, _c_sz,
                    _c_p], _c_int),
@@ -147,9 +148,10 @@ def pa_copy_blocks(k_cache, v_cache, block_mapping, stream=None) -> None:
                                  _ptr(block_mapping) if n else None, n, _stream(stream)))
 
 
-def pa_decode_workspace_size(num_seqs, num_heads, head_size, max_seq_len, partition_size) -> int:
-    return int(load().pa_decode_workspace_size(num_seqs, num_heads, head_size, max_seq_len,
-                                               partition_size))
+def pa_decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_size, max_seq_len,
+                             partition_size) -> int:
+    return int(load().pa_decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_size,
+                                               max_seq_len, partition_size))
 
 
 def pa_decode(out, query, k_cache, v_cache, block_tables, seq_lens, max_seq_len: int,
@@ -157,13 +159,16 @@ def pa_decode(out, query, k_cache, v_cache, block_tables, seq_lens, max_seq_len:
               partition_size: int = 0, workspace=None, stream=None) -> None:
     """Decode attention of query [num_seqs, num_heads, head_size] into out.
 
+    partition_size: 0 (no split), a multiple of the block size (fixed
+    partitions), or PA_PARTITION_BALANCED (equal block runs per wavefront).
+
     With ``workspace=None`` and a split that needs one, a workspace tensor
     is taken from torch's allocator."""
     import torch
 
     nb, hkv, bs, d = _pool_dims(k_cache, v_cache)
     S, H = int(query.shape[0]), int(query.shape[1])
-    need = pa_decode_workspace_size(S, H, d, max_seq_len, partition_size)
+    need = pa_decode_workspace_size(S, H, hkv, d, max_seq_len, partition_size)
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=query.device)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0

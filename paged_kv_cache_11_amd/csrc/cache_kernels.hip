@@ -31,28 +31,33 @@ __global__ __launch_bounds__(256) void cache_write_kernel(
   const int h = (int)(row % num_kv_heads);
   const int64_t t = row / num_kv_heads;
   const int64_t slot = slot_mapping[t];
+  const int64_t src_elem = row * (int64_t)head_size + (int64_t)c * EPC;
+  // The source chunks do not depend on the slot: load them before testing
+  // it, so the two loads overlap.
+  constexpr int NSRC = EPC * SB / 16;  // 16-byte source vectors per chunk
+  u32x4 ks[NSRC], vs[NSRC];
+#pragma unroll
+  for (int j = 0; j < NSRC; ++j) {
+    ks[j] = ((const u32x4*)(key + src_elem * SB))[j];
+    vs[j] = ((const u32x4*)(value + src_elem * SB))[j];
+  }
   if (slot < 0) return;
   const int64_t blk = slot / block_size;
   const int off = (int)(slot % block_size);
   const int64_t dst_elem =
       ((blk * num_kv_heads + h) * block_size + off) * (int64_t)head_size + (int64_t)c * EPC;
-  const int64_t src_elem = row * (int64_t)head_size + (int64_t)c * EPC;
 #pragma unroll
   for (int kv = 0; kv < 2; ++kv) {
-    const uint8_t* src = (kv ? value : key) + src_elem * SB;
+    const u32x4* src = kv ? vs : ks;
     uint8_t* dst = (kv ? v_cache : k_cache) + dst_elem * DB;
     if constexpr (std::is_same<SRC, DST>::value) {
-      *(u32x4*)dst = *(const u32x4*)src;
+      *(u32x4*)dst = src[0];
     } else {
       static_assert(std::is_same<DST, FP8>::value, "only fp8 caches quantise");
       const float sc = kv ? v_scale : k_scale;
       float x[EPC];
-      constexpr int NSRC = EPC * SB / 16;  // 16-byte source vectors per chunk
 #pragma unroll
-      for (int j = 0; j < NSRC; ++j) {
-        const u32x4 w = ((const u32x4*)src)[j];
-        Vec<SRC>::to_f32(w, x + j * Vec<SRC>::n);
-      }
+      for (int j = 0; j < NSRC; ++j) Vec<SRC>::to_f32(src[j], x + j * Vec<SRC>::n);
       uint32_t out[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {

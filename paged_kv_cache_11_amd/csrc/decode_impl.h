@@ -3,47 +3,123 @@
 // What it computes ("vLLM：大语言模型推理与服务库" §4.4 item 3): for every
 // sequence s and query head h, walk the physical blocks of s through its
 // block table, score q·k for every cached token, take the softmax and weight
-// V.  Grid axes follow the partitioned grid the openeuler.csdn.net essay
-// describes ("PagedAttention：把操作系统的分页搬上 GPU": one workgroup per
-// head group, sequence and partition of the context), re-cut for gfx950:
+// V.  The grid has the partition axis the openeuler.csdn.net essay describes
+// ("PagedAttention：把操作系统的分页搬上 GPU": one workgroup per head group,
+// sequence and partition of the context), re-cut for gfx950:
 //
-//   * one workgroup = one (partition, KV head, sequence); its 4 wavefronts
-//     take the partition's blocks round-robin, so all G = Hq/Hkv query heads
-//     of the group share every K/V byte read from HBM;
-//   * a (block, KV head) tile is contiguous in the pool, so a wavefront reads
-//     it with NLOAD fully coalesced 1 KiB loads (16 bytes per lane) straight
-//     into VGPRs; one token row occupies LPR = 4/8/16 lanes, i.e. sits inside
-//     a DPP row, and q·k reduces with 2-4 DPP adds;
-//   * the next block's loads are issued before the current block is
-//     computed (register double buffering);
-//   * softmax is online in fp32 in the log2 domain (exp2 on v_exp_f32); each
-//     DPP row of a wavefront keeps its own running max / sum over the tokens
-//     it saw, so the per-block update needs no cross-row traffic; rows, then
-//     wavefronts (through LDS), are merged once per partition;
-//   * with several partitions per sequence each workgroup writes its
-//     (max, sum, normalised output) and a second kernel merges them.
+//   * one workgroup = one (partition, KV head, sequence) with 1, 2 or 4
+//     wavefronts that take the partition's blocks round-robin; all
+//     G = Hq/Hkv query heads of the group share every K/V byte read;
+//   * a (block, KV head) tile is contiguous in the pool, so a wavefront
+//     reads it with NLOAD fully coalesced 1 KiB loads (16 bytes per lane)
+//     straight into VGPRs, one tile ahead of the one being computed
+//     (ping-pong register buffers);
+//   * one token row occupies LPR = 4, 8 or 16 lanes, i.e. sits inside a DPP
+//     row.  With 16-lane rows the G x NLOAD partial dot products of a lane
+//     are reduce-scattered over the row in 4 DPP steps, so every lane ends
+//     with whole scores (one per lane for G = 4) and the softmax runs once
+//     per score; probabilities return to the row with row_newbcast.  With
+//     shorter rows the partials are all-reduced instead;
+//   * the softmax is online, in fp32, in the log2 domain (v_exp_f32); each
+//     token row keeps its own reference maximum per head and rescales its
+//     accumulators only when a score exceeds that reference by more than
+//     2^8 — exact, because the sum and the accumulators share the reference;
+//   * P·V for a bf16 cache pairs two tokens per v_dot2_f32_bf16 (P rounded
+//     to bf16, accumulation in fp32); f32 and fp8 caches use fp32 FMAs;
+//   * rows, then wavefronts (through LDS), are merged once per partition;
+//     with several partitions a second kernel merges their
+//     (max, sum, normalised output) triples with log-sum-exp weights.
 #pragma once
+
+#include <utility>
+
+
 
 #include "pa_internal.h"
 
 namespace pa {
 
-constexpr int kDecodeWaves = 4;
+constexpr int kMaxDecodeWaves = 4;
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kRescaleSlack = 8.0f;  // log2 units a score may exceed the reference by
 
-template <typename KV, int D, int BS>
-struct TileShape {
+template <typename KV, int D, int BS, int G>
+struct Geom {
   static constexpr int EB = Elem<KV>::bytes;
   static constexpr int EPL = 16 / EB;        // elements per lane per load
   static constexpr int LPR = D / EPL;        // lanes per token row
   static constexpr int RPL = kWave / LPR;    // token rows per wavefront load
   static constexpr int NLOAD = BS / RPL;     // loads per (block, head) tile
+  static constexpr int N = NLOAD * G;        // partial scores per lane (index i*G + h)
+  static constexpr bool kScatter = LPR == 16 && N % 16 == 0;
+  static constexpr int NV = kScatter ? N / 16 : N;  // whole scores per lane
   static constexpr int64_t TILE_VECS = (int64_t)BS * D * EB / 16;
   static_assert(LPR == 4 || LPR == 8 || LPR == 16, "a token row must fit a DPP row");
   static_assert(NLOAD >= 1 && BS % RPL == 0, "a tile must be whole wavefront loads");
 };
 
+template <int... Is, typename F>
+__device__ __forceinline__ void static_for_impl(std::integer_sequence<int, Is...>, F&& f) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(std::make_integer_sequence<int, N>{}, f);
+}
+
+constexpr int rev4(int x) { return ((x & 1) << 3) | ((x & 2) << 1) | ((x & 4) >> 1) | ((x & 8) >> 3); }
+constexpr int kRowNewBcast = 0x150;  // row_newbcast:k, k = 0..15
+
+template <int K>
+__device__ __forceinline__ float bcast16(float x) {
+  return u2f((uint32_t)__builtin_amdgcn_mov_dpp((int)f2u(x), kRowNewBcast + K, 0xF, 0xF, false));
+}
+
+template <int N>
+__device__ __forceinline__ float group_max(float x) {
+  if constexpr (N >= 2) x = fmaxf(x, dpp<kQuadXor1>(x));
+  if constexpr (N >= 4) x = fmaxf(x, dpp<kQuadXor2>(x));
+  if constexpr (N >= 8) x = fmaxf(x, dpp<kRowHalfMirror>(x));
+  if constexpr (N >= 16) x = fmaxf(x, dpp<kRowMirror>(x));
+  return x;
+}
+template <int N>
+__device__ __forceinline__ float group_add(float x) {
+  if constexpr (N == 1) return x;
+  else if constexpr (N == 2) return x + dpp<kQuadXor1>(x);
+  else return group_sum<N>(x);
+}
+
+// One reduce-scatter step: the lane keeps the half of each pair picked by
+// its bit and adds the partner's copy of that half (the partner sends the
+// other half it does not keep).
+template <int CTRL>
+__device__ __forceinline__ float rs_pair(float x0, float x1, bool bit) {
+  const float keep = bit ? x1 : x0;
+  const float send = bit ? x0 : x1;
+  return keep + dpp<CTRL>(send);
+}
+
+// Reduce-scatter N partial sums over a 16-lane DPP row: afterwards lane l
+// holds r[j] = full sum of v[16 j + rev4(l & 15)].
+template <int N>
+__device__ __forceinline__ void reduce_scatter16(const float (&v)[N], float (&r)[N / 16], int lane) {
+  const bool b3 = lane & 8, b2 = lane & 4, b1 = lane & 2, b0 = lane & 1;
+  float a[N / 2], b[N / 4], c[N / 8];
+#pragma unroll
+  for (int j = 0; j < N / 2; ++j) a[j] = rs_pair<kRowMirror>(v[2 * j], v[2 * j + 1], b3);
+#pragma unroll
+  for (int j = 0; j < N / 4; ++j) b[j] = rs_pair<kRowHalfMirror>(a[2 * j], a[2 * j + 1], b2);
+#pragma unroll
+  for (int j = 0; j < N / 8; ++j) c[j] = rs_pair<kQuadXor2>(b[2 * j], b[2 * j + 1], b1);
+#pragma unroll
+  for (int j = 0; j < N / 16; ++j) r[j] = rs_pair<kQuadXor1>(c[2 * j], c[2 * j + 1], b0);
+}
+
 __device__ __forceinline__ bf16x2 as_bf16x2(uint32_t u) { return __builtin_bit_cast(bf16x2, u); }
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
+}
 
 // Query registers of one lane: its EPL dims of each of the G heads.
 // bf16 cache: kept packed for v_dot2_f32_bf16; otherwise widened to fp32.
@@ -98,21 +174,285 @@ __device__ __forceinline__ void store_out(void* out, int64_t idx, float v) {
   else ((uint16_t*)out)[idx] = f32_to_bf16_rne(v);
 }
 
+// Per-wavefront attention state of one (sequence, KV head) over a run of
+// blocks: the lane geometry, the query registers, the online-softmax state
+// and the per-block update.
 template <typename KV, typename QT, int D, int BS, int G>
-__global__ __launch_bounds__(kDecodeWaves * kWave) void decode_kernel(
+struct WaveAttn {
+  using GM = Geom<KV, D, BS, G>;
+  static constexpr int EPL = GM::EPL, LPR = GM::LPR, RPL = GM::RPL, NLOAD = GM::NLOAD;
+  static constexpr int N = GM::N, NV = GM::NV;
+  static constexpr bool kScatter = GM::kScatter;
+
+  int lane, col, row;
+  float qk_scale_log2;
+  QRegs<KV, QT, G, EPL> q;
+  // m_ref[h]: the row's reference maximum for head h (uniform over the
+  // row).  Scatter layout: every score of a lane belongs to head
+  // rev4(lane) % G; lane_ref is that head's reference and l_lane the lane's
+  // share of its probability sum.  All-reduce layout: l_row[h], row-uniform.
+  float m_ref[G], acc[G][EPL];
+  float lane_ref, l_lane;
+  float l_row[kScatter ? 1 : G];
+
+  __device__ __forceinline__ void init(int lane_, float qk) {
+    lane = lane_;
+    col = lane % LPR;
+    row = lane / LPR;
+    qk_scale_log2 = qk;
+  }
+
+  __device__ __forceinline__ void reset() {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      m_ref[h] = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
+    }
+    lane_ref = -INFINITY;
+    l_lane = 0.f;
+#pragma unroll
+    for (int h = 0; h < (kScatter ? 1 : G); ++h) l_row[h] = 0.f;
+  }
+
+  // P·V for one tile: pb[i*G + h] is the probability of token row i, head h.
+  __device__ __forceinline__ void accumulate_pv(const float (&pb)[N], const u32x4 (&vt)[NLOAD]) {
+    if constexpr (std::is_same<KV, BF16>::value) {
+#pragma unroll
+      for (int k = 0; k < NLOAD / 2; ++k) {
+        const u32x4 va = vt[2 * k], vb = vt[2 * k + 1];
+        const uint32_t wa[4] = {va.x, va.y, va.z, va.w}, wb[4] = {vb.x, vb.y, vb.z, vb.w};
+        uint32_t vp[8];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          vp[2 * d] = __builtin_amdgcn_perm(wb[d], wa[d], 0x05040100u);      // low halves
+          vp[2 * d + 1] = __builtin_amdgcn_perm(wb[d], wa[d], 0x07060302u);  // high halves
+        }
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const bf16x2 pp = as_bf16x2(pack_bf16(pb[(2 * k) * G + h], pb[(2 * k + 1) * G + h]));
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            acc[h][e] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(vp[e]), pp, acc[h][e], false);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NLOAD; ++i) {
+        float vf[EPL];
+        Vec<KV>::to_f32(vt[i], vf);
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) acc[h][e] = __builtin_fmaf(pb[i * G + h], vf[e], acc[h][e]);
+      }
+    }
+  }
+
+  // One (block, KV head) tile: scores, online softmax, P·V.  kMasked: the
+  // sequence's last block, whose slots at or past L are padding.
+  template <bool kMasked>
+  __device__ __forceinline__ void block(const u32x4 (&kt)[NLOAD], u32x4 (&vt)[NLOAD], int blk,
+                                        int L) {
+    float v[N];
+#pragma unroll
+    for (int i = 0; i < NLOAD; ++i) {
+      float kf[std::is_same<KV, BF16>::value ? 1 : EPL];
+      if constexpr (!std::is_same<KV, BF16>::value) Vec<KV>::to_f32(kt[i], kf);
+#pragma unroll
+      for (int h = 0; h < G; ++h) v[i * G + h] = q.dot(h, kt[i], kf);
+    }
+    float pb[N];
+    if constexpr (kScatter) {
+      float r[NV];
+      reduce_scatter16<N>(v, r, lane);
+      const int c = rev4(lane & 15);
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+        r[j] *= qk_scale_log2;
+        if constexpr (kMasked) {
+          const int i = (16 * j + c) / G;
+          if (blk * BS + row + i * RPL >= L) r[j] = -INFINITY;
+        }
+      }
+      bool ex = false;
+#pragma unroll
+      for (int j = 0; j < NV; ++j) ex |= r[j] > lane_ref + kRescaleSlack;
+      if (__builtin_amdgcn_ballot_w64(ex)) {
+        // Raise the row's references: per-head row maxima, broadcast.
+        float lm = r[0];
+#pragma unroll
+        for (int j = 1; j < NV; ++j) lm = fmaxf(lm, r[j]);
+        lm = group_max<16 / G>(lm);
+        const float own_new = fmaxf(lane_ref, lm);
+        l_lane *= own_new == -INFINITY ? 1.f : fast_exp2(lane_ref - own_new);
+        lane_ref = own_new;
+        static_for<G>([&](auto hc) {
+          constexpr int h = decltype(hc)::value;
+          const float mn = fmaxf(m_ref[h], bcast16<rev4(h)>(lm));
+          const float alpha = mn == -INFINITY ? 1.f : fast_exp2(m_ref[h] - mn);
+          m_ref[h] = mn;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) acc[h][e] *= alpha;
+        });
+      }
+      float p[NV];
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+        p[j] = fast_exp2(r[j] - lane_ref);
+        if constexpr (kMasked) p[j] = r[j] == -INFINITY ? 0.f : p[j];
+        l_lane += p[j];
+      }
+      static_for<N>([&](auto nc) {
+        constexpr int n = decltype(nc)::value;
+        pb[n] = bcast16<rev4(n % 16)>(p[n / 16]);
+      });
+    } else {
+#pragma unroll
+      for (int n = 0; n < N; ++n) {
+        v[n] = group_sum<LPR>(v[n]) * qk_scale_log2;
+        if constexpr (kMasked) {
+          if (blk * BS + row + (n / G) * RPL >= L) v[n] = -INFINITY;
+        }
+      }
+      bool ex = false;
+#pragma unroll
+      for (int n = 0; n < N; ++n) ex |= v[n] > m_ref[n % G] + kRescaleSlack;
+      if (__builtin_amdgcn_ballot_w64(ex)) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          float rm = v[h];
+#pragma unroll
+          for (int i = 1; i < NLOAD; ++i) rm = fmaxf(rm, v[i * G + h]);
+          const float mn = fmaxf(m_ref[h], rm);
+          const float alpha = mn == -INFINITY ? 1.f : fast_exp2(m_ref[h] - mn);
+          m_ref[h] = mn;
+          l_row[h] *= alpha;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) acc[h][e] *= alpha;
+        }
+      }
+#pragma unroll
+      for (int n = 0; n < N; ++n) {
+        float p = fast_exp2(v[n] - m_ref[n % G]);
+        if constexpr (kMasked) p = v[n] == -INFINITY ? 0.f : p;
+        pb[n] = p;
+        l_row[n % G] += p;
+      }
+    }
+    if constexpr (kMasked) {  // padding slots of the last block may hold anything
+#pragma unroll
+      for (int i = 0; i < NLOAD; ++i) {
+        const bool valid = blk * BS + row + i * RPL < L;
+        vt[i].x = valid ? vt[i].x : 0u; vt[i].y = valid ? vt[i].y : 0u;
+        vt[i].z = valid ? vt[i].z : 0u; vt[i].w = valid ? vt[i].w : 0u;
+      }
+    }
+    accumulate_pv(pb, vt);
+  }
+
+  // Streams blocks first, first+stride, ... (count of them) of a sequence of
+  // L tokens for KV head g through the pipeline: each tile's loads are
+  // issued one tile ahead of its computation (ping-pong registers).  The
+  // sequence's last block, if partly filled and in the run, comes last.
+  __device__ __forceinline__ void stream(const void* k_cache, const void* v_cache,
+                                         const int32_t* tbl, int g, int num_kv_heads, int first,
+                                         int count, int stride, int L) {
+    if (count <= 0) return;
+    const int nblk = (L + BS - 1) / BS;
+    const bool last_partial = (L % BS) != 0 && first + stride * (count - 1) == nblk - 1;
+    const int nfull = count - (last_partial ? 1 : 0);
+    const int64_t block_vecs = (int64_t)num_kv_heads * GM::TILE_VECS;
+    const u32x4* kbase = (const u32x4*)k_cache + (int64_t)g * GM::TILE_VECS + lane;
+    const u32x4* vbase = (const u32x4*)v_cache + (int64_t)g * GM::TILE_VECS + lane;
+    // Block ids of the run, 64 at a time, one per lane.
+    int bid_v = 0;
+    auto block_id = [&](int j) -> int {
+      if ((j & (kWave - 1)) == 0) {
+        const int jj = j + lane;
+        bid_v = jj < count ? tbl[first + stride * jj] : 0;
+      }
+      return __builtin_amdgcn_readlane(bid_v, j & (kWave - 1));
+    };
+    auto load_tile = [&](int bid, u32x4 (&kt)[NLOAD], u32x4 (&vt)[NLOAD]) {
+      const u32x4* kp = kbase + (int64_t)bid * block_vecs;
+      const u32x4* vp = vbase + (int64_t)bid * block_vecs;
+#pragma unroll
+      for (int i = 0; i < NLOAD; ++i) kt[i] = kp[i * kWave];
+#pragma unroll
+      for (int i = 0; i < NLOAD; ++i) vt[i] = vp[i * kWave];
+    };
+    auto blk_of = [&](int j) { return first + stride * j; };
+    if (nfull > 0) {
+      u32x4 ka[NLOAD], va[NLOAD], kb[NLOAD], vb[NLOAD];
+      load_tile(block_id(0), ka, va);
+      int j = 0;
+      for (; j + 2 < nfull; j += 2) {
+        load_tile(block_id(j + 1), kb, vb);
+        block<false>(ka, va, blk_of(j), L);
+        load_tile(block_id(j + 2), ka, va);
+        block<false>(kb, vb, blk_of(j + 1), L);
+      }
+      if (nfull - j == 2) {
+        load_tile(block_id(j + 1), kb, vb);
+        block<false>(ka, va, blk_of(j), L);
+        block<false>(kb, vb, blk_of(j + 1), L);
+      } else {
+        block<false>(ka, va, blk_of(j), L);
+      }
+    }
+    if (last_partial) {
+      u32x4 kt[NLOAD], vt[NLOAD];
+      load_tile(block_id(count - 1), kt, vt);
+      block<true>(kt, vt, blk_of(count - 1), L);
+    }
+  }
+
+  // Sums per row and merges the token rows of the wavefront: afterwards
+  // every lane holds, for its col, the wavefront's (m_ref, l_h, acc).
+  __device__ __forceinline__ void merge_rows(float (&l_h)[G]) {
+    if constexpr (kScatter) {
+      const float lg = group_add<16 / G>(l_lane);
+      static_for<G>([&](auto hc) {
+        constexpr int h = decltype(hc)::value;
+        l_h[h] = bcast16<rev4(h)>(lg);
+      });
+    } else {
+#pragma unroll
+      for (int h = 0; h < G; ++h) l_h[h] = l_row[h];
+    }
+#pragma unroll
+    for (int mask = LPR; mask < kWave; mask <<= 1) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float mo = shfl_xor(m_ref[h], mask);
+        const float lo = shfl_xor(l_h[h], mask);
+        const float M = fmaxf(m_ref[h], mo);
+        const float mu = M == -INFINITY ? 0.f : M;
+        const float f = fast_exp2(m_ref[h] - mu), fo = fast_exp2(mo - mu);
+        l_h[h] = l_h[h] * f + lo * fo;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[h][e] = acc[h][e] * f + shfl_xor(acc[h][e], mask) * fo;
+        m_ref[h] = M;
+      }
+    }
+  }
+};
+
+template <typename KV, typename QT, int D, int BS, int G>
+__global__ __launch_bounds__(kMaxDecodeWaves * kWave) void decode_kernel(
     void* __restrict__ out, float* __restrict__ part_o, float* __restrict__ part_ml,
     const void* __restrict__ query, const void* __restrict__ k_cache,
     const void* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
     const int32_t* __restrict__ seq_lens, int max_blocks_per_seq, int num_kv_heads,
     int partition_blocks, int max_parts, float qk_scale_log2, float v_scale) {
-  using TS = TileShape<KV, D, BS>;
-  constexpr int EPL = TS::EPL, LPR = TS::LPR, RPL = TS::RPL, NLOAD = TS::NLOAD;
-  constexpr int NW = kDecodeWaves;
+  using WA = WaveAttn<KV, QT, D, BS, G>;
+  constexpr int EPL = WA::EPL, RPL = WA::RPL;
   using OT = QT;
 
   const int part = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
+  const int NW = blockDim.x / kWave;
   const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
-  const int col = lane % LPR, row = lane / LPR;
   const int num_heads = num_kv_heads * G;
 
   const int L = seq_lens[s];
@@ -123,154 +463,21 @@ __global__ __launch_bounds__(kDecodeWaves * kWave) void decode_kernel(
   const int b0 = part * pb;
   const int b1 = min(b0 + pb, nblk);
 
-  QRegs<KV, QT, G, EPL> q;
-  q.load(query, (int64_t)s * num_heads + (int64_t)g * G, D, col);
-
-  float m[G], l[G], acc[G][EPL];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    m[h] = -INFINITY;
-    l[h] = 0.f;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
-  }
-
-  const int32_t* tbl = block_tables + (int64_t)s * max_blocks_per_seq;
+  WA A;
+  A.init(lane, qk_scale_log2);
+  A.reset();
+  A.q.load(query, (int64_t)s * num_heads + (int64_t)g * G, D, A.col);
   const int span = b1 - b0;
   const int nmine = span > w ? (span - w + NW - 1) / NW : 0;
-  const int64_t block_vecs = (int64_t)num_kv_heads * TS::TILE_VECS;
-  const u32x4* kbase = (const u32x4*)k_cache + (int64_t)g * TS::TILE_VECS + lane;
-  const u32x4* vbase = (const u32x4*)v_cache + (int64_t)g * TS::TILE_VECS + lane;
+  A.stream(k_cache, v_cache, block_tables + (int64_t)s * max_blocks_per_seq, g, num_kv_heads,
+           b0 + w, nmine, NW, L);
+  float l_h[G];
+  A.merge_rows(l_h);
 
-  // Block ids of this wavefront's blocks, 64 at a time, one per lane.
-  int bid_v = 0;
-  auto block_id = [&](int j) -> int {
-    if ((j & (kWave - 1)) == 0) {
-      const int jj = j + lane;
-      bid_v = jj < nmine ? tbl[b0 + w + NW * jj] : 0;
-    }
-    return __builtin_amdgcn_readlane(bid_v, j & (kWave - 1));
-  };
-  auto load_tile = [&](int bid, u32x4 (&kt)[NLOAD], u32x4 (&vt)[NLOAD]) {
-    const u32x4* kp = kbase + (int64_t)bid * block_vecs;
-    const u32x4* vp = vbase + (int64_t)bid * block_vecs;
-#pragma unroll
-    for (int i = 0; i < NLOAD; ++i) kt[i] = kp[i * kWave];
-#pragma unroll
-    for (int i = 0; i < NLOAD; ++i) vt[i] = vp[i * kWave];
-  };
-  auto process = [&](const u32x4 (&kt)[NLOAD], const u32x4 (&vt)[NLOAD], int blk) {
-    float sc[NLOAD][G];
-#pragma unroll
-    for (int i = 0; i < NLOAD; ++i) {
-      float kf[std::is_same<KV, BF16>::value ? 1 : EPL];
-      if constexpr (!std::is_same<KV, BF16>::value) Vec<KV>::to_f32(kt[i], kf);
-#pragma unroll
-      for (int h = 0; h < G; ++h) sc[i][h] = q.dot(h, kt[i], kf);
-    }
-#pragma unroll
-    for (int i = 0; i < NLOAD; ++i)
-#pragma unroll
-      for (int h = 0; h < G; ++h) sc[i][h] = group_sum<LPR>(sc[i][h]) * qk_scale_log2;
-
-    float vf[NLOAD][EPL];
-#pragma unroll
-    for (int i = 0; i < NLOAD; ++i) Vec<KV>::to_f32(vt[i], vf[i]);
-
-    if ((blk + 1) * BS > L) {  // the sequence's last, partly filled block
-      const int tok0 = blk * BS + row;
-#pragma unroll
-      for (int i = 0; i < NLOAD; ++i) {
-        const bool valid = tok0 + i * RPL < L;
-#pragma unroll
-        for (int h = 0; h < G; ++h) sc[i][h] = valid ? sc[i][h] : -INFINITY;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) vf[i][e] = valid ? vf[i][e] : 0.f;
-      }
-    }
-
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float bm = sc[0][h];
-#pragma unroll
-      for (int i = 1; i < NLOAD; ++i) bm = fmaxf(bm, sc[i][h]);
-      const float mn = fmaxf(m[h], bm);
-      const float mu = mn == -INFINITY ? 0.f : mn;
-      const float alpha = fast_exp2(m[h] - mu);
-      float ps = 0.f;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[h][e] *= alpha;
-#pragma unroll
-      for (int i = 0; i < NLOAD; ++i) {
-        const float p = fast_exp2(sc[i][h] - mu);
-        ps += p;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[h][e] = __builtin_fmaf(p, vf[i][e], acc[h][e]);
-      }
-      l[h] = l[h] * alpha + ps;
-      m[h] = mn;
-    }
-  };
-
-  if (nmine > 0) {
-    u32x4 kc[NLOAD], vc[NLOAD];
-    load_tile(block_id(0), kc, vc);
-    for (int j = 0; j + 1 < nmine; ++j) {
-      u32x4 kn[NLOAD], vn[NLOAD];
-      load_tile(block_id(j + 1), kn, vn);
-      process(kc, vc, b0 + w + NW * j);
-#pragma unroll
-      for (int i = 0; i < NLOAD; ++i) { kc[i] = kn[i]; vc[i] = vn[i]; }
-    }
-    process(kc, vc, b0 + w + NW * (nmine - 1));
-  }
-
-  // Merge the DPP rows of this wavefront (lanes with equal col).
-#pragma unroll
-  for (int mask = LPR; mask < kWave; mask <<= 1) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float mo = shfl_xor(m[h], mask);
-      const float lo = shfl_xor(l[h], mask);
-      const float M = fmaxf(m[h], mo);
-      const float mu = M == -INFINITY ? 0.f : M;
-      const float f = fast_exp2(m[h] - mu), fo = fast_exp2(mo - mu);
-      l[h] = l[h] * f + lo * fo;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[h][e] = acc[h][e] * f + shfl_xor(acc[h][e], mask) * fo;
-      m[h] = M;
-    }
-  }
-
-  // Merge the wavefronts through LDS and finish.
-  __shared__ float sm_ml[NW][G][2];
-  __shared__ float sm_acc[NW][G][D];
-  if (row == 0) {
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) sm_acc[w][h][col * EPL + e] = acc[h][e];
-  }
-  if (lane == 0) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) { sm_ml[w][h][0] = m[h]; sm_ml[w][h][1] = l[h]; }
-  }
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < G * D; idx += NW * kWave) {
-    const int h = idx / D, d = idx % D;
-    float M = sm_ml[0][h][0];
-#pragma unroll
-    for (int ww = 1; ww < NW; ++ww) M = fmaxf(M, sm_ml[ww][h][0]);
-    const float mu = M == -INFINITY ? 0.f : M;
-    float den = 0.f, num = 0.f;
-#pragma unroll
-    for (int ww = 0; ww < NW; ++ww) {
-      const float f = fast_exp2(sm_ml[ww][h][0] - mu);
-      den += f * sm_ml[ww][h][1];
-      num += f * sm_acc[ww][h][d];
-    }
+  const int64_t hq0 = (int64_t)s * num_heads + (int64_t)g * G;
+  auto emit = [&](int h, int d, float M, float den, float num) {
     const float o = den > 0.f ? num / den * v_scale : 0.f;
-    const int64_t hq = (int64_t)s * num_heads + (int64_t)g * G + h;
+    const int64_t hq = hq0 + h;
     if (nparts == 1) {
       store_out<OT>(out, hq * D + d, o);
     } else {
@@ -280,40 +487,295 @@ __global__ __launch_bounds__(kDecodeWaves * kWave) void decode_kernel(
         part_ml[(hq * max_parts + part) * 2 + 1] = den;
       }
     }
+  };
+
+  if (NW == 1) {
+    // Every row now holds the merged state; row r writes heads r, r+RPL, ...
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      if (h % RPL != A.row) continue;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) emit(h, A.col * EPL + e, A.m_ref[h], l_h[h], A.acc[h][e]);
+    }
+    return;
+  }
+
+  // Merge the wavefronts through LDS and finish.
+  __shared__ float sm_ml[kMaxDecodeWaves][G][2];
+  __shared__ float sm_acc[kMaxDecodeWaves][G][D];
+  if (A.row == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) sm_acc[w][h][A.col * EPL + e] = A.acc[h][e];
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) { sm_ml[w][h][0] = A.m_ref[h]; sm_ml[w][h][1] = l_h[h]; }
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < G * D; idx += NW * kWave) {
+    const int h = idx / D, d = idx % D;
+    float M = sm_ml[0][h][0];
+    for (int ww = 1; ww < NW; ++ww) M = fmaxf(M, sm_ml[ww][h][0]);
+    const float mu = M == -INFINITY ? 0.f : M;
+    float den = 0.f, num = 0.f;
+    for (int ww = 0; ww < NW; ++ww) {
+      const float f = fast_exp2(sm_ml[ww][h][0] - mu);
+      den += f * sm_ml[ww][h][1];
+      num += f * sm_acc[ww][h][d];
+    }
+    emit(h, d, M, den, num);
   }
 }
 
-// Log-sum-exp merge of the partitions of one (sequence, query head):
-// M = max_p m_p, w_p = 2^(m_p - M) * l_p, out = sum_p w_p o_p / sum_p w_p.
-template <typename OT, int D>
-__global__ __launch_bounds__(kWave) void lse_reduce_kernel(
+// ---------------------------------------------------------------------------
+// Balanced split-K.  Per KV head g, the blocks of all sequences form one
+// flattened list (sequence after sequence, T blocks in all); it is cut into
+// W equal contiguous ranges, one per wavefront ("worker").  A worker walks
+// its range sequence by sequence: a sequence it covers entirely is finished
+// in place; a sequence cut between workers leaves one partial state per
+// worker — at most two per worker, its first and its last piece — which the
+// merge kernel combines.  Workers of the KV heads of one block range are
+// adjacent, so the heads' tiles of a block (contiguous in the pool) are read
+// together.
+// ---------------------------------------------------------------------------
+constexpr int kBalancedMinBlocks = 16;  // fewest blocks a worker is given
+
+
+__device__ __forceinline__ int nblocks_of(int L, int bs) { return (L + bs - 1) / bs; }
+
+// Total blocks of all sequences (wavefront-uniform result).
+__device__ __forceinline__ int64_t total_blocks(const int32_t* seq_lens, int num_seqs, int bs,
+                                                int lane) {
+  int64_t t = 0;
+  for (int s = lane; s < num_seqs; s += kWave) t += nblocks_of(seq_lens[s], bs);
+  int32_t lo = (int32_t)t;  // per-lane partial sums stay far below 2^31
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) lo += __shfl_xor(lo, m, kWave);
+  return lo;
+}
+
+// The sequence whose blocks hold flattened position x, and the flattened
+// position of its first block (wavefront-uniform).
+__device__ __forceinline__ void locate_block(const int32_t* seq_lens, int num_seqs, int bs,
+                                             int64_t x, int lane, int& s_out, int64_t& base_out) {
+  int64_t base = 0;
+  for (int c = 0; c < num_seqs; c += kWave) {
+    const int s = c + lane;
+    const int nb = s < num_seqs ? nblocks_of(seq_lens[s], bs) : 0;
+    int incl = nb;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+      const int t = __shfl_up(incl, d, kWave);
+      if (lane >= d) incl += t;
+    }
+    const int chunk = __shfl(incl, kWave - 1, kWave);
+    if (base + chunk > x) {
+      const uint64_t hit = __builtin_amdgcn_ballot_w64(base + incl > x);
+      const int k = __builtin_ctzll(hit);
+      s_out = c + k;
+      base_out = base + __shfl(incl - nb, k, kWave);
+      return;
+    }
+    base += chunk;
+  }
+  s_out = num_seqs;
+  base_out = base;
+}
+
+__device__ __forceinline__ int64_t worker_start(int64_t T, int v, int W) { return T * v / W; }
+
+// The worker whose range holds flattened position x.
+__device__ __forceinline__ int worker_of(int64_t T, int64_t x, int W) {
+  return (int)(((x + 1) * W + T - 1) / T - 1);
+}
+
+__device__ __forceinline__ int effective_workers(int64_t T, int W) {
+  const int64_t want = (T + kBalancedMinBlocks - 1) / kBalancedMinBlocks;
+  return (int)(want < W ? (want > 0 ? want : 1) : W);
+}
+
+// Online log-sum-exp merge, for one output element, of np partial states:
+// state p has maximum m_p, sum l_p and accumulator a_p (normalised by l_p
+// when kNormalised).  Returns sum_p 2^(m_p - M) a'_p / sum_p 2^(m_p - M) l_p
+// with M = max_p m_p and a'_p the unnormalised accumulator.  The loads of
+// eight states are issued together.
+template <bool kNormalised, typename StateFn>
+__device__ __forceinline__ float merge_element(const float* acc, const float* ml, int np, int D,
+                                               int h, int d, StateFn state) {
+  constexpr int kBatch = 8;
+  float M = -INFINITY, num = 0.f, den = 0.f;
+  for (int p0 = 0; p0 < np; p0 += kBatch) {
+    float m[kBatch], l[kBatch], a[kBatch];
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q) {
+      const int p = p0 + q < np ? p0 + q : np - 1;
+      const int64_t st = state(p, h);
+      m[q] = ml[2 * st];
+      l[q] = ml[2 * st + 1];
+      a[q] = acc[st * D + d];
+    }
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q) {
+      if (p0 + q >= np) break;
+      if (m[q] > M) {
+        const float f = M == -INFINITY ? 0.f : fast_exp2(M - m[q]);
+        num *= f;
+        den *= f;
+        M = m[q];
+      }
+      const float e = M == -INFINITY ? 0.f : fast_exp2(m[q] - M);
+      num = __builtin_fmaf(e * (kNormalised ? l[q] : 1.f), a[q], num);
+      den = __builtin_fmaf(e, l[q], den);
+    }
+  }
+  return den > 0.f ? num / den : 0.f;
+}
+
+template <typename KV, typename QT, int D, int BS, int G>
+__global__ __launch_bounds__(kMaxDecodeWaves * kWave) void decode_balanced_kernel(
+    void* __restrict__ out, float* __restrict__ part_acc, float* __restrict__ part_ml,
+    int32_t* __restrict__ cuts, const void* __restrict__ query,
+    const void* __restrict__ k_cache, const void* __restrict__ v_cache,
+    const int32_t* __restrict__ block_tables, const int32_t* __restrict__ seq_lens, int num_seqs,
+    int max_blocks_per_seq, int num_kv_heads, int workers_per_head, float qk_scale_log2,
+    float v_scale) {
+  using WA = WaveAttn<KV, QT, D, BS, G>;
+  constexpr int EPL = WA::EPL, RPL = WA::RPL;
+  using OT = QT;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int worker = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+  const int g = worker % num_kv_heads, vw = worker / num_kv_heads;
+  if (vw >= workers_per_head) return;
+  const int num_heads = num_kv_heads * G;
+
+  const int64_t T = total_blocks(seq_lens, num_seqs, BS, lane);
+  const int W = effective_workers(T, workers_per_head);
+  if (vw >= W) return;
+  const int64_t start = worker_start(T, vw, W), end = worker_start(T, vw + 1, W);
+  if (start >= end) return;
+  int s;
+  int64_t base;
+  locate_block(seq_lens, num_seqs, BS, start, lane, s, base);
+
+  WA A;
+  A.init(lane, qk_scale_log2);
+  int64_t pos = start;
+  while (pos < end && s < num_seqs) {
+    const int L = seq_lens[s];
+    const int nblk = nblocks_of(L, BS);
+    const int64_t seg_end = base + nblk;
+    if (nblk > 0) {
+      const int b_lo = (int)(pos - base);
+      const int b_hi = (int)((end < seg_end ? end : seg_end) - base);
+      A.reset();
+      A.q.load(query, (int64_t)s * num_heads + (int64_t)g * G, D, A.col);
+      A.stream(k_cache, v_cache, block_tables + (int64_t)s * max_blocks_per_seq, g, num_kv_heads,
+               b_lo, b_hi - b_lo, 1, L);
+      float l_h[G];
+      A.merge_rows(l_h);
+      const bool whole = b_lo == 0 && b_hi == nblk;
+      const int slot = pos == start ? 0 : 1;
+      const int64_t hq0 = (int64_t)s * num_heads + (int64_t)g * G;
+      if (b_lo == 0 && lane == 0) {
+        // The worker holding the sequence's first block describes its cut:
+        // first worker, number of pieces, and the first piece's slot.
+        const int np = whole ? 1 : worker_of(T, seg_end - 1, W) - vw + 1;
+        cuts[2 * ((int64_t)s * num_kv_heads + g) + 0] = vw;
+        cuts[2 * ((int64_t)s * num_kv_heads + g) + 1] = np * 2 + slot;
+      }
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        if (h % RPL != A.row) continue;
+        if (whole) {
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) {
+            const float o = l_h[h] > 0.f ? A.acc[h][e] / l_h[h] * v_scale : 0.f;
+            store_out<OT>(out, (hq0 + h) * D + A.col * EPL + e, o);
+          }
+        } else {
+          const int64_t pslot = ((int64_t)worker * 2 + slot) * G + h;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) part_acc[pslot * D + A.col * EPL + e] = A.acc[h][e];
+          if (A.col == 0) {
+            part_ml[pslot * 2 + 0] = A.m_ref[h];
+            part_ml[pslot * 2 + 1] = l_h[h];
+          }
+        }
+      }
+      pos = base + b_hi;
+    }
+    if (pos >= seg_end) {
+      base = seg_end;
+      ++s;
+    }
+  }
+}
+
+// Finishes what the balanced kernel left: one workgroup per (KV head,
+// sequence).  Empty sequences get zeros; a sequence cut between workers is
+// merged from its pieces' (m, l, acc), found through the cut record its
+// first worker wrote; a whole sequence was finished by its worker.
+template <typename OT, int D, int G>
+__global__ __launch_bounds__(256) void balanced_reduce_kernel(
+    void* __restrict__ out, const float* __restrict__ part_acc,
+    const float* __restrict__ part_ml, const int32_t* __restrict__ cuts,
+    const int32_t* __restrict__ seq_lens, int num_kv_heads, float v_scale) {
+  const int g = blockIdx.x, s = blockIdx.y;
+  const int num_heads = num_kv_heads * G;
+  const int64_t hq0 = (int64_t)s * num_heads + (int64_t)g * G;
+  const int L = seq_lens[s];
+  const int va = cuts[2 * ((int64_t)s * num_kv_heads + g) + 0];
+  const int code = cuts[2 * ((int64_t)s * num_kv_heads + g) + 1];
+  if (L == 0) {
+    for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x) store_out<OT>(out, hq0 * D + idx, 0.f);
+    return;
+  }
+  const int np = code >> 1, slot0 = code & 1;
+  if (np <= 1) return;
+  auto state = [&](int p, int h) -> int64_t {
+    return ((int64_t)((va + p) * num_kv_heads + g) * 2 + (p == 0 ? slot0 : 0)) * G + h;
+  };
+  for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x) {
+    const int h = idx / D, d = idx % D;
+    const float o = merge_element<false>(part_acc, part_ml, np, D, h, d, state);
+    store_out<OT>(out, (hq0 + h) * D + d, o * v_scale);
+  }
+}
+
+// Log-sum-exp merge of the fixed partitions of one (KV head, sequence):
+// partition p of query head h left (m_p, l_p, o_p) with o_p normalised;
+// out = sum_p 2^(m_p - M) l_p o_p / sum_p 2^(m_p - M) l_p.
+template <typename OT, int D, int G>
+__global__ __launch_bounds__(256) void lse_reduce_kernel(
     void* __restrict__ out, const float* __restrict__ part_o,
-    const float* __restrict__ part_ml, const int32_t* __restrict__ seq_lens, int num_heads,
+    const float* __restrict__ part_ml, const int32_t* __restrict__ seq_lens, int num_kv_heads,
     int block_size, int partition_blocks, int max_parts) {
-  const int hq_in_seq = blockIdx.x, s = blockIdx.y, lane = threadIdx.x;
+  const int g = blockIdx.x, s = blockIdx.y;
   const int L = seq_lens[s];
   const int nblk = (L + block_size - 1) / block_size;
   const int nparts = nblk > partition_blocks ? (nblk + partition_blocks - 1) / partition_blocks : 1;
   if (nparts <= 1) return;
-  const int64_t hq = (int64_t)s * num_heads + hq_in_seq;
-  const float* ml = part_ml + hq * max_parts * 2;
-  float M = -INFINITY;
-  for (int p = 0; p < nparts; ++p) M = fmaxf(M, ml[2 * p]);
-  const float mu = M == -INFINITY ? 0.f : M;
-  constexpr int DPL = D / kWave;
-  float num[DPL], den = 0.f;
-#pragma unroll
-  for (int e = 0; e < DPL; ++e) num[e] = 0.f;
-  const float* po = part_o + hq * max_parts * D + lane * DPL;
-  for (int p = 0; p < nparts; ++p) {
-    const float wgt = fast_exp2(ml[2 * p] - mu) * ml[2 * p + 1];
-    den += wgt;
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) num[e] = __builtin_fmaf(wgt, po[(int64_t)p * D + e], num[e]);
+  const int num_heads = num_kv_heads * G;
+  const int64_t hq0 = (int64_t)s * num_heads + (int64_t)g * G;
+  // Partition p of head h is state (hq0 + h) * max_parts + p; the decode
+  // kernel already applied the value scale and normalised each output.
+  auto state = [&](int p, int h) -> int64_t { return (hq0 + h) * max_parts + p; };
+  for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x) {
+    const int h = idx / D, d = idx % D;
+    store_out<OT>(out, (hq0 + h) * D + d, merge_element<true>(part_o, part_ml, nparts, D, h, d, state));
   }
-#pragma unroll
-  for (int e = 0; e < DPL; ++e)
-    store_out<OT>(out, hq * D + lane * DPL + e, den > 0.f ? num[e] / den : 0.f);
+}
+
+// Wavefronts per workgroup: enough blocks per wavefront to keep its
+// one-tile-ahead pipeline busy, at most four.
+inline int decode_waves(int partition_blocks, int max_seq_len, int block_size) {
+  const int blocks = partition_blocks > 0 ? partition_blocks
+                                          : (max_seq_len + block_size - 1) / block_size;
+  if (blocks >= 64) return 4;
+  if (blocks >= 24) return 2;
+  return 1;
 }
 
 template <typename KV, typename QT, int D, int BS, int G>
@@ -321,16 +783,34 @@ hipError_t launch_decode(const DecodeArgs& a) {
   const float k_scale = std::is_same<KV, FP8>::value ? a.k_scale : 1.0f;
   const float v_scale = std::is_same<KV, FP8>::value ? a.v_scale : 1.0f;
   const float qk = a.scale * k_scale * kLog2e;
+  if (a.balanced_workers > 0) {
+    const int per_head = a.balanced_workers / a.num_kv_heads;
+    const int workers = per_head * a.num_kv_heads;
+    const int wg = (workers + kMaxDecodeWaves - 1) / kMaxDecodeWaves;
+    hipLaunchKernelGGL((decode_balanced_kernel<KV, QT, D, BS, G>), dim3((unsigned)wg),
+                       dim3(kMaxDecodeWaves * kWave), 0, a.stream, a.out, a.part_o, a.part_ml,
+                       a.cuts, a.query, a.k_cache, a.v_cache, a.block_tables, a.seq_lens,
+                       a.num_seqs, a.max_blocks_per_seq, a.num_kv_heads, per_head, qk, v_scale);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((balanced_reduce_kernel<QT, D, G>),
+                       dim3((unsigned)a.num_kv_heads, (unsigned)a.num_seqs), dim3(256), 0, a.stream,
+                       a.out, a.part_o, a.part_ml, a.cuts, a.seq_lens, a.num_kv_heads, v_scale);
+    return hipGetLastError();
+  }
+  const int nw = a.num_waves > 0 ? a.num_waves
+                                 : decode_waves(a.partition_blocks, a.max_seq_len, BS);
   hipLaunchKernelGGL((decode_kernel<KV, QT, D, BS, G>),
                      dim3((unsigned)a.max_parts, (unsigned)a.num_kv_heads, (unsigned)a.num_seqs),
-                     dim3(kDecodeWaves * kWave), 0, a.stream, a.out, a.part_o, a.part_ml, a.query,
+                     dim3(nw * kWave), 0, a.stream, a.out, a.part_o, a.part_ml, a.query,
                      a.k_cache, a.v_cache, a.block_tables, a.seq_lens, a.max_blocks_per_seq,
                      a.num_kv_heads, a.partition_blocks, a.max_parts, qk, v_scale);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.max_parts <= 1) return e;
-  hipLaunchKernelGGL((lse_reduce_kernel<QT, D>), dim3((unsigned)a.num_heads, (unsigned)a.num_seqs),
-                     dim3(kWave), 0, a.stream, a.out, a.part_o, a.part_ml, a.seq_lens, a.num_heads,
-                     a.block_size, a.partition_blocks, a.max_parts);
+  hipLaunchKernelGGL((lse_reduce_kernel<QT, D, G>),
+                     dim3((unsigned)a.num_kv_heads, (unsigned)a.num_seqs), dim3(256), 0, a.stream,
+                     a.out, a.part_o, a.part_ml, a.seq_lens, a.num_kv_heads, a.block_size,
+                     a.partition_blocks, a.max_parts);
   return hipGetLastError();
 }
 

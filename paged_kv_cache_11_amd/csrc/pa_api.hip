@@ -4,6 +4,7 @@
 // before anything is enqueued.
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 
 #include <string>
 
@@ -61,6 +62,35 @@ int64_t decode_max_parts(int32_t max_seq_len, int32_t partition_size) {
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// PA_DECODE_WAVES=1|2|4 pins the wavefronts per decode workgroup (a tuning
+// knob); otherwise the library picks from the partition size.
+int32_t decode_waves_override() {
+  static const int32_t v = [] {
+    const char* e = getenv("PA_DECODE_WAVES");
+    const int x = e ? atoi(e) : 0;
+    return (x == 1 || x == 2 || x == 4) ? x : 0;
+  }();
+  return v;
+}
+
+// Wavefronts of the balanced split: PA_BALANCED_WAVES_PER_CU (default 8,
+// two per SIMD: enough loads in flight to saturate HBM while the score and
+// softmax arithmetic of the other wavefronts hides behind them) per compute
+// unit of the current device, capped by the workspace layout.
+int32_t balanced_workers_for_device() {
+  static const int per_cu = [] {
+    const char* e = getenv("PA_BALANCED_WAVES_PER_CU");
+    const int x = e ? atoi(e) : 0;
+    return (x >= 1 && x <= 32) ? x : 8;
+  }();
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  const int64_t w = (int64_t)cus * per_cu;
+  return (int32_t)(w < pa::kMaxBalancedWorkers ? w : pa::kMaxBalancedWorkers);
+}
 
 }  // namespace
 
@@ -128,9 +158,16 @@ int32_t pa_copy_blocks(void* k_cache, void* v_cache, int32_t cache_dtype, int32_
   return hip_result(pa::copy_blocks(a), "pa_copy_blocks");
 }
 
-size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t head_size,
-                                int32_t max_seq_len, int32_t partition_size) {
-  if (num_seqs <= 0 || num_heads <= 0 || head_size <= 0) return 0;
+size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                int32_t head_size, int32_t max_seq_len, int32_t partition_size) {
+  if (num_seqs <= 0 || num_heads <= 0 || num_kv_heads <= 0 || head_size <= 0 ||
+      num_heads % num_kv_heads != 0)
+    return 0;
+  if (partition_size == PA_PARTITION_BALANCED) {
+    const size_t n = (size_t)pa::kMaxBalancedWorkers * 2 * (num_heads / num_kv_heads);
+    return align256(n * head_size * sizeof(float)) + align256(n * 2 * sizeof(float)) +
+           align256((size_t)num_seqs * num_kv_heads * 2 * sizeof(int32_t));
+  }
   const int64_t mp = decode_max_parts(max_seq_len, partition_size);
   if (mp <= 1) return 0;
   const size_t n = (size_t)num_seqs * num_heads * mp;
@@ -156,8 +193,10 @@ int32_t pa_decode(void* out, const void* query, int32_t q_dtype, int32_t num_seq
   if (max_seq_len < 0 || (int64_t)max_seq_len > (int64_t)max_blocks_per_seq * block_size)
     return fail(PA_ERR_INVALID, "max_seq_len %d does not fit %d blocks of %d tokens", max_seq_len,
                 max_blocks_per_seq, block_size);
-  if (partition_size < 0 || partition_size % block_size != 0)
-    return fail(PA_ERR_INVALID, "partition_size %d must be >= 0 and a multiple of block_size %d",
+  const bool balanced = partition_size == PA_PARTITION_BALANCED;
+  if (!balanced && (partition_size < 0 || partition_size % block_size != 0))
+    return fail(PA_ERR_INVALID,
+                "partition_size %d must be PA_PARTITION_BALANCED, 0 or a multiple of block_size %d",
                 partition_size, block_size);
   if (!(scale == scale) || !(k_scale == k_scale) || !(v_scale == v_scale))
     return fail(PA_ERR_INVALID, "scales must not be NaN");
@@ -169,19 +208,29 @@ int32_t pa_decode(void* out, const void* query, int32_t q_dtype, int32_t num_seq
   if (num_seqs == 0) return ok();
   if (!out || !query || !block_tables || !seq_lens)
     return fail(PA_ERR_INVALID, "out / query / block_tables / seq_lens is NULL");
-  const int64_t mp = decode_max_parts(max_seq_len, partition_size);
+  const int64_t mp = balanced ? 1 : decode_max_parts(max_seq_len, partition_size);
   if (mp > 65535) return fail(PA_ERR_INVALID, "too many partitions (%lld)", (long long)mp);
   float* part_o = nullptr;
   float* part_ml = nullptr;
-  if (mp > 1) {
-    const size_t need = pa_decode_workspace_size(num_seqs, num_heads, head_size, max_seq_len,
-                                                 partition_size);
+  int32_t workers = 0;
+  int32_t* a_cuts = nullptr;
+  if (mp > 1 || balanced) {
+    const size_t need = pa_decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_size,
+                                                 max_seq_len, partition_size);
     if (!workspace || workspace_bytes < need)
       return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
                   workspace ? workspace_bytes : (size_t)0);
-    const size_t n = (size_t)num_seqs * num_heads * mp;
+    const size_t n = balanced ? (size_t)pa::kMaxBalancedWorkers * 2 * (num_heads / num_kv_heads)
+                              : (size_t)num_seqs * num_heads * mp;
     part_o = (float*)workspace;
     part_ml = (float*)((char*)workspace + align256(n * head_size * sizeof(float)));
+    if (balanced) {
+      a_cuts = (int32_t*)((char*)part_ml + align256(n * 2 * sizeof(float)));
+      const int32_t w = balanced_workers_for_device();
+      if (w <= 0) return fail(PA_ERR_HIP, "cannot query the device's compute units");
+      workers = (w / num_kv_heads) * num_kv_heads;
+      if (workers < num_kv_heads) workers = num_kv_heads;
+    }
   }
   pa::DecodeArgs a{};
   a.out = out; a.query = query; a.q_dtype = q_dtype;
@@ -194,6 +243,9 @@ int32_t pa_decode(void* out, const void* query, int32_t q_dtype, int32_t num_seq
   a.partition_blocks = mp > 1 ? partition_size / block_size : 0;
   a.max_parts = (int32_t)mp;
   a.part_o = part_o; a.part_ml = part_ml;
+  a.num_waves = decode_waves_override();
+  a.balanced_workers = workers;
+  a.cuts = a_cuts;
   a.stream = (hipStream_t)stream;
   hipError_t e;
   if (cache_dtype == PA_F32) e = pa::decode_f32(a);

@@ -14,6 +14,10 @@ namespace pa {
 
 inline int dtype_bytes(int32_t dt) { return dt == PA_F32 ? 4 : dt == PA_BF16 ? 2 : 1; }
 
+// Upper bound on the wavefronts of the balanced split; the workspace of a
+// balanced decode holds two partial states per wavefront.
+constexpr int kMaxBalancedWorkers = 4096;
+
 struct CacheWriteArgs {
   const void* key;
   const void* value;
@@ -56,6 +60,9 @@ struct DecodeArgs {
   int32_t max_parts;         // grid extent over partitions
   float* part_o;             // [num_seqs][num_heads][max_parts][head_size]
   float* part_ml;            // [num_seqs][num_heads][max_parts][2]
+  int32_t num_waves;         // wavefronts per workgroup; 0 = chosen from the partition size
+  int32_t balanced_workers;  // > 0: balanced split over this many wavefronts (multiple of Hkv)
+  int32_t* cuts;             // balanced split: per (sequence, KV head) {first worker, 2*pieces+slot}
   hipStream_t stream;
 };
 

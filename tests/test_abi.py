@@ -38,11 +38,16 @@ def test_pool_bytes_and_workspace_sizes():
     assert pa.pa_pool_bytes(10, 8, 16, 128, pa.PA_BF16) == 10 * 8 * 16 * 128 * 2
     assert pa.pa_pool_bytes(10, 8, 32, 128, pa.PA_FP8_E4M3) == 10 * 8 * 32 * 128
     assert pa.pa_pool_bytes(0, 8, 16, 128, pa.PA_BF16) == 0
-    assert pa.pa_decode_workspace_size(64, 32, 128, 4096, 0) == 0
-    assert pa.pa_decode_workspace_size(64, 32, 128, 512, 512) == 0
+    assert pa.pa_decode_workspace_size(64, 32, 8, 128, 4096, 0) == 0
+    assert pa.pa_decode_workspace_size(64, 32, 8, 128, 512, 512) == 0
     n = 8 * 32 * 64
     want = ((n * 128 * 4 + 255) // 256) * 256 + ((n * 2 * 4 + 255) // 256) * 256
-    assert pa.pa_decode_workspace_size(8, 32, 128, 32768, 512) == want
+    assert pa.pa_decode_workspace_size(8, 32, 8, 128, 32768, 512) == want
+    nb = 4096 * 2 * 4  # two partial states of 4 heads per wavefront of the largest grid
+    want_b = (((nb * 128 * 4 + 255) // 256) * 256 + ((nb * 2 * 4 + 255) // 256) * 256
+              + ((64 * 8 * 8 + 255) // 256) * 256)   # + a two-word cut record per (seq, KV head)
+    assert pa.pa_decode_workspace_size(64, 32, 8, 128, 4096, pa.PA_PARTITION_BALANCED) == want_b
+    assert pa.pa_decode_workspace_size(64, 30, 8, 128, 4096, 0) == 0
 
 
 P = ctypes.c_void_p(16)  # never dereferenced: every call below fails validation first
@@ -72,6 +77,8 @@ def _decode(**kw):
     (dict(scale=float("nan")), pa.PA_ERR_INVALID),
     (dict(partition_size=32), pa.PA_ERR_WORKSPACE),
     (dict(partition_size=32, workspace=P, workspace_bytes=100), pa.PA_ERR_WORKSPACE),
+    (dict(partition_size=pa.PA_PARTITION_BALANCED), pa.PA_ERR_WORKSPACE),
+    (dict(partition_size=-2), pa.PA_ERR_INVALID),
     (dict(out=None), pa.PA_ERR_INVALID),
 ])
 def test_decode_rejects_bad_host_arguments(kw, code):
