@@ -1,0 +1,99 @@
+"""GPU parity of pa_prefill_chunk (matrix-core causal chunked prefill)
+against the oracle, on the 70B-shape fp8 mixed step and on varlen bf16/fp8
+chunk sets, plus the cross-kernel invariant that a prefill row equals a
+decode of the same query at that position."""
+import numpy as np
+import pytest
+import torch
+
+import pa_gpu as G
+from oracle import paged as opg
+from paged_kv_cache_11_amd import binding as pa
+from paged_kv_cache_11_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+
+def run_prefill(b, kp, vp, cq, qsl, lens, tables, max_q):
+    qt = wl.storage_tensor(cq, "bf16").to(G.DEV)
+    out = torch.empty_like(qt)
+    pa.pa_prefill_chunk(out, qt, torch.from_numpy(np.ascontiguousarray(qsl)).to(G.DEV), max_q, kp, vp,
+                        torch.from_numpy(np.ascontiguousarray(tables)).to(G.DEV),
+                        torch.from_numpy(np.ascontiguousarray(lens)).to(G.DEV), b.scale, b.k_scale,
+                        b.v_scale)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy().astype(np.float64), G.query_f64(qt)
+
+
+def test_prefill_mixed_step_fp8_70b_shape():
+    """512 queries at positions 1536..2047 of a 2048-token prompt, 64/8 heads,
+    fp8 E4M3 cache with per-tensor scales, block 32."""
+    b = wl.mixed_fp8_step()
+    G.say(f"[mixed] {len(b.slot_mapping)} tokens, {b.num_blocks} blocks, scales {b.k_scale:.4g} {b.v_scale:.4g}")
+    kp, vp = G.gpu_pool(b)
+    G.gpu_fill(b, kp, vp)
+    okp, ovp = G.oracle_pool(b)
+    assert G.raw_equal(kp, okp) and G.raw_equal(vp, ovp)
+    got, q64 = run_prefill(b, kp, vp, b.chunk_q, b.chunk_query_start, b.chunk_seq_lens,
+                           b.chunk_block_tables, int(b.chunk_q.shape[0]))
+    rows = list(range(0, 512, 5)) + [511]
+    ref = opg.paged_prefill(q64, b.chunk_query_start, okp, ovp, b.chunk_block_tables,
+                            b.chunk_seq_lens, b.scale, kv_dtype="fp8", k_scale=b.k_scale,
+                            v_scale=b.v_scale, rows=rows)
+    G.assert_close(got, ref, "fp8", "fp8 prefill chunk", rows=rows)
+    # Cross-kernel: prefill row i equals a decode of the same query with the
+    # context cut at its position.
+    pick = [0, 100, 511]
+    L = int(b.chunk_seq_lens[0])
+    lens = np.array([L - 512 + i + 1 for i in pick], dtype=np.int32)
+    tables = np.repeat(b.chunk_block_tables, len(pick), axis=0)
+    qd = torch.from_numpy(np.ascontiguousarray(b.chunk_q[pick])).to(torch.bfloat16).to(G.DEV)
+    dec = G.run_decode(b, kp, vp, qd, partition_size=0, seq_lens=lens, tables=tables)
+    G.assert_close(got[pick], dec, "fp8", "prefill rows vs decode")
+
+
+def _varlen_case(Hq, Hkv, bs, kv, seed):
+    rng = np.random.default_rng(seed)
+    D = 128
+    # (queries in the chunk, keys including the chunk)
+    chunks = [(1, 1), (37, 100), (300, 300), (129, 777), (64, 1024)]
+    lens = np.array([L for _, L in chunks], dtype=np.int32)
+    qsl = np.concatenate([[0], np.cumsum([n for n, _ in chunks])]).astype(np.int32)
+    nblk = (lens + bs - 1) // bs
+    nb = int(nblk.sum()) + 5
+    perm = rng.permutation(nb).astype(np.int32)
+    tables = np.full((len(chunks), int(nblk.max()) + 1), -1, np.int32)
+    cur, slots = 0, []
+    for c, n in enumerate(nblk):
+        tables[c, :n] = perm[cur:cur + n]
+        cur += n
+        t = np.arange(lens[c])
+        slots.append(tables[c, t // bs].astype(np.int64) * bs + t % bs)
+    T = int(lens.sum())
+    k = rng.standard_normal((T, Hkv, D), dtype=np.float32)
+    v = rng.standard_normal((T, Hkv, D), dtype=np.float32)
+    cq = rng.standard_normal((int(qsl[-1]), Hq, D), dtype=np.float32)
+    ks = float(np.float32(np.abs(k).max()) / np.float32(448)) if kv == "fp8" else 1.0
+    vs = float(np.float32(np.abs(v).max()) / np.float32(448)) if kv == "fp8" else 1.0
+    b = wl.PagedBatch("prefill_varlen", Hq, Hkv, D, bs, nb, "bf16", "bf16", kv, 1 / np.sqrt(D),
+                      cq[:1], k, v, np.concatenate(slots), lens, tables, k_scale=ks, v_scale=vs)
+    return b, cq, qsl, lens, tables, max(n for n, _ in chunks)
+
+
+@pytest.mark.parametrize("Hq,Hkv,bs,kv", [
+    (8, 8, 16, "bf16"), (16, 8, 32, "bf16"), (32, 8, 16, "bf16"), (64, 8, 32, "bf16"),
+    (32, 8, 32, "fp8"), (16, 4, 16, "fp8"),
+])
+def test_prefill_varlen_chunks(Hq, Hkv, bs, kv):
+    """Five chunks: a single-query prompt, a chunk inside a longer context,
+    a whole prompt from position 0, and tiles that end mid-way."""
+    b, cq, qsl, lens, tables, max_q = _varlen_case(Hq, Hkv, bs, kv, seed=Hq + bs)
+    kp, vp = G.gpu_pool(b)
+    G.gpu_fill(b, kp, vp)
+    okp, ovp = G.oracle_pool(b)
+    got, q64 = run_prefill(b, kp, vp, cq, qsl, lens, tables, max_q)
+    rows = sorted(set(list(range(0, int(qsl[-1]), 7)) + [int(x) - 1 for x in qsl[1:]] +
+                      [int(x) for x in qsl[:-1]]))
+    ref = opg.paged_prefill(q64, qsl, okp, ovp, tables, lens, b.scale, kv_dtype=kv,
+                            k_scale=b.k_scale, v_scale=b.v_scale, rows=rows)
+    G.assert_close(got, ref, kv, f"prefill {Hq}/{Hkv} bs{bs} {kv}", rows=rows)
