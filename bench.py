@@ -61,6 +61,45 @@ def stored_traffic(workload: str, launches_per_step: float):
     return d.get("hbm_bytes_per_launch")
 
 
+def summarize_counters(fetch_csv: str, write_csv: str, workload: str, out_path: str) -> dict:
+    """Turn two rocprofv3 --pmc runs of this bench (FETCH_SIZE, then
+    WRITE_SIZE, both with --copy-calibration-mib) into HBM bytes per
+    pa_decode call.  Each counter is scaled by the ratio of the bytes the
+    calibration copy (pa_copy_blocks) really moved to what the counter read
+    for it; the decode call's kernels are the balanced decode kernel and its
+    reduce kernel."""
+    import csv
+    import statistics
+
+    def per_kernel(path, counter):
+        acc = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]) * 1024.0)
+        return acc
+
+    f, w = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
+    copy_name = next(k for k in f if "copy_blocks_kernel" in k)
+    # The calibration copy reads and writes 256 MiB (K and V halves).
+    true_bytes = 256.0 * (1 << 20)
+    f_scale = true_bytes / statistics.mean(f[copy_name])
+    w_scale = true_bytes / statistics.mean(w[copy_name])
+    parts = {}
+    for tag in ("decode_balanced_kernel", "balanced_reduce_kernel"):
+        kf = next(k for k in f if tag in k)
+        kw = next(k for k in w if tag in k)
+        parts[tag] = {"fetch_bytes": statistics.median(f[kf]) * f_scale,
+                      "write_bytes": statistics.median(w[kw]) * w_scale}
+    total = sum(v["fetch_bytes"] + v["write_bytes"] for v in parts.values())
+    d = {"workload": workload, "source_digest": kernel_source_digest(),
+         "fetch_scale": f_scale, "write_scale": w_scale, "kernels": parts,
+         "hbm_bytes_per_launch": round(total)}
+    with open(out_path, "w") as fh:
+        json.dump(d, fh, indent=1)
+    return d
+
+
 def cpu_baseline(b, budget_s: float = 12.0):
     """Time the float64 CPU oracle (test infrastructure) on this workload:
     build its pool with its cache write, then run its decode over the
@@ -99,6 +138,163 @@ def cpu_baseline(b, budget_s: float = 12.0):
                   f"read) in {dt:.1f} s; host has {os.cpu_count()} logical cpus",
     }
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def _gpu_pools(b, dev, copies=1):
+    """K/V pools filled through pa_cache_write (plus extra copies on the GPU)."""
+    import torch
+
+    from paged_kv_cache_11_amd import binding as pa
+    from paged_kv_cache_11_amd import workloads as wl
+
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}[b.kv_dtype]
+    shape = (b.num_blocks, b.num_kv_heads, b.block_size, b.head_size)
+    k0 = torch.zeros(shape, dtype=tdt, device=dev)
+    v0 = torch.zeros(shape, dtype=tdt, device=dev)
+    chunk = 1 << 16
+    for a in range(0, len(b.slot_mapping), chunk):
+        pa.pa_cache_write(wl.storage_tensor(b.k[a:a + chunk], b.kv_src_dtype).to(dev),
+                          wl.storage_tensor(b.v[a:a + chunk], b.kv_src_dtype).to(dev), k0, v0,
+                          torch.from_numpy(b.slot_mapping[a:a + chunk]).to(dev), b.k_scale,
+                          b.v_scale)
+    return [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(copies - 1)]
+
+
+def _time_us(fn, iters, warmup=3):
+    """Average duration of fn(i) over iters calls, HIP events on the current stream."""
+    import torch
+
+    for i in range(warmup):
+        fn(i)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for i in range(iters):
+        fn(i)
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / iters * 1e3
+
+
+def row_measurements(dev, iters=20):
+    """Timings of the other rows of the hot path, one workload each."""
+    import torch
+
+    from paged_kv_cache_11_amd import binding as pa
+    from paged_kv_cache_11_amd import workloads as wl
+
+    rows = {}
+    # Long-context split-K: 8 x 32768 tokens, 512-token partitions + LSE reduce.
+    b = wl.long_context_decode()
+    sets = _gpu_pools(b, dev)
+    q = wl.storage_tensor(b.q, b.q_dtype).to(dev)
+    out = torch.empty_like(q)
+    tb, ln = torch.from_numpy(b.block_tables).to(dev), torch.from_numpy(b.seq_lens).to(dev)
+    for name, ps in (("long_context_splitk_512", 512), ("long_context_balanced", -1)):
+        ws = torch.empty(max(1, pa.pa_decode_workspace_size(b.num_seqs, b.num_heads, b.num_kv_heads,
+                                                            b.head_size, b.max_seq_len, ps)),
+                         dtype=torch.uint8, device=dev)
+        us = _time_us(lambda i: pa.pa_decode(out, q, sets[0][0], sets[0][1], tb, ln, b.max_seq_len,
+                                             b.scale, partition_size=ps, workspace=ws), iters)
+        by = b.decode_kv_bytes()
+        rows[name] = {"us": round(us, 2), "kv_bytes": by, "gbs": round(by / us / 1e3, 1),
+                      "pct_hbm_peak": round(100 * by / us / 1e3 / HBM_PEAK_GBS, 2),
+                      "tokens_per_s": round(b.num_seqs / us * 1e6, 1)}
+    del sets
+    torch.cuda.empty_cache()
+
+    # Shared prefix: 256 forks of a 2040-token prefix -> 256 copy-on-write
+    # block copies, then decode.
+    b = wl.shared_prefix_decode(prefix_len=2040)
+    sets = _gpu_pools(b, dev)
+    pairs = torch.from_numpy(b.copy_pairs).to(dev)
+    blk_bytes = 2 * b.num_kv_heads * b.block_size * b.head_size * 2
+    us = _time_us(lambda i: pa.pa_copy_blocks(sets[0][0], sets[0][1], pairs), iters)
+    rows["copy_blocks_cow_256"] = {"us": round(us, 2), "pairs": len(b.copy_pairs),
+                                   "bytes_read_written": 2 * len(b.copy_pairs) * blk_bytes,
+                                   "gbs": round(2 * len(b.copy_pairs) * blk_bytes / us / 1e3, 1)}
+    q = wl.storage_tensor(b.q, b.q_dtype).to(dev)
+    out = torch.empty_like(q)
+    tb, ln = torch.from_numpy(b.block_tables).to(dev), torch.from_numpy(b.seq_lens).to(dev)
+    ws = torch.empty(pa.pa_decode_workspace_size(b.num_seqs, b.num_heads, b.num_kv_heads,
+                                                 b.head_size, b.max_seq_len, -1),
+                     dtype=torch.uint8, device=dev)
+    us = _time_us(lambda i: pa.pa_decode(out, q, sets[0][0], sets[0][1], tb, ln, b.max_seq_len,
+                                         b.scale, partition_size=-1, workspace=ws), iters)
+    logical = b.decode_kv_bytes()
+    unique = (int(np.unique(b.block_tables[b.block_tables >= 0]).size) * b.block_size
+              * b.kv_bytes_per_token())
+    rows["shared_prefix_decode"] = {"us": round(us, 2), "logical_kv_bytes": logical,
+                                    "unique_kv_bytes": unique,
+                                    "effective_gbs_logical": round(logical / us / 1e3, 1),
+                                    "gbs_unique": round(unique / us / 1e3, 1),
+                                    "tokens_per_s": round(b.num_seqs / us * 1e6, 1)}
+    del sets
+    torch.cuda.empty_cache()
+
+    # Mixed fp8 step (70B shape): cache write of the step's new tokens,
+    # decode of 32 sequences, prefill of a 512-query chunk.
+    b = wl.mixed_fp8_step()
+    sets = _gpu_pools(b, dev, copies=2)
+    q = wl.storage_tensor(b.q, b.q_dtype).to(dev)
+    out = torch.empty_like(q)
+    tb, ln = torch.from_numpy(b.block_tables).to(dev), torch.from_numpy(b.seq_lens).to(dev)
+    ws = torch.empty(pa.pa_decode_workspace_size(b.num_seqs, b.num_heads, b.num_kv_heads,
+                                                 b.head_size, b.max_seq_len, -1),
+                     dtype=torch.uint8, device=dev)
+    ends = np.cumsum(b.seq_lens.astype(np.int64))
+    dec_new = ends - 1
+    chunk_idx = np.arange(int(ends[-1]) + 1536, int(ends[-1]) + 2048)
+    new_idx = np.concatenate([dec_new, chunk_idx])
+    k_new = wl.storage_tensor(b.k[new_idx], b.kv_src_dtype).to(dev)
+    v_new = wl.storage_tensor(b.v[new_idx], b.kv_src_dtype).to(dev)
+    s_new = torch.from_numpy(b.slot_mapping[new_idx]).to(dev)
+    cq = wl.storage_tensor(b.chunk_q, "bf16").to(dev)
+    cout = torch.empty_like(cq)
+    cqs = torch.from_numpy(b.chunk_query_start).to(dev)
+    ctb = torch.from_numpy(b.chunk_block_tables).to(dev)
+    cln = torch.from_numpy(b.chunk_seq_lens).to(dev)
+    nq = int(b.chunk_q.shape[0])
+
+    def cw(i):
+        kc, vc = sets[i % 2]
+        pa.pa_cache_write(k_new, v_new, kc, vc, s_new, b.k_scale, b.v_scale)
+
+    def dec(i):
+        kc, vc = sets[i % 2]
+        pa.pa_decode(out, q, kc, vc, tb, ln, b.max_seq_len, b.scale, b.k_scale, b.v_scale, -1, ws)
+
+    def pre(i):
+        kc, vc = sets[i % 2]
+        pa.pa_prefill_chunk(cout, cq, cqs, nq, kc, vc, ctb, cln, b.scale, b.k_scale, b.v_scale)
+
+    us_cw = _time_us(cw, iters)
+    n_new = len(new_idx)
+    cw_bytes = n_new * b.num_kv_heads * b.head_size * (2 * 2 + 2 * 1)  # bf16 in, fp8 out, K and V
+    rows["cache_write_fp8_mixed_step"] = {"us": round(us_cw, 2), "tokens": n_new,
+                                          "bytes_moved": cw_bytes,
+                                          "gbs": round(cw_bytes / us_cw / 1e3, 1)}
+    us_dec = _time_us(dec, iters)
+    by = b.decode_kv_bytes()
+    rows["decode_fp8_70b_shape"] = {"us": round(us_dec, 2), "kv_bytes": by,
+                                    "gbs": round(by / us_dec / 1e3, 1),
+                                    "pct_hbm_peak": round(100 * by / us_dec / 1e3 / HBM_PEAK_GBS, 2),
+                                    "tokens_per_s": round(b.num_seqs / us_dec * 1e6, 1)}
+    us_pre = _time_us(pre, iters)
+    L, n = int(b.chunk_seq_lens[0]), nq
+    pairs = sum(L - n + i + 1 for i in range(n))  # causal (query, key) pairs per head
+    flops = 4.0 * b.num_heads * b.head_size * pairs
+    rows["prefill_chunk_fp8_70b_shape"] = {
+        "us": round(us_pre, 2), "causal_flops": flops, "tflops": round(flops / us_pre / 1e6, 1),
+        "pct_mfma_bf16_peak": round(100 * flops / us_pre / 1e6 / MFMA_BF16_PEAK_TFLOPS, 2),
+        "queries_per_s": round(n / us_pre * 1e6, 1)}
+    us_step = _time_us(lambda i: (cw(i), dec(i), pre(i)), iters)
+    rows["mixed_step_fp8"] = {"us": round(us_step, 2),
+                              "step": "cache_write(544 tokens) + decode(32 seqs) + prefill(512 queries)"}
+    return rows
+
+
 
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
@@ -109,9 +305,18 @@ def main(argv=None):
     ap.add_argument("--partition-size", type=int, default=-1,
                     help="pa_decode partition_size: -1 balanced split (default), 0 none, or tokens")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--no-rows", action="store_true",
+                    help="skip the per-row measurements of the other workloads")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run pa_copy_blocks over this many MiB (counter calibration)")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/decode_kernel_<workload>_counters.json from two "
+                         "rocprofv3 --pmc counter_collection.csv files and exit")
     args = ap.parse_args(argv)
+    if args.summarize_counters:
+        outp = os.path.join(ROOT, "profiles", f"decode_kernel_{args.workload}_counters.json")
+        print(json.dumps(summarize_counters(*args.summarize_counters, args.workload, outp)))
+        return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the decode path "
               "shards by sequence or KV head with no exchange, so it is not run on several "
@@ -208,6 +413,11 @@ def main(argv=None):
         calib = {"copy_bytes_read": int(2 * nbk * k0[0].numel() * k0.element_size())}
 
     traffic = stored_traffic(b.name, 1)
+    rows = None
+    if not args.no_rows:
+        del sets
+        torch.cuda.empty_cache()
+        rows = row_measurements(dev)
     cpu = cpu_baseline(b, args.cpu_budget)
     tokens_per_s = b.num_seqs / (ms_per_step / 1e3)
     res = {
@@ -242,6 +452,8 @@ def main(argv=None):
         },
         "cpu_baseline": cpu,
     }
+    if rows:
+        res["rows"] = rows
     if calib:
         res["copy_calibration"] = calib
     print(json.dumps(res), flush=True)
