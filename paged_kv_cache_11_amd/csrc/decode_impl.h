@@ -11,29 +11,33 @@
 //     wavefronts that take the partition's blocks round-robin; all
 //     G = Hq/Hkv query heads of the group share every K/V byte read;
 //   * a (block, KV head) tile is contiguous in the pool, so a wavefront
-//     reads it with NLOAD fully coalesced 1 KiB loads (16 bytes per lane)
-//     straight into VGPRs, one tile ahead of the one being computed
-//     (ping-pong register buffers);
+//     reads it with NLOAD fully coalesced loads (16 bytes per lane, 8 for an
+//     fp8 cache, so a lane always holds 8 dims of a bf16/fp8 row) straight
+//     into VGPRs, one tile ahead of the one being computed (ping-pong
+//     register buffers);
 //   * one token row occupies LPR = 4, 8 or 16 lanes, i.e. sits inside a DPP
-//     row.  With 16-lane rows the G x NLOAD partial dot products of a lane
-//     are reduce-scattered over the row in 4 DPP steps, so every lane ends
-//     with whole scores (one per lane for G = 4) and the softmax runs once
-//     per score; probabilities return to the row with row_newbcast.  With
-//     shorter rows the partials are all-reduced instead;
+//     row.  A tile is processed in chunks of SUB loads; with 16-lane rows the
+//     G x SUB partial dot products of a lane (16 of them) are
+//     reduce-scattered over the row in 4 DPP steps, so every lane ends with
+//     one whole score per chunk and the softmax runs once per score;
+//     probabilities return to the row with row_newbcast.  With shorter rows
+//     the partials are all-reduced instead;
 //   * the softmax is online, in fp32, in the log2 domain (v_exp_f32); each
 //     token row keeps its own reference maximum per head and rescales its
 //     accumulators only when a score exceeds that reference by more than
 //     2^8 — exact, because the sum and the accumulators share the reference;
-//   * P·V for a bf16 cache pairs two tokens per v_dot2_f32_bf16 (P rounded
-//     to bf16, accumulation in fp32); f32 and fp8 caches use fp32 FMAs;
+//   * fp8 codes are widened exactly to bf16 (v_cvt_scalef32_pk_bf16_fp8,
+//     scale 1; the per-tensor scales are applied to q·k and to the output),
+//     so bf16 and fp8 caches share one datapath: q·k by v_dot2_f32_bf16
+//     against the packed bf16 query, P·V pairing two tokens per
+//     v_dot2_f32_bf16 (P rounded to bf16, accumulation in fp32); an f32
+//     cache uses fp32 FMAs;
 //   * rows, then wavefronts (through LDS), are merged once per partition;
 //     with several partitions a second kernel merges their
 //     (max, sum, normalised output) triples with log-sum-exp weights.
 #pragma once
 
 #include <utility>
-
-
 
 #include "pa_internal.h"
 
@@ -43,19 +47,34 @@ constexpr int kMaxDecodeWaves = 4;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleSlack = 8.0f;  // log2 units a score may exceed the reference by
 
+// Bytes each lane loads per wavefront load: 16 (one dwordx4), except fp8
+// caches, whose lanes take 8 bytes so a lane always holds 8 dims of a token
+// row (the query and accumulator registers for a GQA group of 8 stay small).
+template <typename KV> struct LaneBytes { static constexpr int value = 16; };
+template <> struct LaneBytes<FP8> { static constexpr int value = 8; };
+
 template <typename KV, int D, int BS, int G>
 struct Geom {
   static constexpr int EB = Elem<KV>::bytes;
-  static constexpr int EPL = 16 / EB;        // elements per lane per load
-  static constexpr int LPR = D / EPL;        // lanes per token row
-  static constexpr int RPL = kWave / LPR;    // token rows per wavefront load
-  static constexpr int NLOAD = BS / RPL;     // loads per (block, head) tile
-  static constexpr int N = NLOAD * G;        // partial scores per lane (index i*G + h)
+  static constexpr int LB = LaneBytes<KV>::value;  // bytes per lane per load
+  static constexpr int LW = LB / 4;                // dwords per lane per load
+  static constexpr int EPL = LB / EB;              // elements per lane per load
+  static constexpr int LPR = D / EPL;              // lanes per token row
+  static constexpr int RPL = kWave / LPR;          // token rows per wavefront load
+  static constexpr int NLOAD = BS / RPL;           // loads per (block, head) tile
+  // Loads handled together: enough for 16 partial scores per lane when a
+  // token row fills a DPP row (then reduce-scattered to one score per lane
+  // per 16), else the whole tile (all-reduced).
+  static constexpr int SUB0 = LPR == 16 ? (16 / G > 2 ? 16 / G : 2) : NLOAD;
+  static constexpr int SUB = SUB0 < NLOAD ? SUB0 : NLOAD;
+  static constexpr int NCHUNK = NLOAD / SUB;
+  static constexpr int N = SUB * G;                // partial scores per lane per chunk
   static constexpr bool kScatter = LPR == 16 && N % 16 == 0;
-  static constexpr int NV = kScatter ? N / 16 : N;  // whole scores per lane
-  static constexpr int64_t TILE_VECS = (int64_t)BS * D * EB / 16;
+  static constexpr int NV = kScatter ? N / 16 : N;  // whole scores per lane per chunk
+  static constexpr int64_t TILE_BYTES = (int64_t)BS * D * EB;
   static_assert(LPR == 4 || LPR == 8 || LPR == 16, "a token row must fit a DPP row");
   static_assert(NLOAD >= 1 && BS % RPL == 0, "a tile must be whole wavefront loads");
+  static_assert(NLOAD % SUB == 0, "chunks must tile the loads");
 };
 
 template <int... Is, typename F>
@@ -121,11 +140,14 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
 }
 
-// Query registers of one lane: its EPL dims of each of the G heads.
-// bf16 cache: kept packed for v_dot2_f32_bf16; otherwise widened to fp32.
+// Query registers of one lane: its EPL dims of each of the G heads.  With a
+// bf16 or fp8 cache the bf16 query stays packed for v_dot2_f32_bf16 (the
+// cache words are widened to bf16 first); with an f32 cache it is fp32.
 template <typename KV, typename QT, int G, int EPL>
 struct QRegs {
-  static constexpr bool kPacked = std::is_same<KV, BF16>::value && std::is_same<QT, BF16>::value;
+  static constexpr bool kPacked = !std::is_same<KV, F32>::value;
+  static_assert(!kPacked || (EPL == 8 && std::is_same<QT, BF16>::value),
+                "packed queries are 8 bf16 per lane");
   uint32_t w[kPacked ? G : 1][4];
   float f[kPacked ? 1 : G][kPacked ? 1 : EPL];
 
@@ -136,37 +158,46 @@ struct QRegs {
       if constexpr (kPacked) {
         const u32x4 v = *(const u32x4*)((const uint16_t*)query + e0);
         w[h][0] = v.x; w[h][1] = v.y; w[h][2] = v.z; w[h][3] = v.w;
-      } else if constexpr (std::is_same<QT, F32>::value) {
-        static_assert(EPL == 4, "f32 queries pair with an f32 cache");
+      } else {
+        static_assert(std::is_same<QT, F32>::value && EPL == 4, "f32 cache, f32 queries");
         const u32x4 v = *(const u32x4*)((const float*)query + e0);
         Vec<F32>::to_f32(v, f[h]);
-      } else {  // bf16 query, widened
-#pragma unroll
-        for (int j = 0; j < EPL / 8; ++j) {
-          const u32x4 v = *(const u32x4*)((const uint16_t*)query + e0 + 8 * j);
-          Vec<BF16>::to_f32(v, f[h] + 8 * j);
-        }
       }
     }
   }
 
-  // Partial q·k over this lane's EPL dims for head h; kf holds the widened
-  // key (unused on the packed path).
-  __device__ __forceinline__ float dot(int h, const u32x4& k, const float* kf) const {
+  // Partial q·k over this lane's EPL dims for head h: kw holds the key as 4
+  // packed bf16 dwords (packed path) or its 4 fp32 values' bits.
+  __device__ __forceinline__ float dot(int h, const uint32_t (&kw)[4]) const {
     if constexpr (kPacked) {
-      float a = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(k.x), as_bf16x2(w[h][0]), 0.f, false);
-      a = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(k.y), as_bf16x2(w[h][1]), a, false);
-      a = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(k.z), as_bf16x2(w[h][2]), a, false);
-      a = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(k.w), as_bf16x2(w[h][3]), a, false);
+      float a = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(kw[0]), as_bf16x2(w[h][0]), 0.f, false);
+      a = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(kw[1]), as_bf16x2(w[h][1]), a, false);
+      a = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(kw[2]), as_bf16x2(w[h][2]), a, false);
+      a = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(kw[3]), as_bf16x2(w[h][3]), a, false);
       return a;
     } else {
       float a = 0.f;
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) a = __builtin_fmaf(f[h][e], kf[e], a);
+      for (int e = 0; e < 4; ++e) a = __builtin_fmaf(f[h][e], u2f(kw[e]), a);
       return a;
     }
   }
 };
+
+// One lane's load of a cache tile as 4 dwords of the form the math uses:
+// bf16 words as stored; fp8 codes widened exactly to 8 bf16 (gfx950's scaled
+// convert with scale 1); f32 words as stored.
+template <typename KV>
+__device__ __forceinline__ void widen(const uint32_t* src, uint32_t (&o)[4]) {
+  if constexpr (std::is_same<KV, FP8>::value) {
+    o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(src[0], 1.0f, false));
+    o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(src[0], 1.0f, true));
+    o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(src[1], 1.0f, false));
+    o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(src[1], 1.0f, true));
+  } else {
+    o[0] = src[0]; o[1] = src[1]; o[2] = src[2]; o[3] = src[3];
+  }
+}
 
 template <typename OT>
 __device__ __forceinline__ void store_out(void* out, int64_t idx, float v) {
@@ -181,6 +212,7 @@ template <typename KV, typename QT, int D, int BS, int G>
 struct WaveAttn {
   using GM = Geom<KV, D, BS, G>;
   static constexpr int EPL = GM::EPL, LPR = GM::LPR, RPL = GM::RPL, NLOAD = GM::NLOAD;
+  static constexpr int LW = GM::LW, SUB = GM::SUB, NCHUNK = GM::NCHUNK;
   static constexpr int N = GM::N, NV = GM::NV;
   static constexpr bool kScatter = GM::kScatter;
 
@@ -215,18 +247,17 @@ struct WaveAttn {
     for (int h = 0; h < (kScatter ? 1 : G); ++h) l_row[h] = 0.f;
   }
 
-  // P·V for one tile: pb[i*G + h] is the probability of token row i, head h.
-  __device__ __forceinline__ void accumulate_pv(const float (&pb)[N], const u32x4 (&vt)[NLOAD]) {
-    if constexpr (std::is_same<KV, BF16>::value) {
+  // P·V for one chunk: pb[i*G + h] is the probability of the chunk's token
+  // row i, head h; vw[i] the widened V words of that row.
+  __device__ __forceinline__ void accumulate_pv(const float (&pb)[N], const uint32_t (&vw)[SUB][4]) {
+    if constexpr (!std::is_same<KV, F32>::value) {
 #pragma unroll
-      for (int k = 0; k < NLOAD / 2; ++k) {
-        const u32x4 va = vt[2 * k], vb = vt[2 * k + 1];
-        const uint32_t wa[4] = {va.x, va.y, va.z, va.w}, wb[4] = {vb.x, vb.y, vb.z, vb.w};
+      for (int k = 0; k < SUB / 2; ++k) {
         uint32_t vp[8];
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
-          vp[2 * d] = __builtin_amdgcn_perm(wb[d], wa[d], 0x05040100u);      // low halves
-          vp[2 * d + 1] = __builtin_amdgcn_perm(wb[d], wa[d], 0x07060302u);  // high halves
+          vp[2 * d] = __builtin_amdgcn_perm(vw[2 * k + 1][d], vw[2 * k][d], 0x05040100u);      // low halves
+          vp[2 * d + 1] = __builtin_amdgcn_perm(vw[2 * k + 1][d], vw[2 * k][d], 0x07060302u);  // high halves
         }
 #pragma unroll
         for (int h = 0; h < G; ++h) {
@@ -238,41 +269,37 @@ struct WaveAttn {
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < NLOAD; ++i) {
-        float vf[EPL];
-        Vec<KV>::to_f32(vt[i], vf);
+      for (int i = 0; i < SUB; ++i)
 #pragma unroll
         for (int h = 0; h < G; ++h)
 #pragma unroll
-          for (int e = 0; e < EPL; ++e) acc[h][e] = __builtin_fmaf(pb[i * G + h], vf[e], acc[h][e]);
-      }
+          for (int e = 0; e < EPL; ++e) acc[h][e] = __builtin_fmaf(pb[i * G + h], u2f(vw[i][e]), acc[h][e]);
     }
   }
 
-  // One (block, KV head) tile: scores, online softmax, P·V.  kMasked: the
-  // sequence's last block, whose slots at or past L are padding.
+  // One chunk of a (block, KV head) tile: loads c*SUB .. c*SUB+SUB-1.
   template <bool kMasked>
-  __device__ __forceinline__ void block(const u32x4 (&kt)[NLOAD], u32x4 (&vt)[NLOAD], int blk,
-                                        int L) {
+  __device__ __forceinline__ void chunk(const uint32_t (&kt)[NLOAD][LW], const uint32_t (&vt)[NLOAD][LW],
+                                        int c, int blk, int L) {
     float v[N];
 #pragma unroll
-    for (int i = 0; i < NLOAD; ++i) {
-      float kf[std::is_same<KV, BF16>::value ? 1 : EPL];
-      if constexpr (!std::is_same<KV, BF16>::value) Vec<KV>::to_f32(kt[i], kf);
+    for (int i = 0; i < SUB; ++i) {
+      uint32_t kw[4];
+      widen<KV>(kt[c * SUB + i], kw);
 #pragma unroll
-      for (int h = 0; h < G; ++h) v[i * G + h] = q.dot(h, kt[i], kf);
+      for (int h = 0; h < G; ++h) v[i * G + h] = q.dot(h, kw);
     }
+    auto tok = [&](int i) { return blk * BS + row + (c * SUB + i) * RPL; };
     float pb[N];
     if constexpr (kScatter) {
       float r[NV];
       reduce_scatter16<N>(v, r, lane);
-      const int c = rev4(lane & 15);
+      const int cl = rev4(lane & 15);
 #pragma unroll
       for (int j = 0; j < NV; ++j) {
         r[j] *= qk_scale_log2;
         if constexpr (kMasked) {
-          const int i = (16 * j + c) / G;
-          if (blk * BS + row + i * RPL >= L) r[j] = -INFINITY;
+          if (tok((16 * j + cl) / G) >= L) r[j] = -INFINITY;
         }
       }
       bool ex = false;
@@ -312,7 +339,7 @@ struct WaveAttn {
       for (int n = 0; n < N; ++n) {
         v[n] = group_sum<LPR>(v[n]) * qk_scale_log2;
         if constexpr (kMasked) {
-          if (blk * BS + row + (n / G) * RPL >= L) v[n] = -INFINITY;
+          if (tok(n / G) >= L) v[n] = -INFINITY;
         }
       }
       bool ex = false;
@@ -323,7 +350,7 @@ struct WaveAttn {
         for (int h = 0; h < G; ++h) {
           float rm = v[h];
 #pragma unroll
-          for (int i = 1; i < NLOAD; ++i) rm = fmaxf(rm, v[i * G + h]);
+          for (int i = 1; i < SUB; ++i) rm = fmaxf(rm, v[i * G + h]);
           const float mn = fmaxf(m_ref[h], rm);
           const float alpha = mn == -INFINITY ? 1.f : fast_exp2(m_ref[h] - mn);
           m_ref[h] = mn;
@@ -340,15 +367,26 @@ struct WaveAttn {
         l_row[n % G] += p;
       }
     }
-    if constexpr (kMasked) {  // padding slots of the last block may hold anything
+    uint32_t vw[SUB][4];
 #pragma unroll
-      for (int i = 0; i < NLOAD; ++i) {
-        const bool valid = blk * BS + row + i * RPL < L;
-        vt[i].x = valid ? vt[i].x : 0u; vt[i].y = valid ? vt[i].y : 0u;
-        vt[i].z = valid ? vt[i].z : 0u; vt[i].w = valid ? vt[i].w : 0u;
+    for (int i = 0; i < SUB; ++i) {
+      widen<KV>(vt[c * SUB + i], vw[i]);
+      if constexpr (kMasked) {  // padding slots of the last block may hold anything
+        const bool valid = tok(i) < L;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) vw[i][d] = valid ? vw[i][d] : 0u;
       }
     }
-    accumulate_pv(pb, vt);
+    accumulate_pv(pb, vw);
+  }
+
+  // One (block, KV head) tile, chunk by chunk.  kMasked: the sequence's
+  // last block, whose slots at or past L are padding.
+  template <bool kMasked>
+  __device__ __forceinline__ void block(const uint32_t (&kt)[NLOAD][LW], const uint32_t (&vt)[NLOAD][LW],
+                                        int blk, int L) {
+#pragma unroll
+    for (int c = 0; c < NCHUNK; ++c) chunk<kMasked>(kt, vt, c, blk, L);
   }
 
   // Streams blocks first, first+stride, ... (count of them) of a sequence of
@@ -362,9 +400,9 @@ struct WaveAttn {
     const int nblk = (L + BS - 1) / BS;
     const bool last_partial = (L % BS) != 0 && first + stride * (count - 1) == nblk - 1;
     const int nfull = count - (last_partial ? 1 : 0);
-    const int64_t block_vecs = (int64_t)num_kv_heads * GM::TILE_VECS;
-    const u32x4* kbase = (const u32x4*)k_cache + (int64_t)g * GM::TILE_VECS + lane;
-    const u32x4* vbase = (const u32x4*)v_cache + (int64_t)g * GM::TILE_VECS + lane;
+    const int64_t block_bytes = (int64_t)num_kv_heads * GM::TILE_BYTES;
+    const uint8_t* kbase = (const uint8_t*)k_cache + (int64_t)g * GM::TILE_BYTES + lane * GM::LB;
+    const uint8_t* vbase = (const uint8_t*)v_cache + (int64_t)g * GM::TILE_BYTES + lane * GM::LB;
     // Block ids of the run, 64 at a time, one per lane.
     int bid_v = 0;
     auto block_id = [&](int j) -> int {
@@ -374,17 +412,33 @@ struct WaveAttn {
       }
       return __builtin_amdgcn_readlane(bid_v, j & (kWave - 1));
     };
-    auto load_tile = [&](int bid, u32x4 (&kt)[NLOAD], u32x4 (&vt)[NLOAD]) {
-      const u32x4* kp = kbase + (int64_t)bid * block_vecs;
-      const u32x4* vp = vbase + (int64_t)bid * block_vecs;
+    auto load_tile = [&](int bid, uint32_t (&kt)[NLOAD][LW], uint32_t (&vt)[NLOAD][LW]) {
+      const uint8_t* kp = kbase + (int64_t)bid * block_bytes;
+      const uint8_t* vp = vbase + (int64_t)bid * block_bytes;
 #pragma unroll
-      for (int i = 0; i < NLOAD; ++i) kt[i] = kp[i * kWave];
+      for (int i = 0; i < NLOAD; ++i) {
+        if constexpr (LW == 4) {
+          const u32x4 x = *(const u32x4*)(kp + i * kWave * GM::LB);
+          kt[i][0] = x.x; kt[i][1] = x.y; kt[i][2] = x.z; kt[i][3] = x.w;
+        } else {
+          const u32x2 x = *(const u32x2*)(kp + i * kWave * GM::LB);
+          kt[i][0] = x.x; kt[i][1] = x.y;
+        }
+      }
 #pragma unroll
-      for (int i = 0; i < NLOAD; ++i) vt[i] = vp[i * kWave];
+      for (int i = 0; i < NLOAD; ++i) {
+        if constexpr (LW == 4) {
+          const u32x4 x = *(const u32x4*)(vp + i * kWave * GM::LB);
+          vt[i][0] = x.x; vt[i][1] = x.y; vt[i][2] = x.z; vt[i][3] = x.w;
+        } else {
+          const u32x2 x = *(const u32x2*)(vp + i * kWave * GM::LB);
+          vt[i][0] = x.x; vt[i][1] = x.y;
+        }
+      }
     };
     auto blk_of = [&](int j) { return first + stride * j; };
     if (nfull > 0) {
-      u32x4 ka[NLOAD], va[NLOAD], kb[NLOAD], vb[NLOAD];
+      uint32_t ka[NLOAD][LW], va[NLOAD][LW], kb[NLOAD][LW], vb[NLOAD][LW];
       load_tile(block_id(0), ka, va);
       int j = 0;
       for (; j + 2 < nfull; j += 2) {
@@ -402,7 +456,7 @@ struct WaveAttn {
       }
     }
     if (last_partial) {
-      u32x4 kt[NLOAD], vt[NLOAD];
+      uint32_t kt[NLOAD][LW], vt[NLOAD][LW];
       load_tile(block_id(count - 1), kt, vt);
       block<true>(kt, vt, blk_of(count - 1), L);
     }

@@ -3,8 +3,8 @@
 // wavefront reductions through DPP, and the fp8 / bf16 conversions.
 //
 // Written for CDNA4 (gfx950, wave64).  The DPP row is 16 lanes; one token
-// row of a K/V tile (head_size elements) spans 4, 8 or 16 lanes at 16 bytes
-// per lane, so its dot products reduce inside a DPP row.
+// row of a K/V tile (head_size elements) spans 4, 8 or 16 lanes (16 bytes
+// per lane, 8 for fp8), so its dot products reduce inside a DPP row.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -13,6 +13,7 @@
 namespace pa {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
