@@ -11,72 +11,75 @@
 // Shape of the work on gfx950:
 //   * a workgroup takes 128 rows = (query, head) pairs of one KV head group
 //     (128/G queries x G heads, so the G heads share every K/V tile) and
-//     walks the keys 32 at a time; its 4 wavefronts own 32 rows each;
-//   * the 32-key K tile and the transposed V tile are staged in LDS as
+//     walks the keys 64 at a time; its 8 wavefronts are 4 row groups of 32
+//     rows times 2 key halves: wavefront (r, h) computes rows 32r..32r+31
+//     against keys 32h..32h+31 of every 64-key step, so two wavefronts per
+//     SIMD interleave their matrix and softmax work, and the two halves'
+//     states are merged through LDS at the end;
+//   * the 64-key K tile and the transposed V tile are staged in LDS as
 //     bf16 (fp8 E4M3 widens to bf16 exactly; the per-tensor scales are
 //     applied in fp32, k_scale inside the score scale, v_scale on the
-//     output); the next tile's global loads are in flight while the current
+//     output); the next step's global loads are in flight while the current
 //     one is computed;
 //   * scores are computed transposed, S^T = K · Q^T, with
-//     v_mfma_f32_32x32x16_bf16 (8 per tile), so each lane holds 16 keys of
-//     one query row: the row maximum needs one cross-lane step and the
-//     probabilities are already in the B-operand layout of O^T = V^T · P^T
-//     (8 more MFMAs), with the keys taken in a consistent permuted order;
+//     v_mfma_f32_32x32x16_bf16 (8 per 32-key tile), so each lane holds 16
+//     keys of one query row: the row maximum needs one cross-lane step and
+//     the probabilities are already in the B-operand layout of
+//     O^T = V^T · P^T (8 more MFMAs), with the keys taken in a consistent
+//     permuted order;
 //   * online softmax in fp32 in the log2 domain, rescaling the accumulators
 //     only when a score exceeds the running reference by 2^8;
-//   * tiles that cross the diagonal are masked per element (key > position).
+//   * tiles that cross the diagonal are masked per element (key > position);
+//     tiles past every row of a wavefront are skipped.
 #include "pa_internal.h"
 
 namespace pa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kPD = 128;         // head size
-constexpr int kKB = 32;          // keys per tile
-constexpr int kRows = 128;       // rows per workgroup
-constexpr int kPWaves = 4;
-constexpr int kKStride = kPD + 8;   // LDS row stride of K (bf16 elements)
-constexpr int kVStride = kKB + 4;   // LDS row stride of V^T (bf16 elements)
+constexpr int kPD = 128;             // head size
+constexpr int kKB = 32;              // keys per wavefront tile
+constexpr int kStep = 2 * kKB;       // keys staged per step
+constexpr int kRows = 128;           // rows per workgroup
+constexpr int kRowGroups = kRows / 32;
+constexpr int kPWaves = 2 * kRowGroups;
+constexpr int kPThreads = kPWaves * kWave;
+constexpr int kKStride = kPD + 8;    // LDS row stride of K (bf16 elements)
+constexpr int kVStride = kStep + 4;  // LDS row stride of V^T (bf16 elements)
 constexpr float kPLog2e = 1.4426950408889634f;
 constexpr float kPSlack = 8.0f;
+static_assert(kPThreads / 8 == kStep && kPThreads / 16 * 2 == kStep,
+              "the staging maps cover one step exactly");
 
 __device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
 }
 
-// 16 bytes of the cache -> bf16 words.  bf16: 8 elements (1 vector); fp8: 16
-// elements from one vector, returned as 8 packed dwords.
-template <typename KV> struct Stage;
-template <> struct Stage<BF16> {
-  static constexpr int kVecPerRow16 = 2;  // 16 elements = 2 vectors
-};
-template <> struct Stage<FP8> {
-  static constexpr int kVecPerRow16 = 1;
-};
-
 __device__ __forceinline__ void fp8x4_to_bf16x2x2(uint32_t w, uint32_t& lo, uint32_t& hi) {
-  const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
-  const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
-  lo = pk_bf16(a[0], a[1]);  // exact: every E4M3 value is a bf16 value
-  hi = pk_bf16(b[0], b[1]);
+  // Exact: every E4M3 value is a bf16 value (scale 1).
+  lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+  hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
 }
 
 template <typename KV, int BS, int G>
-__global__ __launch_bounds__(kPWaves * kWave) void prefill_kernel(
+__global__ __launch_bounds__(kPThreads) void prefill_kernel(
     void* __restrict__ out, const void* __restrict__ query,
     const int32_t* __restrict__ query_start_loc, const void* __restrict__ k_cache,
     const void* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
     int max_blocks_per_seq, const int32_t* __restrict__ seq_lens, int num_kv_heads,
-    float qk_scale_log2, float v_scale) {
+    float qk_scale_log2, bool negate_q, float v_scale) {
   constexpr int EB = Elem<KV>::bytes;
   static_assert(kRows % G == 0, "rows hold whole queries");
-  __shared__ __attribute__((aligned(16))) __bf16 k_lds[kKB * kKStride];
+  __shared__ __attribute__((aligned(16))) __bf16 k_lds[kStep * kKStride];
   __shared__ __attribute__((aligned(16))) __bf16 vt_lds[kPD * kVStride];
+  // Merge area: the second key half's accumulators, maxima and sums.
+  __shared__ float mo_lds[kRowGroups][kPD / 2][kWave];
+  __shared__ float mm_lds[kRowGroups][kWave], ml_lds[kRowGroups][kWave];
 
   const int tile = blockIdx.x, g = blockIdx.y, c = blockIdx.z;
   const int t = threadIdx.x, lane = t & (kWave - 1), w = t / kWave;
+  const int rg = w % kRowGroups, kh = w / kRowGroups;
   const int half = lane / 32;
   const int qs = query_start_loc[c], n = query_start_loc[c + 1] - qs;
   const int L = seq_lens[c];
@@ -84,17 +87,19 @@ __global__ __launch_bounds__(kPWaves * kWave) void prefill_kernel(
   const int q_first = tile * kRows / G;
   const int q_last = min(q_first + kRows / G, n) - 1;
   const int min_pos = L - n + q_first, max_pos = L - n + q_last;
-  const int nkb = (max_pos + kKB) / kKB;
+  const int nsteps = (max_pos + kStep) / kStep;
   const int nblk = (L + BS - 1) / BS;
   const int num_heads = num_kv_heads * G;
   const int32_t* tbl = block_tables + (int64_t)c * max_blocks_per_seq;
 
   // This lane's row: query qi, head hq.
-  const int row = 32 * w + (lane & 31);
+  const int row = 32 * rg + (lane & 31);
   const int qi = q_first + row / G;
   const int hq = g * G + row % G;
   const bool row_ok = qi < n;
   const int pos = L - n + qi;
+  // Last position among this wavefront's rows: later tiles are all masked.
+  const int wave_max_pos = L - n + min(q_first + (32 * rg + 31) / G, q_last);
 
   // Q^T operand: k-step s holds dims 16 s + 8 half .. +8 of the row.
   bf16x8 qreg[kPD / 16];
@@ -104,6 +109,7 @@ __global__ __launch_bounds__(kPWaves * kWave) void prefill_kernel(
     for (int s = 0; s < kPD / 16; ++s) {
       u32x4 v = {0u, 0u, 0u, 0u};
       if (row_ok) v = *(const u32x4*)(qrow + 16 * s + 8 * half);
+      if (negate_q) v ^= 0x80008000u;  // exact: -(q·k) = (-q)·k
       qreg[s] = __builtin_bit_cast(bf16x8, v);
     }
   }
@@ -116,94 +122,94 @@ __global__ __launch_bounds__(kPWaves * kWave) void prefill_kernel(
   float m_ref = -INFINITY, l_part = 0.f;
 
   // Staging: K — thread t covers key t/8, dims 16 (t%8) .. +16;
-  //          V — thread t covers keys 2 (t/16) and +1, dims 8 (t%16) .. +8.
+  //          V — thread t covers keys 2 (t/16) and +1, dims 8 (t%16) .. +8
+  //          (one block: keys come in even pairs and blocks are even).
+  // Each step's loads are issued two steps ahead (two register stages), and
+  // the block-table entries they need one step before that.
   const int kk = t / 8, kd = (t % 8) * 16;
   const int vk = 2 * (t / 16), vd = (t % 16) * 8;
   constexpr int KVEC = 16 * EB / 16;  // 16-byte vectors per 16 K elements
   constexpr int VW = 8 * EB / 4;      // dwords per 8 V elements
-  u32x4 kst[KVEC];
-  uint32_t vst[2][VW];
+  struct Stage {
+    u32x4 k[KVEC];
+    uint32_t v[2][VW];
+  };
   const int64_t head_off = (int64_t)g * BS * kPD;  // element offset of head g in a block
   const int64_t block_elems = (int64_t)num_kv_heads * BS * kPD;
 
-  auto load_stage = [&](int kb) {
-    const int key = kb * kKB + kk;
-    const int j = key / BS;
+  // Physical blocks of this thread's K key and V key pair in a step; -1 past L.
+  auto block_ids = [&](int step, int& kid, int& vid) {
+    const int key = step * kStep + kk, key2 = step * kStep + vk;
+    kid = key < L ? tbl[key / BS] : -1;
+    vid = key2 < L ? tbl[key2 / BS] : -1;
+  };
+  auto load_stage = [&](int step, int kid, int vid, Stage& S) {
 #pragma unroll
-    for (int v = 0; v < KVEC; ++v) kst[v] = u32x4{0u, 0u, 0u, 0u};
-    if (key < L && j < nblk) {
-      const int64_t e0 = (int64_t)tbl[j] * block_elems + head_off + (int64_t)(key % BS) * kPD + kd;
+    for (int v = 0; v < KVEC; ++v) S.k[v] = u32x4{0u, 0u, 0u, 0u};
+    if (kid >= 0) {
+      const int key = step * kStep + kk;
+      const int64_t e0 = (int64_t)kid * block_elems + head_off + (int64_t)(key % BS) * kPD + kd;
       const u32x4* p = (const u32x4*)((const uint8_t*)k_cache + e0 * EB);
 #pragma unroll
-      for (int v = 0; v < KVEC; ++v) kst[v] = p[v];
+      for (int v = 0; v < KVEC; ++v) S.k[v] = p[v];
     }
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
-      const int key2 = kb * kKB + vk + r;
-      const int j2 = key2 / BS;
+      const int key2 = step * kStep + vk + r;
 #pragma unroll
-      for (int x = 0; x < VW; ++x) vst[r][x] = 0u;
-      if (key2 < L && j2 < nblk) {
-        const int64_t e0 =
-            (int64_t)tbl[j2] * block_elems + head_off + (int64_t)(key2 % BS) * kPD + vd;
+      for (int x = 0; x < VW; ++x) S.v[r][x] = 0u;
+      if (vid >= 0 && key2 < L) {
+        const int64_t e0 = (int64_t)vid * block_elems + head_off + (int64_t)(key2 % BS) * kPD + vd;
         const uint32_t* p = (const uint32_t*)((const uint8_t*)v_cache + e0 * EB);
         if constexpr (VW == 4) {
           const u32x4 x4 = *(const u32x4*)p;
-          vst[r][0] = x4.x; vst[r][1] = x4.y; vst[r][2] = x4.z; vst[r][3] = x4.w;
+          S.v[r][0] = x4.x; S.v[r][1] = x4.y; S.v[r][2] = x4.z; S.v[r][3] = x4.w;
         } else {
           const u32x2 x2 = *(const u32x2*)p;
-          vst[r][0] = x2.x; vst[r][1] = x2.y;
+          S.v[r][0] = x2.x; S.v[r][1] = x2.y;
         }
       }
     }
   };
-  auto store_stage = [&]() {
+  auto store_stage = [&](const Stage& S) {
     // K row: 16 bf16 at k_lds[kk][kd..].
     uint32_t kw[8];
     if constexpr (std::is_same<KV, BF16>::value) {
-      kw[0] = kst[0].x; kw[1] = kst[0].y; kw[2] = kst[0].z; kw[3] = kst[0].w;
-      kw[4] = kst[1].x; kw[5] = kst[1].y; kw[6] = kst[1].z; kw[7] = kst[1].w;
+      kw[0] = S.k[0].x; kw[1] = S.k[0].y; kw[2] = S.k[0].z; kw[3] = S.k[0].w;
+      kw[4] = S.k[1].x; kw[5] = S.k[1].y; kw[6] = S.k[1].z; kw[7] = S.k[1].w;
     } else {
-      fp8x4_to_bf16x2x2(kst[0].x, kw[0], kw[1]);
-      fp8x4_to_bf16x2x2(kst[0].y, kw[2], kw[3]);
-      fp8x4_to_bf16x2x2(kst[0].z, kw[4], kw[5]);
-      fp8x4_to_bf16x2x2(kst[0].w, kw[6], kw[7]);
+      fp8x4_to_bf16x2x2(S.k[0].x, kw[0], kw[1]);
+      fp8x4_to_bf16x2x2(S.k[0].y, kw[2], kw[3]);
+      fp8x4_to_bf16x2x2(S.k[0].z, kw[4], kw[5]);
+      fp8x4_to_bf16x2x2(S.k[0].w, kw[6], kw[7]);
     }
     u32x4* kdst = (u32x4*)(k_lds + kk * kKStride + kd);
     kdst[0] = u32x4{kw[0], kw[1], kw[2], kw[3]};
     kdst[1] = u32x4{kw[4], kw[5], kw[6], kw[7]};
     // V^T: dims vd..vd+7, keys vk and vk+1 packed as one dword per dim.
-    uint16_t va[8], vb[8];
+    uint32_t va[4], vb[4];  // bf16 pairs (dims 2x, 2x+1) of keys vk and vk+1
     if constexpr (std::is_same<KV, BF16>::value) {
 #pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        va[2 * x] = (uint16_t)(vst[0][x] & 0xFFFFu); va[2 * x + 1] = (uint16_t)(vst[0][x] >> 16);
-        vb[2 * x] = (uint16_t)(vst[1][x] & 0xFFFFu); vb[2 * x + 1] = (uint16_t)(vst[1][x] >> 16);
-      }
+      for (int x = 0; x < 4; ++x) { va[x] = S.v[0][x]; vb[x] = S.v[1][x]; }
     } else {
 #pragma unroll
       for (int x = 0; x < 2; ++x) {
-        uint32_t lo, hi;
-        fp8x4_to_bf16x2x2(vst[0][x], lo, hi);
-        va[4 * x] = (uint16_t)(lo & 0xFFFFu); va[4 * x + 1] = (uint16_t)(lo >> 16);
-        va[4 * x + 2] = (uint16_t)(hi & 0xFFFFu); va[4 * x + 3] = (uint16_t)(hi >> 16);
-        fp8x4_to_bf16x2x2(vst[1][x], lo, hi);
-        vb[4 * x] = (uint16_t)(lo & 0xFFFFu); vb[4 * x + 1] = (uint16_t)(lo >> 16);
-        vb[4 * x + 2] = (uint16_t)(hi & 0xFFFFu); vb[4 * x + 3] = (uint16_t)(hi >> 16);
+        fp8x4_to_bf16x2x2(S.v[0][x], va[2 * x], va[2 * x + 1]);
+        fp8x4_to_bf16x2x2(S.v[1][x], vb[2 * x], vb[2 * x + 1]);
       }
     }
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      *(uint32_t*)(vt_lds + (vd + e) * kVStride + vk) = (uint32_t)va[e] | ((uint32_t)vb[e] << 16);
+    for (int x = 0; x < 4; ++x) {
+      // dim 2x: low halves of both keys; dim 2x+1: high halves.
+      *(uint32_t*)(vt_lds + (vd + 2 * x) * kVStride + vk) = __builtin_amdgcn_perm(vb[x], va[x], 0x05040100u);
+      *(uint32_t*)(vt_lds + (vd + 2 * x + 1) * kVStride + vk) = __builtin_amdgcn_perm(vb[x], va[x], 0x07060302u);
+    }
   };
 
-  load_stage(0);
-  for (int kb = 0; kb < nkb; ++kb) {
-    __syncthreads();  // every wavefront is done with the previous tile
-    store_stage();
-    __syncthreads();
-    if (kb + 1 < nkb) load_stage(kb + 1);  // in flight during this tile's math
-
+  // One step's math on the staged tile: this wavefront's 32 keys.
+  auto compute = [&](int step) {
+    const int key0 = step * kStep + kh * kKB;  // first key of this wavefront's tile
+    if (key0 > wave_max_pos) return;           // every row of the wavefront masks it
     // S^T = K Q^T: lane holds keys m(i) = (i/4)*8 + 4 half + i%4 of its row.
     f32x16 st;
 #pragma unroll
@@ -211,22 +217,20 @@ __global__ __launch_bounds__(kPWaves * kWave) void prefill_kernel(
 #pragma unroll
     for (int s = 0; s < kPD / 16; ++s) {
       const bf16x8 a =
-          *(const bf16x8*)(k_lds + (lane & 31) * kKStride + 16 * s + 8 * half);
+          *(const bf16x8*)(k_lds + (kh * kKB + (lane & 31)) * kKStride + 16 * s + 8 * half);
       st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[s], st, 0, 0, 0);
     }
-    const bool masked = kb * kKB + kKB - 1 > min_pos;
-    float mx = -INFINITY;
+    const bool diagonal = key0 + kKB - 1 > min_pos;
+    auto key_masked = [&](int i) { return key0 + (i / 4) * 8 + 4 * half + (i % 4) > pos; };
+    if (diagonal) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float x = st[i] * qk_scale_log2;
-      if (masked) {
-        const int key = kb * kKB + (i / 4) * 8 + 4 * half + (i % 4);
-        x = key > pos ? -INFINITY : x;
-      }
-      st[i] = x;
-      mx = fmaxf(mx, x);
+      for (int i = 0; i < 16; ++i) st[i] = key_masked(i) ? -INFINITY : st[i];
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+    // The maximum of the raw scores, scaled (the scale is not negative).
+    float mx = st[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, st[i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave)) * qk_scale_log2;
     if (__builtin_amdgcn_ballot_w64(mx > m_ref + kPSlack)) {
       const float mn = fmaxf(m_ref, mx);
       const float alpha = mn == -INFINITY ? 1.f : fast_exp2(m_ref - mn);
@@ -237,12 +241,18 @@ __global__ __launch_bounds__(kPWaves * kWave) void prefill_kernel(
         for (int i = 0; i < 16; ++i) oacc[mt][i] *= alpha;
       m_ref = mn;
     }
+    // A row with every key so far masked has m_ref = -inf; its masked
+    // scores must still give 0, not NaN.
+    const float neg_m = m_ref == -INFINITY ? 0.f : -m_ref;
     float p[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      p[i] = st[i] == -INFINITY ? 0.f : fast_exp2(st[i] - m_ref);
-      l_part += p[i];
+    for (int i = 0; i < 16; ++i) p[i] = fast_exp2(__builtin_fmaf(st[i], qk_scale_log2, neg_m));
+    if (diagonal) {  // with a zero scale, -inf * 0 is NaN
+#pragma unroll
+      for (int i = 0; i < 16; ++i) p[i] = key_masked(i) ? 0.f : p[i];
     }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) l_part += p[i];
     // O^T += V^T P^T over two 16-key steps (keys in the permuted order).
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
@@ -251,13 +261,61 @@ __global__ __launch_bounds__(kPWaves * kWave) void prefill_kernel(
       const bf16x8 b = __builtin_bit_cast(bf16x8, pw);
 #pragma unroll
       for (int mt = 0; mt < kPD / 32; ++mt) {
-        const __bf16* vrow = vt_lds + (32 * mt + (lane & 31)) * kVStride + 16 * ks + 4 * half;
+        const __bf16* vrow =
+            vt_lds + (32 * mt + (lane & 31)) * kVStride + kh * kKB + 16 * ks + 4 * half;
         const u32x2 lo = *(const u32x2*)vrow;
         const u32x2 hi = *(const u32x2*)(vrow + 8);
         const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
         oacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, oacc[mt], 0, 0, 0);
       }
     }
+  };
+
+  // Pipeline: step s is stored to LDS from stage s%2 while the loads of
+  // step s+1 (other stage) are in flight; then stage s%2 takes step s+2.
+  Stage sa, sb;
+  int kid, vid;
+  block_ids(0, kid, vid);
+  load_stage(0, kid, vid, sa);
+  block_ids(1, kid, vid);
+  load_stage(1, kid, vid, sb);
+  block_ids(2, kid, vid);
+  auto iteration = [&](int step, Stage& S) {
+    __syncthreads();  // every wavefront is done with the previous step
+    store_stage(S);
+    __syncthreads();
+    if (step + 2 < nsteps) {
+      load_stage(step + 2, kid, vid, S);
+      block_ids(step + 3, kid, vid);
+    }
+    compute(step);
+  };
+  for (int step = 0; step < nsteps; step += 2) {
+    iteration(step, sa);
+    if (step + 1 < nsteps) iteration(step + 1, sb);
+  }
+
+  // Merge the key halves: the second half hands its state to the first.
+  if (kh == 1) {
+    mm_lds[rg][lane] = m_ref;
+    ml_lds[rg][lane] = l_part;
+#pragma unroll
+    for (int mt = 0; mt < kPD / 32; ++mt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mo_lds[rg][16 * mt + i][lane] = oacc[mt][i];
+  }
+  __syncthreads();
+  if (kh == 1) return;
+  {
+    const float m1 = mm_lds[rg][lane], l1 = ml_lds[rg][lane];
+    const float M = fmaxf(m_ref, m1);
+    const float mu = M == -INFINITY ? 0.f : M;
+    const float f0 = fast_exp2(m_ref - mu), f1 = fast_exp2(m1 - mu);
+    l_part = l_part * f0 + l1 * f1;
+#pragma unroll
+    for (int mt = 0; mt < kPD / 32; ++mt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) oacc[mt][i] = oacc[mt][i] * f0 + mo_lds[rg][16 * mt + i][lane] * f1;
   }
 
   // Finish: the two halves of the wave hold the same rows' other keys.
@@ -280,13 +338,16 @@ template <typename KV, int BS, int G>
 static hipError_t launch_prefill(const PrefillArgs& a) {
   const float k_scale = std::is_same<KV, FP8>::value ? a.k_scale : 1.0f;
   const float v_scale = std::is_same<KV, FP8>::value ? a.v_scale : 1.0f;
+  // The kernel takes a non-negative score scale: a negative one is moved
+  // onto the query's sign.
+  const float qk = a.scale * k_scale * kPLog2e;
   const int tiles = (a.max_query_len * G + kRows - 1) / kRows;
   if (tiles == 0) return hipSuccess;
   hipLaunchKernelGGL((prefill_kernel<KV, BS, G>),
                      dim3((unsigned)tiles, (unsigned)a.num_kv_heads, (unsigned)a.num_chunks),
-                     dim3(kPWaves * kWave), 0, a.stream, a.out, a.query, a.query_start_loc,
+                     dim3(kPThreads), 0, a.stream, a.out, a.query, a.query_start_loc,
                      a.k_cache, a.v_cache, a.block_tables, a.max_blocks_per_seq, a.seq_lens,
-                     a.num_kv_heads, a.scale * k_scale * kPLog2e, v_scale);
+                     a.num_kv_heads, fabsf(qk), qk < 0.f, v_scale);
   return hipGetLastError();
 }
 

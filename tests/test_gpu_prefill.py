@@ -97,3 +97,18 @@ def test_prefill_varlen_chunks(Hq, Hkv, bs, kv):
     ref = opg.paged_prefill(q64, qsl, okp, ovp, tables, lens, b.scale, kv_dtype=kv,
                             k_scale=b.k_scale, v_scale=b.v_scale, rows=rows)
     G.assert_close(got, ref, kv, f"prefill {Hq}/{Hkv} bs{bs} {kv}", rows=rows)
+
+
+@pytest.mark.parametrize("scale", [-0.07, 0.0])
+def test_prefill_negative_and_zero_scale(scale):
+    """The softmax scale enters only as scale * q·k: a negative scale flips
+    the scores and a zero scale gives the mean of V over the causal keys."""
+    b, cq, qsl, lens, tables, max_q = _varlen_case(16, 8, 16, "bf16", seed=77)
+    b.scale = scale
+    kp, vp = G.gpu_pool(b)
+    G.gpu_fill(b, kp, vp)
+    okp, ovp = G.oracle_pool(b)
+    got, q64 = run_prefill(b, kp, vp, cq, qsl, lens, tables, max_q)
+    rows = sorted(set(list(range(0, int(qsl[-1]), 11)) + [int(x) - 1 for x in qsl[1:]]))
+    ref = opg.paged_prefill(q64, qsl, okp, ovp, tables, lens, scale, kv_dtype="bf16", rows=rows)
+    G.assert_close(got, ref, "bf16", f"prefill scale {scale}", rows=rows)
