@@ -51,6 +51,16 @@ constexpr float kPLog2e = 1.4426950408889634f;
 constexpr float kPSlack = 8.0f;
 static_assert(kPThreads / 8 == kStep && kPThreads / 16 * 2 == kStep,
               "the staging maps cover one step exactly");
+constexpr int kKBytes = kStep * kKStride * 2;
+constexpr int kVBytes = kPD * kVStride * 2;
+constexpr int kBufBytes = kKBytes + kVBytes;
+constexpr int kMergeFloats = kRowGroups * (kPD / 2) * kWave + 2 * kRowGroups * kWave;
+constexpr int kLdsBytes = 3 * kBufBytes > kMergeFloats * 4 ? 3 * kBufBytes : kMergeFloats * 4;
+
+// How the query enters: the kernel's score scale is always positive, so a
+// negative scale moves onto the query's sign and a zero scale zeroes the
+// query (all scores 0, the same softmax as any positive scale on them).
+constexpr int kQAsIs = 0, kQNegate = 1, kQZero = 2;
 
 __device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
@@ -62,20 +72,27 @@ __device__ __forceinline__ void fp8x4_to_bf16x2x2(uint32_t w, uint32_t& lo, uint
   hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
 }
 
+// max(x[lane], x[lane ^ 32]): v_permlane32_swap(x, x) returns the low
+// half-wave's values in both halves and the high half-wave's in both.
+__device__ __forceinline__ float xor32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(f2u(x), f2u(x), false, false);
+  return fmaxf(u2f(r[0]), u2f(r[1]));
+}
+
 template <typename KV, int BS, int G>
 __global__ __launch_bounds__(kPThreads) void prefill_kernel(
     void* __restrict__ out, const void* __restrict__ query,
     const int32_t* __restrict__ query_start_loc, const void* __restrict__ k_cache,
     const void* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
     int max_blocks_per_seq, const int32_t* __restrict__ seq_lens, int num_kv_heads,
-    float qk_scale_log2, bool negate_q, float v_scale) {
+    float qk_scale_log2, int q_mode, float v_scale) {
   constexpr int EB = Elem<KV>::bytes;
   static_assert(kRows % G == 0, "rows hold whole queries");
-  __shared__ __attribute__((aligned(16))) __bf16 k_lds[kStep * kKStride];
-  __shared__ __attribute__((aligned(16))) __bf16 vt_lds[kPD * kVStride];
-  // Merge area: the second key half's accumulators, maxima and sums.
-  __shared__ float mo_lds[kRowGroups][kPD / 2][kWave];
-  __shared__ float mm_lds[kRowGroups][kWave], ml_lds[kRowGroups][kWave];
+  // Three LDS buffers, each one step's K tile and V^T tile; after the key
+  // walk the same bytes hold the merge of the two key halves.
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
+  auto k_lds = [&](int b) { return (__bf16*)(lds + b * kBufBytes); };
+  auto vt_lds = [&](int b) { return (__bf16*)(lds + b * kBufBytes + kKBytes); };
 
   const int tile = blockIdx.x, g = blockIdx.y, c = blockIdx.z;
   const int t = threadIdx.x, lane = t & (kWave - 1), w = t / kWave;
@@ -109,7 +126,8 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(
     for (int s = 0; s < kPD / 16; ++s) {
       u32x4 v = {0u, 0u, 0u, 0u};
       if (row_ok) v = *(const u32x4*)(qrow + 16 * s + 8 * half);
-      if (negate_q) v ^= 0x80008000u;  // exact: -(q·k) = (-q)·k
+      if (q_mode == kQNegate) v ^= 0x80008000u;  // exact: -(q·k) = (-q)·k
+      if (q_mode == kQZero) v = u32x4{0u, 0u, 0u, 0u};  // every score is 0
       qreg[s] = __builtin_bit_cast(bf16x8, v);
     }
   }
@@ -122,8 +140,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(
   float m_ref = -INFINITY, l_part = 0.f;
 
   // Staging: K — thread t covers key t/8, dims 16 (t%8) .. +16;
-  //          V — thread t covers keys 2 (t/16) and +1, dims 8 (t%16) .. +8
-  //          (one block: keys come in even pairs and blocks are even).
+  //          V — thread t covers keys 2 (t/16) and +1, dims 8 (t%16) .. +8.
   // Each step's loads are issued two steps ahead (two register stages), and
   // the block-table entries they need one step before that.
   const int kk = t / 8, kd = (t % 8) * 16;
@@ -137,41 +154,56 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(
   const int64_t head_off = (int64_t)g * BS * kPD;  // element offset of head g in a block
   const int64_t block_elems = (int64_t)num_kv_heads * BS * kPD;
 
-  // Physical blocks of this thread's K key and V key pair in a step; -1 past L.
-  auto block_ids = [&](int step, int& kid, int& vid) {
-    const int key = step * kStep + kk, key2 = step * kStep + vk;
-    kid = key < L ? tbl[key / BS] : -1;
-    vid = key2 < L ? tbl[key2 / BS] : -1;
-  };
-  auto load_stage = [&](int step, int kid, int vid, Stage& S) {
+  // A wavefront stages keys 8w .. 8w+7 of a step for K and for V, which lie
+  // in one block (blocks hold a multiple of 8 keys, and a step a multiple
+  // of a block): its physical block is one wave-uniform table entry, read
+  // with a scalar load so that waiting for it never waits for the vector
+  // loads in flight, and a thread's offset inside the block is the same
+  // every step.  Past the last block the last one is re-read; keys at or
+  // past L are zeroed when stored, so every step issues the same loads
+  // unconditionally and the wait for a stage counts only later loads.
+  static_assert(kStep % BS == 0 && BS % 8 == 0, "a step is whole blocks of 8-key groups");
+  const int wkey = __builtin_amdgcn_readfirstlane(8 * w);
+  const int last_blk = nblk - 1;
+  auto block_id = [&](int step) -> int { return tbl[min((step * kStep + wkey) / BS, last_blk)]; };
+  const uint8_t* k_head = (const uint8_t*)k_cache + head_off * EB;
+  const uint8_t* v_head = (const uint8_t*)v_cache + head_off * EB;
+  const int k_off = ((kk % BS) * kPD + kd) * EB;
+  const int v_off0 = ((vk % BS) * kPD + vd) * EB, v_off1 = v_off0 + kPD * EB;
+  auto load_stage = [&](int bid, Stage& S) {
+    const int64_t base = (int64_t)bid * block_elems * EB;
+    const u32x4* kp = (const u32x4*)(k_head + base + k_off);
 #pragma unroll
-    for (int v = 0; v < KVEC; ++v) S.k[v] = u32x4{0u, 0u, 0u, 0u};
-    if (kid >= 0) {
-      const int key = step * kStep + kk;
-      const int64_t e0 = (int64_t)kid * block_elems + head_off + (int64_t)(key % BS) * kPD + kd;
-      const u32x4* p = (const u32x4*)((const uint8_t*)k_cache + e0 * EB);
-#pragma unroll
-      for (int v = 0; v < KVEC; ++v) S.k[v] = p[v];
-    }
+    for (int v = 0; v < KVEC; ++v) S.k[v] = kp[v];
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
-      const int key2 = step * kStep + vk + r;
-#pragma unroll
-      for (int x = 0; x < VW; ++x) S.v[r][x] = 0u;
-      if (vid >= 0 && key2 < L) {
-        const int64_t e0 = (int64_t)vid * block_elems + head_off + (int64_t)(key2 % BS) * kPD + vd;
-        const uint32_t* p = (const uint32_t*)((const uint8_t*)v_cache + e0 * EB);
-        if constexpr (VW == 4) {
-          const u32x4 x4 = *(const u32x4*)p;
-          S.v[r][0] = x4.x; S.v[r][1] = x4.y; S.v[r][2] = x4.z; S.v[r][3] = x4.w;
-        } else {
-          const u32x2 x2 = *(const u32x2*)p;
-          S.v[r][0] = x2.x; S.v[r][1] = x2.y;
-        }
+      const uint32_t* vp = (const uint32_t*)(v_head + base + (r ? v_off1 : v_off0));
+      if constexpr (VW == 4) {
+        const u32x4 x4 = *(const u32x4*)vp;
+        S.v[r][0] = x4.x; S.v[r][1] = x4.y; S.v[r][2] = x4.z; S.v[r][3] = x4.w;
+      } else {
+        const u32x2 x2 = *(const u32x2*)vp;
+        S.v[r][0] = x2.x; S.v[r][1] = x2.y;
       }
     }
   };
-  auto store_stage = [&](const Stage& S) {
+  // LDS layout of a buffer.  K: key rows of kKStride bf16.  V^T: dim rows
+  // of kVStride bf16, keys in pairs (one dword per key pair); the key-pair
+  // column is XORed with 4 x (dim / 32), which spreads the staging writes
+  // of a wavefront (16 dims 8 apart) over distinct banks, and leaves each
+  // 32-dim MFMA tile reading its columns uniformly shifted.
+  // In chunks 4..7 of a K row (16 dims each) the two 8-dim halves are
+  // stored swapped: the first 16-byte write of the 8 threads of a row then
+  // lands on distinct banks also with 32 banks.  Readers undo the swap.
+  const int k_wr_lo = kk * kKStride + kd + ((t % 8) >= 4 ? 8 : 0);  // bf16 elements
+  const int k_wr_hi = kk * kKStride + kd + ((t % 8) >= 4 ? 0 : 8);
+  const int v_wr = vd * kVStride + 2 * ((vk / 2) ^ (4 * (vd / 32)));
+  // Zeroing keys past L happens here, where the stage is consumed, so the
+  // wait for its loads stays two steps after their issue.
+  auto store_stage = [&](int step, const Stage& S, int b) {
+    const bool tail = step * kStep + kStep > L;  // some keys of the step are past L
+    const bool k_ok = step * kStep + kk < L;
+    const bool v_ok[2] = {step * kStep + vk < L, step * kStep + vk + 1 < L};
     // K row: 16 bf16 at k_lds[kk][kd..].
     uint32_t kw[8];
     if constexpr (std::is_same<KV, BF16>::value) {
@@ -183,9 +215,12 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(
       fp8x4_to_bf16x2x2(S.k[0].z, kw[4], kw[5]);
       fp8x4_to_bf16x2x2(S.k[0].w, kw[6], kw[7]);
     }
-    u32x4* kdst = (u32x4*)(k_lds + kk * kKStride + kd);
-    kdst[0] = u32x4{kw[0], kw[1], kw[2], kw[3]};
-    kdst[1] = u32x4{kw[4], kw[5], kw[6], kw[7]};
+    if (tail) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) kw[i] = k_ok ? kw[i] : 0u;
+    }
+    *(u32x4*)(k_lds(b) + k_wr_lo) = u32x4{kw[0], kw[1], kw[2], kw[3]};
+    *(u32x4*)(k_lds(b) + k_wr_hi) = u32x4{kw[4], kw[5], kw[6], kw[7]};
     // V^T: dims vd..vd+7, keys vk and vk+1 packed as one dword per dim.
     uint32_t va[4], vb[4];  // bf16 pairs (dims 2x, 2x+1) of keys vk and vk+1
     if constexpr (std::is_same<KV, BF16>::value) {
@@ -198,39 +233,49 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(
         fp8x4_to_bf16x2x2(S.v[1][x], vb[2 * x], vb[2 * x + 1]);
       }
     }
+    if (tail) {
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        va[x] = v_ok[0] ? va[x] : 0u;
+        vb[x] = v_ok[1] ? vb[x] : 0u;
+      }
+    }
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
       // dim 2x: low halves of both keys; dim 2x+1: high halves.
-      *(uint32_t*)(vt_lds + (vd + 2 * x) * kVStride + vk) = __builtin_amdgcn_perm(vb[x], va[x], 0x05040100u);
-      *(uint32_t*)(vt_lds + (vd + 2 * x + 1) * kVStride + vk) = __builtin_amdgcn_perm(vb[x], va[x], 0x07060302u);
+      *(uint32_t*)(vt_lds(b) + v_wr + (2 * x) * kVStride) = __builtin_amdgcn_perm(vb[x], va[x], 0x05040100u);
+      *(uint32_t*)(vt_lds(b) + v_wr + (2 * x + 1) * kVStride) = __builtin_amdgcn_perm(vb[x], va[x], 0x07060302u);
     }
   };
 
-  // One step's math on the staged tile: this wavefront's 32 keys.
-  auto compute = [&](int step) {
-    const int key0 = step * kStep + kh * kKB;  // first key of this wavefront's tile
-    if (key0 > wave_max_pos) return;           // every row of the wavefront masks it
-    // S^T = K Q^T: lane holds keys m(i) = (i/4)*8 + 4 half + i%4 of its row.
-    f32x16 st;
+  // The math of a step on its LDS buffer b, for this wavefront's 32 keys,
+  // in two parts so that the next step's score MFMAs can be interleaved
+  // with this step's exponentials.
+  auto active = [&](int step) { return step * kStep + kh * kKB <= wave_max_pos; };
+
+  // S^T = K Q^T: lane holds keys m(i) = (i/4)*8 + 4 half + i%4 of its row.
+  auto score_mfma = [&](f32x16& st, int b, int s) {
+    const bf16x8 a = *(const bf16x8*)(k_lds(b) + (kh * kKB + (lane & 31)) * kKStride + 16 * s +
+                                      8 * (s >= 4 ? 1 - half : half));
+    st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[s], st, 0, 0, 0);
+  };
+
+  // Masks the diagonal, raises the reference maximum where needed; returns
+  // the exponent offset (-reference, or 0 for a row with nothing unmasked).
+  auto softmax_head = [&](int step, f32x16& st) -> float {
+    const int key0 = step * kStep + kh * kKB;
+    if (key0 + kKB - 1 > min_pos) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) st[i] = 0.f;
-#pragma unroll
-    for (int s = 0; s < kPD / 16; ++s) {
-      const bf16x8 a =
-          *(const bf16x8*)(k_lds + (kh * kKB + (lane & 31)) * kKStride + 16 * s + 8 * half);
-      st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[s], st, 0, 0, 0);
+      for (int i = 0; i < 16; ++i) {
+        const bool masked = key0 + (i / 4) * 8 + 4 * half + (i % 4) > pos;
+        st[i] = masked ? -INFINITY : st[i];
+      }
     }
-    const bool diagonal = key0 + kKB - 1 > min_pos;
-    auto key_masked = [&](int i) { return key0 + (i / 4) * 8 + 4 * half + (i % 4) > pos; };
-    if (diagonal) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) st[i] = key_masked(i) ? -INFINITY : st[i];
-    }
-    // The maximum of the raw scores, scaled (the scale is not negative).
+    // The maximum of the raw scores, scaled (the scale is positive).
     float mx = st[0];
 #pragma unroll
     for (int i = 1; i < 16; ++i) mx = fmaxf(mx, st[i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave)) * qk_scale_log2;
+    mx = xor32_max(mx) * qk_scale_log2;
     if (__builtin_amdgcn_ballot_w64(mx > m_ref + kPSlack)) {
       const float mn = fmaxf(m_ref, mx);
       const float alpha = mn == -INFINITY ? 1.f : fast_exp2(m_ref - mn);
@@ -241,73 +286,106 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(
         for (int i = 0; i < 16; ++i) oacc[mt][i] *= alpha;
       m_ref = mn;
     }
-    // A row with every key so far masked has m_ref = -inf; its masked
-    // scores must still give 0, not NaN.
-    const float neg_m = m_ref == -INFINITY ? 0.f : -m_ref;
-    float p[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) p[i] = fast_exp2(__builtin_fmaf(st[i], qk_scale_log2, neg_m));
-    if (diagonal) {  // with a zero scale, -inf * 0 is NaN
-#pragma unroll
-      for (int i = 0; i < 16; ++i) p[i] = key_masked(i) ? 0.f : p[i];
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) l_part += p[i];
-    // O^T += V^T P^T over two 16-key steps (keys in the permuted order).
+    return m_ref == -INFINITY ? 0.f : -m_ref;
+  };
+
+  // Probability of element i (masked scores are -inf; the scale is > 0).
+  auto prob = [&](const f32x16& st, int i, float neg_m) {
+    return fast_exp2(__builtin_fmaf(st[i], qk_scale_log2, neg_m));
+  };
+
+  // O^T += V^T P^T over two 16-key steps (keys in the permuted order).
+  auto pv = [&](const uint32_t (&pw)[8], int b) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      const u32x4 pw = {pk_bf16(p[8 * ks + 0], p[8 * ks + 1]), pk_bf16(p[8 * ks + 2], p[8 * ks + 3]),
-                        pk_bf16(p[8 * ks + 4], p[8 * ks + 5]), pk_bf16(p[8 * ks + 6], p[8 * ks + 7])};
-      const bf16x8 b = __builtin_bit_cast(bf16x8, pw);
+      const bf16x8 pb = __builtin_bit_cast(
+          bf16x8, u32x4{pw[4 * ks + 0], pw[4 * ks + 1], pw[4 * ks + 2], pw[4 * ks + 3]});
 #pragma unroll
       for (int mt = 0; mt < kPD / 32; ++mt) {
-        const __bf16* vrow =
-            vt_lds + (32 * mt + (lane & 31)) * kVStride + kh * kKB + 16 * ks + 4 * half;
-        const u32x2 lo = *(const u32x2*)vrow;
-        const u32x2 hi = *(const u32x2*)(vrow + 8);
+        // key pairs kh*16 + 8ks + 2half (+4), column-swizzled by 4 mt
+        const __bf16* vrow = vt_lds(b) + (32 * mt + (lane & 31)) * kVStride + kh * kKB + 4 * half;
+        const u32x2 lo = *(const u32x2*)(vrow + 2 * ((8 * ks) ^ (4 * mt)));
+        const u32x2 hi = *(const u32x2*)(vrow + 2 * ((8 * ks + 4) ^ (4 * mt)));
         const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
-        oacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, oacc[mt], 0, 0, 0);
+        oacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, oacc[mt], 0, 0, 0);
       }
     }
   };
 
-  // Pipeline: step s is stored to LDS from stage s%2 while the loads of
-  // step s+1 (other stage) are in flight; then stage s%2 takes step s+2.
+  // Pipeline over steps j: buffer j%3 holds step j.  Iteration j: barrier
+  // (every wavefront is past iteration j-1, so buffer (j+2)%3, last read
+  // there, is free and buffer (j+1)%3, written there, is complete); store
+  // step j+2 from its register stage and issue that stage's loads for step
+  // j+4; then step j+1's score MFMAs interleaved with step j's softmax,
+  // then step j's P·V.  Register stages alternate (sa: even steps).
+  // (The scheduling barriers keep the stages' loads in issue order, which
+  // the waits for them count on.)
   Stage sa, sb;
-  int kid, vid;
-  block_ids(0, kid, vid);
-  load_stage(0, kid, vid, sa);
-  block_ids(1, kid, vid);
-  load_stage(1, kid, vid, sb);
-  block_ids(2, kid, vid);
-  auto iteration = [&](int step, Stage& S) {
-    __syncthreads();  // every wavefront is done with the previous step
-    store_stage(S);
+  load_stage(block_id(0), sa);
+  __builtin_amdgcn_sched_barrier(0);
+  load_stage(block_id(1), sb);
+  __builtin_amdgcn_sched_barrier(0);
+  int bid = block_id(2);
+  store_stage(0, sa, 0);
+  load_stage(bid, sa);
+  bid = block_id(3);
+  __builtin_amdgcn_sched_barrier(0);
+  store_stage(1, sb, 1);
+  load_stage(bid, sb);
+  bid = block_id(4);
+  __syncthreads();
+  // Scores of even steps live in st_a, of odd steps in st_b.
+  f32x16 st_a, st_b;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) st_a[i] = 0.f;
+#pragma unroll
+  for (int s = 0; s < kPD / 16; ++s) score_mfma(st_a, 0, s);
+
+  int bj = 0;  // buffer of step j
+  auto iteration = [&](int j, Stage& S, f32x16& st_cur, f32x16& st_next) {
+    const int bj1 = bj == 2 ? 0 : bj + 1, bj2 = bj1 == 2 ? 0 : bj1 + 1;
     __syncthreads();
-    if (step + 2 < nsteps) {
-      load_stage(step + 2, kid, vid, S);
-      block_ids(step + 3, kid, vid);
+    store_stage(j + 2, S, bj2);
+    load_stage(bid, S);  // step j+4; past the last step: harmless re-reads
+    bid = block_id(j + 5);
+    if (active(j)) {  // later steps are inactive too: nothing is left to do
+      const float neg_m = softmax_head(j, st_cur);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) st_next[i] = 0.f;
+      uint32_t pw[8];
+#pragma unroll
+      for (int s = 0; s < kPD / 16; ++s) {
+        score_mfma(st_next, bj1, s);  // step j+1 (unused if it is inactive)
+        const float p0 = prob(st_cur, 2 * s, neg_m), p1 = prob(st_cur, 2 * s + 1, neg_m);
+        l_part += p0 + p1;
+        pw[s] = pk_bf16(p0, p1);
+      }
+      pv(pw, bj);
     }
-    compute(step);
+    bj = bj1;
   };
-  for (int step = 0; step < nsteps; step += 2) {
-    iteration(step, sa);
-    if (step + 1 < nsteps) iteration(step + 1, sb);
+  for (int j = 0; j < nsteps; j += 2) {
+    iteration(j, sa, st_a, st_b);
+    iteration(j + 1, sb, st_b, st_a);
   }
+  __syncthreads();  // the buffers become the merge area
+  float* mo_lds = (float*)lds;                             // [rg][kPD/2][kWave]
+  float* mm_lds = mo_lds + kRowGroups * (kPD / 2) * kWave;  // [rg][kWave]
+  float* ml_lds = mm_lds + kRowGroups * kWave;              // [rg][kWave]
 
   // Merge the key halves: the second half hands its state to the first.
   if (kh == 1) {
-    mm_lds[rg][lane] = m_ref;
-    ml_lds[rg][lane] = l_part;
+    mm_lds[rg * kWave + lane] = m_ref;
+    ml_lds[rg * kWave + lane] = l_part;
 #pragma unroll
     for (int mt = 0; mt < kPD / 32; ++mt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mo_lds[rg][16 * mt + i][lane] = oacc[mt][i];
+      for (int i = 0; i < 16; ++i) mo_lds[(rg * (kPD / 2) + 16 * mt + i) * kWave + lane] = oacc[mt][i];
   }
   __syncthreads();
   if (kh == 1) return;
   {
-    const float m1 = mm_lds[rg][lane], l1 = ml_lds[rg][lane];
+    const float m1 = mm_lds[rg * kWave + lane], l1 = ml_lds[rg * kWave + lane];
     const float M = fmaxf(m_ref, m1);
     const float mu = M == -INFINITY ? 0.f : M;
     const float f0 = fast_exp2(m_ref - mu), f1 = fast_exp2(m1 - mu);
@@ -315,7 +393,8 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(
 #pragma unroll
     for (int mt = 0; mt < kPD / 32; ++mt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) oacc[mt][i] = oacc[mt][i] * f0 + mo_lds[rg][16 * mt + i][lane] * f1;
+      for (int i = 0; i < 16; ++i)
+        oacc[mt][i] = oacc[mt][i] * f0 + mo_lds[(rg * (kPD / 2) + 16 * mt + i) * kWave + lane] * f1;
   }
 
   // Finish: the two halves of the wave hold the same rows' other keys.
@@ -338,8 +417,7 @@ template <typename KV, int BS, int G>
 static hipError_t launch_prefill(const PrefillArgs& a) {
   const float k_scale = std::is_same<KV, FP8>::value ? a.k_scale : 1.0f;
   const float v_scale = std::is_same<KV, FP8>::value ? a.v_scale : 1.0f;
-  // The kernel takes a non-negative score scale: a negative one is moved
-  // onto the query's sign.
+  // The kernel takes a positive score scale (see kQNegate, kQZero).
   const float qk = a.scale * k_scale * kPLog2e;
   const int tiles = (a.max_query_len * G + kRows - 1) / kRows;
   if (tiles == 0) return hipSuccess;
@@ -347,7 +425,8 @@ static hipError_t launch_prefill(const PrefillArgs& a) {
                      dim3((unsigned)tiles, (unsigned)a.num_kv_heads, (unsigned)a.num_chunks),
                      dim3(kPThreads), 0, a.stream, a.out, a.query, a.query_start_loc,
                      a.k_cache, a.v_cache, a.block_tables, a.max_blocks_per_seq, a.seq_lens,
-                     a.num_kv_heads, fabsf(qk), qk < 0.f, v_scale);
+                     a.num_kv_heads, qk == 0.f ? 1.f : fabsf(qk),
+                     qk == 0.f ? kQZero : (qk < 0.f ? kQNegate : kQAsIs), v_scale);
   return hipGetLastError();
 }
 
