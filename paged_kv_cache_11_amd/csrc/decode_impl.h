@@ -824,6 +824,18 @@ __global__ __launch_bounds__(256) void lse_reduce_kernel(
 
 // Wavefronts per workgroup: enough blocks per wavefront to keep its
 // one-tile-ahead pipeline busy, at most four.
+}  // namespace pa
+
+#include "decode_mfma.h"
+
+namespace pa {
+
+// Whether a (cache, query, head size, group) combination has the
+// matrix-core engine.
+template <typename KV, typename QT, int D, int G>
+constexpr bool kHasMfma = D == kMD && (G == 4 || G == 8) && !std::is_same<KV, F32>::value &&
+                          std::is_same<QT, BF16>::value;
+
 inline int decode_waves(int partition_blocks, int max_seq_len, int block_size) {
   const int blocks = partition_blocks > 0 ? partition_blocks
                                           : (max_seq_len + block_size - 1) / block_size;
@@ -841,10 +853,20 @@ hipError_t launch_decode(const DecodeArgs& a) {
     const int per_head = a.balanced_workers / a.num_kv_heads;
     const int workers = per_head * a.num_kv_heads;
     const int wg = (workers + kMaxDecodeWaves - 1) / kMaxDecodeWaves;
-    hipLaunchKernelGGL((decode_balanced_kernel<KV, QT, D, BS, G>), dim3((unsigned)wg),
-                       dim3(kMaxDecodeWaves * kWave), 0, a.stream, a.out, a.part_o, a.part_ml,
-                       a.cuts, a.query, a.k_cache, a.v_cache, a.block_tables, a.seq_lens,
-                       a.num_seqs, a.max_blocks_per_seq, a.num_kv_heads, per_head, qk, v_scale);
+    bool mfma = false;
+    if constexpr (kHasMfma<KV, QT, D, G>) mfma = a.engine == kEngineMfma;
+    if constexpr (kHasMfma<KV, QT, D, G>) {
+      if (mfma)
+        hipLaunchKernelGGL((decode_balanced_mfma_kernel<KV, QT, BS, G>), dim3((unsigned)wg),
+                           dim3(kMaxDecodeWaves * kWave), 0, a.stream, a.out, a.part_o, a.part_ml,
+                           a.cuts, a.query, a.k_cache, a.v_cache, a.block_tables, a.seq_lens,
+                           a.num_seqs, a.max_blocks_per_seq, a.num_kv_heads, per_head, qk, v_scale);
+    }
+    if (!mfma)
+      hipLaunchKernelGGL((decode_balanced_kernel<KV, QT, D, BS, G>), dim3((unsigned)wg),
+                         dim3(kMaxDecodeWaves * kWave), 0, a.stream, a.out, a.part_o, a.part_ml,
+                         a.cuts, a.query, a.k_cache, a.v_cache, a.block_tables, a.seq_lens,
+                         a.num_seqs, a.max_blocks_per_seq, a.num_kv_heads, per_head, qk, v_scale);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((balanced_reduce_kernel<QT, D, G>),

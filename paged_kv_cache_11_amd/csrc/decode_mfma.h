@@ -1,0 +1,391 @@
+// decode_mfma.h — the paged decode of a GQA group on the matrix cores.
+//
+// Same computation as the wavefront engine in decode_impl.h ("vLLM：大语言
+// 模型推理与服务库" §4.4 item 3: gather each sequence's K/V through its block
+// table, softmax of the scaled scores, weighted sum of V), for head size 128
+// and groups of G = 4 or 8 query heads.  Where the group is large (an fp8
+// cache with G = 8 does 16 multiply-adds per cached byte), the vector ALU
+// path runs out of issue slots long before HBM runs out of bandwidth, so
+// here both contractions go to v_mfma_f32_16x16x32_bf16 with the G query
+// heads as the 16-wide N side (G real columns, the rest zero):
+//
+//   * S^T = K · Q^T per 32-key tile: A = K (16 keys x 32 dims per MFMA)
+//     straight from the pool into registers (16 bytes per lane, a key row
+//     read by 4 lanes as 64 contiguous bytes; fp8 widened exactly to bf16),
+//     B = Q^T (the dims permuted the same way, loaded once).  C leaves each
+//     lane 4 keys x 1 head per 16-key group;
+//   * online softmax in fp32, log2 domain, with the same lazy reference as
+//     the vector path: one reference per head, raised (and the
+//     accumulators rescaled) only when a score exceeds it by 2^8, so the
+//     common step needs no cross-lane reduction;
+//   * O^T += V^T · P^T: P^T is already in the B layout (the 8 keys of a
+//     lane are its two groups' 4), V^T comes from a per-wavefront LDS tile
+//     that each lane fills with 4 keys x 16 dims (packed key pairs), read
+//     back as 8 keys of one dim per lane.
+//
+// The tile loop runs one tile ahead in registers (ping-pong), as the vector
+// path does.  Only runs of consecutive blocks of one sequence (the balanced
+// split) use this engine.
+#pragma once
+
+namespace pa {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+
+constexpr int kMD = 128;                // head size
+constexpr int kMKeys = 32;              // keys per tile
+constexpr int kVtStride = kMKeys + 4;   // V^T LDS row stride, bf16 (18 dwords)
+constexpr int kVtElems = kMD * kVtStride;
+
+__device__ __forceinline__ f32x4 mfma16(const uint32_t (&a)[4], const uint32_t (&b)[4], f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+      __builtin_bit_cast(bf16x8_t, u32x4{a[0], a[1], a[2], a[3]}),
+      __builtin_bit_cast(bf16x8_t, u32x4{b[0], b[1], b[2], b[3]}), c, 0, 0, 0);
+}
+
+template <typename KV, int BS, int G>
+struct MfmaAttn {
+  static constexpr int EB = Elem<KV>::bytes;
+  static constexpr int NBT = kMKeys / BS;                   // blocks per tile
+  static constexpr int KL = 16 * kMD * EB / (kWave * 16);   // K loads per 16-key group
+  static constexpr int VL = kMKeys * kMD * EB / (kWave * 16);  // V loads per tile
+  static constexpr int VPK = VL / 4;                        // V loads per key of a lane
+  static_assert(G == 4 || G == 8, "the matrix-core path takes groups of 4 or 8");
+  static_assert(kMKeys % BS == 0, "a tile is whole blocks");
+
+  // One tile's raw cache words: K for 2 key groups, V for 4 keys x 16 dims.
+  struct Tile {
+    u32x4 k[2][KL];
+    u32x4 v[VL];
+  };
+
+  int lane, n, g4;        // head column n = lane % 16, lane group g4 = lane / 16
+  int kq, dg;             // V staging: keys 4kq..4kq+3, dims 16dg..16dg+15
+  float qk_scale_log2;
+  uint32_t q[4][4];       // Q^T operand per k-step (packed bf16)
+  f32x4 acc[kMD / 16];    // O^T: dims 16mb + 4g4 + i, head n
+  float m_ref, l_lane;
+  __bf16* vt;             // this wavefront's V^T tile in LDS
+
+  __device__ __forceinline__ void init(int lane_, float qk, __bf16* vt_) {
+    lane = lane_;
+    n = lane % 16;
+    g4 = lane / 16;
+    kq = lane % 8;
+    dg = lane / 8;
+    qk_scale_log2 = qk;
+    vt = vt_;
+  }
+
+  __device__ __forceinline__ void reset() {
+#pragma unroll
+    for (int mb = 0; mb < kMD / 16; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_ref = -INFINITY;
+    l_lane = 0.f;
+  }
+
+  // Dims of k-step s (8 consecutive) as read from K by lane group g4.
+  __device__ __forceinline__ int kstep_dim0(int s) const {
+    if constexpr (EB == 1) return 16 * g4 + 64 * (s / 2) + 8 * (s % 2);
+    else return 8 * g4 + 32 * s;
+  }
+
+  // Query rows row0 .. row0+G-1 (bf16) as the B operand; columns >= G zero.
+  __device__ __forceinline__ void load_q(const void* query, int64_t row0) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (n < G) v = *(const u32x4*)((const uint16_t*)query + (row0 + n) * kMD + kstep_dim0(s));
+      q[s][0] = v.x; q[s][1] = v.y; q[s][2] = v.z; q[s][3] = v.w;
+    }
+  }
+
+  // Byte offsets of a lane's loads inside a (block, head) tile.
+  __device__ __forceinline__ int k_off(int kg, int i) const {
+    const int key = (16 * kg + n) % BS;
+    return key * kMD * EB + 16 * g4 + 64 * i;
+  }
+  __device__ __forceinline__ int v_off(int r, int h) const {
+    const int key = (4 * kq + r) % BS;
+    return key * kMD * EB + 16 * dg * EB + 16 * h;
+  }
+
+  // Loads the tile whose blocks are b[0..NBT-1] (physical ids).
+  __device__ __forceinline__ void load_tile(const uint8_t* kh, const uint8_t* vh, int64_t block_bytes,
+                                            const int (&b)[NBT], Tile& T) const {
+#pragma unroll
+    for (int kg = 0; kg < 2; ++kg) {
+      const uint8_t* kb = kh + (int64_t)b[(16 * kg) / BS] * block_bytes;
+#pragma unroll
+      for (int i = 0; i < KL; ++i) T.k[kg][i] = *(const u32x4*)(kb + k_off(kg, i));
+    }
+    const int bv = b[(4 * kq) / BS];
+    const uint8_t* vb = vh + (int64_t)bv * block_bytes;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int h = 0; h < VPK; ++h) T.v[r * VPK + h] = *(const u32x4*)(vb + v_off(r, h));
+  }
+
+  // K operand of key group kg, k-step s, as 4 dwords of packed bf16.
+  __device__ __forceinline__ void k_operand(const Tile& T, int kg, int s, uint32_t (&a)[4]) const {
+    if constexpr (EB == 1) {
+      const u32x4& w = T.k[kg][s / 2];
+      const uint32_t lo = (s % 2) ? w.z : w.x, hi = (s % 2) ? w.w : w.y;
+      a[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false));
+      a[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true));
+      a[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false));
+      a[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true));
+    } else {
+      const u32x4& w = T.k[kg][s];
+      a[0] = w.x; a[1] = w.y; a[2] = w.z; a[3] = w.w;
+    }
+  }
+
+  // Writes the tile's V as V^T into LDS: dims 16dg + d, keys 4kq .. 4kq+3
+  // as one 8-byte word per dim.  Keys at or past lim are zeroed (the
+  // padding slots of a block may hold anything, and 0 * NaN is NaN).
+  __device__ __forceinline__ void stage_v(const Tile& T, int lim) const {
+    uint32_t w[4][8];  // key r, dims (2x, 2x+1) as a bf16 pair
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if constexpr (EB == 1) {
+        const u32x4& x = T.v[r];
+        const uint32_t src[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          w[r][2 * c] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(src[c], 1.0f, false));
+          w[r][2 * c + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(src[c], 1.0f, true));
+        }
+      } else {
+        const u32x4& a = T.v[r * 2], &b = T.v[r * 2 + 1];
+        w[r][0] = a.x; w[r][1] = a.y; w[r][2] = a.z; w[r][3] = a.w;
+        w[r][4] = b.x; w[r][5] = b.y; w[r][6] = b.z; w[r][7] = b.w;
+      }
+    }
+    if (lim < kMKeys) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const bool ok = 4 * kq + r < lim;
+#pragma unroll
+        for (int x = 0; x < 8; ++x) w[r][x] = ok ? w[r][x] : 0u;
+      }
+    }
+    __bf16* base = vt + (16 * dg) * kVtStride + 4 * kq;
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+      const u32x2 lo = {__builtin_amdgcn_perm(w[1][x], w[0][x], 0x05040100u),
+                        __builtin_amdgcn_perm(w[3][x], w[2][x], 0x05040100u)};
+      const u32x2 hi = {__builtin_amdgcn_perm(w[1][x], w[0][x], 0x07060302u),
+                        __builtin_amdgcn_perm(w[3][x], w[2][x], 0x07060302u)};
+      *(u32x2*)(base + (2 * x) * kVtStride) = lo;
+      *(u32x2*)(base + (2 * x + 1) * kVtStride) = hi;
+    }
+  }
+
+  // One tile: lim valid keys (tile-relative, a prefix).
+  __device__ __forceinline__ void tile(const Tile& T, int lim) {
+    // S^T for the two 16-key groups: two independent chains of 4 MFMAs.
+    f32x4 c[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int kg = 0; kg < 2; ++kg) {
+        uint32_t a[4];
+        k_operand(T, kg, s, a);
+        c[kg] = mfma16(a, q[s], c[kg]);
+      }
+    stage_v(T, lim);
+
+    float x[2][4];
+#pragma unroll
+    for (int kg = 0; kg < 2; ++kg)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[kg][i] = c[kg][i] * qk_scale_log2;
+    if (lim < kMKeys) {
+#pragma unroll
+      for (int kg = 0; kg < 2; ++kg)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[kg][i] = 16 * kg + 4 * g4 + i < lim ? x[kg][i] : -INFINITY;
+    }
+    float lm = x[0][0];
+#pragma unroll
+    for (int kg = 0; kg < 2; ++kg)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) lm = fmaxf(lm, x[kg][i]);
+    if (__builtin_amdgcn_ballot_w64(lm > m_ref + kRescaleSlack)) {
+      // Raise the head's reference to the maximum over its 4 lanes.
+      float gm = fmaxf(lm, __shfl_xor(lm, 16, kWave));
+      gm = fmaxf(gm, __shfl_xor(gm, 32, kWave));
+      const float mn = fmaxf(m_ref, gm);
+      const float alpha = mn == -INFINITY ? 1.f : fast_exp2(m_ref - mn);
+      l_lane *= alpha;
+#pragma unroll
+      for (int mb = 0; mb < kMD / 16; ++mb) acc[mb] *= alpha;
+      m_ref = mn;
+    }
+    const float neg_m = m_ref == -INFINITY ? 0.f : -m_ref;
+    float p[2][4];
+#pragma unroll
+    for (int kg = 0; kg < 2; ++kg)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[kg][i] = fast_exp2(x[kg][i] + neg_m);
+        l_lane += p[kg][i];
+      }
+    const uint32_t pw[4] = {pack_bf16(p[0][0], p[0][1]), pack_bf16(p[0][2], p[0][3]),
+                            pack_bf16(p[1][0], p[1][1]), pack_bf16(p[1][2], p[1][3])};
+    // O^T += V^T P^T; V^T rows 16mb + n, keys 4g4.. and 16 + 4g4..
+#pragma unroll
+    for (int mb = 0; mb < kMD / 16; ++mb) {
+      const __bf16* row = vt + (16 * mb + n) * kVtStride + 4 * g4;
+      const u32x2 lo = *(const u32x2*)row;
+      const u32x2 hi = *(const u32x2*)(row + 16);
+      const uint32_t a[4] = {lo.x, lo.y, hi.x, hi.y};
+      acc[mb] = mfma16(a, pw, acc[mb]);
+    }
+  }
+
+  // Blocks first .. first+count-1 of a sequence of L tokens, KV head g.
+  __device__ __forceinline__ void stream(const void* k_cache, const void* v_cache, const int32_t* tbl,
+                                         int g, int num_kv_heads, int first, int count, int L) {
+    if (count <= 0) return;
+    const int64_t tile_bytes = (int64_t)BS * kMD * EB;
+    const int64_t block_bytes = (int64_t)num_kv_heads * tile_bytes;
+    const uint8_t* kh = (const uint8_t*)k_cache + (int64_t)g * tile_bytes;
+    const uint8_t* vh = (const uint8_t*)v_cache + (int64_t)g * tile_bytes;
+    const int ntiles = (count + NBT - 1) / NBT;
+    // Block ids of the run, 64 at a time, one per lane (the requests come
+    // in non-decreasing order); past the run the last block is repeated
+    // (its keys are masked).
+    int bid_v = 0, cached = -1;
+    auto block_id = [&](int j) -> int {
+      j = j < count ? j : count - 1;
+      const int chunk = j / kWave;
+      if (chunk != cached) {
+        const int jj = chunk * kWave + lane;
+        bid_v = tbl[first + (jj < count ? jj : count - 1)];
+        cached = chunk;
+      }
+      return __builtin_amdgcn_readlane(bid_v, j % kWave);
+    };
+    auto tile_ids = [&](int t, int (&b)[NBT]) {
+#pragma unroll
+      for (int u = 0; u < NBT; ++u) b[u] = block_id(t * NBT + u);
+    };
+    auto limit = [&](int t) {
+      const int b0 = first + t * NBT;                       // first block of the tile
+      const int run_end = (first + count) * BS;             // keys past the run
+      const int end = run_end < L ? run_end : L;
+      const int lim = end - b0 * BS;
+      return lim < kMKeys ? lim : kMKeys;
+    };
+    Tile ta, tb;
+    int b[NBT];
+    tile_ids(0, b);
+    load_tile(kh, vh, block_bytes, b, ta);
+    int t = 0;
+    for (; t + 2 <= ntiles; t += 2) {
+      tile_ids(t + 1, b);
+      load_tile(kh, vh, block_bytes, b, tb);
+      tile(ta, limit(t));
+      tile_ids(t + 2 < ntiles ? t + 2 : t + 1, b);
+      load_tile(kh, vh, block_bytes, b, ta);
+      tile(tb, limit(t + 1));
+    }
+    if (t < ntiles) tile(ta, limit(t));
+  }
+
+  // Sum of the head's probabilities over its 4 lanes.
+  __device__ __forceinline__ float l_total() const {
+    float l = l_lane + __shfl_xor(l_lane, 16, kWave);
+    return l + __shfl_xor(l, 32, kWave);
+  }
+};
+
+// The balanced split of decode_balanced_kernel, on the matrix-core engine.
+template <typename KV, typename QT, int BS, int G>
+__global__ __launch_bounds__(kMaxDecodeWaves * kWave, 2) void decode_balanced_mfma_kernel(
+    void* __restrict__ out, float* __restrict__ part_acc, float* __restrict__ part_ml,
+    int32_t* __restrict__ cuts, const void* __restrict__ query,
+    const void* __restrict__ k_cache, const void* __restrict__ v_cache,
+    const int32_t* __restrict__ block_tables, const int32_t* __restrict__ seq_lens, int num_seqs,
+    int max_blocks_per_seq, int num_kv_heads, int workers_per_head, float qk_scale_log2,
+    float v_scale) {
+  static_assert(std::is_same<QT, BF16>::value, "bf16 queries");
+  using MA = MfmaAttn<KV, BS, G>;
+  constexpr int D = kMD;
+  __shared__ __attribute__((aligned(16))) __bf16 vt_lds[kMaxDecodeWaves][kVtElems];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wv = threadIdx.x / kWave;
+  const int worker = blockIdx.x * (blockDim.x / kWave) + wv;
+  const int g = worker % num_kv_heads, vw = worker / num_kv_heads;
+  if (vw >= workers_per_head) return;
+  const int num_heads = num_kv_heads * G;
+
+  const int64_t T = total_blocks(seq_lens, num_seqs, BS, lane);
+  const int W = effective_workers(T, workers_per_head);
+  if (vw >= W) return;
+  const int64_t start = worker_start(T, vw, W), end = worker_start(T, vw + 1, W);
+  if (start >= end) return;
+  int s;
+  int64_t base;
+  locate_block(seq_lens, num_seqs, BS, start, lane, s, base);
+
+  MA A;
+  A.init(lane, qk_scale_log2, vt_lds[wv]);
+  int64_t pos = start;
+  while (pos < end && s < num_seqs) {
+    const int L = seq_lens[s];
+    const int nblk = nblocks_of(L, BS);
+    const int64_t seg_end = base + nblk;
+    if (nblk > 0) {
+      const int b_lo = (int)(pos - base);
+      const int b_hi = (int)((end < seg_end ? end : seg_end) - base);
+      const int64_t hq0 = (int64_t)s * num_heads + (int64_t)g * G;
+      A.reset();
+      A.load_q(query, hq0);
+      A.stream(k_cache, v_cache, block_tables + (int64_t)s * max_blocks_per_seq, g, num_kv_heads,
+               b_lo, b_hi - b_lo, L);
+      const float l_tot = A.l_total();
+      const bool whole = b_lo == 0 && b_hi == nblk;
+      const int slot = pos == start ? 0 : 1;
+      if (b_lo == 0 && lane == 0) {
+        // The worker holding the sequence's first block describes its cut
+        // (same record as the vector path's).
+        const int np = whole ? 1 : worker_of(T, seg_end - 1, W) - vw + 1;
+        cuts[2 * ((int64_t)s * num_kv_heads + g) + 0] = vw;
+        cuts[2 * ((int64_t)s * num_kv_heads + g) + 1] = np * 2 + slot;
+      }
+      if (A.n < G) {
+        const int h = A.n;
+        if (whole) {
+          const float inv = l_tot > 0.f ? v_scale / l_tot : 0.f;
+#pragma unroll
+          for (int mb = 0; mb < D / 16; ++mb) {
+            const int d0 = 16 * mb + 4 * A.g4;
+            const uint32_t w0 = pack_bf16(A.acc[mb][0] * inv, A.acc[mb][1] * inv);
+            const uint32_t w1 = pack_bf16(A.acc[mb][2] * inv, A.acc[mb][3] * inv);
+            *(u32x2*)((uint16_t*)out + (hq0 + h) * D + d0) = u32x2{w0, w1};
+          }
+        } else {
+          const int64_t pslot = ((int64_t)worker * 2 + slot) * G + h;
+#pragma unroll
+          for (int mb = 0; mb < D / 16; ++mb)
+            *(f32x4*)(part_acc + pslot * D + 16 * mb + 4 * A.g4) = A.acc[mb];
+          if (A.g4 == 0) {
+            part_ml[pslot * 2 + 0] = A.m_ref;
+            part_ml[pslot * 2 + 1] = l_tot;
+          }
+        }
+      }
+      pos = base + b_hi;
+    }
+    if (pos >= seg_end) {
+      base = seg_end;
+      ++s;
+    }
+  }
+}
+
+}  // namespace pa

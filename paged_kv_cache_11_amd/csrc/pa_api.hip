@@ -8,6 +8,8 @@
 
 #include <string>
 
+#include <string.h>
+
 #include "pa_internal.h"
 
 namespace {
@@ -90,6 +92,22 @@ int32_t balanced_workers_for_device() {
     return 0;
   const int64_t w = (int64_t)cus * per_cu;
   return (int32_t)(w < pa::kMaxBalancedWorkers ? w : pa::kMaxBalancedWorkers);
+}
+
+// The balanced decode's engine: PA_DECODE_ENGINE=valu|mfma pins it (a
+// tuning knob); by default groups of 8 take the matrix cores, whose
+// issue rate the 16 multiply-adds per cached byte of such a group need,
+// and smaller groups the vector engine.
+int32_t decode_engine(int32_t group) {
+  static const int pinned = [] {
+    const char* e = getenv("PA_DECODE_ENGINE");
+    if (!e) return -1;
+    if (!strcmp(e, "valu")) return (int)pa::kEngineValu;
+    if (!strcmp(e, "mfma")) return (int)pa::kEngineMfma;
+    return -1;
+  }();
+  if (pinned >= 0) return pinned;
+  return group >= 8 ? pa::kEngineMfma : pa::kEngineValu;
 }
 
 }  // namespace
@@ -246,6 +264,7 @@ int32_t pa_decode(void* out, const void* query, int32_t q_dtype, int32_t num_seq
   a.num_waves = decode_waves_override();
   a.balanced_workers = workers;
   a.cuts = a_cuts;
+  a.engine = decode_engine(num_heads / num_kv_heads);
   a.stream = (hipStream_t)stream;
   hipError_t e;
   if (cache_dtype == PA_F32) e = pa::decode_f32(a);

@@ -63,8 +63,13 @@ struct DecodeArgs {
   int32_t num_waves;         // wavefronts per workgroup; 0 = chosen from the partition size
   int32_t balanced_workers;  // > 0: balanced split over this many wavefronts (multiple of Hkv)
   int32_t* cuts;             // balanced split: per (sequence, KV head) {first worker, 2*pieces+slot}
+  int32_t engine;            // balanced split: kEngineValu or kEngineMfma (where compiled)
   hipStream_t stream;
 };
+
+// Engines of the balanced decode: the wavefront (vector ALU) engine, or the
+// matrix-core engine for head size 128 with groups of 4 or 8.
+constexpr int32_t kEngineValu = 0, kEngineMfma = 1;
 
 struct PrefillArgs {
   void* out;
