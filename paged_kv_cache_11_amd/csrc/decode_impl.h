@@ -654,11 +654,11 @@ __device__ __forceinline__ int effective_workers(int64_t T, int W) {
 // state p has maximum m_p, sum l_p and accumulator a_p (normalised by l_p
 // when kNormalised).  Returns sum_p 2^(m_p - M) a'_p / sum_p 2^(m_p - M) l_p
 // with M = max_p m_p and a'_p the unnormalised accumulator.  The loads of
-// eight states are issued together.
+// sixteen states are issued together.
 template <bool kNormalised, typename StateFn>
 __device__ __forceinline__ float merge_element(const float* acc, const float* ml, int np, int D,
                                                int h, int d, StateFn state) {
-  constexpr int kBatch = 8;
+  constexpr int kBatch = 16;
   float M = -INFINITY, num = 0.f, den = 0.f;
   for (int p0 = 0; p0 < np; p0 += kBatch) {
     float m[kBatch], l[kBatch], a[kBatch];
@@ -670,16 +670,19 @@ __device__ __forceinline__ float merge_element(const float* acc, const float* ml
       l[q] = ml[2 * st + 1];
       a[q] = acc[st * D + d];
     }
+    // One rescale per batch: raise M to the batch maximum first.
+    float bm = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q) bm = p0 + q < np ? fmaxf(bm, m[q]) : bm;
+    if (bm > M) {
+      const float f = M == -INFINITY ? 0.f : fast_exp2(M - bm);
+      num *= f;
+      den *= f;
+      M = bm;
+    }
 #pragma unroll
     for (int q = 0; q < kBatch; ++q) {
-      if (p0 + q >= np) break;
-      if (m[q] > M) {
-        const float f = M == -INFINITY ? 0.f : fast_exp2(M - m[q]);
-        num *= f;
-        den *= f;
-        M = m[q];
-      }
-      const float e = M == -INFINITY ? 0.f : fast_exp2(m[q] - M);
+      const float e = (p0 + q >= np || M == -INFINITY) ? 0.f : fast_exp2(m[q] - M);
       num = __builtin_fmaf(e * (kNormalised ? l[q] : 1.f), a[q], num);
       den = __builtin_fmaf(e, l[q], den);
     }
@@ -767,46 +770,45 @@ __global__ __launch_bounds__(kMaxDecodeWaves * kWave) void decode_balanced_kerne
   }
 }
 
-// Finishes what the balanced kernel left: one workgroup per (KV head,
-// sequence).  Empty sequences get zeros; a sequence cut between workers is
-// merged from its pieces' (m, l, acc), found through the cut record its
-// first worker wrote; a whole sequence was finished by its worker.
+// Finishes what the balanced kernel left: one workgroup of D threads per
+// (query head, KV head, sequence), one output element per thread.  Empty
+// sequences get zeros; a sequence cut between workers is merged from its
+// pieces' (m, l, acc), found through the cut record its first worker
+// wrote; a whole sequence was finished by its worker.
 template <typename OT, int D, int G>
-__global__ __launch_bounds__(256) void balanced_reduce_kernel(
+__global__ __launch_bounds__(D) void balanced_reduce_kernel(
     void* __restrict__ out, const float* __restrict__ part_acc,
     const float* __restrict__ part_ml, const int32_t* __restrict__ cuts,
     const int32_t* __restrict__ seq_lens, int num_kv_heads, float v_scale) {
-  const int g = blockIdx.x, s = blockIdx.y;
+  const int h = blockIdx.x, g = blockIdx.y, s = blockIdx.z, d = threadIdx.x;
   const int num_heads = num_kv_heads * G;
-  const int64_t hq0 = (int64_t)s * num_heads + (int64_t)g * G;
+  const int64_t row = (int64_t)s * num_heads + (int64_t)g * G + h;
   const int L = seq_lens[s];
   const int va = cuts[2 * ((int64_t)s * num_kv_heads + g) + 0];
   const int code = cuts[2 * ((int64_t)s * num_kv_heads + g) + 1];
   if (L == 0) {
-    for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x) store_out<OT>(out, hq0 * D + idx, 0.f);
+    store_out<OT>(out, row * D + d, 0.f);
     return;
   }
   const int np = code >> 1, slot0 = code & 1;
   if (np <= 1) return;
-  auto state = [&](int p, int h) -> int64_t {
-    return ((int64_t)((va + p) * num_kv_heads + g) * 2 + (p == 0 ? slot0 : 0)) * G + h;
+  auto state = [&](int p, int hh) -> int64_t {
+    return ((int64_t)((va + p) * num_kv_heads + g) * 2 + (p == 0 ? slot0 : 0)) * G + hh;
   };
-  for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x) {
-    const int h = idx / D, d = idx % D;
-    const float o = merge_element<false>(part_acc, part_ml, np, D, h, d, state);
-    store_out<OT>(out, (hq0 + h) * D + d, o * v_scale);
-  }
+  const float o = merge_element<false>(part_acc, part_ml, np, D, h, d, state);
+  store_out<OT>(out, row * D + d, o * v_scale);
 }
 
-// Log-sum-exp merge of the fixed partitions of one (KV head, sequence):
-// partition p of query head h left (m_p, l_p, o_p) with o_p normalised;
+// Log-sum-exp merge of the fixed partitions of one (query head, KV head,
+// sequence), one output element per thread: partition p of query head h
+// left (m_p, l_p, o_p) with o_p normalised;
 // out = sum_p 2^(m_p - M) l_p o_p / sum_p 2^(m_p - M) l_p.
 template <typename OT, int D, int G>
-__global__ __launch_bounds__(256) void lse_reduce_kernel(
+__global__ __launch_bounds__(D) void lse_reduce_kernel(
     void* __restrict__ out, const float* __restrict__ part_o,
     const float* __restrict__ part_ml, const int32_t* __restrict__ seq_lens, int num_kv_heads,
     int block_size, int partition_blocks, int max_parts) {
-  const int g = blockIdx.x, s = blockIdx.y;
+  const int h = blockIdx.x, g = blockIdx.y, s = blockIdx.z, d = threadIdx.x;
   const int L = seq_lens[s];
   const int nblk = (L + block_size - 1) / block_size;
   const int nparts = nblk > partition_blocks ? (nblk + partition_blocks - 1) / partition_blocks : 1;
@@ -815,11 +817,8 @@ __global__ __launch_bounds__(256) void lse_reduce_kernel(
   const int64_t hq0 = (int64_t)s * num_heads + (int64_t)g * G;
   // Partition p of head h is state (hq0 + h) * max_parts + p; the decode
   // kernel already applied the value scale and normalised each output.
-  auto state = [&](int p, int h) -> int64_t { return (hq0 + h) * max_parts + p; };
-  for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x) {
-    const int h = idx / D, d = idx % D;
-    store_out<OT>(out, (hq0 + h) * D + d, merge_element<true>(part_o, part_ml, nparts, D, h, d, state));
-  }
+  auto state = [&](int p, int hh) -> int64_t { return (hq0 + hh) * max_parts + p; };
+  store_out<OT>(out, (hq0 + h) * D + d, merge_element<true>(part_o, part_ml, nparts, D, h, d, state));
 }
 
 // Wavefronts per workgroup: enough blocks per wavefront to keep its
@@ -870,7 +869,8 @@ hipError_t launch_decode(const DecodeArgs& a) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((balanced_reduce_kernel<QT, D, G>),
-                       dim3((unsigned)a.num_kv_heads, (unsigned)a.num_seqs), dim3(256), 0, a.stream,
+                       dim3((unsigned)G, (unsigned)a.num_kv_heads, (unsigned)a.num_seqs), dim3(D), 0,
+                       a.stream,
                        a.out, a.part_o, a.part_ml, a.cuts, a.seq_lens, a.num_kv_heads, v_scale);
     return hipGetLastError();
   }
@@ -884,7 +884,8 @@ hipError_t launch_decode(const DecodeArgs& a) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.max_parts <= 1) return e;
   hipLaunchKernelGGL((lse_reduce_kernel<QT, D, G>),
-                     dim3((unsigned)a.num_kv_heads, (unsigned)a.num_seqs), dim3(256), 0, a.stream,
+                     dim3((unsigned)G, (unsigned)a.num_kv_heads, (unsigned)a.num_seqs), dim3(D), 0,
+                     a.stream,
                      a.out, a.part_o, a.part_ml, a.seq_lens, a.num_kv_heads, a.block_size,
                      a.partition_blocks, a.max_parts);
   return hipGetLastError();
