@@ -33,9 +33,6 @@ namespace pa {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
 constexpr int kMD = 128;                // head size
-constexpr int kMKeys = 32;              // keys per tile
-constexpr int kVtStride = kMKeys + 4;   // V^T LDS row stride, bf16 (18 dwords)
-constexpr int kVtElems = kMD * kVtStride;
 
 __device__ __forceinline__ f32x4 mfma16(const uint32_t (&a)[4], const uint32_t (&b)[4], f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(
@@ -43,36 +40,60 @@ __device__ __forceinline__ f32x4 mfma16(const uint32_t (&a)[4], const uint32_t (
       __builtin_bit_cast(bf16x8_t, u32x4{b[0], b[1], b[2], b[3]}), c, 0, 0, 0);
 }
 
+// v_mfma_f32_16x16x16_bf16: A[m = l%16][k = 4(l/16) + j], B[k][n = l%16],
+// C[4(l/16) + i][l%16] (the 16x16x32 layout with 4 k per lane).
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f32x4 mfma16k16(const uint32_t (&a)[2], const uint32_t (&b)[2], f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, u32x2{a[0], a[1]}),
+                                                  __builtin_bit_cast(s16x4_t, u32x2{b[0], b[1]}), c,
+                                                  0, 0, 0);
+}
+
+// Keys per tile: 32 (two 16-key groups, P·V with k = 32) where a tile's raw
+// words fit the registers twice over, else 16 (bf16: one group, P·V with
+// k = 16).
+template <typename KV> struct MfmaTileKeys { static constexpr int value = 32; };
+template <> struct MfmaTileKeys<BF16> { static constexpr int value = 16; };
+
+template <int KEYS> struct VtStride;  // V^T LDS row stride in bf16, chosen for few bank conflicts
+template <> struct VtStride<32> { static constexpr int value = 36; };
+template <> struct VtStride<16> { static constexpr int value = 20; };
+
 template <typename KV, int BS, int G>
 struct MfmaAttn {
   static constexpr int EB = Elem<KV>::bytes;
-  static constexpr int NBT = kMKeys / BS;                   // blocks per tile
-  static constexpr int KL = 16 * kMD * EB / (kWave * 16);   // K loads per 16-key group
-  static constexpr int VL = kMKeys * kMD * EB / (kWave * 16);  // V loads per tile
-  static constexpr int VPK = VL / 4;                        // V loads per key of a lane
+  static constexpr int KEYS = MfmaTileKeys<KV>::value;     // keys per tile
+  static constexpr int KG = KEYS / 16;                      // 16-key groups per tile
+  static constexpr int NBT = KEYS > BS ? KEYS / BS : 1;     // blocks a tile touches
+  static constexpr int KL = 16 * kMD * EB / (kWave * 16);   // K 16-byte loads per key group
+  static constexpr int VDL = KEYS * kMD / (kWave * 4);      // V dims per lane (4 keys each)
+  static constexpr int VW = VDL * EB / 4;                   // V dwords per key of a lane
+  static constexpr int VT = VtStride<KEYS>::value;
   static_assert(G == 4 || G == 8, "the matrix-core path takes groups of 4 or 8");
-  static_assert(kMKeys % BS == 0, "a tile is whole blocks");
+  static_assert(KEYS % BS == 0 || BS % KEYS == 0, "tiles and blocks nest");
 
-  // One tile's raw cache words: K for 2 key groups, V for 4 keys x 16 dims.
+  // One tile's raw cache words: K for its key groups, V for 4 keys x VDL dims.
   struct Tile {
-    u32x4 k[2][KL];
-    u32x4 v[VL];
+    u32x4 k[KG][KL];
+    uint32_t v[4][VW];
   };
 
   int lane, n, g4;        // head column n = lane % 16, lane group g4 = lane / 16
-  int kq, dg;             // V staging: keys 4kq..4kq+3, dims 16dg..16dg+15
+  int kq, dg;             // V staging: keys 4kq..4kq+3, dims VDL*dg .. +VDL
   float qk_scale_log2;
   uint32_t q[4][4];       // Q^T operand per k-step (packed bf16)
   f32x4 acc[kMD / 16];    // O^T: dims 16mb + 4g4 + i, head n
   float m_ref, l_lane;
   __bf16* vt;             // this wavefront's V^T tile in LDS
 
+  static constexpr int kLdsElems = kMD * VT;
+
   __device__ __forceinline__ void init(int lane_, float qk, __bf16* vt_) {
     lane = lane_;
     n = lane % 16;
     g4 = lane / 16;
-    kq = lane % 8;
-    dg = lane / 8;
+    kq = lane % (KEYS / 4);
+    dg = lane / (KEYS / 4);
     qk_scale_log2 = qk;
     vt = vt_;
   }
@@ -100,31 +121,41 @@ struct MfmaAttn {
     }
   }
 
-  // Byte offsets of a lane's loads inside a (block, head) tile.
-  __device__ __forceinline__ int k_off(int kg, int i) const {
-    const int key = (16 * kg + n) % BS;
-    return key * kMD * EB + 16 * g4 + 64 * i;
-  }
-  __device__ __forceinline__ int v_off(int r, int h) const {
-    const int key = (4 * kq + r) % BS;
-    return key * kMD * EB + 16 * dg * EB + 16 * h;
-  }
-
-  // Loads the tile whose blocks are b[0..NBT-1] (physical ids).
+  // Loads tile t of a run: its keys are run keys t*KEYS .. +KEYS, block j of
+  // the run holding keys j*BS .. +BS; bid(j) gives physical block ids.
+  template <typename BidFn>
   __device__ __forceinline__ void load_tile(const uint8_t* kh, const uint8_t* vh, int64_t block_bytes,
-                                            const int (&b)[NBT], Tile& T) const {
+                                            int t, BidFn bid, Tile& T) const {
+    const int k0 = t * KEYS;  // first run key of the tile
+    int b[NBT];
 #pragma unroll
-    for (int kg = 0; kg < 2; ++kg) {
-      const uint8_t* kb = kh + (int64_t)b[(16 * kg) / BS] * block_bytes;
+    for (int u = 0; u < NBT; ++u) b[u] = bid(k0 / BS + u);
 #pragma unroll
-      for (int i = 0; i < KL; ++i) T.k[kg][i] = *(const u32x4*)(kb + k_off(kg, i));
+    for (int kg = 0; kg < KG; ++kg) {
+      const int key = k0 + 16 * kg;  // a 16-key group lies in one block
+      const uint8_t* kb = kh + (int64_t)b[(16 * kg) / BS] * block_bytes +
+                          ((key % BS) + n) * kMD * EB + 16 * g4;
+#pragma unroll
+      for (int i = 0; i < KL; ++i) T.k[kg][i] = *(const u32x4*)(kb + 64 * i);
     }
-    const int bv = b[(4 * kq) / BS];
-    const uint8_t* vb = vh + (int64_t)bv * block_bytes;
+    // A lane's 4 V keys lie in one block.
+    const int vkey = k0 + 4 * kq;
+    const uint8_t* vb = vh + (int64_t)b[(4 * kq) / BS] * block_bytes +
+                        (vkey % BS) * kMD * EB + VDL * dg * EB;
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
+    for (int r = 0; r < 4; ++r) {
+      const uint8_t* p = vb + r * kMD * EB;
+      if constexpr (VW == 2) {
+        const u32x2 x = *(const u32x2*)p;
+        T.v[r][0] = x.x; T.v[r][1] = x.y;
+      } else {
 #pragma unroll
-      for (int h = 0; h < VPK; ++h) T.v[r * VPK + h] = *(const u32x4*)(vb + v_off(r, h));
+        for (int h = 0; h < VW / 4; ++h) {
+          const u32x4 x = *(const u32x4*)(p + 16 * h);
+          T.v[r][4 * h] = x.x; T.v[r][4 * h + 1] = x.y; T.v[r][4 * h + 2] = x.z; T.v[r][4 * h + 3] = x.w;
+        }
+      }
+    }
   }
 
   // K operand of key group kg, k-step s, as 4 dwords of packed bf16.
@@ -142,75 +173,79 @@ struct MfmaAttn {
     }
   }
 
-  // Writes the tile's V as V^T into LDS: dims 16dg + d, keys 4kq .. 4kq+3
-  // as one 8-byte word per dim.  Keys at or past lim are zeroed (the
-  // padding slots of a block may hold anything, and 0 * NaN is NaN).
+  // Writes the tile's V as V^T into LDS: dims VDL*dg + d, keys 4kq .. 4kq+3
+  // as one 8-byte word per dim, 8 dims at a time.  Keys at or past lim are
+  // zeroed (the padding slots of a block may hold anything, and 0 * NaN is
+  // NaN).
   __device__ __forceinline__ void stage_v(const Tile& T, int lim) const {
-    uint32_t w[4][8];  // key r, dims (2x, 2x+1) as a bf16 pair
+    __bf16* base = vt + (VDL * dg) * VT + 4 * kq;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      if constexpr (EB == 1) {
-        const u32x4& x = T.v[r];
-        const uint32_t src[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          w[r][2 * c] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(src[c], 1.0f, false));
-          w[r][2 * c + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(src[c], 1.0f, true));
-        }
-      } else {
-        const u32x4& a = T.v[r * 2], &b = T.v[r * 2 + 1];
-        w[r][0] = a.x; w[r][1] = a.y; w[r][2] = a.z; w[r][3] = a.w;
-        w[r][4] = b.x; w[r][5] = b.y; w[r][6] = b.z; w[r][7] = b.w;
-      }
-    }
-    if (lim < kMKeys) {
+    for (int hf = 0; hf < VDL / 8; ++hf) {
+      uint32_t w[4][4];  // key r, dims (8hf + 2x, +1) as a bf16 pair
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const bool ok = 4 * kq + r < lim;
+        if constexpr (EB == 1) {
 #pragma unroll
-        for (int x = 0; x < 8; ++x) w[r][x] = ok ? w[r][x] : 0u;
+          for (int c = 0; c < 2; ++c) {
+            const uint32_t src = T.v[r][2 * hf + c];
+            w[r][2 * c] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(src, 1.0f, false));
+            w[r][2 * c + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(src, 1.0f, true));
+          }
+        } else {
+#pragma unroll
+          for (int x = 0; x < 4; ++x) w[r][x] = T.v[r][4 * hf + x];
+        }
       }
-    }
-    __bf16* base = vt + (16 * dg) * kVtStride + 4 * kq;
+      if (lim < KEYS) {
 #pragma unroll
-    for (int x = 0; x < 8; ++x) {
-      const u32x2 lo = {__builtin_amdgcn_perm(w[1][x], w[0][x], 0x05040100u),
-                        __builtin_amdgcn_perm(w[3][x], w[2][x], 0x05040100u)};
-      const u32x2 hi = {__builtin_amdgcn_perm(w[1][x], w[0][x], 0x07060302u),
-                        __builtin_amdgcn_perm(w[3][x], w[2][x], 0x07060302u)};
-      *(u32x2*)(base + (2 * x) * kVtStride) = lo;
-      *(u32x2*)(base + (2 * x + 1) * kVtStride) = hi;
+        for (int r = 0; r < 4; ++r) {
+          const bool ok = 4 * kq + r < lim;
+#pragma unroll
+          for (int x = 0; x < 4; ++x) w[r][x] = ok ? w[r][x] : 0u;
+        }
+      }
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const u32x2 lo = {__builtin_amdgcn_perm(w[1][x], w[0][x], 0x05040100u),
+                          __builtin_amdgcn_perm(w[3][x], w[2][x], 0x05040100u)};
+        const u32x2 hi = {__builtin_amdgcn_perm(w[1][x], w[0][x], 0x07060302u),
+                          __builtin_amdgcn_perm(w[3][x], w[2][x], 0x07060302u)};
+        *(u32x2*)(base + (8 * hf + 2 * x) * VT) = lo;
+        *(u32x2*)(base + (8 * hf + 2 * x + 1) * VT) = hi;
+      }
     }
   }
 
   // One tile: lim valid keys (tile-relative, a prefix).
   __device__ __forceinline__ void tile(const Tile& T, int lim) {
-    // S^T for the two 16-key groups: two independent chains of 4 MFMAs.
-    f32x4 c[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    // S^T per 16-key group: independent chains of 4 MFMAs.
+    f32x4 c[KG];
+#pragma unroll
+    for (int kg = 0; kg < KG; ++kg) c[kg] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 4; ++s)
 #pragma unroll
-      for (int kg = 0; kg < 2; ++kg) {
+      for (int kg = 0; kg < KG; ++kg) {
         uint32_t a[4];
         k_operand(T, kg, s, a);
         c[kg] = mfma16(a, q[s], c[kg]);
       }
     stage_v(T, lim);
 
-    float x[2][4];
+    float x[KG][4];
 #pragma unroll
-    for (int kg = 0; kg < 2; ++kg)
+    for (int kg = 0; kg < KG; ++kg)
 #pragma unroll
       for (int i = 0; i < 4; ++i) x[kg][i] = c[kg][i] * qk_scale_log2;
-    if (lim < kMKeys) {
+    if (lim < KEYS) {
 #pragma unroll
-      for (int kg = 0; kg < 2; ++kg)
+      for (int kg = 0; kg < KG; ++kg)
 #pragma unroll
         for (int i = 0; i < 4; ++i) x[kg][i] = 16 * kg + 4 * g4 + i < lim ? x[kg][i] : -INFINITY;
     }
     float lm = x[0][0];
 #pragma unroll
-    for (int kg = 0; kg < 2; ++kg)
+    for (int kg = 0; kg < KG; ++kg)
 #pragma unroll
       for (int i = 0; i < 4; ++i) lm = fmaxf(lm, x[kg][i]);
     if (__builtin_amdgcn_ballot_w64(lm > m_ref + kRescaleSlack)) {
@@ -225,24 +260,35 @@ struct MfmaAttn {
       m_ref = mn;
     }
     const float neg_m = m_ref == -INFINITY ? 0.f : -m_ref;
-    float p[2][4];
+    float p[KG][4];
 #pragma unroll
-    for (int kg = 0; kg < 2; ++kg)
+    for (int kg = 0; kg < KG; ++kg)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         p[kg][i] = fast_exp2(x[kg][i] + neg_m);
         l_lane += p[kg][i];
       }
-    const uint32_t pw[4] = {pack_bf16(p[0][0], p[0][1]), pack_bf16(p[0][2], p[0][3]),
-                            pack_bf16(p[1][0], p[1][1]), pack_bf16(p[1][2], p[1][3])};
-    // O^T += V^T P^T; V^T rows 16mb + n, keys 4g4.. and 16 + 4g4..
+    // O^T += V^T P^T; V^T rows 16mb + n.  k = 32: keys 4g4.. and 16 + 4g4..;
+    // k = 16: keys 4g4..
+    if constexpr (KG == 2) {
+      const uint32_t pw[4] = {pack_bf16(p[0][0], p[0][1]), pack_bf16(p[0][2], p[0][3]),
+                              pack_bf16(p[1][0], p[1][1]), pack_bf16(p[1][2], p[1][3])};
 #pragma unroll
-    for (int mb = 0; mb < kMD / 16; ++mb) {
-      const __bf16* row = vt + (16 * mb + n) * kVtStride + 4 * g4;
-      const u32x2 lo = *(const u32x2*)row;
-      const u32x2 hi = *(const u32x2*)(row + 16);
-      const uint32_t a[4] = {lo.x, lo.y, hi.x, hi.y};
-      acc[mb] = mfma16(a, pw, acc[mb]);
+      for (int mb = 0; mb < kMD / 16; ++mb) {
+        const __bf16* row = vt + (16 * mb + n) * VT + 4 * g4;
+        const u32x2 lo = *(const u32x2*)row;
+        const u32x2 hi = *(const u32x2*)(row + 16);
+        const uint32_t a[4] = {lo.x, lo.y, hi.x, hi.y};
+        acc[mb] = mfma16(a, pw, acc[mb]);
+      }
+    } else {
+      const uint32_t pw[2] = {pack_bf16(p[0][0], p[0][1]), pack_bf16(p[0][2], p[0][3])};
+#pragma unroll
+      for (int mb = 0; mb < kMD / 16; ++mb) {
+        const u32x2 lo = *(const u32x2*)(vt + (16 * mb + n) * VT + 4 * g4);
+        const uint32_t a[2] = {lo.x, lo.y};
+        acc[mb] = mfma16k16(a, pw, acc[mb]);
+      }
     }
   }
 
@@ -254,12 +300,14 @@ struct MfmaAttn {
     const int64_t block_bytes = (int64_t)num_kv_heads * tile_bytes;
     const uint8_t* kh = (const uint8_t*)k_cache + (int64_t)g * tile_bytes;
     const uint8_t* vh = (const uint8_t*)v_cache + (int64_t)g * tile_bytes;
-    const int ntiles = (count + NBT - 1) / NBT;
+    // Keys of the run: first*BS .. min(L, (first+count)*BS).
+    const int run_keys = ((first + count) * BS < L ? (first + count) * BS : L) - first * BS;
+    const int ntiles = (count * BS + KEYS - 1) / KEYS;
     // Block ids of the run, 64 at a time, one per lane (the requests come
     // in non-decreasing order); past the run the last block is repeated
     // (its keys are masked).
     int bid_v = 0, cached = -1;
-    auto block_id = [&](int j) -> int {
+    auto bid = [&](int j) -> int {
       j = j < count ? j : count - 1;
       const int chunk = j / kWave;
       if (chunk != cached) {
@@ -269,28 +317,17 @@ struct MfmaAttn {
       }
       return __builtin_amdgcn_readlane(bid_v, j % kWave);
     };
-    auto tile_ids = [&](int t, int (&b)[NBT]) {
-#pragma unroll
-      for (int u = 0; u < NBT; ++u) b[u] = block_id(t * NBT + u);
-    };
     auto limit = [&](int t) {
-      const int b0 = first + t * NBT;                       // first block of the tile
-      const int run_end = (first + count) * BS;             // keys past the run
-      const int end = run_end < L ? run_end : L;
-      const int lim = end - b0 * BS;
-      return lim < kMKeys ? lim : kMKeys;
+      const int lim = run_keys - t * KEYS;
+      return lim < KEYS ? lim : KEYS;
     };
     Tile ta, tb;
-    int b[NBT];
-    tile_ids(0, b);
-    load_tile(kh, vh, block_bytes, b, ta);
+    load_tile(kh, vh, block_bytes, 0, bid, ta);
     int t = 0;
     for (; t + 2 <= ntiles; t += 2) {
-      tile_ids(t + 1, b);
-      load_tile(kh, vh, block_bytes, b, tb);
+      load_tile(kh, vh, block_bytes, t + 1, bid, tb);
       tile(ta, limit(t));
-      tile_ids(t + 2 < ntiles ? t + 2 : t + 1, b);
-      load_tile(kh, vh, block_bytes, b, ta);
+      load_tile(kh, vh, block_bytes, t + 2 < ntiles ? t + 2 : t + 1, bid, ta);
       tile(tb, limit(t + 1));
     }
     if (t < ntiles) tile(ta, limit(t));
@@ -315,7 +352,7 @@ __global__ __launch_bounds__(kMaxDecodeWaves * kWave, 2) void decode_balanced_mf
   static_assert(std::is_same<QT, BF16>::value, "bf16 queries");
   using MA = MfmaAttn<KV, BS, G>;
   constexpr int D = kMD;
-  __shared__ __attribute__((aligned(16))) __bf16 vt_lds[kMaxDecodeWaves][kVtElems];
+  __shared__ __attribute__((aligned(16))) __bf16 vt_lds[kMaxDecodeWaves][MA::kLdsElems];
   const int lane = threadIdx.x & (kWave - 1);
   const int wv = threadIdx.x / kWave;
   const int worker = blockIdx.x * (blockDim.x / kWave) + wv;

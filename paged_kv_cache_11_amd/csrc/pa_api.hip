@@ -95,19 +95,17 @@ int32_t balanced_workers_for_device() {
 }
 
 // The balanced decode's engine: PA_DECODE_ENGINE=valu|mfma pins it (a
-// tuning knob); by default groups of 8 take the matrix cores, whose
-// issue rate the 16 multiply-adds per cached byte of such a group need,
-// and smaller groups the vector engine.
+// tuning knob); by default the matrix cores, wherever that engine is
+// compiled (head size 128, groups of 4 or 8, bf16 queries; elsewhere the
+// launch falls back to the vector engine).
 int32_t decode_engine(int32_t group) {
-  static const int pinned = [] {
-    const char* e = getenv("PA_DECODE_ENGINE");
-    if (!e) return -1;
-    if (!strcmp(e, "valu")) return (int)pa::kEngineValu;
-    if (!strcmp(e, "mfma")) return (int)pa::kEngineMfma;
-    return -1;
-  }();
-  if (pinned >= 0) return pinned;
-  return group >= 8 ? pa::kEngineMfma : pa::kEngineValu;
+  // Read on every call (a few hundred nanoseconds), so that a process can
+  // compare the engines.
+  const char* e = getenv("PA_DECODE_ENGINE");
+  if (e && !strcmp(e, "valu")) return pa::kEngineValu;
+  if (e && !strcmp(e, "mfma")) return pa::kEngineMfma;
+  (void)group;
+  return pa::kEngineMfma;
 }
 
 }  // namespace

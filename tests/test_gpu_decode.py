@@ -182,3 +182,47 @@ def test_decode_balanced_reuses_one_workspace():
         fresh = G.run_decode(b, kp, vp, qt, partition_size=BAL, seq_lens=lens)
         assert np.array_equal(got, fresh)
     assert np.array_equal(got, ref)
+
+
+def _shape_batch(Hq, Hkv, D, bs, kv, lens, seed):
+    rng = np.random.default_rng(seed)
+    lens = np.asarray(lens, dtype=np.int32)
+    nblk = (lens + bs - 1) // bs
+    nb = int(nblk.sum()) + 7
+    perm = rng.permutation(nb).astype(np.int32)
+    tables = np.full((len(lens), int(nblk.max()) + 2), -1, np.int32)
+    cur, slots = 0, []
+    for s, n in enumerate(nblk):
+        tables[s, :n] = perm[cur:cur + n]
+        cur += n
+        t = np.arange(lens[s])
+        slots.append(tables[s, t // bs].astype(np.int64) * bs + t % bs)
+    T = int(lens.sum())
+    k = rng.standard_normal((T, Hkv, D), dtype=np.float32)
+    v = rng.standard_normal((T, Hkv, D), dtype=np.float32)
+    q = rng.standard_normal((len(lens), Hq, D), dtype=np.float32)
+    ks = float(np.float32(np.abs(k).max()) / np.float32(448)) if kv == "fp8" else 1.0
+    vs = float(np.float32(np.abs(v).max()) / np.float32(448)) if kv == "fp8" else 1.0
+    return wl.PagedBatch("engines", Hq, Hkv, D, bs, nb, "bf16", "bf16", kv, 1 / np.sqrt(D), q, k, v,
+                         np.concatenate(slots), lens, tables, k_scale=ks, v_scale=vs)
+
+
+@pytest.mark.parametrize("engine", ["valu", "mfma"])
+@pytest.mark.parametrize("Hq,Hkv,bs,kv", [
+    (32, 8, 16, "bf16"), (32, 8, 32, "bf16"), (64, 8, 16, "bf16"), (64, 8, 32, "fp8"),
+    (32, 8, 16, "fp8"), (16, 2, 32, "fp8"),
+])
+def test_decode_balanced_engines(engine, Hq, Hkv, bs, kv, monkeypatch):
+    """Both engines of the balanced split (vector ALU and matrix cores) on
+    head size 128, groups of 4 and 8, with lengths that end inside blocks,
+    inside 16-key groups and on block edges, and a one-token sequence."""
+    monkeypatch.setenv("PA_DECODE_ENGINE", engine)
+    lens = [1, 15, 16, 17, 31, 33, 47, 500, 1000, 2049, 63, 64]
+    b = _shape_batch(Hq, Hkv, 128, bs, kv, lens, seed=Hq + 7 * bs + (kv == "fp8"))
+    kp, vp = G.gpu_pool(b)
+    G.gpu_fill(b, kp, vp)
+    okp, ovp = G.oracle_pool(b)
+    qt = G.query_tensor(b)
+    ref = G.oracle_decode(b, okp, ovp, G.query_f64(qt))
+    got = G.run_decode(b, kp, vp, qt, partition_size=BAL)
+    G.assert_close(got, ref, kv, f"{engine} engine {Hq}/{Hkv} bs{bs} {kv}")
