@@ -40,9 +40,10 @@ N_SETS = 3
 
 
 def kernel_source_digest() -> str:
-    """Digest of the decode kernel sources, to tie stored counter data to code."""
+    """Digest of the decode kernel sources (and the engine and worker-count
+    choice in the C ABI), to tie stored counter data to code."""
     h = hashlib.sha256()
-    for f in ("decode_impl.h", "pa_device.h"):
+    for f in ("decode_impl.h", "decode_mfma.h", "pa_device.h", "pa_api.hip"):
         with open(os.path.join(ROOT, "paged_kv_cache_11_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -86,7 +87,7 @@ def summarize_counters(fetch_csv: str, write_csv: str, workload: str, out_path: 
     f_scale = true_bytes / statistics.mean(f[copy_name])
     w_scale = true_bytes / statistics.mean(w[copy_name])
     parts = {}
-    for tag in ("decode_balanced_kernel", "balanced_reduce_kernel"):
+    for tag in ("decode_balanced", "balanced_reduce_kernel"):
         kf = next(k for k in f if tag in k)
         kw = next(k for k in w if tag in k)
         parts[tag] = {"fetch_bytes": statistics.median(f[kf]) * f_scale,
@@ -445,7 +446,7 @@ def main(argv=None):
         "tokens_per_s": round(tokens_per_s, 1),
         "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "roofline": {
-            "kernel": "pa_decode (decode_kernel + lse_reduce_kernel)",
+            "kernel": "pa_decode (balanced decode kernel + split-K reduce kernel)",
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic, "avg_us": round(dec_avg_s * 1e6, 2),

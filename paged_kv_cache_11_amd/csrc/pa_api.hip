@@ -76,36 +76,40 @@ int32_t decode_waves_override() {
   return v;
 }
 
-// Wavefronts of the balanced split: PA_BALANCED_WAVES_PER_CU (default 8,
-// two per SIMD: enough loads in flight to saturate HBM while the score and
-// softmax arithmetic of the other wavefronts hides behind them) per compute
-// unit of the current device, capped by the workspace layout.
-int32_t balanced_workers_for_device() {
-  static const int per_cu = [] {
+// The balanced decode's engine: PA_DECODE_ENGINE=valu|mfma pins it (a
+// tuning knob); by default the matrix cores, wherever that engine is
+// compiled (head size 128, groups of 4 or 8, bf16 queries; elsewhere the
+// launch falls back to the vector engine).  Read on every call (a few
+// hundred nanoseconds), so that a process can compare the engines.
+int32_t decode_engine(int32_t q_dtype, int32_t cache_dtype, int32_t head_size, int32_t group) {
+  const bool has_mfma = head_size == 128 && (group == 4 || group == 8) && q_dtype == PA_BF16 &&
+                        cache_dtype != PA_F32;
+  const char* e = getenv("PA_DECODE_ENGINE");
+  if (!has_mfma || (e && !strcmp(e, "valu"))) return pa::kEngineValu;
+  return pa::kEngineMfma;
+}
+
+// Wavefronts of the balanced split per compute unit of the current device,
+// capped by the workspace layout: PA_BALANCED_WAVES_PER_CU pins it (a
+// tuning knob); by default 4 (one workgroup per CU) for the matrix-core
+// engine, whose wavefronts keep two tiles in flight with little arithmetic
+// between them, and 8 (two per SIMD, so that one's loads hide the other's
+// score and softmax arithmetic) for the vector engine.  Whole workgroups
+// per CU matter: a fraction leaves some CUs with one more workgroup than
+// others for the whole kernel.
+int32_t balanced_workers_for_device(int32_t engine) {
+  static const int pinned = [] {
     const char* e = getenv("PA_BALANCED_WAVES_PER_CU");
     const int x = e ? atoi(e) : 0;
-    return (x >= 1 && x <= 32) ? x : 8;
+    return (x >= 1 && x <= 32) ? x : 0;
   }();
+  const int per_cu = pinned ? pinned : (engine == pa::kEngineMfma ? 4 : 8);
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return 0;
   const int64_t w = (int64_t)cus * per_cu;
   return (int32_t)(w < pa::kMaxBalancedWorkers ? w : pa::kMaxBalancedWorkers);
-}
-
-// The balanced decode's engine: PA_DECODE_ENGINE=valu|mfma pins it (a
-// tuning knob); by default the matrix cores, wherever that engine is
-// compiled (head size 128, groups of 4 or 8, bf16 queries; elsewhere the
-// launch falls back to the vector engine).
-int32_t decode_engine(int32_t group) {
-  // Read on every call (a few hundred nanoseconds), so that a process can
-  // compare the engines.
-  const char* e = getenv("PA_DECODE_ENGINE");
-  if (e && !strcmp(e, "valu")) return pa::kEngineValu;
-  if (e && !strcmp(e, "mfma")) return pa::kEngineMfma;
-  (void)group;
-  return pa::kEngineMfma;
 }
 
 }  // namespace
@@ -230,6 +234,7 @@ int32_t pa_decode(void* out, const void* query, int32_t q_dtype, int32_t num_seq
   float* part_ml = nullptr;
   int32_t workers = 0;
   int32_t* a_cuts = nullptr;
+  const int32_t engine = decode_engine(q_dtype, cache_dtype, head_size, num_heads / num_kv_heads);
   if (mp > 1 || balanced) {
     const size_t need = pa_decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_size,
                                                  max_seq_len, partition_size);
@@ -242,7 +247,7 @@ int32_t pa_decode(void* out, const void* query, int32_t q_dtype, int32_t num_seq
     part_ml = (float*)((char*)workspace + align256(n * head_size * sizeof(float)));
     if (balanced) {
       a_cuts = (int32_t*)((char*)part_ml + align256(n * 2 * sizeof(float)));
-      const int32_t w = balanced_workers_for_device();
+      const int32_t w = balanced_workers_for_device(engine);
       if (w <= 0) return fail(PA_ERR_HIP, "cannot query the device's compute units");
       workers = (w / num_kv_heads) * num_kv_heads;
       if (workers < num_kv_heads) workers = num_kv_heads;
@@ -262,7 +267,7 @@ int32_t pa_decode(void* out, const void* query, int32_t q_dtype, int32_t num_seq
   a.num_waves = decode_waves_override();
   a.balanced_workers = workers;
   a.cuts = a_cuts;
-  a.engine = decode_engine(num_heads / num_kv_heads);
+  a.engine = engine;
   a.stream = (hipStream_t)stream;
   hipError_t e;
   if (cache_dtype == PA_F32) e = pa::decode_f32(a);
