@@ -178,121 +178,128 @@ def _time_us(fn, iters, warmup=3):
     return a.elapsed_time(b) / iters * 1e3
 
 
-def row_measurements(dev, iters=20):
-    """Timings of the other rows of the hot path, one workload each."""
+ROW_GROUPS = ("long_context", "shared_prefix", "mixed_fp8")
+
+
+def row_measurements(dev, iters=20, groups=ROW_GROUPS):
+    """Timings of the other rows of the hot path, one workload each; groups
+    picks which workloads run (all by default)."""
     import torch
 
     from paged_kv_cache_11_amd import binding as pa
     from paged_kv_cache_11_amd import workloads as wl
 
     rows = {}
-    # Long-context split-K: 8 x 32768 tokens, 512-token partitions + LSE reduce.
-    b = wl.long_context_decode()
-    sets = _gpu_pools(b, dev)
-    q = wl.storage_tensor(b.q, b.q_dtype).to(dev)
-    out = torch.empty_like(q)
-    tb, ln = torch.from_numpy(b.block_tables).to(dev), torch.from_numpy(b.seq_lens).to(dev)
-    for name, ps in (("long_context_splitk_512", 512), ("long_context_balanced", -1)):
-        ws = torch.empty(max(1, pa.pa_decode_workspace_size(b.num_seqs, b.num_heads, b.num_kv_heads,
-                                                            b.head_size, b.max_seq_len, ps)),
+    if "long_context" in groups:
+        # Long-context split-K: 8 x 32768 tokens, 512-token partitions + LSE reduce.
+        b = wl.long_context_decode()
+        sets = _gpu_pools(b, dev)
+        q = wl.storage_tensor(b.q, b.q_dtype).to(dev)
+        out = torch.empty_like(q)
+        tb, ln = torch.from_numpy(b.block_tables).to(dev), torch.from_numpy(b.seq_lens).to(dev)
+        for name, ps in (("long_context_splitk_512", 512), ("long_context_balanced", -1)):
+            ws = torch.empty(max(1, pa.pa_decode_workspace_size(b.num_seqs, b.num_heads, b.num_kv_heads,
+                                                                b.head_size, b.max_seq_len, ps)),
+                             dtype=torch.uint8, device=dev)
+            us = _time_us(lambda i: pa.pa_decode(out, q, sets[0][0], sets[0][1], tb, ln, b.max_seq_len,
+                                                 b.scale, partition_size=ps, workspace=ws), iters)
+            by = b.decode_kv_bytes()
+            rows[name] = {"us": round(us, 2), "kv_bytes": by, "gbs": round(by / us / 1e3, 1),
+                          "pct_hbm_peak": round(100 * by / us / 1e3 / HBM_PEAK_GBS, 2),
+                          "tokens_per_s": round(b.num_seqs / us * 1e6, 1)}
+        del sets
+        torch.cuda.empty_cache()
+
+    if "shared_prefix" in groups:
+        # Shared prefix: 256 forks of a 2040-token prefix -> 256 copy-on-write
+        # block copies, then decode.
+        b = wl.shared_prefix_decode(prefix_len=2040)
+        sets = _gpu_pools(b, dev)
+        pairs = torch.from_numpy(b.copy_pairs).to(dev)
+        blk_bytes = 2 * b.num_kv_heads * b.block_size * b.head_size * 2
+        us = _time_us(lambda i: pa.pa_copy_blocks(sets[0][0], sets[0][1], pairs), iters)
+        rows["copy_blocks_cow_256"] = {"us": round(us, 2), "pairs": len(b.copy_pairs),
+                                       "bytes_read_written": 2 * len(b.copy_pairs) * blk_bytes,
+                                       "gbs": round(2 * len(b.copy_pairs) * blk_bytes / us / 1e3, 1)}
+        q = wl.storage_tensor(b.q, b.q_dtype).to(dev)
+        out = torch.empty_like(q)
+        tb, ln = torch.from_numpy(b.block_tables).to(dev), torch.from_numpy(b.seq_lens).to(dev)
+        ws = torch.empty(pa.pa_decode_workspace_size(b.num_seqs, b.num_heads, b.num_kv_heads,
+                                                     b.head_size, b.max_seq_len, -1),
                          dtype=torch.uint8, device=dev)
         us = _time_us(lambda i: pa.pa_decode(out, q, sets[0][0], sets[0][1], tb, ln, b.max_seq_len,
-                                             b.scale, partition_size=ps, workspace=ws), iters)
+                                             b.scale, partition_size=-1, workspace=ws), iters)
+        logical = b.decode_kv_bytes()
+        unique = (int(np.unique(b.block_tables[b.block_tables >= 0]).size) * b.block_size
+                  * b.kv_bytes_per_token())
+        rows["shared_prefix_decode"] = {"us": round(us, 2), "logical_kv_bytes": logical,
+                                        "unique_kv_bytes": unique,
+                                        "effective_gbs_logical": round(logical / us / 1e3, 1),
+                                        "gbs_unique": round(unique / us / 1e3, 1),
+                                        "tokens_per_s": round(b.num_seqs / us * 1e6, 1)}
+        del sets
+        torch.cuda.empty_cache()
+
+    if "mixed_fp8" in groups:
+        # Mixed fp8 step (70B shape): cache write of the step's new tokens,
+        # decode of 32 sequences, prefill of a 512-query chunk.
+        b = wl.mixed_fp8_step()
+        sets = _gpu_pools(b, dev, copies=2)
+        q = wl.storage_tensor(b.q, b.q_dtype).to(dev)
+        out = torch.empty_like(q)
+        tb, ln = torch.from_numpy(b.block_tables).to(dev), torch.from_numpy(b.seq_lens).to(dev)
+        ws = torch.empty(pa.pa_decode_workspace_size(b.num_seqs, b.num_heads, b.num_kv_heads,
+                                                     b.head_size, b.max_seq_len, -1),
+                         dtype=torch.uint8, device=dev)
+        ends = np.cumsum(b.seq_lens.astype(np.int64))
+        dec_new = ends - 1
+        chunk_idx = np.arange(int(ends[-1]) + 1536, int(ends[-1]) + 2048)
+        new_idx = np.concatenate([dec_new, chunk_idx])
+        k_new = wl.storage_tensor(b.k[new_idx], b.kv_src_dtype).to(dev)
+        v_new = wl.storage_tensor(b.v[new_idx], b.kv_src_dtype).to(dev)
+        s_new = torch.from_numpy(b.slot_mapping[new_idx]).to(dev)
+        cq = wl.storage_tensor(b.chunk_q, "bf16").to(dev)
+        cout = torch.empty_like(cq)
+        cqs = torch.from_numpy(b.chunk_query_start).to(dev)
+        ctb = torch.from_numpy(b.chunk_block_tables).to(dev)
+        cln = torch.from_numpy(b.chunk_seq_lens).to(dev)
+        nq = int(b.chunk_q.shape[0])
+
+        def cw(i):
+            kc, vc = sets[i % 2]
+            pa.pa_cache_write(k_new, v_new, kc, vc, s_new, b.k_scale, b.v_scale)
+
+        def dec(i):
+            kc, vc = sets[i % 2]
+            pa.pa_decode(out, q, kc, vc, tb, ln, b.max_seq_len, b.scale, b.k_scale, b.v_scale, -1, ws)
+
+        def pre(i):
+            kc, vc = sets[i % 2]
+            pa.pa_prefill_chunk(cout, cq, cqs, nq, kc, vc, ctb, cln, b.scale, b.k_scale, b.v_scale)
+
+        us_cw = _time_us(cw, iters)
+        n_new = len(new_idx)
+        cw_bytes = n_new * b.num_kv_heads * b.head_size * (2 * 2 + 2 * 1)  # bf16 in, fp8 out, K and V
+        rows["cache_write_fp8_mixed_step"] = {"us": round(us_cw, 2), "tokens": n_new,
+                                              "bytes_moved": cw_bytes,
+                                              "gbs": round(cw_bytes / us_cw / 1e3, 1)}
+        us_dec = _time_us(dec, iters)
         by = b.decode_kv_bytes()
-        rows[name] = {"us": round(us, 2), "kv_bytes": by, "gbs": round(by / us / 1e3, 1),
-                      "pct_hbm_peak": round(100 * by / us / 1e3 / HBM_PEAK_GBS, 2),
-                      "tokens_per_s": round(b.num_seqs / us * 1e6, 1)}
-    del sets
-    torch.cuda.empty_cache()
-
-    # Shared prefix: 256 forks of a 2040-token prefix -> 256 copy-on-write
-    # block copies, then decode.
-    b = wl.shared_prefix_decode(prefix_len=2040)
-    sets = _gpu_pools(b, dev)
-    pairs = torch.from_numpy(b.copy_pairs).to(dev)
-    blk_bytes = 2 * b.num_kv_heads * b.block_size * b.head_size * 2
-    us = _time_us(lambda i: pa.pa_copy_blocks(sets[0][0], sets[0][1], pairs), iters)
-    rows["copy_blocks_cow_256"] = {"us": round(us, 2), "pairs": len(b.copy_pairs),
-                                   "bytes_read_written": 2 * len(b.copy_pairs) * blk_bytes,
-                                   "gbs": round(2 * len(b.copy_pairs) * blk_bytes / us / 1e3, 1)}
-    q = wl.storage_tensor(b.q, b.q_dtype).to(dev)
-    out = torch.empty_like(q)
-    tb, ln = torch.from_numpy(b.block_tables).to(dev), torch.from_numpy(b.seq_lens).to(dev)
-    ws = torch.empty(pa.pa_decode_workspace_size(b.num_seqs, b.num_heads, b.num_kv_heads,
-                                                 b.head_size, b.max_seq_len, -1),
-                     dtype=torch.uint8, device=dev)
-    us = _time_us(lambda i: pa.pa_decode(out, q, sets[0][0], sets[0][1], tb, ln, b.max_seq_len,
-                                         b.scale, partition_size=-1, workspace=ws), iters)
-    logical = b.decode_kv_bytes()
-    unique = (int(np.unique(b.block_tables[b.block_tables >= 0]).size) * b.block_size
-              * b.kv_bytes_per_token())
-    rows["shared_prefix_decode"] = {"us": round(us, 2), "logical_kv_bytes": logical,
-                                    "unique_kv_bytes": unique,
-                                    "effective_gbs_logical": round(logical / us / 1e3, 1),
-                                    "gbs_unique": round(unique / us / 1e3, 1),
-                                    "tokens_per_s": round(b.num_seqs / us * 1e6, 1)}
-    del sets
-    torch.cuda.empty_cache()
-
-    # Mixed fp8 step (70B shape): cache write of the step's new tokens,
-    # decode of 32 sequences, prefill of a 512-query chunk.
-    b = wl.mixed_fp8_step()
-    sets = _gpu_pools(b, dev, copies=2)
-    q = wl.storage_tensor(b.q, b.q_dtype).to(dev)
-    out = torch.empty_like(q)
-    tb, ln = torch.from_numpy(b.block_tables).to(dev), torch.from_numpy(b.seq_lens).to(dev)
-    ws = torch.empty(pa.pa_decode_workspace_size(b.num_seqs, b.num_heads, b.num_kv_heads,
-                                                 b.head_size, b.max_seq_len, -1),
-                     dtype=torch.uint8, device=dev)
-    ends = np.cumsum(b.seq_lens.astype(np.int64))
-    dec_new = ends - 1
-    chunk_idx = np.arange(int(ends[-1]) + 1536, int(ends[-1]) + 2048)
-    new_idx = np.concatenate([dec_new, chunk_idx])
-    k_new = wl.storage_tensor(b.k[new_idx], b.kv_src_dtype).to(dev)
-    v_new = wl.storage_tensor(b.v[new_idx], b.kv_src_dtype).to(dev)
-    s_new = torch.from_numpy(b.slot_mapping[new_idx]).to(dev)
-    cq = wl.storage_tensor(b.chunk_q, "bf16").to(dev)
-    cout = torch.empty_like(cq)
-    cqs = torch.from_numpy(b.chunk_query_start).to(dev)
-    ctb = torch.from_numpy(b.chunk_block_tables).to(dev)
-    cln = torch.from_numpy(b.chunk_seq_lens).to(dev)
-    nq = int(b.chunk_q.shape[0])
-
-    def cw(i):
-        kc, vc = sets[i % 2]
-        pa.pa_cache_write(k_new, v_new, kc, vc, s_new, b.k_scale, b.v_scale)
-
-    def dec(i):
-        kc, vc = sets[i % 2]
-        pa.pa_decode(out, q, kc, vc, tb, ln, b.max_seq_len, b.scale, b.k_scale, b.v_scale, -1, ws)
-
-    def pre(i):
-        kc, vc = sets[i % 2]
-        pa.pa_prefill_chunk(cout, cq, cqs, nq, kc, vc, ctb, cln, b.scale, b.k_scale, b.v_scale)
-
-    us_cw = _time_us(cw, iters)
-    n_new = len(new_idx)
-    cw_bytes = n_new * b.num_kv_heads * b.head_size * (2 * 2 + 2 * 1)  # bf16 in, fp8 out, K and V
-    rows["cache_write_fp8_mixed_step"] = {"us": round(us_cw, 2), "tokens": n_new,
-                                          "bytes_moved": cw_bytes,
-                                          "gbs": round(cw_bytes / us_cw / 1e3, 1)}
-    us_dec = _time_us(dec, iters)
-    by = b.decode_kv_bytes()
-    rows["decode_fp8_70b_shape"] = {"us": round(us_dec, 2), "kv_bytes": by,
-                                    "gbs": round(by / us_dec / 1e3, 1),
-                                    "pct_hbm_peak": round(100 * by / us_dec / 1e3 / HBM_PEAK_GBS, 2),
-                                    "tokens_per_s": round(b.num_seqs / us_dec * 1e6, 1)}
-    us_pre = _time_us(pre, iters)
-    L, n = int(b.chunk_seq_lens[0]), nq
-    pairs = sum(L - n + i + 1 for i in range(n))  # causal (query, key) pairs per head
-    flops = 4.0 * b.num_heads * b.head_size * pairs
-    rows["prefill_chunk_fp8_70b_shape"] = {
-        "us": round(us_pre, 2), "causal_flops": flops, "tflops": round(flops / us_pre / 1e6, 1),
-        "pct_mfma_bf16_peak": round(100 * flops / us_pre / 1e6 / MFMA_BF16_PEAK_TFLOPS, 2),
-        "queries_per_s": round(n / us_pre * 1e6, 1)}
-    us_step = _time_us(lambda i: (cw(i), dec(i), pre(i)), iters)
-    rows["mixed_step_fp8"] = {"us": round(us_step, 2),
-                              "step": "cache_write(544 tokens) + decode(32 seqs) + prefill(512 queries)"}
+        rows["decode_fp8_70b_shape"] = {"us": round(us_dec, 2), "kv_bytes": by,
+                                        "gbs": round(by / us_dec / 1e3, 1),
+                                        "pct_hbm_peak": round(100 * by / us_dec / 1e3 / HBM_PEAK_GBS, 2),
+                                        "tokens_per_s": round(b.num_seqs / us_dec * 1e6, 1)}
+        us_pre = _time_us(pre, iters)
+        L, n = int(b.chunk_seq_lens[0]), nq
+        pairs = sum(L - n + i + 1 for i in range(n))  # causal (query, key) pairs per head
+        flops = 4.0 * b.num_heads * b.head_size * pairs
+        rows["prefill_chunk_fp8_70b_shape"] = {
+            "us": round(us_pre, 2), "causal_flops": flops, "tflops": round(flops / us_pre / 1e6, 1),
+            "pct_mfma_bf16_peak": round(100 * flops / us_pre / 1e6 / MFMA_BF16_PEAK_TFLOPS, 2),
+            "queries_per_s": round(n / us_pre * 1e6, 1)}
+        us_step = _time_us(lambda i: (cw(i), dec(i), pre(i)), iters)
+        rows["mixed_step_fp8"] = {"us": round(us_step, 2),
+                                  "step": "cache_write(544 tokens) + decode(32 seqs) + prefill(512 queries)"}
     return rows
 
 
@@ -308,6 +315,9 @@ def main(argv=None):
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-rows", action="store_true",
                     help="skip the per-row measurements of the other workloads")
+    ap.add_argument("--rows-only", choices=ROW_GROUPS,
+                    help="measure only this group of rows (no headline step) and print them; "
+                         "for per-kernel profiling of one row")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run pa_copy_blocks over this many MiB (counter calibration)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -328,6 +338,11 @@ def main(argv=None):
 
     from paged_kv_cache_11_amd import binding as pa
     from paged_kv_cache_11_amd import workloads as wl
+
+    if args.rows_only:
+        print(json.dumps({"rows": row_measurements(torch.device("cuda:0"), groups=(args.rows_only,))}),
+              flush=True)
+        return 0
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)

@@ -19,9 +19,11 @@
 //     accumulators rescaled) only when a score exceeds it by 2^8, so the
 //     common step needs no cross-lane reduction;
 //   * O^T += V^T · P^T: P^T is already in the B layout (the 8 keys of a
-//     lane are its two groups' 4), V^T comes from a per-wavefront LDS tile
-//     that each lane fills with 4 keys x 16 dims (packed key pairs), read
-//     back as 8 keys of one dim per lane.
+//     lane are its two groups' 4).  V goes through a per-wavefront LDS tile
+//     row-major, as read from the pool (fp8 widened to bf16), with fully
+//     coalesced loads and conflict-free 16-byte writes; gfx950's transposing
+//     LDS read (ds_read_b64_tr_b16) then hands each lane 4 keys of one dim,
+//     the A layout, with no repacking.
 //
 // The tile loop runs one tile ahead in registers (ping-pong), as the vector
 // path does.  Only runs of consecutive blocks of one sequence (the balanced
@@ -55,9 +57,20 @@ __device__ __forceinline__ f32x4 mfma16k16(const uint32_t (&a)[2], const uint32_
 template <typename KV> struct MfmaTileKeys { static constexpr int value = 32; };
 template <> struct MfmaTileKeys<BF16> { static constexpr int value = 16; };
 
-template <int KEYS> struct VtStride;  // V^T LDS row stride in bf16, chosen for few bank conflicts
-template <> struct VtStride<32> { static constexpr int value = 36; };
-template <> struct VtStride<16> { static constexpr int value = 20; };
+// Row stride of the LDS V tile (bf16): a 256-byte key row plus 32 bytes, so
+// the 4 rows a 16-lane group reads with one transposing load, and the 8
+// rows of a 32-lane pass, fall on distinct banks.
+constexpr int kVRow = kMD + 16;
+
+// ds_read_b64_tr_b16: in each 16-lane group, lane t supplies the address of
+// 4 consecutive 16-bit elements F[t][0..3]; lane j receives
+// {F[4k + j/4][j%4] : k = 0..3} (layout probed on gfx950).
+typedef short s16x4_t2 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x2 lds_read_tr16(const __bf16* p) {
+  const s16x4_t2 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4_t2*)(p));
+  return __builtin_bit_cast(u32x2, v);
+}
 
 template <typename KV, int BS, int G>
 struct MfmaAttn {
@@ -66,34 +79,35 @@ struct MfmaAttn {
   static constexpr int KG = KEYS / 16;                      // 16-key groups per tile
   static constexpr int NBT = KEYS > BS ? KEYS / BS : 1;     // blocks a tile touches
   static constexpr int KL = 16 * kMD * EB / (kWave * 16);   // K 16-byte loads per key group
-  static constexpr int VDL = KEYS * kMD / (kWave * 4);      // V dims per lane (4 keys each)
-  static constexpr int VW = VDL * EB / 4;                   // V dwords per key of a lane
-  static constexpr int VT = VtStride<KEYS>::value;
+  static constexpr int CPR = kMD * EB / 16;                 // 16-byte chunks of a V row
+  static constexpr int VRL = kWave / CPR;                   // V rows per wavefront load
+  static constexpr int VL = KEYS / VRL;                     // V loads per tile
   static_assert(G == 4 || G == 8, "the matrix-core path takes groups of 4 or 8");
   static_assert(KEYS % BS == 0 || BS % KEYS == 0, "tiles and blocks nest");
 
-  // One tile's raw cache words: K for its key groups, V for 4 keys x VDL dims.
+  // One tile's raw cache words: K for its key groups; V rows vr + VRL*i,
+  // 16-byte chunk vc of each.
   struct Tile {
     u32x4 k[KG][KL];
-    uint32_t v[4][VW];
+    u32x4 v[VL];
   };
 
   int lane, n, g4;        // head column n = lane % 16, lane group g4 = lane / 16
-  int kq, dg;             // V staging: keys 4kq..4kq+3, dims VDL*dg .. +VDL
+  int vr, vc;             // V staging: rows vr + VRL*i, 16-byte chunk vc
   float qk_scale_log2;
   uint32_t q[4][4];       // Q^T operand per k-step (packed bf16)
   f32x4 acc[kMD / 16];    // O^T: dims 16mb + 4g4 + i, head n
   float m_ref, l_lane;
   __bf16* vt;             // this wavefront's V^T tile in LDS
 
-  static constexpr int kLdsElems = kMD * VT;
+  static constexpr int kLdsElems = KEYS * kVRow;
 
   __device__ __forceinline__ void init(int lane_, float qk, __bf16* vt_) {
     lane = lane_;
     n = lane % 16;
     g4 = lane / 16;
-    kq = lane % (KEYS / 4);
-    dg = lane / (KEYS / 4);
+    vr = lane / CPR;
+    vc = lane % CPR;
     qk_scale_log2 = qk;
     vt = vt_;
   }
@@ -138,23 +152,13 @@ struct MfmaAttn {
 #pragma unroll
       for (int i = 0; i < KL; ++i) T.k[kg][i] = *(const u32x4*)(kb + 64 * i);
     }
-    // A lane's 4 V keys lie in one block.
-    const int vkey = k0 + 4 * kq;
-    const uint8_t* vb = vh + (int64_t)b[(4 * kq) / BS] * block_bytes +
-                        (vkey % BS) * kMD * EB + VDL * dg * EB;
+    // V: wavefront load i reads rows VRL*i .. +VRL of the tile, whole rows.
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const uint8_t* p = vb + r * kMD * EB;
-      if constexpr (VW == 2) {
-        const u32x2 x = *(const u32x2*)p;
-        T.v[r][0] = x.x; T.v[r][1] = x.y;
-      } else {
-#pragma unroll
-        for (int h = 0; h < VW / 4; ++h) {
-          const u32x4 x = *(const u32x4*)(p + 16 * h);
-          T.v[r][4 * h] = x.x; T.v[r][4 * h + 1] = x.y; T.v[r][4 * h + 2] = x.z; T.v[r][4 * h + 3] = x.w;
-        }
-      }
+    for (int i = 0; i < VL; ++i) {
+      const int r = vr + VRL * i;  // tile row; the tile's rows are keys k0 + r
+      const int u = ((k0 % BS) + r) / BS;
+      const int bb = NBT == 1 ? b[0] : b[u < NBT ? u : NBT - 1];
+      T.v[i] = *(const u32x4*)(vh + (int64_t)bb * block_bytes + ((k0 + r) % BS) * kMD * EB + 16 * vc);
     }
   }
 
@@ -173,45 +177,34 @@ struct MfmaAttn {
     }
   }
 
-  // Writes the tile's V as V^T into LDS: dims VDL*dg + d, keys 4kq .. 4kq+3
-  // as one 8-byte word per dim, 8 dims at a time.  Keys at or past lim are
-  // zeroed (the padding slots of a block may hold anything, and 0 * NaN is
-  // NaN).
+  // Writes the tile's V rows into LDS as bf16 (fp8 widened exactly), rows
+  // at or past lim zeroed (the padding slots of a block may hold anything,
+  // and 0 * NaN is NaN).
   __device__ __forceinline__ void stage_v(const Tile& T, int lim) const {
-    __bf16* base = vt + (VDL * dg) * VT + 4 * kq;
 #pragma unroll
-    for (int hf = 0; hf < VDL / 8; ++hf) {
-      uint32_t w[4][4];  // key r, dims (8hf + 2x, +1) as a bf16 pair
+    for (int i = 0; i < VL; ++i) {
+      const int r = vr + VRL * i;
+      const bool ok = lim >= KEYS || r < lim;
+      __bf16* row = vt + r * kVRow;
+      if constexpr (EB == 1) {
+        const uint32_t src[4] = {T.v[i].x, T.v[i].y, T.v[i].z, T.v[i].w};
+        uint32_t w[8];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        if constexpr (EB == 1) {
-#pragma unroll
-          for (int c = 0; c < 2; ++c) {
-            const uint32_t src = T.v[r][2 * hf + c];
-            w[r][2 * c] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(src, 1.0f, false));
-            w[r][2 * c + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(src, 1.0f, true));
-          }
-        } else {
-#pragma unroll
-          for (int x = 0; x < 4; ++x) w[r][x] = T.v[r][4 * hf + x];
+        for (int c = 0; c < 4; ++c) {
+          w[2 * c] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(src[c], 1.0f, false));
+          w[2 * c + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(src[c], 1.0f, true));
         }
-      }
-      if (lim < KEYS) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const bool ok = 4 * kq + r < lim;
-#pragma unroll
-          for (int x = 0; x < 4; ++x) w[r][x] = ok ? w[r][x] : 0u;
-        }
-      }
-#pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        const u32x2 lo = {__builtin_amdgcn_perm(w[1][x], w[0][x], 0x05040100u),
-                          __builtin_amdgcn_perm(w[3][x], w[2][x], 0x05040100u)};
-        const u32x2 hi = {__builtin_amdgcn_perm(w[1][x], w[0][x], 0x07060302u),
-                          __builtin_amdgcn_perm(w[3][x], w[2][x], 0x07060302u)};
-        *(u32x2*)(base + (8 * hf + 2 * x) * VT) = lo;
-        *(u32x2*)(base + (8 * hf + 2 * x + 1) * VT) = hi;
+        for (int x = 0; x < 8; ++x) w[x] = ok ? w[x] : 0u;
+        // 16 dims = 32 bytes per lane; odd rows write their halves in the
+        // other order so that a 16-lane pass covers distinct banks.
+        const int h0 = r & 1;
+        u32x4* dst = (u32x4*)(row + 16 * vc);
+        dst[h0] = h0 ? u32x4{w[4], w[5], w[6], w[7]} : u32x4{w[0], w[1], w[2], w[3]};
+        dst[1 - h0] = h0 ? u32x4{w[0], w[1], w[2], w[3]} : u32x4{w[4], w[5], w[6], w[7]};
+      } else {
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        *(u32x4*)(row + 8 * vc) = ok ? T.v[i] : z;
       }
     }
   }
@@ -268,24 +261,26 @@ struct MfmaAttn {
         p[kg][i] = fast_exp2(x[kg][i] + neg_m);
         l_lane += p[kg][i];
       }
-    // O^T += V^T P^T; V^T rows 16mb + n.  k = 32: keys 4g4.. and 16 + 4g4..;
-    // k = 16: keys 4g4..
+    // O^T += V^T P^T.  k = 32: keys 4g4.. and 16 + 4g4..; k = 16: keys 4g4..
     if constexpr (KG == 2) {
       const uint32_t pw[4] = {pack_bf16(p[0][0], p[0][1]), pack_bf16(p[0][2], p[0][3]),
                               pack_bf16(p[1][0], p[1][1]), pack_bf16(p[1][2], p[1][3])};
+      // Lane (n, g4) addresses row 4g4 + n/4, dims 16mb + 4(n%4): the
+      // transposing read returns keys 4g4..4g4+3 of dim 16mb + n.
+      const __bf16* base = vt + (4 * g4 + n / 4) * kVRow + 4 * (n % 4);
 #pragma unroll
       for (int mb = 0; mb < kMD / 16; ++mb) {
-        const __bf16* row = vt + (16 * mb + n) * VT + 4 * g4;
-        const u32x2 lo = *(const u32x2*)row;
-        const u32x2 hi = *(const u32x2*)(row + 16);
+        const u32x2 lo = lds_read_tr16(base + 16 * mb);
+        const u32x2 hi = lds_read_tr16(base + 16 * kVRow + 16 * mb);
         const uint32_t a[4] = {lo.x, lo.y, hi.x, hi.y};
         acc[mb] = mfma16(a, pw, acc[mb]);
       }
     } else {
       const uint32_t pw[2] = {pack_bf16(p[0][0], p[0][1]), pack_bf16(p[0][2], p[0][3])};
+      const __bf16* base = vt + (4 * g4 + n / 4) * kVRow + 4 * (n % 4);
 #pragma unroll
       for (int mb = 0; mb < kMD / 16; ++mb) {
-        const u32x2 lo = *(const u32x2*)(vt + (16 * mb + n) * VT + 4 * g4);
+        const u32x2 lo = lds_read_tr16(base + 16 * mb);
         const uint32_t a[2] = {lo.x, lo.y};
         acc[mb] = mfma16k16(a, pw, acc[mb]);
       }
