@@ -195,8 +195,14 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num
  *                  ceil(seq_len / block_size) <= max_blocks_per_seq
  *   max_seq_len    host upper bound of seq_lens (sizes the grid)
  *   workspace      device buffer of >= pa_decode_workspace_size(...) bytes
- * Supported: head_size 64 or 128, block_size 16 or 32, num_heads /
- * num_kv_heads in {1, 2, 4, 8}, except f32 with head_size 128.
+ * Supported: head_size 64 or 128, block_size 16, 32, 64 or 128 (the range
+ * [EVAL] gives for a physical block), num_heads / num_kv_heads in
+ * {1, 2, 4, 8}, except f32 with head_size 128.
+ * Engines (results agree within the bf16 rounding of P): with
+ * PA_PARTITION_BALANCED, head_size 128, groups of 4 or 8 and bf16 queries
+ * run on the matrix cores; everything else on the vector ALUs.  The
+ * environment variable PA_DECODE_ENGINE=valu pins the vector engine (read
+ * on every call).
  */
 int32_t pa_decode(void* out, const void* query, int32_t q_dtype,
                   int32_t num_seqs, int32_t num_heads, int32_t head_size,
@@ -228,7 +234,8 @@ int32_t pa_decode(void* out, const void* query, int32_t q_dtype,
  *   max_query_len  host upper bound of the chunks' query counts
  *   block_tables   int32 [num_chunks][max_blocks_per_seq]
  *   seq_lens       int32 [num_chunks]; each >= its chunk's query count
- * Supported: head_size 128, block_size 16 or 32, group size in {1, 2, 4, 8}.
+ * Supported: head_size 128, block_size 16, 32, 64 or 128, group size in
+ * {1, 2, 4, 8}.
  */
 int32_t pa_prefill_chunk(void* out, const void* query, int32_t q_dtype,
                          int32_t num_tokens, int32_t num_heads, int32_t head_size,

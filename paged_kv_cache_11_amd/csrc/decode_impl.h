@@ -393,28 +393,35 @@ struct WaveAttn {
   // L tokens for KV head g through the pipeline: each tile's loads are
   // issued one tile ahead of its computation (ping-pong registers).  The
   // sequence's last block, if partly filled and in the run, comes last.
+  // Blocks here are BS-token tiles: a pool block of 2^sub_shift x BS tokens
+  // (64 or 128) holds 2^sub_shift consecutive ones (the (block, head) tile
+  // of the pool is contiguous), found through table entry index >> sub_shift.
   __device__ __forceinline__ void stream(const void* k_cache, const void* v_cache,
                                          const int32_t* tbl, int g, int num_kv_heads, int first,
-                                         int count, int stride, int L) {
+                                         int count, int stride, int L, int sub_shift) {
     if (count <= 0) return;
     const int nblk = (L + BS - 1) / BS;
     const bool last_partial = (L % BS) != 0 && first + stride * (count - 1) == nblk - 1;
     const int nfull = count - (last_partial ? 1 : 0);
-    const int64_t block_bytes = (int64_t)num_kv_heads * GM::TILE_BYTES;
-    const uint8_t* kbase = (const uint8_t*)k_cache + (int64_t)g * GM::TILE_BYTES + lane * GM::LB;
-    const uint8_t* vbase = (const uint8_t*)v_cache + (int64_t)g * GM::TILE_BYTES + lane * GM::LB;
-    // Block ids of the run, 64 at a time, one per lane.
+    const int sub_mask = (1 << sub_shift) - 1;
+    const int64_t head_bytes = GM::TILE_BYTES << sub_shift;  // one pool block of one head
+    const int64_t block_bytes = (int64_t)num_kv_heads * head_bytes;
+    const uint8_t* kbase = (const uint8_t*)k_cache + (int64_t)g * head_bytes + lane * GM::LB;
+    const uint8_t* vbase = (const uint8_t*)v_cache + (int64_t)g * head_bytes + lane * GM::LB;
+    // Pool block ids of the run, 64 at a time, one per lane.
     int bid_v = 0;
     auto block_id = [&](int j) -> int {
       if ((j & (kWave - 1)) == 0) {
         const int jj = j + lane;
-        bid_v = jj < count ? tbl[first + stride * jj] : 0;
+        bid_v = jj < count ? tbl[(first + stride * jj) >> sub_shift] : 0;
       }
       return __builtin_amdgcn_readlane(bid_v, j & (kWave - 1));
     };
-    auto load_tile = [&](int bid, uint32_t (&kt)[NLOAD][LW], uint32_t (&vt)[NLOAD][LW]) {
-      const uint8_t* kp = kbase + (int64_t)bid * block_bytes;
-      const uint8_t* vp = vbase + (int64_t)bid * block_bytes;
+    auto blk_of = [&](int j) { return first + stride * j; };
+    auto load_tile = [&](int bid, int j, uint32_t (&kt)[NLOAD][LW], uint32_t (&vt)[NLOAD][LW]) {
+      const int64_t off = (int64_t)bid * block_bytes + (int64_t)(blk_of(j) & sub_mask) * GM::TILE_BYTES;
+      const uint8_t* kp = kbase + off;
+      const uint8_t* vp = vbase + off;
 #pragma unroll
       for (int i = 0; i < NLOAD; ++i) {
         if constexpr (LW == 4) {
@@ -436,19 +443,18 @@ struct WaveAttn {
         }
       }
     };
-    auto blk_of = [&](int j) { return first + stride * j; };
     if (nfull > 0) {
       uint32_t ka[NLOAD][LW], va[NLOAD][LW], kb[NLOAD][LW], vb[NLOAD][LW];
-      load_tile(block_id(0), ka, va);
+      load_tile(block_id(0), 0, ka, va);
       int j = 0;
       for (; j + 2 < nfull; j += 2) {
-        load_tile(block_id(j + 1), kb, vb);
+        load_tile(block_id(j + 1), j + 1, kb, vb);
         block<false>(ka, va, blk_of(j), L);
-        load_tile(block_id(j + 2), ka, va);
+        load_tile(block_id(j + 2), j + 2, ka, va);
         block<false>(kb, vb, blk_of(j + 1), L);
       }
       if (nfull - j == 2) {
-        load_tile(block_id(j + 1), kb, vb);
+        load_tile(block_id(j + 1), j + 1, kb, vb);
         block<false>(ka, va, blk_of(j), L);
         block<false>(kb, vb, blk_of(j + 1), L);
       } else {
@@ -457,7 +463,7 @@ struct WaveAttn {
     }
     if (last_partial) {
       uint32_t kt[NLOAD][LW], vt[NLOAD][LW];
-      load_tile(block_id(count - 1), kt, vt);
+      load_tile(block_id(count - 1), count - 1, kt, vt);
       block<true>(kt, vt, blk_of(count - 1), L);
     }
   }
@@ -499,7 +505,7 @@ __global__ __launch_bounds__(kMaxDecodeWaves * kWave) void decode_kernel(
     const void* __restrict__ query, const void* __restrict__ k_cache,
     const void* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
     const int32_t* __restrict__ seq_lens, int max_blocks_per_seq, int num_kv_heads,
-    int partition_blocks, int max_parts, float qk_scale_log2, float v_scale) {
+    int partition_blocks, int max_parts, float qk_scale_log2, float v_scale, int sub_shift) {
   using WA = WaveAttn<KV, QT, D, BS, G>;
   constexpr int EPL = WA::EPL, RPL = WA::RPL;
   using OT = QT;
@@ -524,7 +530,7 @@ __global__ __launch_bounds__(kMaxDecodeWaves * kWave) void decode_kernel(
   const int span = b1 - b0;
   const int nmine = span > w ? (span - w + NW - 1) / NW : 0;
   A.stream(k_cache, v_cache, block_tables + (int64_t)s * max_blocks_per_seq, g, num_kv_heads,
-           b0 + w, nmine, NW, L);
+           b0 + w, nmine, NW, L, sub_shift);
   float l_h[G];
   A.merge_rows(l_h);
 
@@ -697,7 +703,7 @@ __global__ __launch_bounds__(kMaxDecodeWaves * kWave) void decode_balanced_kerne
     const void* __restrict__ k_cache, const void* __restrict__ v_cache,
     const int32_t* __restrict__ block_tables, const int32_t* __restrict__ seq_lens, int num_seqs,
     int max_blocks_per_seq, int num_kv_heads, int workers_per_head, float qk_scale_log2,
-    float v_scale) {
+    float v_scale, int sub_shift) {
   using WA = WaveAttn<KV, QT, D, BS, G>;
   constexpr int EPL = WA::EPL, RPL = WA::RPL;
   using OT = QT;
@@ -729,7 +735,7 @@ __global__ __launch_bounds__(kMaxDecodeWaves * kWave) void decode_balanced_kerne
       A.reset();
       A.q.load(query, (int64_t)s * num_heads + (int64_t)g * G, D, A.col);
       A.stream(k_cache, v_cache, block_tables + (int64_t)s * max_blocks_per_seq, g, num_kv_heads,
-               b_lo, b_hi - b_lo, 1, L);
+               b_lo, b_hi - b_lo, 1, L, sub_shift);
       float l_h[G];
       A.merge_rows(l_h);
       const bool whole = b_lo == 0 && b_hi == nblk;
@@ -843,8 +849,14 @@ inline int decode_waves(int partition_blocks, int max_seq_len, int block_size) {
   return 1;
 }
 
-template <typename KV, typename QT, int D, int BS, int G>
+// PBS: the pool's block size.  The vector engine works on tiles of at most
+// 32 tokens (BS), a pool block of 64 or 128 being 2 or 4 consecutive tiles;
+// the matrix-core engine takes the pool block size directly.
+template <typename KV, typename QT, int D, int PBS, int G>
 hipError_t launch_decode(const DecodeArgs& a) {
+  constexpr int BS = PBS < 32 ? PBS : 32;
+  constexpr int kSubShift = PBS == 128 ? 2 : (PBS == 64 ? 1 : 0);
+  static_assert((BS << kSubShift) == PBS, "pool blocks are whole tiles");
   const float k_scale = std::is_same<KV, FP8>::value ? a.k_scale : 1.0f;
   const float v_scale = std::is_same<KV, FP8>::value ? a.v_scale : 1.0f;
   const float qk = a.scale * k_scale * kLog2e;
@@ -856,7 +868,7 @@ hipError_t launch_decode(const DecodeArgs& a) {
     if constexpr (kHasMfma<KV, QT, D, G>) mfma = a.engine == kEngineMfma;
     if constexpr (kHasMfma<KV, QT, D, G>) {
       if (mfma)
-        hipLaunchKernelGGL((decode_balanced_mfma_kernel<KV, QT, BS, G>), dim3((unsigned)wg),
+        hipLaunchKernelGGL((decode_balanced_mfma_kernel<KV, QT, PBS, G>), dim3((unsigned)wg),
                            dim3(kMaxDecodeWaves * kWave), 0, a.stream, a.out, a.part_o, a.part_ml,
                            a.cuts, a.query, a.k_cache, a.v_cache, a.block_tables, a.seq_lens,
                            a.num_seqs, a.max_blocks_per_seq, a.num_kv_heads, per_head, qk, v_scale);
@@ -865,7 +877,8 @@ hipError_t launch_decode(const DecodeArgs& a) {
       hipLaunchKernelGGL((decode_balanced_kernel<KV, QT, D, BS, G>), dim3((unsigned)wg),
                          dim3(kMaxDecodeWaves * kWave), 0, a.stream, a.out, a.part_o, a.part_ml,
                          a.cuts, a.query, a.k_cache, a.v_cache, a.block_tables, a.seq_lens,
-                         a.num_seqs, a.max_blocks_per_seq, a.num_kv_heads, per_head, qk, v_scale);
+                         a.num_seqs, a.max_blocks_per_seq, a.num_kv_heads, per_head, qk, v_scale,
+                         kSubShift);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((balanced_reduce_kernel<QT, D, G>),
@@ -874,13 +887,13 @@ hipError_t launch_decode(const DecodeArgs& a) {
                        a.out, a.part_o, a.part_ml, a.cuts, a.seq_lens, a.num_kv_heads, v_scale);
     return hipGetLastError();
   }
-  const int nw = a.num_waves > 0 ? a.num_waves
-                                 : decode_waves(a.partition_blocks, a.max_seq_len, BS);
+  const int tiles_per_part = a.partition_blocks << kSubShift;  // 0: whole sequence
+  const int nw = a.num_waves > 0 ? a.num_waves : decode_waves(tiles_per_part, a.max_seq_len, BS);
   hipLaunchKernelGGL((decode_kernel<KV, QT, D, BS, G>),
                      dim3((unsigned)a.max_parts, (unsigned)a.num_kv_heads, (unsigned)a.num_seqs),
                      dim3(nw * kWave), 0, a.stream, a.out, a.part_o, a.part_ml, a.query,
                      a.k_cache, a.v_cache, a.block_tables, a.seq_lens, a.max_blocks_per_seq,
-                     a.num_kv_heads, a.partition_blocks, a.max_parts, qk, v_scale);
+                     a.num_kv_heads, tiles_per_part, a.max_parts, qk, v_scale, kSubShift);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.max_parts <= 1) return e;
   hipLaunchKernelGGL((lse_reduce_kernel<QT, D, G>),
@@ -907,6 +920,8 @@ hipError_t dispatch_block(const DecodeArgs& a) {
   switch (a.block_size) {
     case 16: return dispatch_group<KV, QT, D, 16>(a);
     case 32: return dispatch_group<KV, QT, D, 32>(a);
+    case 64: return dispatch_group<KV, QT, D, 64>(a);
+    case 128: return dispatch_group<KV, QT, D, 128>(a);
     default: return hipErrorInvalidValue;
   }
 }

@@ -323,7 +323,7 @@ namespace pa {
 bool decode_supported(int32_t q_dtype, int32_t cache_dtype, int head_size, int block_size,
                       int group) {
   const bool g_ok = group == 1 || group == 2 || group == 4 || group == 8;
-  const bool bs_ok = block_size == 16 || block_size == 32;
+  const bool bs_ok = block_size == 16 || block_size == 32 || block_size == 64 || block_size == 128;
   if (!g_ok || !bs_ok) return false;
   if (q_dtype == PA_F32 && cache_dtype == PA_F32) return head_size == 64;
   if (q_dtype == PA_BF16 && (cache_dtype == PA_BF16 || cache_dtype == PA_FP8_E4M3))

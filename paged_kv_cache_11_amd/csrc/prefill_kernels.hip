@@ -155,14 +155,17 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(
   const int64_t block_elems = (int64_t)num_kv_heads * BS * kPD;
 
   // A wavefront stages keys 8w .. 8w+7 of a step for K and for V, which lie
-  // in one block (blocks hold a multiple of 8 keys, and a step a multiple
-  // of a block): its physical block is one wave-uniform table entry, read
-  // with a scalar load so that waiting for it never waits for the vector
-  // loads in flight, and a thread's offset inside the block is the same
-  // every step.  Past the last block the last one is re-read; keys at or
-  // past L are zeroed when stored, so every step issues the same loads
-  // unconditionally and the wait for a stage counts only later loads.
-  static_assert(kStep % BS == 0 && BS % 8 == 0, "a step is whole blocks of 8-key groups");
+  // in one block (blocks hold a multiple of 8 keys, and a step is whole
+  // blocks or a whole half or quarter of one): its physical block is one
+  // wave-uniform table entry, read with a scalar load so that waiting for
+  // it never waits for the vector loads in flight, and a thread's offset
+  // inside the block depends on the step only through the step's offset
+  // in a block larger than a step.  Past the last block the last one is
+  // re-read; keys at or past L are zeroed when stored, so every step
+  // issues the same loads unconditionally and the wait for a stage counts
+  // only later loads.
+  static_assert((kStep % BS == 0 || BS % kStep == 0) && BS % 8 == 0,
+                "steps and blocks nest, blocks are whole 8-key groups");
   const int wkey = __builtin_amdgcn_readfirstlane(8 * w);
   const int last_blk = nblk - 1;
   auto block_id = [&](int step) -> int { return tbl[min((step * kStep + wkey) / BS, last_blk)]; };
@@ -170,8 +173,9 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(
   const uint8_t* v_head = (const uint8_t*)v_cache + head_off * EB;
   const int k_off = ((kk % BS) * kPD + kd) * EB;
   const int v_off0 = ((vk % BS) * kPD + vd) * EB, v_off1 = v_off0 + kPD * EB;
-  auto load_stage = [&](int bid, Stage& S) {
-    const int64_t base = (int64_t)bid * block_elems * EB;
+  auto load_stage = [&](int bid, int step, Stage& S) {
+    const int64_t base = (int64_t)bid * block_elems * EB +
+                         (BS > kStep ? (int64_t)((step * kStep) % BS) * kPD * EB : 0);
     const u32x4* kp = (const u32x4*)(k_head + base + k_off);
 #pragma unroll
     for (int v = 0; v < KVEC; ++v) S.k[v] = kp[v];
@@ -321,17 +325,17 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(
   // (The scheduling barriers keep the stages' loads in issue order, which
   // the waits for them count on.)
   Stage sa, sb;
-  load_stage(block_id(0), sa);
+  load_stage(block_id(0), 0, sa);
   __builtin_amdgcn_sched_barrier(0);
-  load_stage(block_id(1), sb);
+  load_stage(block_id(1), 1, sb);
   __builtin_amdgcn_sched_barrier(0);
   int bid = block_id(2);
   store_stage(0, sa, 0);
-  load_stage(bid, sa);
+  load_stage(bid, 2, sa);
   bid = block_id(3);
   __builtin_amdgcn_sched_barrier(0);
   store_stage(1, sb, 1);
-  load_stage(bid, sb);
+  load_stage(bid, 3, sb);
   bid = block_id(4);
   __syncthreads();
   // Scores of even steps live in st_a, of odd steps in st_b.
@@ -346,7 +350,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(
     const int bj1 = bj == 2 ? 0 : bj + 1, bj2 = bj1 == 2 ? 0 : bj1 + 1;
     __syncthreads();
     store_stage(j + 2, S, bj2);
-    load_stage(bid, S);  // step j+4; past the last step: harmless re-reads
+    load_stage(bid, j + 4, S);  // past the last step: harmless re-reads
     bid = block_id(j + 5);
     if (active(j)) {  // later steps are inactive too: nothing is left to do
       const float neg_m = softmax_head(j, st_cur);
@@ -446,6 +450,8 @@ static hipError_t prefill_block(const PrefillArgs& a) {
   switch (a.block_size) {
     case 16: return prefill_group<KV, 16>(a);
     case 32: return prefill_group<KV, 32>(a);
+    case 64: return prefill_group<KV, 64>(a);
+    case 128: return prefill_group<KV, 128>(a);
     default: return hipErrorInvalidValue;
   }
 }
@@ -453,7 +459,8 @@ static hipError_t prefill_block(const PrefillArgs& a) {
 bool prefill_supported(int32_t q_dtype, int32_t cache_dtype, int head_size, int block_size,
                        int group) {
   return q_dtype == PA_BF16 && (cache_dtype == PA_BF16 || cache_dtype == PA_FP8_E4M3) &&
-         head_size == kPD && (block_size == 16 || block_size == 32) &&
+         head_size == kPD &&
+         (block_size == 16 || block_size == 32 || block_size == 64 || block_size == 128) &&
          (group == 1 || group == 2 || group == 4 || group == 8);
 }
 

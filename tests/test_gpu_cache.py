@@ -114,9 +114,10 @@ def test_copy_blocks_copy_on_write_after_fork(prefix_len):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "fp8"])
-def test_copy_blocks_random_pairs(dtype):
-    rng = np.random.default_rng(22)
-    nb, Hkv, bs, D = 64, 4, 32, 128 if dtype != "f32" else 64
+@pytest.mark.parametrize("bs", [32, 128])
+def test_copy_blocks_random_pairs(dtype, bs):
+    rng = np.random.default_rng(22 + bs)
+    nb, Hkv, D = 64, 4, 128 if dtype != "f32" else 64
     kp = torch.from_numpy(rng.integers(0, 255, (nb, Hkv, bs, D * wl.ELEM_BYTES[dtype]),
                                        dtype=np.uint8)).to(G.DEV)
     vp = torch.from_numpy(rng.integers(0, 255, (nb, Hkv, bs, D * wl.ELEM_BYTES[dtype]),

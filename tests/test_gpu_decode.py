@@ -125,9 +125,12 @@ def test_decode_empty_and_single_token_sequences(ps):
     (8, 8, 128, 16, "bf16"), (16, 8, 128, 32, "bf16"), (64, 8, 128, 16, "bf16"),
     (32, 8, 64, 16, "bf16"), (32, 4, 64, 32, "fp8"), (16, 2, 128, 16, "fp8"),
     (8, 8, 64, 32, "f32"), (16, 2, 64, 16, "f32"),
+    # pool blocks of 64 and 128 tokens
+    (8, 8, 128, 64, "bf16"), (16, 8, 128, 128, "bf16"), (32, 8, 128, 64, "bf16"),
+    (64, 8, 128, 128, "fp8"), (32, 4, 64, 64, "fp8"), (16, 2, 64, 128, "f32"),
 ])
 def test_decode_shapes(Hq, Hkv, D, bs, kv):
-    """Group sizes 1/2/4/8, head sizes 64/128, block sizes 16/32, ragged lengths."""
+    """Group sizes 1/2/4/8, head sizes 64/128, block sizes 16 to 128, ragged lengths."""
     rng = np.random.default_rng(Hq * 1000 + Hkv * 100 + D + bs)
     lens = np.array([1, bs - 1, bs, bs + 1, 3 * bs + 5, 700, 1333, 2], dtype=np.int32)
     nblk = (lens + bs - 1) // bs
@@ -210,7 +213,8 @@ def _shape_batch(Hq, Hkv, D, bs, kv, lens, seed):
 @pytest.mark.parametrize("engine", ["valu", "mfma"])
 @pytest.mark.parametrize("Hq,Hkv,bs,kv", [
     (32, 8, 16, "bf16"), (32, 8, 32, "bf16"), (64, 8, 16, "bf16"), (64, 8, 32, "fp8"),
-    (32, 8, 16, "fp8"), (16, 2, 32, "fp8"),
+    (32, 8, 16, "fp8"), (16, 2, 32, "fp8"), (32, 8, 64, "bf16"), (64, 8, 128, "fp8"),
+    (32, 8, 128, "bf16"),
 ])
 def test_decode_balanced_engines(engine, Hq, Hkv, bs, kv, monkeypatch):
     """Both engines of the balanced split (vector ALU and matrix cores) on

@@ -83,6 +83,8 @@ def _varlen_case(Hq, Hkv, bs, kv, seed):
 @pytest.mark.parametrize("Hq,Hkv,bs,kv", [
     (8, 8, 16, "bf16"), (16, 8, 32, "bf16"), (32, 8, 16, "bf16"), (64, 8, 32, "bf16"),
     (32, 8, 32, "fp8"), (16, 4, 16, "fp8"),
+    # pool blocks of 64 and 128 tokens (a 64-key step spans a whole block or half of one)
+    (32, 8, 64, "bf16"), (64, 8, 128, "fp8"), (16, 8, 128, "bf16"),
 ])
 def test_prefill_varlen_chunks(Hq, Hkv, bs, kv):
     """Five chunks: a single-query prompt, a chunk inside a longer context,
