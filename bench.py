@@ -178,7 +178,7 @@ def _time_us(fn, iters, warmup=3):
     return a.elapsed_time(b) / iters * 1e3
 
 
-ROW_GROUPS = ("long_context", "shared_prefix", "mixed_fp8")
+ROW_GROUPS = ("long_context", "shared_prefix", "mixed_fp8", "block_sizes")
 
 
 def row_measurements(dev, iters=20, groups=ROW_GROUPS):
@@ -300,6 +300,27 @@ def row_measurements(dev, iters=20, groups=ROW_GROUPS):
         us_step = _time_us(lambda i: (cw(i), dec(i), pre(i)), iters)
         rows["mixed_step_fp8"] = {"us": round(us_step, 2),
                                   "step": "cache_write(544 tokens) + decode(32 seqs) + prefill(512 queries)"}
+    if "block_sizes" in groups:
+        # The headline decode over pool blocks of 64 and 128 tokens (same
+        # lengths and values), balanced split, three pool copies rotated.
+        for bs in (64, 128):
+            b = wl.llama3_8b_decode(block_size=bs)
+            sets = _gpu_pools(b, dev, copies=N_SETS)
+            q = wl.storage_tensor(b.q, b.q_dtype).to(dev)
+            out = torch.empty_like(q)
+            tb, ln = torch.from_numpy(b.block_tables).to(dev), torch.from_numpy(b.seq_lens).to(dev)
+            ws = torch.empty(pa.pa_decode_workspace_size(b.num_seqs, b.num_heads, b.num_kv_heads,
+                                                         b.head_size, b.max_seq_len, -1),
+                             dtype=torch.uint8, device=dev)
+            us = _time_us(lambda i: pa.pa_decode(out, q, sets[i % N_SETS][0], sets[i % N_SETS][1],
+                                                 tb, ln, b.max_seq_len, b.scale, partition_size=-1,
+                                                 workspace=ws), iters)
+            by = b.decode_kv_bytes()
+            rows[f"decode_llama3_8b_bs{bs}"] = {"us": round(us, 2), "kv_bytes": by,
+                                               "gbs": round(by / us / 1e3, 1),
+                                               "pct_hbm_peak": round(100 * by / us / 1e3 / HBM_PEAK_GBS, 2)}
+            del sets
+            torch.cuda.empty_cache()
     return rows
 
 

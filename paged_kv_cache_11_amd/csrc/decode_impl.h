@@ -600,7 +600,7 @@ __global__ __launch_bounds__(kMaxDecodeWaves * kWave) void decode_kernel(
 // adjacent, so the heads' tiles of a block (contiguous in the pool) are read
 // together.
 // ---------------------------------------------------------------------------
-constexpr int kBalancedMinBlocks = 16;  // fewest blocks a worker is given
+constexpr int kBalancedMinTokens = 256;  // fewest tokens a worker is given
 
 
 __device__ __forceinline__ int nblocks_of(int L, int bs) { return (L + bs - 1) / bs; }
@@ -651,8 +651,11 @@ __device__ __forceinline__ int worker_of(int64_t T, int64_t x, int W) {
   return (int)(((x + 1) * W + T - 1) / T - 1);
 }
 
-__device__ __forceinline__ int effective_workers(int64_t T, int W) {
-  const int64_t want = (T + kBalancedMinBlocks - 1) / kBalancedMinBlocks;
+// Workers actually used for T blocks of bs tokens: at most W, and none with
+// fewer than kBalancedMinTokens tokens (rounded to whole blocks).
+__device__ __forceinline__ int effective_workers(int64_t T, int W, int bs) {
+  const int min_blocks = kBalancedMinTokens / bs > 1 ? kBalancedMinTokens / bs : 1;
+  const int64_t want = (T + min_blocks - 1) / min_blocks;
   return (int)(want < W ? (want > 0 ? want : 1) : W);
 }
 
@@ -714,7 +717,7 @@ __global__ __launch_bounds__(kMaxDecodeWaves * kWave) void decode_balanced_kerne
   const int num_heads = num_kv_heads * G;
 
   const int64_t T = total_blocks(seq_lens, num_seqs, BS, lane);
-  const int W = effective_workers(T, workers_per_head);
+  const int W = effective_workers(T, workers_per_head, BS);
   if (vw >= W) return;
   const int64_t start = worker_start(T, vw, W), end = worker_start(T, vw + 1, W);
   if (start >= end) return;

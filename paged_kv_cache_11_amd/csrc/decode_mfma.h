@@ -78,6 +78,10 @@ struct MfmaAttn {
   static constexpr int KEYS = MfmaTileKeys<KV>::value;     // keys per tile
   static constexpr int KG = KEYS / 16;                      // 16-key groups per tile
   static constexpr int NBT = KEYS > BS ? KEYS / BS : 1;     // blocks a tile touches
+  // Unit of the balanced split: runs start and end on multiples of UBS
+  // tokens (a pool block, or a 32-token part of a larger one), so that runs
+  // are balanced to 32 tokens whatever the block size.
+  static constexpr int UBS = BS < 32 ? BS : 32;
   static constexpr int KL = 16 * kMD * EB / (kWave * 16);   // K 16-byte loads per key group
   static constexpr int CPR = kMD * EB / 16;                 // 16-byte chunks of a V row
   static constexpr int VRL = kWave / CPR;                   // V rows per wavefront load
@@ -135,19 +139,19 @@ struct MfmaAttn {
     }
   }
 
-  // Loads tile t of a run: its keys are run keys t*KEYS .. +KEYS, block j of
-  // the run holding keys j*BS .. +BS; bid(j) gives physical block ids.
+  // Loads the tile whose first key is k0 (a sequence position; a multiple
+  // of 16, and of KEYS when blocks hold at least 32 tokens); bid(j) gives
+  // the physical id of the sequence's block j.
   template <typename BidFn>
   __device__ __forceinline__ void load_tile(const uint8_t* kh, const uint8_t* vh, int64_t block_bytes,
-                                            int t, BidFn bid, Tile& T) const {
-    const int k0 = t * KEYS;  // first run key of the tile
+                                            int k0, BidFn bid, Tile& T) const {
     int b[NBT];
 #pragma unroll
     for (int u = 0; u < NBT; ++u) b[u] = bid(k0 / BS + u);
 #pragma unroll
     for (int kg = 0; kg < KG; ++kg) {
       const int key = k0 + 16 * kg;  // a 16-key group lies in one block
-      const uint8_t* kb = kh + (int64_t)b[(16 * kg) / BS] * block_bytes +
+      const uint8_t* kb = kh + (int64_t)b[key / BS - k0 / BS] * block_bytes +
                           ((key % BS) + n) * kMD * EB + 16 * g4;
 #pragma unroll
       for (int i = 0; i < KL; ++i) T.k[kg][i] = *(const u32x4*)(kb + 64 * i);
@@ -155,10 +159,10 @@ struct MfmaAttn {
     // V: wavefront load i reads rows VRL*i .. +VRL of the tile, whole rows.
 #pragma unroll
     for (int i = 0; i < VL; ++i) {
-      const int r = vr + VRL * i;  // tile row; the tile's rows are keys k0 + r
-      const int u = ((k0 % BS) + r) / BS;
+      const int key = k0 + vr + VRL * i;  // tile row vr + VRL*i
+      const int u = key / BS - k0 / BS;
       const int bb = NBT == 1 ? b[0] : b[u < NBT ? u : NBT - 1];
-      T.v[i] = *(const u32x4*)(vh + (int64_t)bb * block_bytes + ((k0 + r) % BS) * kMD * EB + 16 * vc);
+      T.v[i] = *(const u32x4*)(vh + (int64_t)bb * block_bytes + (key % BS) * kMD * EB + 16 * vc);
     }
   }
 
@@ -287,7 +291,8 @@ struct MfmaAttn {
     }
   }
 
-  // Blocks first .. first+count-1 of a sequence of L tokens, KV head g.
+  // Units first .. first+count-1 (UBS tokens each) of a sequence of L
+  // tokens, KV head g.
   __device__ __forceinline__ void stream(const void* k_cache, const void* v_cache, const int32_t* tbl,
                                          int g, int num_kv_heads, int first, int count, int L) {
     if (count <= 0) return;
@@ -295,34 +300,38 @@ struct MfmaAttn {
     const int64_t block_bytes = (int64_t)num_kv_heads * tile_bytes;
     const uint8_t* kh = (const uint8_t*)k_cache + (int64_t)g * tile_bytes;
     const uint8_t* vh = (const uint8_t*)v_cache + (int64_t)g * tile_bytes;
-    // Keys of the run: first*BS .. min(L, (first+count)*BS).
-    const int run_keys = ((first + count) * BS < L ? (first + count) * BS : L) - first * BS;
-    const int ntiles = (count * BS + KEYS - 1) / KEYS;
+    // Keys of the run: key0 .. min(L, key0 + count*UBS); its blocks
+    // blk0 .. blk_last.
+    const int key0 = first * UBS;
+    const int run_end = (first + count) * UBS < L ? (first + count) * UBS : L;
+    const int blk0 = key0 / BS, blk_last = ((first + count) * UBS - 1) / BS;
+    const int ntiles = (count * UBS + KEYS - 1) / KEYS;
     // Block ids of the run, 64 at a time, one per lane (the requests come
     // in non-decreasing order); past the run the last block is repeated
     // (its keys are masked).
     int bid_v = 0, cached = -1;
-    auto bid = [&](int j) -> int {
-      j = j < count ? j : count - 1;
+    auto bid = [&](int blk) -> int {
+      const int j = (blk < blk_last ? blk : blk_last) - blk0;
       const int chunk = j / kWave;
       if (chunk != cached) {
-        const int jj = chunk * kWave + lane;
-        bid_v = tbl[first + (jj < count ? jj : count - 1)];
+        const int jj = blk0 + chunk * kWave + lane;
+        bid_v = tbl[jj < blk_last ? jj : blk_last];
         cached = chunk;
       }
       return __builtin_amdgcn_readlane(bid_v, j % kWave);
     };
     auto limit = [&](int t) {
-      const int lim = run_keys - t * KEYS;
+      const int lim = run_end - (key0 + t * KEYS);
       return lim < KEYS ? lim : KEYS;
     };
+    auto k0_of = [&](int t) { return key0 + t * KEYS; };
     Tile ta, tb;
-    load_tile(kh, vh, block_bytes, 0, bid, ta);
+    load_tile(kh, vh, block_bytes, k0_of(0), bid, ta);
     int t = 0;
     for (; t + 2 <= ntiles; t += 2) {
-      load_tile(kh, vh, block_bytes, t + 1, bid, tb);
+      load_tile(kh, vh, block_bytes, k0_of(t + 1), bid, tb);
       tile(ta, limit(t));
-      load_tile(kh, vh, block_bytes, t + 2 < ntiles ? t + 2 : t + 1, bid, ta);
+      load_tile(kh, vh, block_bytes, k0_of(t + 2 < ntiles ? t + 2 : t + 1), bid, ta);
       tile(tb, limit(t + 1));
     }
     if (t < ntiles) tile(ta, limit(t));
@@ -355,21 +364,21 @@ __global__ __launch_bounds__(kMaxDecodeWaves * kWave, 2) void decode_balanced_mf
   if (vw >= workers_per_head) return;
   const int num_heads = num_kv_heads * G;
 
-  const int64_t T = total_blocks(seq_lens, num_seqs, BS, lane);
-  const int W = effective_workers(T, workers_per_head);
+  const int64_t T = total_blocks(seq_lens, num_seqs, MA::UBS, lane);
+  const int W = effective_workers(T, workers_per_head, MA::UBS);
   if (vw >= W) return;
   const int64_t start = worker_start(T, vw, W), end = worker_start(T, vw + 1, W);
   if (start >= end) return;
   int s;
   int64_t base;
-  locate_block(seq_lens, num_seqs, BS, start, lane, s, base);
+  locate_block(seq_lens, num_seqs, MA::UBS, start, lane, s, base);
 
   MA A;
   A.init(lane, qk_scale_log2, vt_lds[wv]);
   int64_t pos = start;
   while (pos < end && s < num_seqs) {
     const int L = seq_lens[s];
-    const int nblk = nblocks_of(L, BS);
+    const int nblk = nblocks_of(L, MA::UBS);  // units of the split
     const int64_t seg_end = base + nblk;
     if (nblk > 0) {
       const int b_lo = (int)(pos - base);

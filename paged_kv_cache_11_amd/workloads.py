@@ -145,12 +145,15 @@ def tiny_decode(seed: int = 1235) -> PagedBatch:
 
 
 def llama3_8b_decode(seed: int = 1236, num_seqs: int = 64, min_len: int = 512,
-                     max_len: int = 4096, kv_dtype: str = "bf16") -> PagedBatch:
+                     max_len: int = 4096, kv_dtype: str = "bf16",
+                     block_size: int = 16) -> PagedBatch:
     """Llama-3-8B-shape decode: 64 sequences with lengths uniform in
-    [512, 4096], 32 query heads over 8 KV heads, head size 128, block 16,
-    pool sized 1.25x the blocks needed, tables drawn from a shuffled pool."""
+    [512, 4096], 32 query heads over 8 KV heads, head size 128, block 16
+    (64 and 128 are the larger blocks of the same workload: same lengths and
+    values, fewer and larger table entries), pool sized 1.25x the blocks
+    needed, tables drawn from a shuffled pool."""
     rng = np.random.default_rng(seed)
-    Hq, Hkv, D, bs = 32, 8, 128, 16
+    Hq, Hkv, D, bs = 32, 8, 128, block_size
     seq_lens = rng.integers(min_len, max_len + 1, size=num_seqs, dtype=np.int64).astype(np.int32)
     needed = int(sum((int(L) + bs - 1) // bs for L in seq_lens))
     nb = _pool_blocks(needed)
@@ -161,7 +164,8 @@ def llama3_8b_decode(seed: int = 1236, num_seqs: int = 64, min_len: int = 512,
     k = _normal(rng, (T, Hkv, D))
     v = _normal(rng, (T, Hkv, D))
     slots = np.concatenate([_slots_for(tables[s], seq_lens[s], bs) for s in range(num_seqs)])
-    return PagedBatch("llama3_8b_decode_bf16", Hq, Hkv, D, bs, nb, "bf16", "bf16", kv_dtype,
+    name = "llama3_8b_decode_bf16" if bs == 16 else f"llama3_8b_decode_bf16_bs{bs}"
+    return PagedBatch(name, Hq, Hkv, D, bs, nb, "bf16", "bf16", kv_dtype,
                       1.0 / math.sqrt(D), q, k, v, slots, seq_lens, tables)
 
 
