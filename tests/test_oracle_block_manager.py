@@ -1,0 +1,174 @@
+"""Pins of the reference block manager (oracle/block_manager.py) to the
+pages' figures and to invariants checked by brute force."""
+import random
+
+import pytest
+
+from conftest import load_golden
+from oracle.block_manager import BlockManager, OutOfBlocks
+
+
+def test_deep_interleaved_figure():
+    """Two requests growing token by token into a 9-block pool reproduce the
+    figure of "vLLM 深度解析" §3.1: R1 (41 tokens) in blocks [1, 3, 5], R2
+    (56 tokens) in [0, 2, 4, 6], blocks 7 and 8 free.  The interleaving
+    (R2's block before R1's at every block boundary) and the first-in
+    first-out free list are what make the physical picture."""
+    g = load_golden("deep_two_requests.json")
+    bs = g["printed"]["block_size"]
+    m = BlockManager(g["printed"]["num_physical_blocks"], bs)
+    m.add("R2", 0)
+    m.add("R1", 0)
+    lens = g["derived_by_hand"]["seq_lens"]
+    last = {}
+    for t in range(max(lens.values())):
+        ids = [r for r in ("R2", "R1") if t < lens[r]]
+        slots, pairs = m.append(ids)
+        assert pairs == []
+        for r, s in zip(ids, slots):
+            last[r] = s
+    for r in ("R1", "R2"):
+        assert m.table(r) == g["printed"]["requests"][r]["block_table"]
+        assert m.seq_len(r) == lens[r]
+        assert last[r] == g["derived_by_hand"]["last_token_slot"][r]
+        assert len(m.table(r)) * bs - m.seq_len(r) == g["derived_by_hand"]["waste_tokens"][r]
+    owner = g["printed"]["physical_owner"]
+    for b, o in enumerate(owner):
+        if o == "FREE":
+            assert m.ref[b] == 0 and b in m.free
+        else:
+            r, i = o.split("-")
+            assert m.table(r)[int(i)] == b and m.ref[b] == 1
+
+
+def test_lib_worked_example():
+    """A 50-token sequence at block size 16 takes 4 blocks; with the free
+    list starting 102, 205, 78, 33 its table is the page's [102, 205, 78, 33]
+    and its slots are the hand-derived ranges."""
+    g = load_golden("lib_block_table_example.json")
+    p, d = g["printed"], g["derived_by_hand"]
+    order = p["block_table"] + [b for b in range(256) if b not in p["block_table"]]
+    m = BlockManager(256, p["block_size"], free_order=order)
+    slots = m.add("S", p["seq_len"])
+    assert m.table("S") == p["block_table"]
+    ranges = [[slots[i * 16], slots[min(i * 16 + 15, p["seq_len"] - 1)]] for i in range(p["num_blocks"])]
+    assert ranges == d["slot_ranges"]
+    assert p["seq_len"] - (p["num_blocks"] - 1) * p["block_size"] == d["last_block_fill"]
+    assert p["num_blocks"] * p["block_size"] - p["seq_len"] == d["waste_tokens"]
+
+
+def test_deep_prefix_sharing_and_copy_on_write():
+    """A 20-token system prompt (blocks 0 and 1) shared by A, B, C: both
+    blocks are held three times.  The first own token of A and of B lands in
+    a shared, partly filled block, so each copies it first; C, by then the
+    block's only holder, writes in place.  Block 0 (full) is never copied."""
+    g = load_golden("deep_prefix_sharing.json")
+    bs = g["printed"]["block_size"]
+    m = BlockManager(16, bs)
+    m.add("A", g["printed"]["system_prompt_tokens"])
+    m.fork("A", "B")
+    m.fork("A", "C")
+    assert m.table("A") == g["printed"]["shared"]
+    assert [m.ref[b] for b in g["printed"]["shared"]] == [3, 3]
+    slots, pairs = m.append(["A", "B", "C"])
+    assert pairs == [(1, 2), (1, 3)]
+    assert m.table("A") == [0, 2] and m.table("B") == [0, 3] and m.table("C") == [0, 1]
+    assert slots == [2 * bs + 4, 3 * bs + 4, 1 * bs + 4]
+    assert m.ref[0] == 3 and m.ref[1] == 1
+    # Filling A's copied block and opening the next never copies again.
+    for _ in range(12):
+        _, pairs = m.append(["A"])
+        assert pairs == []
+    assert m.table("A") == [0, 2, 4]
+
+
+def _check_content(m, mem, content):
+    """Every live sequence reads back exactly its tokens through its table."""
+    bs = m.block_size
+    for sid, toks in content.items():
+        tbl = m.table(sid)
+        assert len(toks) == m.seq_len(sid)
+        assert len(tbl) == -(-len(toks) // bs)
+        for t, tok in enumerate(toks):
+            assert mem[tbl[t // bs] * bs + t % bs] == tok, (sid, t)
+
+
+def _check_counts(m):
+    held = [0] * m.num_blocks
+    for sid in m.seqs:
+        for b in m.table(sid):
+            held[b] += 1
+    assert held == m.ref
+    assert len(set(m.free)) == len(m.free)
+    assert sorted(m.free) == [b for b in range(m.num_blocks) if m.ref[b] == 0]
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_traces_keep_every_sequence_readable(seed):
+    """Random add / fork / append / free traces over a small pool, with a
+    brute-force token memory: block copies are applied as the pairs say,
+    writes go to the returned slots, and every live sequence must read back
+    its own tokens; reference counts equal table occurrences and the free
+    list is exactly the unreferenced blocks.  Out-of-blocks requests must
+    leave everything unchanged."""
+    rng = random.Random(seed)
+    bs = rng.choice([2, 4, 16])
+    m = BlockManager(rng.randint(8, 40), bs)
+    mem = [None] * (m.num_blocks * bs)
+    content = {}
+    next_id, next_tok = 0, 0
+    for _ in range(400):
+        op = rng.random()
+        live = list(content)
+        try:
+            if op < 0.2 or not live:
+                n = rng.randint(0, 3 * bs)
+                slots = m.add(next_id, n)
+                toks = list(range(next_tok, next_tok + n))
+                next_tok += n
+                for s, tok in zip(slots, toks):
+                    mem[s] = tok
+                content[next_id] = toks
+                next_id += 1
+            elif op < 0.35:
+                p = rng.choice(live)
+                m.fork(p, next_id)
+                content[next_id] = list(content[p])
+                next_id += 1
+            elif op < 0.85:
+                ids = rng.sample(live, rng.randint(1, len(live)))
+                before = (list(m.free), list(m.ref), {k: dict(v, blocks=list(v["blocks"])) for k, v in m.seqs.items()})
+                try:
+                    slots, pairs = m.append(ids)
+                except OutOfBlocks:
+                    assert (m.free, m.ref, m.seqs) == before
+                    continue
+                for src, dst in pairs:  # the block copy happens before the writes
+                    mem[dst * bs:(dst + 1) * bs] = mem[src * bs:(src + 1) * bs]
+                for sid, s in zip(ids, slots):
+                    mem[s] = next_tok
+                    content[sid].append(next_tok)
+                    next_tok += 1
+            else:
+                sid = rng.choice(live)
+                m.release(sid)
+                del content[sid]
+        except OutOfBlocks:
+            pass
+        _check_counts(m)
+        _check_content(m, mem, content)
+
+
+def test_out_of_blocks_changes_nothing():
+    m = BlockManager(3, 4)
+    m.add("a", 4)
+    m.add("b", 4)
+    m.fork("a", "c")
+    # a and c share a full block: appending to all three needs 3 new blocks.
+    before = (list(m.free), list(m.ref), {k: dict(v, blocks=list(v["blocks"])) for k, v in m.seqs.items()})
+    with pytest.raises(OutOfBlocks):
+        m.append(["a", "b", "c"])
+    assert (m.free, m.ref, m.seqs) == before
+    with pytest.raises(OutOfBlocks):
+        m.add("d", 5)
+    assert m.num_free() == 1
