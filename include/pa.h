@@ -79,7 +79,8 @@ enum {
   PA_ERR_INVALID = -1,     /* null pointer, bad size, inconsistent arguments   */
   PA_ERR_UNSUPPORTED = -2, /* dtype / head_size / block_size / group not built */
   PA_ERR_WORKSPACE = -3,   /* workspace missing or too small                   */
-  PA_ERR_HIP = -4          /* the HIP runtime refused a launch                 */
+  PA_ERR_HIP = -4,         /* the HIP runtime refused a launch                 */
+  PA_ERR_NO_BLOCKS = -5    /* block manager: the free list cannot cover it     */
 };
 
 /* Library version, major * 10000 + minor * 100 + patch. */
@@ -246,6 +247,72 @@ int32_t pa_prefill_chunk(void* out, const void* query, int32_t q_dtype,
                          const int32_t* block_tables, int32_t max_blocks_per_seq,
                          const int32_t* seq_lens,
                          float scale, float k_scale, float v_scale, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Host block manager ([LIB] §4.2 item 3 block pool, §4.3 item 2 new token;
+ * [EVAL] the fork / append / free primitives and copy-on-write; [DEEP] §3.1)
+ * ---------------------------------------------------------------------------
+ * A host-side pool of num_blocks physical block ids, handed out first in,
+ * first out (the order that reproduces [DEEP] §3.1's interleaved 9-block
+ * figure), with a reference count per block and one block table per
+ * sequence, keyed by a caller-chosen int64 id.  It produces the inputs of
+ * the device calls: slot mappings for pa_cache_write, copy-on-write pairs
+ * for pa_copy_blocks, block tables and lengths for pa_decode and
+ * pa_prefill_chunk.  Unlike the device calls, every array argument here is
+ * a HOST pointer owned by the caller; the manager owns its own host memory
+ * (released by pa_bm_destroy) and no device memory.  Calls on one manager
+ * must not overlap (no locking); each costs O(1) per token, block or
+ * sequence it touches.
+ * Errors: PA_ERR_INVALID (NULL pointer, negative size, unknown or
+ * duplicate id), PA_ERR_NO_BLOCKS (the free list cannot cover the request;
+ * the manager is left unchanged).  Running out of host memory is fatal.
+ */
+typedef struct pa_block_manager pa_block_manager;
+
+/* A manager of blocks 0 .. num_blocks-1 of block_size tokens, all free.
+ * Returns NULL (and sets pa_last_error) for non-positive sizes. */
+pa_block_manager* pa_bm_create(int32_t num_blocks, int32_t block_size);
+void pa_bm_destroy(pa_block_manager* bm);
+
+/* Number of free blocks (>= 0), or PA_ERR_INVALID. */
+int32_t pa_bm_num_free(const pa_block_manager* bm);
+
+/* A new sequence of num_tokens tokens (its prompt): takes
+ * ceil(num_tokens / block_size) blocks and writes the slot of every token to
+ * slot_mapping[0 .. num_tokens-1]. */
+int32_t pa_bm_add(pa_block_manager* bm, int64_t seq_id, int32_t num_tokens, int64_t* slot_mapping);
+
+/* One new token for each of seq_ids[0 .. num_seqs-1], in order (a decode
+ * step; an id may repeat).  slot_mapping[i] receives the slot of token i.
+ * A sequence whose last block is full takes a new block; one whose last
+ * block is shared and not full first copies it (copy-on-write): the pair
+ * (shared block, fresh block) is written to cow_pairs[2c], cow_pairs[2c+1]
+ * (int64 [num_seqs][2] capacity) and *num_cow counts the pairs.  The copies
+ * must happen (pa_copy_blocks) before the new tokens are written
+ * (pa_cache_write). */
+int32_t pa_bm_append(pa_block_manager* bm, int32_t num_seqs, const int64_t* seq_ids,
+                     int64_t* slot_mapping, int64_t* cow_pairs, int32_t* num_cow);
+
+/* child_id becomes a sequence sharing every block of parent_id (one more
+ * reference each); nothing is copied. */
+int32_t pa_bm_fork(pa_block_manager* bm, int64_t parent_id, int64_t child_id);
+
+/* Releases a sequence: one reference less on each of its blocks; blocks at
+ * zero return to the back of the free list, in table order. */
+int32_t pa_bm_free(pa_block_manager* bm, int64_t seq_id);
+
+/* Tokens of a sequence (>= 0), or PA_ERR_INVALID. */
+int32_t pa_bm_seq_len(const pa_block_manager* bm, int64_t seq_id);
+
+/* Block tables of seq_ids[0 .. num_seqs-1] into block_tables (int32
+ * [num_seqs][max_blocks_per_seq], entries past a table's end set to -1) and
+ * their lengths into seq_lens (int32 [num_seqs]); PA_ERR_INVALID (nothing
+ * written) if a table is longer than max_blocks_per_seq. */
+int32_t pa_bm_block_tables(const pa_block_manager* bm, int32_t num_seqs, const int64_t* seq_ids,
+                           int32_t max_blocks_per_seq, int32_t* block_tables, int32_t* seq_lens);
+
+/* References held on a block (0 = free), or PA_ERR_INVALID. */
+int32_t pa_bm_ref_count(const pa_block_manager* bm, int32_t block);
 
 #ifdef __cplusplus
 }

@@ -5,6 +5,7 @@ The compute lives in ``libpa.so`` (hand-written HIP, C ABI in include/pa.h);
 ``workloads`` holds the seeded synthetic input generators.
 """
 from .binding import (  # noqa: F401
-    PA_BF16, PA_F32, PA_FP8_E4M3, PA_PARTITION_BALANCED, PagedAttentionError, load, pa_cache_write, pa_copy_blocks,
+    PA_BF16, PA_F32, PA_FP8_E4M3, PA_PARTITION_BALANCED, BlockManager, PagedAttentionError, load,
+    pa_cache_write, pa_copy_blocks,
     pa_decode, pa_decode_workspace_size, pa_pool_bytes, pa_prefill_chunk, pa_version,
 )

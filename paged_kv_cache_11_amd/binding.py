@@ -24,6 +24,7 @@ from typing import Optional
 PA_F32, PA_BF16, PA_FP8_E4M3 = 0, 1, 2
 PA_PARTITION_BALANCED = -1
 PA_OK, PA_ERR_INVALID, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = 0, -1, -2, -3, -4
+PA_ERR_NO_BLOCKS = -5
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
 
@@ -45,6 +46,17 @@ _SIGNATURES = {
     "pa_prefill_chunk": ([_c_p, _c_p, _c_int, _c_int, _c_int, _c_int, _c_p, _c_int, _c_int, _c_p,
                           _c_p, _c_int, _c_int, _c_int, _c_int, _c_p, _c_int, _c_p, _c_f, _c_f,
                           _c_f, _c_p], _c_int),
+    # host block manager
+    "pa_bm_create": ([_c_int, _c_int], _c_p),
+    "pa_bm_destroy": ([_c_p], None),
+    "pa_bm_num_free": ([_c_p], _c_int),
+    "pa_bm_add": ([_c_p, ctypes.c_int64, _c_int, _c_p], _c_int),
+    "pa_bm_append": ([_c_p, _c_int, _c_p, _c_p, _c_p, _c_p], _c_int),
+    "pa_bm_fork": ([_c_p, ctypes.c_int64, ctypes.c_int64], _c_int),
+    "pa_bm_free": ([_c_p, ctypes.c_int64], _c_int),
+    "pa_bm_seq_len": ([_c_p, ctypes.c_int64], _c_int),
+    "pa_bm_block_tables": ([_c_p, _c_int, _c_p, _c_int, _c_p, _c_p], _c_int),
+    "pa_bm_ref_count": ([_c_p, _c_int], _c_int),
 }
 
 
@@ -191,3 +203,77 @@ def pa_prefill_chunk(out, query, query_start_loc, max_query_len: int, k_cache, v
                                    dtype_code(k_cache), nb, bs, hkv, _ptr(block_tables),
                                    int(block_tables.shape[1]), _ptr(seq_lens), float(scale),
                                    float(k_scale), float(v_scale), _stream(stream)))
+
+
+class BlockManager:
+    """The host block manager of the library (pa_bm_*): a first-in first-out
+    free list of physical blocks, reference counts, and fork / append / free
+    with copy-on-write.  Arrays are numpy host arrays; copy them to the
+    device for pa_cache_write, pa_copy_blocks and pa_decode."""
+
+    def __init__(self, num_blocks: int, block_size: int):
+        self._lib = load()
+        self._h = self._lib.pa_bm_create(int(num_blocks), int(block_size))
+        if not self._h:
+            raise PagedAttentionError(PA_ERR_INVALID, self._lib.pa_last_error().decode())
+        self.num_blocks, self.block_size = int(num_blocks), int(block_size)
+
+    def __del__(self):
+        h, self._h = getattr(self, "_h", None), None
+        if h:
+            self._lib.pa_bm_destroy(h)
+
+    def num_free(self) -> int:
+        return int(self._lib.pa_bm_num_free(self._h))
+
+    def add(self, seq_id: int, num_tokens: int):
+        """A new sequence of num_tokens tokens; returns their slots (int64)."""
+        import numpy as np
+
+        slots = np.empty(max(int(num_tokens), 1), dtype=np.int64)
+        _check(self._lib.pa_bm_add(self._h, int(seq_id), int(num_tokens), slots.ctypes.data))
+        return slots[:int(num_tokens)]
+
+    def append(self, seq_ids):
+        """One token for each id (in order); returns (slots int64 [n],
+        copy-on-write pairs int64 [c, 2])."""
+        import numpy as np
+
+        ids = np.ascontiguousarray(np.asarray(seq_ids, dtype=np.int64).reshape(-1))
+        n = ids.size
+        slots = np.empty(max(n, 1), dtype=np.int64)
+        pairs = np.empty((max(n, 1), 2), dtype=np.int64)
+        nc = ctypes.c_int32(0)
+        _check(self._lib.pa_bm_append(self._h, n, ids.ctypes.data, slots.ctypes.data,
+                                      pairs.ctypes.data, ctypes.byref(nc)))
+        return slots[:n], pairs[:nc.value]
+
+    def fork(self, parent_id: int, child_id: int) -> None:
+        _check(self._lib.pa_bm_fork(self._h, int(parent_id), int(child_id)))
+
+    def release(self, seq_id: int) -> None:
+        _check(self._lib.pa_bm_free(self._h, int(seq_id)))
+
+    def seq_len(self, seq_id: int) -> int:
+        r = int(self._lib.pa_bm_seq_len(self._h, int(seq_id)))
+        if r < 0:
+            _check(r)
+        return r
+
+    def ref_count(self, block: int) -> int:
+        r = int(self._lib.pa_bm_ref_count(self._h, int(block)))
+        if r < 0:
+            _check(r)
+        return r
+
+    def block_tables(self, seq_ids, max_blocks_per_seq: int):
+        """(int32 [n, max_blocks_per_seq] tables padded with -1, int32 [n] lengths)."""
+        import numpy as np
+
+        ids = np.ascontiguousarray(np.asarray(seq_ids, dtype=np.int64).reshape(-1))
+        n = ids.size
+        tables = np.empty((max(n, 1), max(int(max_blocks_per_seq), 1)), dtype=np.int32)
+        lens = np.empty(max(n, 1), dtype=np.int32)
+        _check(self._lib.pa_bm_block_tables(self._h, n, ids.ctypes.data, int(max_blocks_per_seq),
+                                            tables.ctypes.data, lens.ctypes.data))
+        return tables[:n, :int(max_blocks_per_seq)], lens[:n]

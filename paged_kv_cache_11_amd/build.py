@@ -1,8 +1,9 @@
 """Build the gfx950 HIP library ``libpa.so`` in-tree with hipcc.
 
-Every translation unit under ``csrc/`` is compiled to an object for gfx950
-(in parallel), then linked into ``paged_kv_cache_11_amd/libpa.so``.  Packed
-fp32 instructions are disabled for all device code.
+Every HIP translation unit under ``csrc/`` is compiled to an object for
+gfx950 and every host-only C++ one with the host compiler (in parallel),
+then all are linked into ``paged_kv_cache_11_amd/libpa.so``.  Packed fp32
+instructions are disabled for all device code.
 """
 from __future__ import annotations
 
@@ -34,13 +35,21 @@ COMMON = [
 ]
 
 
+# Host-only translation units (the block manager) are plain C++.
+HOST_COMMON = ["-O2", "-std=c++17", "-fPIC", "-I", os.path.join(ROOT, "include"), "-Wall"]
+
+
 def sources():
-    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
+    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC)
+                  if f.endswith(".hip") or f.endswith(".cpp"))
 
 
 def _compile(src: str, extra) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *COMMON, *extra, "-c", src, "-o", obj]
+    if src.endswith(".cpp"):
+        cmd = [os.environ.get("CXX", "g++"), *HOST_COMMON, "-c", src, "-o", obj]
+    else:
+        cmd = [hipcc(), *COMMON, *extra, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

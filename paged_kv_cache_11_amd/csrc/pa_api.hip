@@ -10,6 +10,7 @@
 
 #include <string.h>
 
+#include "pa_error.h"
 #include "pa_internal.h"
 
 namespace {
@@ -114,6 +115,12 @@ int32_t balanced_workers_for_device(int32_t engine) {
 
 }  // namespace
 
+int32_t pa::record_error(int32_t code, const char* msg) {
+  if (code == PA_OK) g_last_error.clear();
+  else g_last_error = msg;
+  return code;
+}
+
 extern "C" {
 
 int32_t pa_version(void) { return 100; }
@@ -125,6 +132,7 @@ const char* pa_strerror(int32_t code) {
     case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED: combination not built";
     case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: workspace missing or too small";
     case PA_ERR_HIP: return "PA_ERR_HIP: HIP runtime error";
+    case PA_ERR_NO_BLOCKS: return "PA_ERR_NO_BLOCKS: not enough free blocks";
     default: return "unknown pa error code";
   }
 }
