@@ -178,7 +178,73 @@ def _time_us(fn, iters, warmup=3):
     return a.elapsed_time(b) / iters * 1e3
 
 
-ROW_GROUPS = ("long_context", "shared_prefix", "mixed_fp8", "block_sizes")
+ROW_GROUPS = ("long_context", "shared_prefix", "mixed_fp8", "block_sizes", "block_manager")
+
+
+def _manager_trace(mgr, lens, samples: int, steps: int, budget_s: float = 1e9):
+    """A scheduler's use of a block manager: one prompt per entry of lens,
+    each forked into samples - 1 more samples (parallel sampling), then
+    decode steps that append one token to every sample and read back all
+    block tables.  Returns (seconds per step, steps run, copy-on-write pairs,
+    logical tokens per allocated slot: below 1 is the waste of partly filled
+    last blocks, above 1 the saving of shared blocks)."""
+    import time as _t
+
+    ids, next_id = [], 0
+    for L in lens:
+        mgr.add(next_id, int(L))
+        parent = next_id
+        ids.append(next_id)
+        next_id += 1
+        for _ in range(samples - 1):
+            mgr.fork(parent, next_id)
+            ids.append(next_id)
+            next_id += 1
+    width = int(max(lens)) // mgr.block_size + steps // mgr.block_size + 2
+    pairs, done, t0 = 0, 0, _t.perf_counter()
+    for _ in range(steps):
+        _, p = mgr.append(ids)
+        pairs += len(p)
+        if hasattr(mgr, "block_tables"):
+            mgr.block_tables(ids, width)
+        else:  # the reference manager: padded rows built from its tables
+            np.array([mgr.table(i) + [-1] * (width - len(mgr.table(i))) for i in ids], np.int32)
+        done += 1
+        if _t.perf_counter() - t0 > budget_s:
+            break
+    dt = _t.perf_counter() - t0
+    used = int(sum(int(L) * samples for L in lens)) + done * len(ids)  # logical tokens
+    held = (mgr.num_blocks - mgr.num_free()) * mgr.block_size
+    return dt / done, done, pairs, used / held
+
+
+def block_manager_rows(steps: int = 512):
+    """Host cost of the library's block manager per decode step (append one
+    token to every sequence + read all block tables), through the Python
+    binding, on two traces of the headline shape: 64 private sequences, and
+    8 prompts x 8 samples with copy-on-write.  Beside it, the reference
+    block manager (test infrastructure) on the same traces, as its CPU
+    baseline."""
+    from oracle.block_manager import BlockManager as RefManager
+    from paged_kv_cache_11_amd import binding as pa
+    from paged_kv_cache_11_amd import workloads as wl
+
+    bs = 16
+    rows = {}
+    for name, lens, samples in (("private_64", wl.llama3_8b_lengths(), 1),
+                                ("sampling_8x8", wl.llama3_8b_lengths(num_seqs=8), 8)):
+        nb = int(sum(-(-int(L) // bs) for L in lens)) + len(lens) * samples * (steps // bs + 2)
+        lib = _manager_trace(pa.BlockManager(nb, bs), lens, samples, steps)
+        ref = _manager_trace(RefManager(nb, bs), lens, samples, steps, budget_s=5.0)
+        rows[f"block_manager_{name}"] = {
+            "us_per_step": round(lib[0] * 1e6, 2), "seqs": len(lens) * samples, "steps": lib[1],
+            "block_size": bs, "cow_pairs": lib[2], "logical_tokens_per_slot": round(lib[3], 4),
+            "appends_per_s": round(len(lens) * samples / lib[0], 1),
+            "cpu_baseline": {"us_per_step": round(ref[0] * 1e6, 2), "steps": ref[1],
+                             "kind": "oracle", "cores": 1}}
+        if ref[1] == lib[1] and ref[2] != lib[2]:
+            raise RuntimeError(f"{name}: the library and the reference manager disagree")
+    return rows
 
 
 def row_measurements(dev, iters=20, groups=ROW_GROUPS):
@@ -300,6 +366,8 @@ def row_measurements(dev, iters=20, groups=ROW_GROUPS):
         us_step = _time_us(lambda i: (cw(i), dec(i), pre(i)), iters)
         rows["mixed_step_fp8"] = {"us": round(us_step, 2),
                                   "step": "cache_write(544 tokens) + decode(32 seqs) + prefill(512 queries)"}
+    if "block_manager" in groups:
+        rows.update(block_manager_rows())
     if "block_sizes" in groups:
         # The headline decode over pool blocks of 64 and 128 tokens (same
         # lengths and values), balanced split, three pool copies rotated.

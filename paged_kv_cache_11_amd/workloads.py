@@ -144,6 +144,16 @@ def tiny_decode(seed: int = 1235) -> PagedBatch:
                       1.0 / math.sqrt(D), q, k, v, slots, seq_lens, tables)
 
 
+def _uniform_lengths(rng, num_seqs: int, min_len: int, max_len: int) -> np.ndarray:
+    return rng.integers(min_len, max_len + 1, size=num_seqs, dtype=np.int64).astype(np.int32)
+
+
+def llama3_8b_lengths(seed: int = 1236, num_seqs: int = 64, min_len: int = 512,
+                      max_len: int = 4096) -> np.ndarray:
+    """The context lengths of ``llama3_8b_decode`` alone (same seed, same draw)."""
+    return _uniform_lengths(np.random.default_rng(seed), num_seqs, min_len, max_len)
+
+
 def llama3_8b_decode(seed: int = 1236, num_seqs: int = 64, min_len: int = 512,
                      max_len: int = 4096, kv_dtype: str = "bf16",
                      block_size: int = 16) -> PagedBatch:
@@ -154,7 +164,7 @@ def llama3_8b_decode(seed: int = 1236, num_seqs: int = 64, min_len: int = 512,
     needed, tables drawn from a shuffled pool."""
     rng = np.random.default_rng(seed)
     Hq, Hkv, D, bs = 32, 8, 128, block_size
-    seq_lens = rng.integers(min_len, max_len + 1, size=num_seqs, dtype=np.int64).astype(np.int32)
+    seq_lens = _uniform_lengths(rng, num_seqs, min_len, max_len)
     needed = int(sum((int(L) + bs - 1) // bs for L in seq_lens))
     nb = _pool_blocks(needed)
     perm = rng.permutation(nb).astype(np.int32)
