@@ -178,7 +178,8 @@ def _time_us(fn, iters, warmup=3):
     return a.elapsed_time(b) / iters * 1e3
 
 
-ROW_GROUPS = ("long_context", "shared_prefix", "mixed_fp8", "block_sizes", "block_manager")
+ROW_GROUPS = ("long_context", "shared_prefix", "mixed_fp8", "block_sizes", "block_manager",
+              "chunked_prefill")
 
 
 def _manager_trace(mgr, lens, samples: int, steps: int, budget_s: float = 1e9):
@@ -366,6 +367,29 @@ def row_measurements(dev, iters=20, groups=ROW_GROUPS):
         us_step = _time_us(lambda i: (cw(i), dec(i), pre(i)), iters)
         rows["mixed_step_fp8"] = {"us": round(us_step, 2),
                                   "step": "cache_write(544 tokens) + decode(32 seqs) + prefill(512 queries)"}
+    if "chunked_prefill" in groups:
+        # One scheduler step of varlen chunked prefill under a 512- and a
+        # 2048-token budget (Llama-3-8B shape, bf16 pool): one call per step.
+        for budget in (512, 2048):
+            b = wl.make(f"chunked_prefill_budget{budget}_bf16")
+            sets = _gpu_pools(b, dev, copies=2)
+            cq = wl.storage_tensor(b.chunk_q, "bf16").to(dev)
+            cout = torch.empty_like(cq)
+            cqs = torch.from_numpy(b.chunk_query_start).to(dev)
+            ctb = torch.from_numpy(b.chunk_block_tables).to(dev)
+            cln = torch.from_numpy(b.chunk_seq_lens).to(dev)
+            max_q = int(np.diff(b.chunk_query_start).max())
+            us = _time_us(lambda i: pa.pa_prefill_chunk(cout, cq, cqs, max_q, sets[i % 2][0],
+                                                        sets[i % 2][1], ctb, cln, b.scale), iters)
+            pairs = sum(sum(first + i + 1 for i in range(n)) for _, first, n in b.chunks)
+            flops = 4.0 * b.num_heads * b.head_size * pairs
+            rows[f"prefill_budget{budget}_llama3_8b"] = {
+                "us": round(us, 2), "chunks": [list(c) for c in b.chunks], "causal_flops": flops,
+                "tflops": round(flops / us / 1e6, 1),
+                "pct_mfma_bf16_peak": round(100 * flops / us / 1e6 / MFMA_BF16_PEAK_TFLOPS, 2),
+                "tokens_per_s": round(budget / us * 1e6, 1)}
+            del sets
+            torch.cuda.empty_cache()
     if "block_manager" in groups:
         rows.update(block_manager_rows())
     if "block_sizes" in groups:

@@ -313,12 +313,73 @@ def mixed_fp8_step(seed: int = 1239, num_decode: int = 32, min_len: int = 1024,
     return b
 
 
+def budget_chunks(prompt_lens, budget: int, step: int):
+    """The chunks of one scheduler step of chunked prefill under a token
+    budget: prompts are served in order, each step takes up to ``budget``
+    tokens, a prompt that does not fit is cut and continues at the next
+    step.  Returns [(prompt index, first position, chunk length)] of step
+    ``step`` (0-based); empty once every prompt is done."""
+    done = [0] * len(prompt_lens)
+    p = 0
+    for s in range(step + 1):
+        left, chunks = budget, []
+        while left > 0 and p < len(prompt_lens):
+            n = min(int(prompt_lens[p]) - done[p], left)
+            chunks.append((p, done[p], n))
+            done[p] += n
+            left -= n
+            if done[p] == int(prompt_lens[p]):
+                p += 1
+        if s == step:
+            return chunks
+    return []
+
+
+def chunked_prefill_step(seed: int = 1240, budget: int = 2048, step: int = 3,
+                         num_prompts: int = 24, min_len: int = 256, max_len: int = 2048,
+                         block_size: int = 16) -> PagedBatch:
+    """One step of varlen chunked prefill under a token budget (512 or 2048
+    batched tokens), Llama-3-8B shape: 32 query heads over 8 KV heads, head
+    size 128, bf16 pool, block 16.  Prompt lengths are uniform in
+    [256, 2048]; the step's chunks are what ``budget_chunks`` gives for step
+    ``step`` (a continued prompt first, then new ones, the last one cut).
+    Each prompt's pool holds its tokens up to the end of its chunk (earlier
+    chunks and the chunk's own K/V already written)."""
+    rng = np.random.default_rng(seed)
+    Hq, Hkv, D, bs = 32, 8, 128, block_size
+    prompt_lens = _uniform_lengths(rng, num_prompts, min_len, max_len)
+    chunks = budget_chunks(prompt_lens, budget, step)
+    if not chunks:
+        raise ValueError("the step is past the last prompt")
+    ends = np.array([first + n for _, first, n in chunks], dtype=np.int32)
+    nblk = [(int(L) + bs - 1) // bs for L in ends]
+    nb = _pool_blocks(sum(nblk))
+    perm = rng.permutation(nb).astype(np.int32)
+    tables, _ = _tables_from_lengths(ends, bs, perm)
+    T = int(ends.sum())
+    k = _normal(rng, (T, Hkv, D))
+    v = _normal(rng, (T, Hkv, D))
+    n_q = [n for _, _, n in chunks]
+    chunk_q = _normal(rng, (sum(n_q), Hq, D))
+    slots = np.concatenate([_slots_for(tables[c], int(ends[c]), bs) for c in range(len(chunks))])
+    b = PagedBatch(f"chunked_prefill_budget{budget}_bf16", Hq, Hkv, D, bs, nb, "bf16", "bf16",
+                   "bf16", 1.0 / math.sqrt(D), chunk_q[:1], k, v, slots, ends, tables,
+                   chunk_q=chunk_q,
+                   chunk_query_start=np.concatenate([[0], np.cumsum(n_q)]).astype(np.int32),
+                   chunk_seq_lens=ends, chunk_block_tables=tables,
+                   notes=f"chunks (prompt, first, len): {chunks}")
+    b.chunks = chunks
+    return b
+
+
 WORKLOADS = {
     "tiny_fp32": tiny_decode,
     "llama3_8b_decode_bf16": llama3_8b_decode,
     "long_context_splitk_bf16": long_context_decode,
     "shared_prefix_bf16": shared_prefix_decode,
     "mixed_prefill_decode_fp8": mixed_fp8_step,
+    "chunked_prefill_budget2048_bf16": chunked_prefill_step,
+    "chunked_prefill_budget512_bf16": lambda **kw: chunked_prefill_step(**{"budget": 512, **kw}),
 }
 
 

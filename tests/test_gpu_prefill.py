@@ -114,3 +114,24 @@ def test_prefill_negative_and_zero_scale(scale):
     rows = sorted(set(list(range(0, int(qsl[-1]), 11)) + [int(x) - 1 for x in qsl[1:]]))
     ref = opg.paged_prefill(q64, qsl, okp, ovp, tables, lens, scale, kv_dtype="bf16", rows=rows)
     G.assert_close(got, ref, "bf16", f"prefill scale {scale}", rows=rows)
+
+
+@pytest.mark.parametrize("budget", [512, 2048])
+def test_prefill_token_budget_step(budget):
+    """One scheduler step of chunked prefill under a 512- or 2048-token
+    budget, Llama-3-8B shape, in one call: a continued prompt, new prompts
+    from position 0, and a prompt cut by the budget.  Sampled rows (every
+    sixth, plus each chunk's first and last) against the oracle."""
+    b = wl.make(f"chunked_prefill_budget{budget}_bf16")
+    G.say(f"[budget {budget}] chunks {b.chunks}")
+    kp, vp = G.gpu_pool(b)
+    G.gpu_fill(b, kp, vp)
+    okp, ovp = G.oracle_pool(b)
+    qsl = b.chunk_query_start
+    got, q64 = run_prefill(b, kp, vp, b.chunk_q, qsl, b.chunk_seq_lens, b.chunk_block_tables,
+                           int(np.diff(qsl).max()))
+    rows = sorted(set(list(range(0, budget, 6)) + [int(x) - 1 for x in qsl[1:]] +
+                      [int(x) for x in qsl[:-1]]))
+    ref = opg.paged_prefill(q64, qsl, okp, ovp, b.chunk_block_tables, b.chunk_seq_lens, b.scale,
+                            kv_dtype="bf16", rows=rows)
+    G.assert_close(got, ref, "bf16", f"budget-{budget} prefill step", rows=rows)
