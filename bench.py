@@ -140,6 +140,8 @@ def cpu_baseline(b, budget_s: float = 12.0):
     }
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0
+# PCIe 5.0 x16, one direction: 32 GT/s x 16 lanes, 128b/130b coding.
+HOST_LINK_PEAK_GBS = 63.0
 
 
 def _gpu_pools(b, dev, copies=1):
@@ -179,7 +181,7 @@ def _time_us(fn, iters, warmup=3):
 
 
 ROW_GROUPS = ("long_context", "shared_prefix", "mixed_fp8", "block_sizes", "block_manager",
-              "chunked_prefill")
+              "chunked_prefill", "swap")
 
 
 def _manager_trace(mgr, lens, samples: int, steps: int, budget_s: float = 1e9):
@@ -390,6 +392,55 @@ def row_measurements(dev, iters=20, groups=ROW_GROUPS):
                 "tokens_per_s": round(budget / us * 1e6, 1)}
             del sets
             torch.cuda.empty_cache()
+    if "swap" in groups:
+        # SWAP preemption: the blocks of 8 sequences of the headline workload
+        # (lengths U[512, 4096], bf16, 32 KiB per block and pool) moved to a
+        # pinned host pool and back, one call each way; beside it, one DMA
+        # copy of the same bytes as a single contiguous buffer (the host
+        # link's practical rate), and the same blocks moved by one DMA copy
+        # per block and pool.
+        lens = wl.llama3_8b_lengths(num_seqs=8)
+        bs, Hkv, D = 16, 8, 128
+        n = int(sum(-(-int(L) // bs) for L in lens))
+        nb = n + 64
+        rng = np.random.default_rng(7)
+        kd = torch.randn((nb, Hkv, bs, D), device=dev).to(torch.bfloat16)
+        vd = torch.randn((nb, Hkv, bs, D), device=dev).to(torch.bfloat16)
+        hk = torch.empty((n, Hkv, bs, D), dtype=torch.bfloat16, pin_memory=True)
+        hv = torch.empty_like(hk, pin_memory=True)
+        dev_ids = rng.permutation(nb)[:n]
+        out_map = torch.from_numpy(np.stack([dev_ids, np.arange(n)], 1).astype(np.int64)).to(dev)
+        in_map = torch.from_numpy(np.stack([np.arange(n), dev_ids], 1).astype(np.int64)).to(dev)
+        moved = 2 * n * Hkv * bs * D * 2
+        it = max(3, iters // 4)
+        us_out = _time_us(lambda i: pa.pa_swap_blocks(kd, vd, hk, hv, out_map), it)
+        us_in = _time_us(lambda i: pa.pa_swap_blocks(hk, hv, kd, vd, in_map), it)
+        flat_d = torch.empty(moved, dtype=torch.uint8, device=dev)
+        flat_h = torch.empty(moved, dtype=torch.uint8, pin_memory=True)
+        us_dma_out = _time_us(lambda i: flat_h.copy_(flat_d, non_blocking=True), it)
+        us_dma_in = _time_us(lambda i: flat_d.copy_(flat_h, non_blocking=True), it)
+        ids = dev_ids.tolist()
+
+        def per_block(i):
+            for j, d in enumerate(ids):
+                hk[j].copy_(kd[d], non_blocking=True)
+                hv[j].copy_(vd[d], non_blocking=True)
+
+        us_blk = _time_us(per_block, 2, warmup=1)
+        link = HOST_LINK_PEAK_GBS
+        rows["swap_out_8_seqs"] = {"us": round(us_out, 1), "blocks": n, "bytes": moved,
+                                   "gbs": round(moved / us_out / 1e3, 2),
+                                   "pct_host_link_peak": round(100 * moved / us_out / 1e3 / link, 1)}
+        rows["swap_in_8_seqs"] = {"us": round(us_in, 1), "blocks": n, "bytes": moved,
+                                  "gbs": round(moved / us_in / 1e3, 2),
+                                  "pct_host_link_peak": round(100 * moved / us_in / 1e3 / link, 1)}
+        rows["swap_dma_reference"] = {
+            "contiguous_out_gbs": round(moved / us_dma_out / 1e3, 2),
+            "contiguous_in_gbs": round(moved / us_dma_in / 1e3, 2),
+            "per_block_copies_out_gbs": round(moved / us_blk / 1e3, 2),
+            "host_link_peak_gbs": link}
+        del kd, vd, hk, hv, flat_d, flat_h
+        torch.cuda.empty_cache()
     if "block_manager" in groups:
         rows.update(block_manager_rows())
     if "block_sizes" in groups:

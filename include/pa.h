@@ -141,12 +141,43 @@ int32_t pa_cache_write(const void* key, const void* value, int32_t src_dtype,
  *
  *   block_mapping  int64 [num_pairs][2] = (src, dst), device memory
  * Destinations must be distinct and must not be the source of any pair
- * (all copies run concurrently).  num_pairs == 0 is a valid no-op.
+ * (all copies run concurrently); a pair naming a block outside the pool is
+ * skipped.  num_pairs == 0 is a valid no-op.
  */
 int32_t pa_copy_blocks(void* k_cache, void* v_cache, int32_t cache_dtype,
                        int32_t num_blocks, int32_t block_size, int32_t num_kv_heads,
                        int32_t head_size,
                        const int64_t* block_mapping, int32_t num_pairs, void* stream);
+
+/*
+ * pa_swap_blocks — move whole blocks between two pools: the HBM pool and a
+ * pool in pinned host memory, either way.
+ *
+ * The SWAP mode of preemption ([EVAL], its section on preemption; [DEEP]
+ * §3.2, preemption strategies): when the HBM pool runs short, the physical
+ * K/V blocks of a preempted sequence move to host memory over the host link
+ * and come back when it resumes.  For each pair i, every K and V element of
+ * block block_mapping[2i] of the source pools (all heads, all offsets) is
+ * copied bit-exactly into block block_mapping[2i+1] of the destination
+ * pools.
+ *
+ *   src_k, src_v  source pools [src_num_blocks][num_kv_heads][block_size][head_size]
+ *   dst_k, dst_v  destination pools [dst_num_blocks][...] of the same geometry
+ *   block_mapping int64 [num_pairs][2] = (source block, destination block)
+ * Each of the five pointers is device memory or pinned host memory (from
+ * hipHostMalloc, e.g. a torch tensor made with pin_memory=True); pinned host
+ * memory is reached through its device mapping.  Pageable host memory is
+ * refused with PA_ERR_INVALID before anything is enqueued.  All memory is
+ * the caller's.  Destinations must be distinct; a pair naming a block
+ * outside its pool is skipped.  The host must not touch a host pool between
+ * the call and the completion of the work on the stream.  num_pairs == 0 is
+ * a valid no-op (the pointers are still checked).
+ */
+int32_t pa_swap_blocks(const void* src_k, const void* src_v, int32_t src_num_blocks,
+                       void* dst_k, void* dst_v, int32_t dst_num_blocks,
+                       int32_t cache_dtype, int32_t block_size, int32_t num_kv_heads,
+                       int32_t head_size, const int64_t* block_mapping, int32_t num_pairs,
+                       void* stream);
 
 /* partition_size value selecting the balanced split of pa_decode. */
 #define PA_PARTITION_BALANCED (-1)

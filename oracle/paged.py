@@ -242,7 +242,7 @@ def copy_blocks(k_pool, v_pool, pairs):
     physical block src is copied into block dst.  Sources are read before
     any destination is written; a destination must not repeat and must not
     be the source of another pair."""
-    pairs = np.asarray(pairs, dtype=np.int64).reshape(-1, 2)
+    pairs = _pairs_inside(pairs, k_pool.shape[0], k_pool.shape[0])
     srcs, dsts = pairs[:, 0], pairs[:, 1]
     if len(set(dsts.tolist())) != len(dsts) or set(dsts.tolist()) & set(srcs.tolist()):
         raise ValueError("destinations must be distinct and disjoint from sources")
@@ -250,3 +250,31 @@ def copy_blocks(k_pool, v_pool, pairs):
         snap = pool[srcs].copy()
         pool[dsts] = snap
     return k_pool, v_pool
+
+
+def _pairs_inside(pairs, src_blocks: int, dst_blocks: int) -> np.ndarray:
+    """The (src, dst) pairs whose blocks both exist; a pair naming a block
+    outside its pool moves nothing (the pages say nothing of such a pair)."""
+    pairs = np.asarray(pairs, dtype=np.int64).reshape(-1, 2)
+    ok = ((pairs[:, 0] >= 0) & (pairs[:, 0] < src_blocks) &
+          (pairs[:, 1] >= 0) & (pairs[:, 1] < dst_blocks))
+    return pairs[ok]
+
+
+def swap_blocks(src_k, src_v, dst_k, dst_v, pairs):
+    """SWAP preemption ([EVAL], its section on preemption; [DEEP] §3.2,
+    preemption strategies): the K/V blocks of a preempted sequence move from
+    the device pool to a pool in host memory, and back when it resumes.  For
+    each (src, dst) pair every K and V word of block src of the source pools
+    is copied into block dst of the destination pools, which have the same
+    geometry and may hold any number of blocks.  Destinations must be
+    distinct."""
+    if src_k.shape[1:] != dst_k.shape[1:] or src_k.dtype != dst_k.dtype:
+        raise ValueError("source and destination pools differ in geometry")
+    pairs = _pairs_inside(pairs, src_k.shape[0], dst_k.shape[0])
+    if len(set(pairs[:, 1].tolist())) != len(pairs):
+        raise ValueError("destinations must be distinct")
+    for src, dst in ((src_k, dst_k), (src_v, dst_v)):
+        for s, d in pairs:
+            dst[d] = src[s]
+    return dst_k, dst_v

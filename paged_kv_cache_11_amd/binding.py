@@ -39,6 +39,8 @@ _SIGNATURES = {
                         _c_int, _c_p, _c_f, _c_f, _c_p], _c_int),
     "pa_copy_blocks": ([_c_p, _c_p, _c_int, _c_int, _c_int, _c_int, _c_int, _c_p, _c_int, _c_p],
                        _c_int),
+    "pa_swap_blocks": ([_c_p, _c_p, _c_int, _c_p, _c_p, _c_int, _c_int, _c_int, _c_int, _c_int,
+                        _c_p, _c_int, _c_p], _c_int),
     "pa_decode_workspace_size": ([_c_int, _c_int, _c_int, _c_int, _c_int, _c_int], _c_sz),
     "pa_decode": ([_c_p, _c_p, _c_int, _c_int, _c_int, _c_int, _c_p, _c_p, _c_int, _c_int, _c_int,
                    _c_int, _c_p, _c_int, _c_p, _c_int, _c_f, _c_f, _c_f, _c_int, _c_p, _c_sz,
@@ -157,6 +159,21 @@ def pa_copy_blocks(k_cache, v_cache, block_mapping, stream=None) -> None:
     nb, hkv, bs, d = _pool_dims(k_cache, v_cache)
     n = int(block_mapping.shape[0]) if block_mapping is not None else 0
     _check(load().pa_copy_blocks(_ptr(k_cache), _ptr(v_cache), dtype_code(k_cache), nb, bs, hkv, d,
+                                 _ptr(block_mapping) if n else None, n, _stream(stream)))
+
+
+def pa_swap_blocks(src_k, src_v, dst_k, dst_v, block_mapping, stream=None) -> None:
+    """Move whole blocks (src, dst) from the source pools into the
+    destination pools; one side is usually pinned host memory (a tensor made
+    with pin_memory=True), the other the device pool.  block_mapping lives
+    in device or pinned host memory."""
+    snb, hkv, bs, d = _pool_dims(src_k, src_v)
+    dnb, dhkv, dbs, dd = _pool_dims(dst_k, dst_v)
+    if (hkv, bs, d) != (dhkv, dbs, dd) or src_k.dtype != dst_k.dtype:
+        raise PagedAttentionError(PA_ERR_INVALID, "source and destination pools differ in geometry")
+    n = int(block_mapping.shape[0]) if block_mapping is not None else 0
+    _check(load().pa_swap_blocks(_ptr(src_k), _ptr(src_v), snb, _ptr(dst_k), _ptr(dst_v), dnb,
+                                 dtype_code(src_k), bs, hkv, d,
                                  _ptr(block_mapping) if n else None, n, _stream(stream)))
 
 

@@ -4,12 +4,15 @@
 // K/V goes into its sequence's current block; the block (and so the slot)
 // was chosen by the caller's allocator.  Block copy: the copy-on-write step
 // of the fork/append/free primitives in "vLLM 高性能大语言模型推理引擎深度
-// 技术评估与分布式架构展望" and "vLLM 深度解析" §3.1.
+// 技术评估与分布式架构展望" and "vLLM 深度解析" §3.1.  Block swap: the same
+// whole-block move between the HBM pool and a pool in pinned host memory,
+// the SWAP mode of preemption (the first of those pages, its section on
+// preemption; "vLLM 深度解析" §3.2, preemption strategies).
 //
-// Both are HBM-bound scatters/copies of 16-byte chunks: every thread moves
-// one 16-byte chunk of the destination, so each wavefront writes 1 KiB of
-// contiguous pool (one token row of a head is head_size contiguous elements
-// and one block of all heads is contiguous).
+// All move 16-byte chunks: in the cache write every thread moves one chunk
+// of the destination, so each wavefront writes 1 KiB of contiguous pool (one
+// token row of a head is head_size contiguous elements); a block move
+// streams one block of all heads, which is contiguous.
 #include "pa_internal.h"
 
 namespace pa {
@@ -97,28 +100,57 @@ hipError_t cache_write(const CacheWriteArgs& a) {
 }
 
 // grid: x = chunk group of one block, y = pair, z = 0 (K) / 1 (V).
-__global__ __launch_bounds__(256) void copy_blocks_kernel(
-    uint8_t* __restrict__ k_cache, uint8_t* __restrict__ v_cache,
-    const int64_t* __restrict__ block_mapping, int64_t block_chunks) {
-  const int64_t pair = blockIdx.y;
+// Whole-block moves: work item (pair, pool) is one block of all heads of K
+// or V, block_chunks 16-byte chunks, split over wgs_per_block workgroups.
+// Each thread issues kMoveUnroll loads before its stores, so a wavefront
+// keeps 4 KiB in flight: what reads of pinned host memory across the host
+// link need to cover their latency.  Pairs naming a block outside either
+// pool are skipped.
+constexpr int kMoveUnroll = 4;
+constexpr int kMoveThreads = 256;
+
+__global__ __launch_bounds__(kMoveThreads) void move_blocks_kernel(
+    const uint8_t* __restrict__ src_k, const uint8_t* __restrict__ src_v,
+    uint8_t* __restrict__ dst_k, uint8_t* __restrict__ dst_v,
+    const int64_t* __restrict__ block_mapping, int64_t src_blocks, int64_t dst_blocks,
+    int64_t block_chunks, int wgs_per_block) {
+  const int64_t item = blockIdx.x / wgs_per_block;
+  const int part = (int)(blockIdx.x % wgs_per_block);
+  const int64_t pair = item >> 1;
+  const bool is_v = item & 1;
   const int64_t src = block_mapping[2 * pair], dst = block_mapping[2 * pair + 1];
-  uint8_t* pool = blockIdx.z ? v_cache : k_cache;
-  const u32x4* s = (const u32x4*)pool + src * block_chunks;
-  u32x4* d = (u32x4*)pool + dst * block_chunks;
-  for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < block_chunks;
-       c += (int64_t)gridDim.x * blockDim.x)
-    d[c] = s[c];
+  if (src < 0 || src >= src_blocks || dst < 0 || dst >= dst_blocks) return;
+  const u32x4* s = (const u32x4*)(is_v ? src_v : src_k) + src * block_chunks;
+  u32x4* d = (u32x4*)(is_v ? dst_v : dst_k) + dst * block_chunks;
+  constexpr int64_t kPerPass = (int64_t)kMoveThreads * kMoveUnroll;
+  for (int64_t base = part * kPerPass; base < block_chunks; base += wgs_per_block * kPerPass) {
+    u32x4 r[kMoveUnroll];
+#pragma unroll
+    for (int u = 0; u < kMoveUnroll; ++u) {
+      const int64_t c = base + u * kMoveThreads + threadIdx.x;
+      if (c < block_chunks) r[u] = s[c];
+    }
+#pragma unroll
+    for (int u = 0; u < kMoveUnroll; ++u) {
+      const int64_t c = base + u * kMoveThreads + threadIdx.x;
+      if (c < block_chunks) d[c] = r[u];
+    }
+  }
 }
 
-hipError_t copy_blocks(const CopyBlocksArgs& a) {
+hipError_t move_blocks(const MoveBlocksArgs& a) {
   const int64_t block_bytes =
       (int64_t)a.num_kv_heads * a.block_size * a.head_size * dtype_bytes(a.cache_dtype);
   const int64_t block_chunks = block_bytes / 16;
-  int64_t gx = (block_chunks + 255) / 256;
-  if (gx > 64) gx = 64;
-  hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)gx, (unsigned)a.num_pairs, 2), dim3(256),
-                     0, a.stream, (uint8_t*)a.k_cache, (uint8_t*)a.v_cache, a.block_mapping,
-                     block_chunks);
+  const int64_t per_pass = (int64_t)kMoveThreads * kMoveUnroll;
+  int64_t wgs = (block_chunks + per_pass - 1) / per_pass;
+  if (wgs > 16) wgs = 16;
+  const int64_t grid = (int64_t)a.num_pairs * 2 * wgs;
+  if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(move_blocks_kernel, dim3((unsigned)grid), dim3(kMoveThreads), 0, a.stream,
+                     (const uint8_t*)a.src_k, (const uint8_t*)a.src_v, (uint8_t*)a.dst_k,
+                     (uint8_t*)a.dst_v, a.block_mapping, (int64_t)a.src_blocks,
+                     (int64_t)a.dst_blocks, block_chunks, (int)wgs);
   return hipGetLastError();
 }
 

@@ -43,6 +43,8 @@ int32_t check_pool(const void* k_cache, const void* v_cache, int32_t cache_dtype
     return fail(PA_ERR_INVALID,
                 "pool sizes must be positive (num_blocks %d, block_size %d, num_kv_heads %d, "
                 "head_size %d)", num_blocks, block_size, num_kv_heads, head_size);
+  if (((uintptr_t)k_cache | (uintptr_t)v_cache) % 16 != 0)
+    return fail(PA_ERR_INVALID, "k_cache / v_cache must be 16-byte aligned");
   if ((head_size * pa::dtype_bytes(cache_dtype)) % 16 != 0)
     return fail(PA_ERR_UNSUPPORTED, "a head row must be a multiple of 16 bytes (head_size %d)",
                 head_size);
@@ -113,6 +115,28 @@ int32_t balanced_workers_for_device(int32_t engine) {
   return (int32_t)(w < pa::kMaxBalancedWorkers ? w : pa::kMaxBalancedWorkers);
 }
 
+// The address a kernel uses for p: device memory as is, pinned host memory
+// through its device mapping.  Anything else (pageable host memory, an
+// unknown address) is refused, since a kernel touching it would fault.
+int32_t device_view(const void* p, const char* name, const void** out) {
+  hipPointerAttribute_t at;
+  const hipError_t e = hipPointerGetAttributes(&at, p);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();  // clear the sticky error of the failed query
+    return fail(PA_ERR_INVALID, "%s is neither device memory nor pinned host memory", name);
+  }
+  if (at.type == hipMemoryTypeDevice) {
+    *out = p;
+    return PA_OK;
+  }
+  if (at.type == hipMemoryTypeHost && at.devicePointer && at.hostPointer) {
+    *out = (const uint8_t*)at.devicePointer + ((const uint8_t*)p - (const uint8_t*)at.hostPointer);
+    return PA_OK;
+  }
+  return fail(PA_ERR_INVALID, "%s is neither device memory nor pinned host memory", name);
+}
+
+
 }  // namespace
 
 int32_t pa::record_error(int32_t code, const char* msg) {
@@ -181,9 +205,36 @@ int32_t pa_copy_blocks(void* k_cache, void* v_cache, int32_t cache_dtype, int32_
   if (num_pairs < 0) return fail(PA_ERR_INVALID, "num_pairs %d < 0", num_pairs);
   if (num_pairs == 0) return ok();
   if (!block_mapping) return fail(PA_ERR_INVALID, "block_mapping is NULL");
-  pa::CopyBlocksArgs a{k_cache, v_cache, cache_dtype, num_blocks, block_size, num_kv_heads,
-                       head_size, block_mapping, num_pairs, (hipStream_t)stream};
-  return hip_result(pa::copy_blocks(a), "pa_copy_blocks");
+  pa::MoveBlocksArgs a{k_cache,    v_cache,      k_cache,      v_cache,
+                       cache_dtype, num_blocks,  num_blocks,   block_size,
+                       num_kv_heads, head_size,  block_mapping, num_pairs,
+                       (hipStream_t)stream};
+  return hip_result(pa::move_blocks(a), "pa_copy_blocks");
+}
+
+int32_t pa_swap_blocks(const void* src_k, const void* src_v, int32_t src_num_blocks, void* dst_k,
+                       void* dst_v, int32_t dst_num_blocks, int32_t cache_dtype, int32_t block_size,
+                       int32_t num_kv_heads, int32_t head_size, const int64_t* block_mapping,
+                       int32_t num_pairs, void* stream) {
+  if (int32_t r = check_pool(src_k, src_v, cache_dtype, src_num_blocks, block_size, num_kv_heads,
+                             head_size))
+    return r;
+  if (int32_t r = check_pool(dst_k, dst_v, cache_dtype, dst_num_blocks, block_size, num_kv_heads,
+                             head_size))
+    return r;
+  if (num_pairs < 0) return fail(PA_ERR_INVALID, "num_pairs %d < 0", num_pairs);
+  const void *sk, *sv, *dk, *dv, *map = nullptr;
+  if (int32_t r = device_view(src_k, "src_k", &sk)) return r;
+  if (int32_t r = device_view(src_v, "src_v", &sv)) return r;
+  if (int32_t r = device_view(dst_k, "dst_k", &dk)) return r;
+  if (int32_t r = device_view(dst_v, "dst_v", &dv)) return r;
+  if (num_pairs == 0) return ok();
+  if (!block_mapping) return fail(PA_ERR_INVALID, "block_mapping is NULL");
+  if (int32_t r = device_view(block_mapping, "block_mapping", &map)) return r;
+  pa::MoveBlocksArgs a{sk, sv, (void*)dk, (void*)dv, cache_dtype, src_num_blocks, dst_num_blocks,
+                       block_size, num_kv_heads, head_size, (const int64_t*)map, num_pairs,
+                       (hipStream_t)stream};
+  return hip_result(pa::move_blocks(a), "pa_swap_blocks");
 }
 
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,

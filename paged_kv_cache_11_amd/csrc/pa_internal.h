@@ -32,11 +32,15 @@ struct CacheWriteArgs {
   hipStream_t stream;
 };
 
-struct CopyBlocksArgs {
-  void* k_cache;
-  void* v_cache;
+// Whole-block moves between two pools of the same geometry (the same pool
+// for the copy-on-write copy; the HBM pool and a pinned host pool for swap).
+struct MoveBlocksArgs {
+  const void* src_k;
+  const void* src_v;
+  void* dst_k;
+  void* dst_v;
   int32_t cache_dtype;
-  int32_t num_blocks, block_size, num_kv_heads, head_size;
+  int32_t src_blocks, dst_blocks, block_size, num_kv_heads, head_size;
   const int64_t* block_mapping;
   int32_t num_pairs;
   hipStream_t stream;
@@ -90,7 +94,7 @@ struct PrefillArgs {
 };
 
 hipError_t cache_write(const CacheWriteArgs& a);
-hipError_t copy_blocks(const CopyBlocksArgs& a);
+hipError_t move_blocks(const MoveBlocksArgs& a);
 
 // Decode launchers, one per (query, cache) dtype pair; each dispatches on
 // head_size, block_size and group size.  Return hipErrorInvalidValue for a

@@ -130,3 +130,95 @@ def test_copy_blocks_random_pairs(dtype, bs):
     torch.cuda.synchronize()
     opg.copy_blocks(ok, ov, pairs)
     assert np.array_equal(kp.cpu().numpy(), ok) and np.array_equal(vp.cpu().numpy(), ov)
+
+
+def test_copy_blocks_skips_pairs_outside_the_pool():
+    rng = np.random.default_rng(23)
+    nb, Hkv, bs, D = 16, 2, 16, 64
+    kp = torch.from_numpy(rng.integers(0, 1 << 15, (nb, Hkv, bs, D), dtype=np.int16)).to(G.DEV)
+    vp = torch.from_numpy(rng.integers(0, 1 << 15, (nb, Hkv, bs, D), dtype=np.int16)).to(G.DEV)
+    kt, vt = kp.view(torch.bfloat16), vp.view(torch.bfloat16)
+    pairs = np.array([[3, 4], [-1, 5], [16, 6], [2, 16], [7, -3], [9, 10]], np.int64)
+    ok, ov = kp.cpu().numpy().copy(), vp.cpu().numpy().copy()
+    pa.pa_copy_blocks(kt, vt, torch.from_numpy(pairs).to(G.DEV))
+    torch.cuda.synchronize()
+    opg.copy_blocks(ok, ov, pairs)
+    assert np.array_equal(kp.cpu().numpy(), ok) and np.array_equal(vp.cpu().numpy(), ov)
+
+
+def _pinned_pool(nb, Hkv, bs, D, dtype):
+    t = torch.empty((nb, Hkv, bs, D), dtype=G.TORCH_DT[dtype], pin_memory=True)
+    t.view(G.INT_VIEW[dtype]).fill_(wl.POISON_BITS[dtype])
+    return t
+
+
+def _raw(t):
+    t = t.cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16).copy()
+    if t.dtype == torch.float32:
+        return t.view(torch.int32).numpy().view(np.uint32).copy()
+    return t.numpy().copy()
+
+
+@pytest.mark.parametrize("dtype,bs,Hkv,D", [("bf16", 16, 8, 128), ("fp8", 32, 8, 128),
+                                            ("f32", 16, 2, 64), ("bf16", 128, 4, 128)])
+def test_swap_blocks_out_and_back_in(dtype, bs, Hkv, D):
+    """Swap out: blocks of the device pool into a pinned host pool (mapping
+    in device memory); the device blocks are then overwritten; swap in: back
+    into other device blocks (mapping in pinned host memory).  Both pools
+    are compared bit for bit with the oracle's swap after each move, with a
+    NaN-poisoned host pool and two pairs that name no block."""
+    rng = np.random.default_rng(31 + bs + Hkv)
+    nb, nh = 48, 40
+    b = wl.PagedBatch("swap", Hkv, Hkv, D, bs, nb, dtype, "bf16" if dtype == "fp8" else dtype,
+                      dtype, 1.0, np.zeros((1, Hkv, D), np.float32),
+                      rng.standard_normal((nb * bs, Hkv, D)).astype(np.float32),
+                      rng.standard_normal((nb * bs, Hkv, D)).astype(np.float32),
+                      rng.permutation(nb * bs).astype(np.int64), np.zeros(1, np.int32),
+                      np.zeros((1, 1), np.int32), k_scale=0.01, v_scale=0.02)
+    kp, vp = G.gpu_pool(b)
+    G.gpu_fill(b, kp, vp)
+    okp, ovp = G.oracle_pool(b)
+    assert G.raw_equal(kp, okp) and G.raw_equal(vp, ovp)
+    hk, hv = _pinned_pool(nh, Hkv, bs, D, dtype), _pinned_pool(nh, Hkv, bs, D, dtype)
+    ohk, ohv = _raw(hk), _raw(hv)
+    out_src = rng.permutation(nb)[:24]
+    out_dst = rng.permutation(nh)[:24]
+    out_pairs = np.stack([out_src, out_dst], 1).astype(np.int64)
+    out_pairs = np.concatenate([out_pairs, [[nb, 0], [0, -1]]]).astype(np.int64)
+    G.say(f"[swap {dtype} bs{bs}] out {len(out_pairs)} pairs")
+    pa.pa_swap_blocks(kp, vp, hk, hv, torch.from_numpy(out_pairs).to(G.DEV))
+    torch.cuda.synchronize()
+    opg.swap_blocks(okp, ovp, ohk, ohv, out_pairs)
+    assert np.array_equal(_raw(hk), ohk) and np.array_equal(_raw(hv), ohv), "swap out"
+    # The device blocks are reused meanwhile.
+    kp.view(G.INT_VIEW[dtype]).fill_(0)
+    vp.view(G.INT_VIEW[dtype]).fill_(0)
+    okp[...] = 0
+    ovp[...] = 0
+    in_dst = rng.permutation(nb)[:24]
+    in_pairs = np.stack([out_dst, in_dst], 1).astype(np.int64)
+    in_map = torch.from_numpy(in_pairs).pin_memory()
+    G.say(f"[swap {dtype} bs{bs}] in {len(in_pairs)} pairs (mapping in pinned host memory)")
+    pa.pa_swap_blocks(hk, hv, kp, vp, in_map)
+    torch.cuda.synchronize()
+    opg.swap_blocks(ohk, ohv, okp, ovp, in_pairs)
+    assert G.raw_equal(kp, okp) and G.raw_equal(vp, ovp), "swap in"
+    # And the round trip put each block's original words at its new place.
+    full_k, _ = G.oracle_pool(b)
+    for s, d in zip(out_src, in_dst):
+        assert np.array_equal(okp[d], full_k[s])
+
+
+def test_swap_blocks_refuses_pageable_host_memory():
+    """Pageable host memory is refused on the host before any work is
+    enqueued (no pairs are passed, so nothing could be launched anyway)."""
+    kp = torch.zeros((4, 2, 16, 64), dtype=torch.bfloat16, device=G.DEV)
+    vp = torch.zeros_like(kp)
+    hk = torch.zeros((4, 2, 16, 64), dtype=torch.bfloat16)  # not pinned
+    hv = torch.zeros_like(hk)
+    with pytest.raises(pa.PagedAttentionError) as e:
+        pa.pa_swap_blocks(kp, vp, hk, hv, None)
+    assert e.value.code == pa.PA_ERR_INVALID and "pinned" in str(e.value)
+    pa.pa_swap_blocks(kp, vp, hk.pin_memory(), hv.pin_memory(), None)  # pinned: accepted

@@ -82,6 +82,22 @@ def test_deep_prefix_sharing_and_copy_on_write():
     assert m.table("A") == [0, 2, 4]
 
 
+def test_full_shared_block_is_never_copied():
+    """Append copies only the block it writes into ([EVAL] fork / append /
+    free: only the block that changes is copied).  A prompt that ends on a
+    block edge, forked three ways: every sample's first own token opens a
+    fresh block and the full prompt blocks stay shared by all four."""
+    m = BlockManager(16, 4)
+    m.add("P", 8)
+    for c in ("a", "b", "c"):
+        m.fork("P", c)
+    slots, pairs = m.append(["P", "a", "b", "c"])
+    assert pairs == []
+    assert [m.ref[b] for b in (0, 1)] == [4, 4]
+    assert [m.table(s)[-1] for s in ("P", "a", "b", "c")] == [2, 3, 4, 5]
+    assert slots == [8, 12, 16, 20]
+
+
 def _check_content(m, mem, content):
     """Every live sequence reads back exactly its tokens through its table."""
     bs = m.block_size

@@ -6,12 +6,15 @@ import numpy as np
 import pytest
 
 import test_oracle_attention as att
+import test_oracle_block_manager as obm
 import test_oracle_codecs as cod
 import test_oracle_paging as pag
-from oracle import codecs, paged
+from oracle import block_manager, codecs, paged
 
 _orig_attend = paged.attend
 _orig_gather = paged.gather
+_orig_swap = paged.swap_blocks
+_orig_pairs_inside = paged._pairs_inside
 
 
 def _attend_no_scale(q, K, V, scale, visible=None):
@@ -67,6 +70,20 @@ def _encode_ties_away(x):
     return np.where(tie, (up | (out & 0x80)).astype(np.uint8), out)
 
 
+def _swap_k_v_crossed(src_k, src_v, dst_k, dst_v, pairs):
+    return _orig_swap(src_v, src_k, dst_k, dst_v, pairs)
+
+
+def _swap_reversed_pairs(src_k, src_v, dst_k, dst_v, pairs):
+    p = np.asarray(pairs, np.int64).reshape(-1, 2)[:, ::-1]
+    return _orig_swap(src_k, src_v, dst_k, dst_v, p)
+
+
+def _pairs_wrap_negative(pairs, src_blocks, dst_blocks):
+    p = np.asarray(pairs, np.int64).reshape(-1, 2)
+    return np.stack([p[:, 0] % src_blocks, p[:, 1] % dst_blocks], axis=1)
+
+
 MUTATIONS = [
     ("attend", _attend_no_scale, [att.test_decode_matches_torch_sdpa_tiny]),
     ("attend", _attend_transposed, [att.test_decode_matches_torch_sdpa_tiny]),
@@ -75,7 +92,62 @@ MUTATIONS = [
     ("gather", _gather_wrong_offset, [pag.test_lib_worked_example_slots_and_gather]),
     ("_kv_head", _kv_head_modulo, [att.test_decode_matches_torch_sdpa_tiny]),
     ("lse_merge", _merge_without_rescale, [att.test_split_merge_equals_unsplit]),
+    ("swap_blocks", _swap_k_v_crossed, [pag.test_swap_blocks_element_by_element]),
+    ("swap_blocks", _swap_reversed_pairs, [pag.test_swap_out_and_in_restores_the_sequence]),
+    ("_pairs_inside", _pairs_wrap_negative, [pag.test_copy_blocks_skips_pairs_outside_the_pool,
+                                             pag.test_swap_blocks_element_by_element]),
 ]
+
+
+class _LifoManager(block_manager.BlockManager):
+    def _take(self):
+        if not self.free:
+            raise block_manager.OutOfBlocks("no free block")
+        b = self.free.pop()
+        self.ref[b] = 1
+        return b
+
+
+class _CopyFullSharedManager(block_manager.BlockManager):
+    """Copies a shared last block even when it is full."""
+
+    def append(self, sids):
+        slots, pairs = [], []
+        for sid in sids:
+            s = self.seqs[sid]
+            last = s["blocks"][-1] if s["blocks"] else None
+            if last is not None and self.ref[last] > 1 and s["len"] % self.block_size == 0:
+                fresh = self._take()
+                self.ref[last] -= 1
+                s["blocks"][-1] = fresh
+                pairs.append((last, fresh))
+            sl, pr = block_manager.BlockManager.append(self, [sid])
+            slots += sl
+            pairs += pr
+        return slots, pairs
+
+
+class _CowKeepsReferenceManager(block_manager.BlockManager):
+    """Forgets to drop the shared block's reference on copy-on-write."""
+
+    def append(self, sids):
+        slots, pairs = block_manager.BlockManager.append(self, sids)
+        for src, _ in pairs:
+            self.ref[src] += 1
+        return slots, pairs
+
+
+@pytest.mark.parametrize("cls,pins", [
+    (_LifoManager, [obm.test_deep_interleaved_figure]),
+    (_CopyFullSharedManager, [obm.test_full_shared_block_is_never_copied]),
+    (_CowKeepsReferenceManager, [obm.test_deep_prefix_sharing_and_copy_on_write,
+                                 lambda: obm.test_random_traces_keep_every_sequence_readable(0)]),
+])
+def test_planted_block_manager_mistake_is_caught(monkeypatch, cls, pins):
+    monkeypatch.setattr(obm, "BlockManager", cls)
+    for pin in pins:
+        with pytest.raises((AssertionError, block_manager.OutOfBlocks)):
+            pin()
 
 
 @pytest.mark.parametrize("name,fn,pins", MUTATIONS, ids=[f"{m[0]}:{m[1].__name__}" for m in MUTATIONS])

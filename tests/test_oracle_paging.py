@@ -208,3 +208,63 @@ def test_copy_blocks_semantics():
         paged.copy_blocks(kp, vp, [(1, 2), (3, 2)])
     with pytest.raises(ValueError):
         paged.copy_blocks(kp, vp, [(1, 2), (2, 3)])
+
+
+def test_copy_blocks_skips_pairs_outside_the_pool():
+    rng = np.random.default_rng(13)
+    kp = rng.integers(0, 255, (6, 2, 4, 8)).astype(np.uint8)
+    vp = kp[::-1].copy()
+    k0, v0 = kp.copy(), vp.copy()
+    paged.copy_blocks(kp, vp, [(-1, 2), (6, 3), (1, 6), (0, -2), (4, 5)])
+    assert np.array_equal(kp[5], k0[4]) and np.array_equal(vp[5], v0[4])
+    assert np.array_equal(kp[:5], k0[:5]) and np.array_equal(vp[:5], v0[:5])
+
+
+def test_swap_blocks_element_by_element():
+    """Brute force on a tiny case: every word of every destination block is
+    the source word at the same (head, offset, dim); all else is untouched."""
+    rng = np.random.default_rng(14)
+    dev_k = rng.integers(0, 1 << 16, (5, 2, 3, 4)).astype(np.uint16)
+    dev_v = rng.integers(0, 1 << 16, (5, 2, 3, 4)).astype(np.uint16)
+    host_k = np.full((7, 2, 3, 4), 0x7FC1, np.uint16)
+    host_v = np.full((7, 2, 3, 4), 0x7FC1, np.uint16)
+    pairs = [(4, 0), (0, 6), (2, 3), (9, 1), (1, 7)]  # the last two name no block
+    paged.swap_blocks(dev_k, dev_v, host_k, host_v, pairs)
+    moved = {0: 4, 6: 0, 3: 2}
+    for b in range(7):
+        for h in range(2):
+            for o in range(3):
+                for d in range(4):
+                    if b in moved:
+                        assert host_k[b, h, o, d] == dev_k[moved[b], h, o, d]
+                        assert host_v[b, h, o, d] == dev_v[moved[b], h, o, d]
+                    else:
+                        assert host_k[b, h, o, d] == 0x7FC1 == host_v[b, h, o, d]
+    with pytest.raises(ValueError):
+        paged.swap_blocks(dev_k, dev_v, host_k, host_v, [(0, 1), (2, 1)])
+    with pytest.raises(ValueError):
+        paged.swap_blocks(dev_k, dev_v, host_k[:, :1].copy(), host_v[:, :1].copy(), [(0, 0)])
+
+
+def test_swap_out_and_in_restores_the_sequence():
+    """A sequence's blocks swapped out to arbitrary host blocks and back into
+    other device blocks: its gathered K/V is unchanged, and equals the same
+    move done by the block copy within one pool."""
+    rng = np.random.default_rng(15)
+    bs, nb = 4, 12
+    kp = rng.standard_normal((nb, 2, bs, 8))
+    vp = rng.standard_normal((nb, 2, bs, 8))
+    table, L = [7, 2, 9], 10
+    K0, V0 = paged.gather(kp, table, L), paged.gather(vp, table, L)
+    hk, hv = np.zeros((5, 2, bs, 8)), np.zeros((5, 2, bs, 8))
+    paged.swap_blocks(kp, vp, hk, hv, [(7, 3), (2, 0), (9, 4)])
+    kp[table] = np.nan  # the device blocks are reused meanwhile
+    vp[table] = np.nan
+    back = [1, 11, 5]
+    paged.swap_blocks(hk, hv, kp, vp, [(3, 1), (0, 11), (4, 5)])
+    assert np.array_equal(paged.gather(kp, back, L), K0)
+    assert np.array_equal(paged.gather(vp, back, L), V0)
+    kq, vq = kp.copy(), vp.copy()
+    paged.swap_blocks(kp, vp, kp, vp, [(1, 0), (11, 3)])
+    paged.copy_blocks(kq, vq, [(1, 0), (11, 3)])
+    assert np.array_equal(kp, kq, equal_nan=True) and np.array_equal(vp, vq, equal_nan=True)
