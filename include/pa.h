@@ -303,6 +303,10 @@ typedef struct pa_block_manager pa_block_manager;
 /* A manager of blocks 0 .. num_blocks-1 of block_size tokens, all free.
  * Returns NULL (and sets pa_last_error) for non-positive sizes. */
 pa_block_manager* pa_bm_create(int32_t num_blocks, int32_t block_size);
+/* The same with a second pool of num_host_blocks host blocks (>= 0) that
+ * swapped-out sequences occupy (pa_bm_swap_out / pa_bm_swap_in). */
+pa_block_manager* pa_bm_create_swap(int32_t num_blocks, int32_t num_host_blocks,
+                                    int32_t block_size);
 void pa_bm_destroy(pa_block_manager* bm);
 
 /* Number of free blocks (>= 0), or PA_ERR_INVALID. */
@@ -342,8 +346,41 @@ int32_t pa_bm_seq_len(const pa_block_manager* bm, int64_t seq_id);
 int32_t pa_bm_block_tables(const pa_block_manager* bm, int32_t num_seqs, const int64_t* seq_ids,
                            int32_t max_blocks_per_seq, int32_t* block_tables, int32_t* seq_lens);
 
-/* References held on a block (0 = free), or PA_ERR_INVALID. */
+/* References held on a block of the device pool (0 = free), or PA_ERR_INVALID. */
 int32_t pa_bm_ref_count(const pa_block_manager* bm, int32_t block);
+
+/* Swap for preemption ([EVAL], its section on preemption: SWAP moves the
+ * blocks of a preempted sequence to host memory and back when it resumes;
+ * [DEEP] §3.2, preemption strategies).
+ *
+ * pa_bm_swap_out moves seq_ids[0 .. num_seqs-1] (distinct, not swapped out)
+ * to host blocks.  The set must hold its blocks alone: a block also held by
+ * a sequence outside the set cannot move (PA_ERR_INVALID), so forked
+ * siblings go together.  Each distinct block moves once, in order of first
+ * appearance (sequences in the given order, each table front to back), to a
+ * host block taken from the front of the host free list; its reference
+ * count moves with it and the device block returns to the back of the
+ * device free list.  The pairs (device block, host block) are written to
+ * pairs (int64 [max_pairs][2]) and *num_pairs counts them; they are the
+ * block_mapping of the pa_swap_blocks call that must run before the freed
+ * device blocks are written again.  PA_ERR_NO_BLOCKS (nothing changed) if
+ * the host pool cannot hold the set, PA_ERR_INVALID if max_pairs is too
+ * small.  A swapped-out sequence can be freed (its host blocks return to
+ * the host free list) but not appended to, forked, or listed by
+ * pa_bm_block_tables.
+ *
+ * pa_bm_swap_in is the reverse for swapped-out sequences: pairs are (host
+ * block, device block) and PA_ERR_NO_BLOCKS means the device pool is short. */
+int32_t pa_bm_swap_out(pa_block_manager* bm, int32_t num_seqs, const int64_t* seq_ids,
+                       int64_t* pairs, int32_t max_pairs, int32_t* num_pairs);
+int32_t pa_bm_swap_in(pa_block_manager* bm, int32_t num_seqs, const int64_t* seq_ids,
+                      int64_t* pairs, int32_t max_pairs, int32_t* num_pairs);
+
+/* Free host blocks (>= 0), or PA_ERR_INVALID. */
+int32_t pa_bm_num_free_host(const pa_block_manager* bm);
+
+/* 1 if the sequence is swapped out, 0 if not, or PA_ERR_INVALID. */
+int32_t pa_bm_is_swapped(const pa_block_manager* bm, int64_t seq_id);
 
 #ifdef __cplusplus
 }

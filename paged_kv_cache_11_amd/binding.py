@@ -59,6 +59,11 @@ _SIGNATURES = {
     "pa_bm_seq_len": ([_c_p, ctypes.c_int64], _c_int),
     "pa_bm_block_tables": ([_c_p, _c_int, _c_p, _c_int, _c_p, _c_p], _c_int),
     "pa_bm_ref_count": ([_c_p, _c_int], _c_int),
+    "pa_bm_create_swap": ([_c_int, _c_int, _c_int], _c_p),
+    "pa_bm_swap_out": ([_c_p, _c_int, _c_p, _c_p, _c_int, _c_p], _c_int),
+    "pa_bm_swap_in": ([_c_p, _c_int, _c_p, _c_p, _c_int, _c_p], _c_int),
+    "pa_bm_num_free_host": ([_c_p], _c_int),
+    "pa_bm_is_swapped": ([_c_p, ctypes.c_int64], _c_int),
 }
 
 
@@ -228,12 +233,13 @@ class BlockManager:
     with copy-on-write.  Arrays are numpy host arrays; copy them to the
     device for pa_cache_write, pa_copy_blocks and pa_decode."""
 
-    def __init__(self, num_blocks: int, block_size: int):
+    def __init__(self, num_blocks: int, block_size: int, num_host_blocks: int = 0):
         self._lib = load()
-        self._h = self._lib.pa_bm_create(int(num_blocks), int(block_size))
+        self._h = self._lib.pa_bm_create_swap(int(num_blocks), int(num_host_blocks), int(block_size))
         if not self._h:
             raise PagedAttentionError(PA_ERR_INVALID, self._lib.pa_last_error().decode())
         self.num_blocks, self.block_size = int(num_blocks), int(block_size)
+        self.num_host_blocks = int(num_host_blocks)
 
     def __del__(self):
         h, self._h = getattr(self, "_h", None), None
@@ -264,6 +270,34 @@ class BlockManager:
         _check(self._lib.pa_bm_append(self._h, n, ids.ctypes.data, slots.ctypes.data,
                                       pairs.ctypes.data, ctypes.byref(nc)))
         return slots[:n], pairs[:nc.value]
+
+    def _swap(self, fn, seq_ids, max_pairs):
+        import numpy as np
+
+        ids = np.ascontiguousarray(np.asarray(seq_ids, dtype=np.int64).reshape(-1))
+        cap = int(max_pairs) if max_pairs is not None else max(self.num_blocks, self.num_host_blocks)
+        pairs = np.empty((max(cap, 1), 2), dtype=np.int64)
+        n = ctypes.c_int32(0)
+        _check(fn(self._h, ids.size, ids.ctypes.data, pairs.ctypes.data, cap, ctypes.byref(n)))
+        return pairs[:n.value]
+
+    def swap_out(self, seq_ids, max_pairs=None):
+        """Move these sequences to host blocks; returns (device block, host
+        block) pairs int64 [n, 2] for pa_swap_blocks."""
+        return self._swap(self._lib.pa_bm_swap_out, seq_ids, max_pairs)
+
+    def swap_in(self, seq_ids, max_pairs=None):
+        """Move swapped-out sequences back; returns (host block, device block) pairs."""
+        return self._swap(self._lib.pa_bm_swap_in, seq_ids, max_pairs)
+
+    def num_free_host(self) -> int:
+        return int(self._lib.pa_bm_num_free_host(self._h))
+
+    def is_swapped(self, seq_id: int) -> bool:
+        r = int(self._lib.pa_bm_is_swapped(self._h, int(seq_id)))
+        if r < 0:
+            _check(r)
+        return bool(r)
 
     def fork(self, parent_id: int, child_id: int) -> None:
         _check(self._lib.pa_bm_fork(self._h, int(parent_id), int(child_id)))

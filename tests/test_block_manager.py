@@ -11,13 +11,16 @@ import pytest
 from oracle.block_manager import BlockManager as RefManager
 from oracle.block_manager import OutOfBlocks
 from paged_kv_cache_11_amd import binding as pa
+from test_oracle_block_manager import _groups
 
 
 def _same_state(m, r):
-    assert m.num_free() == r.num_free()
+    assert m.num_free() == r.num_free() and m.num_free_host() == r.num_free_host()
     for b in range(r.num_blocks):
         assert m.ref_count(b) == r.ref[b], b
-    ids = sorted(r.seqs)
+    for i in r.seqs:
+        assert m.is_swapped(i) == r.is_swapped(i)
+    ids = sorted(i for i in r.seqs if not r.is_swapped(i))
     if ids:
         width = max(len(r.table(i)) for i in ids) + 1
         tables, lens = m.block_tables(ids, width)
@@ -126,3 +129,106 @@ def test_utilisation_waste_is_under_one_block_per_sequence():
     used_blocks = 16384 - m.num_free()
     assert used_blocks == int(sum(-(-int(n) // bs) for n in lens))
     assert used_blocks * bs - int(lens.sum()) < 64 * bs
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_traces_with_swap_match_the_reference(seed):
+    """As above with swap-out and swap-in of whole sharing groups, refused
+    swaps of a set that shares blocks outside itself, and host pools small
+    enough to run out."""
+    rng = random.Random(300 + seed)
+    bs = rng.choice([1, 4, 16])
+    nb, nh = rng.randint(6, 48), rng.randint(2, 48)
+    m, r = pa.BlockManager(nb, bs, num_host_blocks=nh), RefManager(nb, bs, num_host_blocks=nh)
+    next_id, swaps = 0, 0
+
+    def both(call, *args):
+        """Run on both managers; the library must fail exactly when the
+        reference does, with the matching code, else return equal results."""
+        try:
+            want = getattr(r, call)(*args)
+        except OutOfBlocks:
+            with pytest.raises(pa.PagedAttentionError) as e:
+                getattr(m, call)(*args)
+            assert e.value.code == pa.PA_ERR_NO_BLOCKS
+            return None
+        except (KeyError, ValueError):
+            with pytest.raises(pa.PagedAttentionError) as e:
+                getattr(m, call)(*args)
+            assert e.value.code == pa.PA_ERR_INVALID
+            return None
+        return want, getattr(m, call)(*args)
+
+    for step in range(700):
+        op = rng.random()
+        live = [i for i in r.seqs if not r.is_swapped(i)]
+        out = [i for i in r.seqs if r.is_swapped(i)]
+        if op < 0.15 or not r.seqs:
+            res = both("add", next_id, rng.randint(0, 3 * bs))
+            if res:
+                assert list(res[1]) == res[0]
+            next_id += 1
+        elif op < 0.27:
+            both("fork", rng.choice(list(r.seqs)), next_id)  # may pick a swapped parent
+            next_id += 1
+        elif op < 0.6 and live:
+            res = both("append", [rng.choice(live) for _ in range(rng.randint(1, len(live)))])
+            if res:
+                (ws, wp), (gs, gp) = res
+                assert list(gs) == ws and [tuple(p) for p in gp] == wp
+        elif op < 0.72 and live:
+            groups = _groups(r, False)
+            group = rng.choice(groups)
+            if len(group) > 1 and rng.random() < 0.3:
+                group = group[:1]  # shares blocks outside the set: refused
+            res = both("swap_out", group)
+            if res:
+                assert [tuple(p) for p in res[1]] == res[0]
+                swaps += 1
+        elif op < 0.84 and out:
+            group = rng.choice(_groups(r, True))
+            rng.shuffle(group)
+            res = both("swap_in", group)
+            if res:
+                assert [tuple(p) for p in res[1]] == res[0]
+                swaps += 1
+        else:
+            sid = rng.choice(list(r.seqs))
+            r.release(sid)
+            m.release(sid)
+        if step % 20 == 0:
+            _same_state(m, r)
+    _same_state(m, r)
+    assert swaps > 5
+
+
+def test_swap_errors_leave_the_manager_unchanged():
+    m = pa.BlockManager(8, 4, num_host_blocks=2)
+    m.add(1, 9)   # 3 blocks
+    m.add(2, 4)
+    m.fork(2, 3)
+    with pytest.raises(pa.PagedAttentionError) as e:
+        m.swap_out([1])  # 3 blocks, 2 host blocks
+    assert e.value.code == pa.PA_ERR_NO_BLOCKS
+    with pytest.raises(pa.PagedAttentionError) as e:
+        m.swap_out([2])  # shares its block with 3
+    assert e.value.code == pa.PA_ERR_INVALID
+    for bad in ([2, 3, 2], [9], [2, 3]):
+        if bad == [2, 3]:
+            with pytest.raises(pa.PagedAttentionError):
+                m.swap_out(bad, max_pairs=0)  # room for no pair
+        else:
+            with pytest.raises(pa.PagedAttentionError):
+                m.swap_out(bad)
+    assert m.num_free() == 4 and m.num_free_host() == 2 and m.ref_count(3) == 2
+    assert m.swap_out([3, 2]).tolist() == [[3, 0]]
+    assert m.is_swapped(2) and m.ref_count(3) == 0 and m.num_free() == 5
+    for bad in (lambda: m.append([2]), lambda: m.fork(3, 4), lambda: m.block_tables([2], 4),
+                lambda: m.swap_out([2, 3]), lambda: m.swap_in([1])):
+        with pytest.raises(pa.PagedAttentionError) as e:
+            bad()
+        assert e.value.code == pa.PA_ERR_INVALID
+    m.release(2)
+    assert m.num_free_host() == 1
+    assert m.swap_in([3]).tolist() == [[0, 4]]
+    assert m.num_free_host() == 2 and m.block_tables([3], 2)[0].tolist() == [[4, -1]]

@@ -188,3 +188,134 @@ def test_out_of_blocks_changes_nothing():
     with pytest.raises(OutOfBlocks):
         m.add("d", 5)
     assert m.num_free() == 1
+
+
+def test_swap_out_and_in_by_hand():
+    """A 6-block device pool, 4 host blocks, block size 4.  A (6 tokens) is
+    forked into C; B holds its own blocks.  Swapping out A alone is refused
+    (C shares its blocks); A and C together move their two blocks once each;
+    the freed device blocks serve a new request; A and C come back into
+    other blocks once the device has room."""
+    m = BlockManager(6, 4, num_host_blocks=4)
+    m.add("A", 6)
+    m.add("B", 5)
+    m.fork("A", "C")
+    with pytest.raises(ValueError):
+        m.swap_out(["A"])
+    assert m.swap_out(["A", "C"]) == [(0, 0), (1, 1)]
+    assert m.free == [4, 5, 0, 1] and m.host_ref == [2, 2, 0, 0] and m.ref[:2] == [0, 0]
+    assert m.table("A") == m.table("C") == [0, 1] and m.is_swapped("C")
+    with pytest.raises(KeyError):
+        m.append(["A"])
+    with pytest.raises(KeyError):
+        m.fork("C", "E")
+    assert m.add("D", 9)[:1] == [16]  # blocks 4, 5, 0
+    with pytest.raises(OutOfBlocks):
+        m.swap_in(["A", "C"])
+    m.release("D")
+    assert m.free == [1, 4, 5, 0]
+    assert m.swap_in(["C", "A"]) == [(0, 1), (1, 4)]
+    assert m.table("A") == m.table("C") == [1, 4] and m.ref[1] == m.ref[4] == 2
+    assert m.host_free == [2, 3, 0, 1]
+    slots, pairs = m.append(["A"])  # the shared partial block is copied first
+    assert pairs == [(4, 5)] and slots == [5 * 4 + 2]
+
+
+def _groups(m, swapped: bool):
+    """Sets of sequences that hold their blocks alone: connected components
+    of the sharing relation among sequences on one side."""
+    ids = [s for s in m.seqs if m.is_swapped(s) == swapped]
+    owner, comp = {}, {s: s for s in ids}
+
+    def root(x):
+        while comp[x] != x:
+            x = comp[x]
+        return x
+    for s in ids:
+        for b in m.table(s):
+            if b in owner:
+                comp[root(s)] = root(owner[b])
+            else:
+                owner[b] = s
+    out = {}
+    for s in ids:
+        out.setdefault(root(s), []).append(s)
+    return list(out.values())
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_traces_with_swap_keep_every_sequence_readable(seed):
+    """Random traces with swap-out and swap-in of whole sharing groups over
+    a brute-force device memory and host memory: the pairs are applied as
+    the swap kernel would, and every sequence reads back its own tokens from
+    the side it lives on; reference counts equal table occurrences on both
+    sides and each free list is exactly that side's unreferenced blocks."""
+    rng = random.Random(50 + seed)
+    bs = rng.choice([2, 4, 16])
+    m = BlockManager(rng.randint(8, 40), bs, num_host_blocks=rng.randint(4, 40))
+    dev = [None] * (m.num_blocks * bs)
+    host = [None] * (m.num_host_blocks * bs)
+    content, next_id, next_tok = {}, 0, 0
+    swaps = 0
+    for _ in range(500):
+        op = rng.random()
+        live = [s for s in content if not m.is_swapped(s)]
+        out = [s for s in content if m.is_swapped(s)]
+        try:
+            if op < 0.15 or not content:
+                n = rng.randint(0, 3 * bs)
+                slots = m.add(next_id, n)
+                content[next_id] = list(range(next_tok, next_tok + n))
+                for s, tok in zip(slots, content[next_id]):
+                    dev[s] = tok
+                next_tok += n
+                next_id += 1
+            elif op < 0.27 and live:
+                p = rng.choice(live)
+                m.fork(p, next_id)
+                content[next_id] = list(content[p])
+                next_id += 1
+            elif op < 0.6 and live:
+                ids = rng.sample(live, rng.randint(1, len(live)))
+                slots, pairs = m.append(ids)
+                for src, dst in pairs:
+                    dev[dst * bs:(dst + 1) * bs] = dev[src * bs:(src + 1) * bs]
+                for sid, s in zip(ids, slots):
+                    dev[s] = next_tok
+                    content[sid].append(next_tok)
+                    next_tok += 1
+            elif op < 0.72 and live:
+                group = rng.choice(_groups(m, False))
+                pairs = m.swap_out(group)
+                for d, h in pairs:
+                    host[h * bs:(h + 1) * bs] = dev[d * bs:(d + 1) * bs]
+                    dev[d * bs:(d + 1) * bs] = [None] * bs  # the device block is reused
+                swaps += 1
+            elif op < 0.84 and out:
+                group = rng.choice(_groups(m, True))
+                rng.shuffle(group)
+                pairs = m.swap_in(group)
+                for h, d in pairs:
+                    dev[d * bs:(d + 1) * bs] = host[h * bs:(h + 1) * bs]
+                swaps += 1
+            else:
+                sid = rng.choice(list(content))
+                m.release(sid)
+                del content[sid]
+        except OutOfBlocks:
+            pass
+        for side, mem, ref, free, nb in ((False, dev, m.ref, m.free, m.num_blocks),
+                                         (True, host, m.host_ref, m.host_free, m.num_host_blocks)):
+            held = [0] * nb
+            for sid, toks in content.items():
+                if m.is_swapped(sid) != side:
+                    continue
+                tbl = m.table(sid)
+                assert len(tbl) == -(-len(toks) // bs)
+                for b in tbl:
+                    held[b] += 1
+                for t, tok in enumerate(toks):
+                    assert mem[tbl[t // bs] * bs + t % bs] == tok, (sid, t, side)
+            assert held == ref
+            assert sorted(free) == [b for b in range(nb) if ref[b] == 0] and len(set(free)) == len(free)
+    assert swaps > 10

@@ -137,9 +137,22 @@ class _CowKeepsReferenceManager(block_manager.BlockManager):
         return slots, pairs
 
 
+class _SwapForgetsReferencesManager(block_manager.BlockManager):
+    """Gives every moved block a single reference on the other side."""
+
+    def _move(self, sids, to_host):
+        pairs = block_manager.BlockManager._move(self, sids, to_host)
+        ref = self.host_ref if to_host else self.ref
+        for _, d in pairs:
+            ref[d] = 1
+        return pairs
+
+
 @pytest.mark.parametrize("cls,pins", [
     (_LifoManager, [obm.test_deep_interleaved_figure]),
     (_CopyFullSharedManager, [obm.test_full_shared_block_is_never_copied]),
+    (_SwapForgetsReferencesManager, [obm.test_swap_out_and_in_by_hand,
+                                     lambda: obm.test_random_traces_with_swap_keep_every_sequence_readable(0)]),
     (_CowKeepsReferenceManager, [obm.test_deep_prefix_sharing_and_copy_on_write,
                                  lambda: obm.test_random_traces_keep_every_sequence_readable(0)]),
 ])
