@@ -333,7 +333,7 @@ int32_t pa_bm_append(pa_block_manager* bm, int32_t num_seqs, const int64_t* seq_
 int32_t pa_bm_fork(pa_block_manager* bm, int64_t parent_id, int64_t child_id);
 
 /* Releases a sequence: one reference less on each of its blocks; blocks at
- * zero return to the back of the free list, in table order. */
+ * zero return to the back of the free list, last block first. */
 int32_t pa_bm_free(pa_block_manager* bm, int64_t seq_id);
 
 /* Tokens of a sequence (>= 0), or PA_ERR_INVALID. */
@@ -381,6 +381,50 @@ int32_t pa_bm_num_free_host(const pa_block_manager* bm);
 
 /* 1 if the sequence is swapped out, 0 if not, or PA_ERR_INVALID. */
 int32_t pa_bm_is_swapped(const pa_block_manager* bm, int64_t seq_id);
+
+/* Automatic prefix caching ([EVAL], its section on prefix caching).
+ *
+ * Every full block gets a chained hash of the previous block's hash, the
+ * block's token ids and an extra hash (e.g. an adapter id): 64-bit FNV-1a
+ * over the little-endian bytes of parent_hash (8; 0 for a sequence's first
+ * block), the token ids (4 each) and extra_hash (8) — pa_bm_block_hash.  A
+ * table maps hashes to device blocks.  Unreferenced cached blocks stay in
+ * the free list, whose front block leaves the table when it is taken
+ * (eviction): least recently released first and, since a freed sequence
+ * returns its blocks last block first, the leaves of a chain before the
+ * blocks near its root.  A swapped-out block leaves the cache.
+ *
+ * pa_bm_enable_prefix_caching turns the cache on; it must be called before
+ * the first sequence (PA_ERR_INVALID otherwise).
+ *
+ * pa_bm_add_prompt adds a sequence with its prompt token ids
+ * (tokens int32 [num_tokens]): the chain of its full blocks is looked up
+ * block by block up to the first miss (a hit also compares the block's
+ * stored token ids and extra hash); the hits join its table with one more
+ * reference each (an unreferenced hit leaves the free list), the rest of
+ * the blocks are taken from the free list, and the new full blocks enter
+ * the table (a hash already in the table keeps its block).  slot_mapping
+ * receives every token's slot and *num_cached_tokens the number of leading
+ * tokens whose K/V is already in the pool (a multiple of block_size): the
+ * caller writes K/V for tokens num_cached_tokens .. num_tokens-1 only.
+ * PA_ERR_NO_BLOCKS (nothing changed) if the free list cannot cover the
+ * blocks that missed.
+ *
+ * pa_bm_append_tokens is pa_bm_append with the new token id of each listed
+ * sequence (tokens int32 [num_seqs]); a block that its token fills enters
+ * the table.  Sequences added by pa_bm_add, or appended to by pa_bm_append,
+ * have unknown token ids and commit nothing more. */
+uint64_t pa_bm_block_hash(uint64_t parent_hash, const int32_t* tokens, int32_t num_tokens,
+                          uint64_t extra_hash);
+int32_t pa_bm_enable_prefix_caching(pa_block_manager* bm);
+int32_t pa_bm_add_prompt(pa_block_manager* bm, int64_t seq_id, const int32_t* tokens,
+                         int32_t num_tokens, uint64_t extra_hash, int64_t* slot_mapping,
+                         int32_t* num_cached_tokens);
+int32_t pa_bm_append_tokens(pa_block_manager* bm, int32_t num_seqs, const int64_t* seq_ids,
+                            const int32_t* tokens, int64_t* slot_mapping, int64_t* cow_pairs,
+                            int32_t* num_cow);
+/* Blocks in the prefix cache's table (>= 0), or PA_ERR_INVALID. */
+int32_t pa_bm_num_cached_blocks(const pa_block_manager* bm);
 
 #ifdef __cplusplus
 }

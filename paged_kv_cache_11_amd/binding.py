@@ -64,6 +64,11 @@ _SIGNATURES = {
     "pa_bm_swap_in": ([_c_p, _c_int, _c_p, _c_p, _c_int, _c_p], _c_int),
     "pa_bm_num_free_host": ([_c_p], _c_int),
     "pa_bm_is_swapped": ([_c_p, ctypes.c_int64], _c_int),
+    "pa_bm_block_hash": ([ctypes.c_uint64, _c_p, _c_int, ctypes.c_uint64], ctypes.c_uint64),
+    "pa_bm_enable_prefix_caching": ([_c_p], _c_int),
+    "pa_bm_add_prompt": ([_c_p, ctypes.c_int64, _c_p, _c_int, ctypes.c_uint64, _c_p, _c_p], _c_int),
+    "pa_bm_append_tokens": ([_c_p, _c_int, _c_p, _c_p, _c_p, _c_p, _c_p], _c_int),
+    "pa_bm_num_cached_blocks": ([_c_p], _c_int),
 }
 
 
@@ -167,6 +172,15 @@ def pa_copy_blocks(k_cache, v_cache, block_mapping, stream=None) -> None:
                                  _ptr(block_mapping) if n else None, n, _stream(stream)))
 
 
+def block_hash(parent_hash: int, tokens, extra_hash: int = 0) -> int:
+    """The library's chained hash of one full block of token ids."""
+    import numpy as np
+
+    toks = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32).reshape(-1))
+    return int(load().pa_bm_block_hash(int(parent_hash) & (2 ** 64 - 1), toks.ctypes.data,
+                                       toks.size, int(extra_hash) & (2 ** 64 - 1)))
+
+
 def pa_swap_blocks(src_k, src_v, dst_k, dst_v, block_mapping, stream=None) -> None:
     """Move whole blocks (src, dst) from the source pools into the
     destination pools; one side is usually pinned host memory (a tensor made
@@ -233,13 +247,48 @@ class BlockManager:
     with copy-on-write.  Arrays are numpy host arrays; copy them to the
     device for pa_cache_write, pa_copy_blocks and pa_decode."""
 
-    def __init__(self, num_blocks: int, block_size: int, num_host_blocks: int = 0):
+    def __init__(self, num_blocks: int, block_size: int, num_host_blocks: int = 0,
+                 prefix_caching: bool = False):
         self._lib = load()
         self._h = self._lib.pa_bm_create_swap(int(num_blocks), int(num_host_blocks), int(block_size))
         if not self._h:
             raise PagedAttentionError(PA_ERR_INVALID, self._lib.pa_last_error().decode())
         self.num_blocks, self.block_size = int(num_blocks), int(block_size)
         self.num_host_blocks = int(num_host_blocks)
+        if prefix_caching:
+            _check(self._lib.pa_bm_enable_prefix_caching(self._h))
+
+    def add_prompt(self, seq_id: int, tokens, extra_hash: int = 0):
+        """A new sequence from its prompt token ids, reusing cached blocks;
+        returns (slots int64 [n], num_cached: leading tokens already in the pool)."""
+        import numpy as np
+
+        toks = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32).reshape(-1))
+        slots = np.empty(max(toks.size, 1), dtype=np.int64)
+        nc = ctypes.c_int32(0)
+        _check(self._lib.pa_bm_add_prompt(self._h, int(seq_id), toks.ctypes.data, toks.size,
+                                          int(extra_hash) & (2 ** 64 - 1), slots.ctypes.data,
+                                          ctypes.byref(nc)))
+        return slots[:toks.size], int(nc.value)
+
+    def append_tokens(self, seq_ids, tokens):
+        """``append`` with each sequence's new token id (full blocks enter the cache)."""
+        import numpy as np
+
+        ids = np.ascontiguousarray(np.asarray(seq_ids, dtype=np.int64).reshape(-1))
+        toks = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32).reshape(-1))
+        if toks.size != ids.size:
+            raise PagedAttentionError(PA_ERR_INVALID, "one token per listed sequence")
+        n = ids.size
+        slots = np.empty(max(n, 1), dtype=np.int64)
+        pairs = np.empty((max(n, 1), 2), dtype=np.int64)
+        nc = ctypes.c_int32(0)
+        _check(self._lib.pa_bm_append_tokens(self._h, n, ids.ctypes.data, toks.ctypes.data,
+                                             slots.ctypes.data, pairs.ctypes.data, ctypes.byref(nc)))
+        return slots[:n], pairs[:nc.value]
+
+    def num_cached_blocks(self) -> int:
+        return int(self._lib.pa_bm_num_cached_blocks(self._h))
 
     def __del__(self):
         h, self._h = getattr(self, "_h", None), None

@@ -232,3 +232,87 @@ def test_swap_errors_leave_the_manager_unchanged():
     assert m.num_free_host() == 1
     assert m.swap_in([3]).tolist() == [[0, 4]]
     assert m.num_free_host() == 2 and m.block_tables([3], 2)[0].tolist() == [[4, -1]]
+
+
+def test_block_hash_matches_the_reference():
+    from oracle.block_manager import block_hash
+    rng = random.Random(5)
+    for _ in range(200):
+        n = rng.choice([0, 1, 4, 16, 33])
+        toks = [rng.randint(-2 ** 31, 2 ** 31 - 1) for _ in range(n)]
+        parent, extra = rng.getrandbits(64), rng.choice([0, rng.getrandbits(64)])
+        assert pa.block_hash(parent, toks, extra) == block_hash(parent, toks, extra)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_prefix_cache_traces_match_the_reference(seed):
+    """Prompts from shared prefixes with adapters, decode with token ids,
+    plain adds and appends, forks, frees and swaps, with a pool small
+    enough to evict: the library's slots, cached counts, pairs and state
+    equal the reference manager's at every step."""
+    rng = random.Random(900 + seed)
+    bs = rng.choice([1, 2, 4, 16])
+    nb, nh = rng.randint(8, 64), rng.randint(0, 32)
+    m = pa.BlockManager(nb, bs, num_host_blocks=nh, prefix_caching=True)
+    r = RefManager(nb, bs, num_host_blocks=nh, prefix_caching=True)
+    prefixes = [[rng.randint(0, 3) for _ in range(rng.randint(0, 5 * bs))] for _ in range(5)]
+    next_id, hits = 0, 0
+
+    def both(call, *args):
+        try:
+            want = getattr(r, call)(*args)
+        except OutOfBlocks:
+            with pytest.raises(pa.PagedAttentionError) as e:
+                getattr(m, call)(*args)
+            assert e.value.code == pa.PA_ERR_NO_BLOCKS
+            return None
+        except (KeyError, ValueError):
+            with pytest.raises(pa.PagedAttentionError) as e:
+                getattr(m, call)(*args)
+            assert e.value.code == pa.PA_ERR_INVALID
+            return None
+        return want, getattr(m, call)(*args)
+
+    for step in range(600):
+        op = rng.random()
+        live = [i for i in r.seqs if not r.is_swapped(i)]
+        if op < 0.25 or not r.seqs:
+            toks = rng.choice(prefixes) + [rng.randint(0, 3) for _ in range(rng.randint(0, 2 * bs))]
+            res = both("add_prompt", next_id, toks, rng.choice([0, 0, 2 ** 63 + 5]))
+            if res:
+                (ws, wc), (gs, gc) = res
+                assert list(gs) == ws and gc == wc
+                hits += wc
+            next_id += 1
+        elif op < 0.3:
+            res = both("add", next_id, rng.randint(0, 2 * bs))
+            next_id += 1
+        elif op < 0.38 and r.seqs:
+            both("fork", rng.choice(list(r.seqs)), next_id)
+            next_id += 1
+        elif op < 0.7 and live:
+            ids = [rng.choice(live) for _ in range(rng.randint(1, len(live)))]
+            if rng.random() < 0.85:
+                res = both("append_tokens", ids, [rng.randint(0, 3) for _ in ids])
+            else:
+                res = both("append", ids)
+            if res:
+                (ws, wp), (gs, gp) = res
+                assert list(gs) == ws and [tuple(p) for p in gp] == wp
+        elif op < 0.78 and live and nh:
+            res = both("swap_out", rng.choice(_groups(r, False)))
+            if res:
+                assert [tuple(p) for p in res[1]] == res[0]
+        elif op < 0.84 and nh and any(r.is_swapped(i) for i in r.seqs):
+            res = both("swap_in", rng.choice(_groups(r, True)))
+            if res:
+                assert [tuple(p) for p in res[1]] == res[0]
+        elif r.seqs:
+            sid = rng.choice(list(r.seqs))
+            r.release(sid)
+            m.release(sid)
+        assert m.num_cached_blocks() == r.num_cached_blocks()
+        if step % 20 == 0:
+            _same_state(m, r)
+    _same_state(m, r)
+    assert hits > 0

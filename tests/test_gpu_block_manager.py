@@ -225,3 +225,112 @@ def test_preemption_by_swap_through_the_manager(kv, bs, Hq, Hkv):
         t.append(ids, step)
     assert swapped_at is not None and resumed_at is not None, (swapped_at, resumed_at)
     t.check()
+
+
+def _prefix_rows(keys, Hkv, D, salt):
+    """K or V rows of tokens whose whole context is named by ``keys``: each
+    row is drawn from a generator seeded by its context key, so equal
+    prefixes give equal rows and any other prefix gives other rows."""
+    return np.stack([np.random.default_rng([salt, int(k)]).standard_normal((Hkv, D)).astype(np.float32)
+                     for k in keys]) if len(keys) else np.zeros((0, Hkv, D), np.float32)
+
+
+def _context_keys(tokens, extra):
+    """A running key per position naming (extra, tokens[0..t])."""
+    keys, k = [], (int(extra) * 1000003 + 17) % (1 << 61)
+    for t in tokens:
+        k = (k * 1000003 + int(t) + 1) % (1 << 61)
+        keys.append(k)
+    return keys
+
+
+@pytest.mark.parametrize("kv,bs,Hq,Hkv", [("bf16", 16, 32, 8), ("fp8", 32, 64, 8)])
+def test_prefix_cache_through_the_manager(kv, bs, Hq, Hkv):
+    """Automatic prefix caching end to end.  Requests share a 2000-token
+    system prompt (one with another adapter, one sharing only its first
+    half); each writes K/V only past its cached prefix; some decode with
+    token ids (filling blocks that enter the cache), some finish, and new
+    requests reuse their released cached blocks.  Decode of every live
+    sequence through the manager's tables is compared with attention over
+    its own context computed without any paging, from rows that depend on
+    the whole prefix — a wrong cache hit cannot pass."""
+    D = 128
+    rng = np.random.default_rng(41 + bs)
+    nb = 420 if bs == 16 else 220
+    ks = vs = 0.5 if kv == "fp8" else 1.0
+    m = pa.BlockManager(nb, bs, prefix_caching=True)
+    r = RefManager(nb, bs, prefix_caching=True)
+    b = wl.PagedBatch("apc", Hq, Hkv, D, bs, nb, "bf16", "bf16", kv, 1.0 / np.sqrt(D),
+                      np.zeros((1, Hq, D), np.float32), np.zeros((1, Hkv, D), np.float32),
+                      np.zeros((1, Hkv, D), np.float32), np.zeros(1, np.int64), np.zeros(1, np.int32),
+                      np.zeros((1, 1), np.int32), k_scale=ks, v_scale=vs)
+    kp, vp = G.gpu_pool(b)
+    system = rng.integers(0, 32000, 2000).tolist()
+    seqs = {}  # id -> (tokens, extra)
+
+    def write(keys, slots):
+        if not len(keys):
+            return
+        k, v = _prefix_rows(keys, Hkv, D, 1), _prefix_rows(keys, Hkv, D, 2)
+        pa.pa_cache_write(wl.storage_tensor(k, "bf16").to(G.DEV), wl.storage_tensor(v, "bf16").to(G.DEV),
+                          kp, vp, torch.from_numpy(np.ascontiguousarray(slots, np.int64)).to(G.DEV),
+                          ks, vs)
+
+    def add(sid, tokens, extra=0):
+        slots, nc = m.add_prompt(sid, tokens, extra)
+        want_slots, want_nc = r.add_prompt(sid, tokens, extra)
+        assert list(slots) == want_slots and nc == want_nc
+        write(_context_keys(tokens, extra)[nc:], slots[nc:])  # the cached prefix is in the pool
+        seqs[sid] = (list(tokens), extra)
+        return nc
+
+    assert add(0, system + rng.integers(0, 32000, 150).tolist()) == 0
+    assert add(1, system + rng.integers(0, 32000, 301).tolist()) == 2000 // bs * bs
+    assert add(2, system + rng.integers(0, 32000, 77).tolist(), extra=7) == 0
+    half = system[:1000] + rng.integers(0, 32000, 500).tolist()
+    assert add(3, half) == 1000 // bs * bs
+    for step in range(2 * bs + 3):  # decode: blocks fill and enter the cache
+        ids = sorted(seqs)
+        toks = rng.integers(0, 32000, len(ids)).tolist()
+        slots, pairs = m.append_tokens(ids, toks)
+        want_slots, want_pairs = r.append_tokens(ids, toks)
+        assert list(slots) == want_slots and [tuple(p) for p in pairs] == want_pairs == []
+        keys = []
+        for sid, t in zip(ids, toks):
+            seqs[sid][0].append(t)
+            keys.append(_context_keys(*seqs[sid])[-1])
+        write(keys, slots)
+    cached_before = m.num_cached_blocks()
+    # 0 finishes; a new request continuing 0's whole text reuses all of its
+    # full blocks from the free list (touch), and one more system-prompt
+    # request shares the prompt again.
+    full0 = list(seqs[0][0])
+    m.release(0)
+    r.release(0)
+    del seqs[0]
+    n0 = add(10, full0 + rng.integers(0, 32000, 40).tolist())
+    assert n0 == len(full0) // bs * bs
+    assert add(11, system + [5, 6, 7]) == 2000 // bs * bs
+    assert m.num_cached_blocks() >= cached_before
+    G.say(f"[apc {kv} bs{bs}] {len(seqs)} live, {m.num_cached_blocks()} cached blocks, "
+          f"{nb - m.num_free()} of {nb} in use")
+
+    ids = sorted(seqs)
+    width = max(len(r.table(i)) for i in ids) + 1
+    tables, lens = m.block_tables(ids, width)
+    q = rng.standard_normal((len(ids), Hq, D)).astype(np.float32)
+    qt = wl.storage_tensor(q, "bf16").to(G.DEV)
+    q64 = G.query_f64(qt)
+    ref = np.zeros((len(ids), Hq, D))
+    for i, sid in enumerate(ids):
+        tokens, extra = seqs[sid]
+        keys = _context_keys(tokens, extra)
+        Kb = _rows_bits(_prefix_rows(keys, Hkv, D, 1), kv, ks)
+        Vb = _rows_bits(_prefix_rows(keys, Hkv, D, 2), kv, vs)
+        K, V = opg.pool_values(Kb, kv, ks), opg.pool_values(Vb, kv, vs)
+        for h in range(Hq):
+            g = h // (Hq // Hkv)
+            ref[i, h] = opg.attend(q64[i, h], K[:, g], V[:, g], b.scale)
+    for ps in (pa.PA_PARTITION_BALANCED, 0):
+        got = G.run_decode(b, kp, vp, qt, partition_size=ps, seq_lens=lens, tables=tables)
+        G.assert_close(got, ref, kv, f"decode over cached prefixes, partition {ps}")

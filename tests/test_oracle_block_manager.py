@@ -212,13 +212,13 @@ def test_swap_out_and_in_by_hand():
     assert m.add("D", 9)[:1] == [16]  # blocks 4, 5, 0
     with pytest.raises(OutOfBlocks):
         m.swap_in(["A", "C"])
-    m.release("D")
-    assert m.free == [1, 4, 5, 0]
-    assert m.swap_in(["C", "A"]) == [(0, 1), (1, 4)]
-    assert m.table("A") == m.table("C") == [1, 4] and m.ref[1] == m.ref[4] == 2
+    m.release("D")  # its blocks come back last block first
+    assert m.free == [1, 0, 5, 4]
+    assert m.swap_in(["C", "A"]) == [(0, 1), (1, 0)]
+    assert m.table("A") == m.table("C") == [1, 0] and m.ref[1] == m.ref[0] == 2
     assert m.host_free == [2, 3, 0, 1]
     slots, pairs = m.append(["A"])  # the shared partial block is copied first
-    assert pairs == [(4, 5)] and slots == [5 * 4 + 2]
+    assert pairs == [(0, 5)] and slots == [5 * 4 + 2]
 
 
 def _groups(m, swapped: bool):
@@ -319,3 +319,167 @@ def test_random_traces_with_swap_keep_every_sequence_readable(seed):
             assert held == ref
             assert sorted(free) == [b for b in range(nb) if ref[b] == 0] and len(set(free)) == len(free)
     assert swaps > 10
+
+
+# -- prefix caching -------------------------------------------------------------
+from oracle.block_manager import block_hash, fnv1a64  # noqa: E402
+
+
+def test_fnv1a64_published_vectors():
+    """Test vectors of 64-bit FNV-1a published with its definition."""
+    assert fnv1a64(b"") == 0xCBF29CE484222325
+    assert fnv1a64(b"a") == 0xAF63DC4C8601EC8C
+    assert fnv1a64(b"foobar") == 0x85944171F73967E8
+
+
+def test_block_hash_is_chained():
+    """hash(parent, tokens, extra): equal for equal inputs, different when
+    any of the three differs, so one block's hash names its whole prefix."""
+    a = block_hash(0, [1, 2, 3, 4])
+    assert a == block_hash(0, [1, 2, 3, 4]) and a == fnv1a64(
+        bytes(8) + b"".join(t.to_bytes(4, "little") for t in (1, 2, 3, 4)) + bytes(8))
+    assert len({a, block_hash(0, [1, 2, 3, 5]), block_hash(a, [1, 2, 3, 4]),
+                block_hash(0, [1, 2, 3, 4], extra=7), block_hash(0, [4, 3, 2, 1])}) == 5
+    # The same block after two different first blocks hashes differently.
+    b1 = block_hash(block_hash(0, [9, 9, 9, 9]), [5, 6, 7, 8])
+    b2 = block_hash(block_hash(0, [9, 9, 9, 8]), [5, 6, 7, 8])
+    assert b1 != b2
+
+
+def test_system_prompt_is_shared_through_the_cache():
+    """The page's use case: requests that start with the same system prompt.
+    A (system prompt of 2 full blocks + 3 own tokens) commits its 2 full
+    blocks; B with the same system prompt hits both (8 cached tokens, 2
+    references each) and takes one block for its own tail; C with another
+    adapter (extra hash) hits nothing; D differing in the prompt's second
+    block hits only the first."""
+    bs = 4
+    m = BlockManager(16, bs, prefix_caching=True)
+    sys_prompt = [11, 12, 13, 14, 15, 16, 17, 18]
+    slots_a, ca = m.add_prompt("A", sys_prompt + [1, 2, 3])
+    assert ca == 0 and m.table("A") == [0, 1, 2] and m.num_cached_blocks() == 2
+    slots_b, cb = m.add_prompt("B", sys_prompt + [4, 5])
+    assert cb == 8 and m.table("B") == [0, 1, 3] and m.ref[:2] == [2, 2]
+    assert slots_b[:8] == slots_a[:8] and slots_b[8:] == [12, 13]
+    _, cc = m.add_prompt("C", sys_prompt + [4, 5], extra=99)
+    assert cc == 0 and m.table("C") == [4, 5, 6] and m.num_cached_blocks() == 4
+    _, cd = m.add_prompt("D", sys_prompt[:4] + [0, 0, 0, 0] + [7])
+    assert cd == 4 and m.table("D") == [0, 7, 8] and m.ref[0] == 3
+    # G starts with the tokens of the prompt's second block: that block's K/V
+    # belong after the first block, so nothing is reused.
+    _, cg = m.add_prompt("G", sys_prompt[4:] + [1])
+    assert cg == 0 and m.table("G") == [9, 10]
+    m.release("G")
+    # A fills its third block during decode: it enters the cache, and a new
+    # request with A's whole prompt plus that token hits all three blocks.
+    _, pairs = m.append_tokens(["A"], [9])
+    assert pairs == [] and m.num_cached_blocks() == 7  # A: 0 1 2, C: 4 5, D: 7, G: 9
+    _, ce = m.add_prompt("E", sys_prompt + [1, 2, 3, 9, 10])
+    assert ce == 12 and m.table("E")[:3] == [0, 1, 2]
+
+
+def test_eviction_is_lru_and_leaf_first():
+    """Released cached blocks wait in the free list: a later request takes
+    never-used blocks first, then evicts the least recently released, and
+    within one release the chain's last block before its first."""
+    bs = 2
+    m = BlockManager(6, bs, prefix_caching=True)
+    m.add_prompt("X", [1, 1, 2, 2, 3, 3])   # blocks 0, 1, 2, all cached
+    m.add_prompt("Y", [7, 7])               # block 3, cached
+    m.release("X")                          # free: 4, 5, 2, 1, 0 (X's leaf first)
+    m.release("Y")                          # ... then 3
+    assert m.free == [4, 5, 2, 1, 0, 3] and m.num_cached_blocks() == 4
+    m.add_prompt("Z", [8, 8, 9, 9, 6, 6])   # 3 misses: takes 4, 5 (unused), then evicts 2
+    assert m.table("Z") == [4, 5, 2] and m.num_cached_blocks() == 3 + 3
+    # X's first two blocks survived the eviction of its leaf.
+    _, c = m.add_prompt("X2", [1, 1, 2, 2, 3, 3])
+    assert c == 4 and m.table("X2")[:2] == [0, 1]
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_prefix_cache_traces_keep_every_sequence_readable(seed):
+    """Prompts drawn from a few shared prefixes, with adapters, decode steps
+    with token ids, forks, frees and plain adds over a small pool, against a
+    brute-force memory whose value at a slot names the whole prefix up to
+    that token and the adapter (as K/V depend on the whole context): the
+    caller writes only the tokens past num_cached, so a wrong hit shows as a
+    wrong value.  Reference counts equal table occurrences; the free list is
+    exactly the unreferenced blocks; every cached block holds what its hash
+    names."""
+    rng = random.Random(700 + seed)
+    bs = rng.choice([2, 4])
+    m = BlockManager(rng.randint(12, 40), bs, prefix_caching=True, num_host_blocks=rng.randint(4, 24))
+    mem = [None] * (m.num_blocks * bs)
+    host = [None] * (m.num_host_blocks * bs)
+    prefixes = [[rng.randint(0, 3) for _ in range(rng.randint(0, 4 * bs))] for _ in range(4)]
+    content, next_id, hits = {}, 0, 0
+
+    def value(toks, t, extra):
+        return (tuple(toks[:t + 1]), extra)
+
+    for _ in range(500):
+        op = rng.random()
+        try:
+            if op < 0.3 or not content:
+                toks = rng.choice(prefixes) + [rng.randint(0, 3) for _ in range(rng.randint(0, 2 * bs))]
+                extra = rng.choice([0, 0, 0, 5])
+                slots, nc = m.add_prompt(next_id, toks, extra)
+                assert nc % bs == 0 and nc <= len(toks)
+                for t in range(nc):  # cached: already in the pool
+                    assert mem[slots[t]] == value(toks, t, extra)
+                for t in range(nc, len(toks)):
+                    mem[slots[t]] = value(toks, t, extra)
+                content[next_id] = (list(toks), extra)
+                hits += nc
+                next_id += 1
+            elif op < 0.4:
+                p = rng.choice(list(content))
+                if m.is_swapped(p):
+                    continue
+                m.fork(p, next_id)
+                content[next_id] = (list(content[p][0]), content[p][1])
+                next_id += 1
+            elif op < 0.5:
+                live = [i for i in content if not m.is_swapped(i)]
+                out = [i for i in content if m.is_swapped(i)]
+                if rng.random() < 0.5 and live:
+                    for d, h in m.swap_out(rng.choice(_groups(m, False))):
+                        host[h * bs:(h + 1) * bs] = mem[d * bs:(d + 1) * bs]
+                        mem[d * bs:(d + 1) * bs] = [None] * bs  # reused from now on
+                elif out:
+                    for h, d in m.swap_in(rng.choice(_groups(m, True))):
+                        mem[d * bs:(d + 1) * bs] = host[h * bs:(h + 1) * bs]
+            elif op < 0.75:
+                live = [i for i in content if not m.is_swapped(i)]
+                if not live:
+                    continue
+                ids = rng.sample(live, rng.randint(1, len(live)))
+                toks = [rng.randint(0, 3) for _ in ids]
+                slots, pairs = m.append_tokens(ids, toks)
+                for src, dst in pairs:
+                    mem[dst * bs:(dst + 1) * bs] = mem[src * bs:(src + 1) * bs]
+                for sid, s, t in zip(ids, slots, toks):
+                    seq, extra = content[sid]
+                    seq.append(t)
+                    mem[s] = value(seq, len(seq) - 1, extra)
+            else:
+                sid = rng.choice(list(content))
+                m.release(sid)
+                del content[sid]
+        except OutOfBlocks:
+            pass
+        held = [0] * m.num_blocks
+        for sid, (toks, extra) in content.items():
+            tbl = m.table(sid)
+            side = host if m.is_swapped(sid) else mem
+            for b in ([] if m.is_swapped(sid) else tbl):
+                held[b] += 1
+            for t in range(len(toks)):
+                assert side[tbl[t // bs] * bs + t % bs] == value(toks, t, extra), (sid, t)
+        assert held == m.ref
+        assert sorted(m.free) == [b for b in range(m.num_blocks) if m.ref[b] == 0]
+        for b, (h, toks, extra) in m.cached.items():
+            assert m.table_of[h] == b
+            assert [mem[b * bs + i][0][-1] for i in range(bs)] == list(toks)
+            assert all(mem[b * bs + i][1] == extra for i in range(bs))
+    assert hits > 0

@@ -148,11 +148,64 @@ class _SwapForgetsReferencesManager(block_manager.BlockManager):
         return pairs
 
 
+def _hash_without_parent(parent, tokens, extra=0):
+    return _orig_block_hash(0, tokens, extra)
+
+
+def _hash_without_extra(parent, tokens, extra=0):
+    return _orig_block_hash(parent, tokens, 0)
+
+
+_orig_block_hash = block_manager.block_hash
+
+
+@pytest.mark.parametrize("fn,pins", [
+    (_hash_without_parent, [obm.test_system_prompt_is_shared_through_the_cache,
+                            lambda: obm.test_random_prefix_cache_traces_keep_every_sequence_readable(0)]),
+    (_hash_without_extra, [obm.test_block_hash_is_chained]),
+])
+def test_planted_prefix_hash_mistake_is_caught(monkeypatch, fn, pins):
+    monkeypatch.setattr(block_manager, "block_hash", fn)
+    monkeypatch.setattr(obm, "block_hash", fn)
+    for pin in pins:
+        with pytest.raises(AssertionError):
+            pin()
+
+
+class _NoTouchManager(block_manager.BlockManager):
+    """Reuses cached blocks without taking them off the free list."""
+
+    def add_prompt(self, sid, tokens, extra=0):
+        free = list(self.free)
+        out = block_manager.BlockManager.add_prompt(self, sid, tokens, extra)
+        for b in self.seqs[sid]["blocks"]:
+            if b in free and b not in self.free and self.ref[b] == 1 and b in self.cached:
+                self.free.append(b)
+        return out
+
+
+class _SwapInKeepsCacheManager(block_manager.BlockManager):
+    """Leaves a cached device block in the cache when swap-in overwrites it."""
+
+    def _move(self, sids, to_host):
+        before = dict(self.cached)
+        pairs = block_manager.BlockManager._move(self, sids, to_host)
+        if not to_host:
+            for _, d in pairs:
+                if d in before and d not in self.cached and before[d][0] not in self.table_of:
+                    self.cached[d] = before[d]
+                    self.table_of[before[d][0]] = d
+        return pairs
+
+
 @pytest.mark.parametrize("cls,pins", [
     (_LifoManager, [obm.test_deep_interleaved_figure]),
     (_CopyFullSharedManager, [obm.test_full_shared_block_is_never_copied]),
     (_SwapForgetsReferencesManager, [obm.test_swap_out_and_in_by_hand,
                                      lambda: obm.test_random_traces_with_swap_keep_every_sequence_readable(0)]),
+    (_SwapInKeepsCacheManager, [lambda: [obm.test_random_prefix_cache_traces_keep_every_sequence_readable(i)
+                                         for i in range(6)]]),
+    (_NoTouchManager, [lambda: obm.test_random_prefix_cache_traces_keep_every_sequence_readable(1)]),
     (_CowKeepsReferenceManager, [obm.test_deep_prefix_sharing_and_copy_on_write,
                                  lambda: obm.test_random_traces_keep_every_sequence_readable(0)]),
 ])
