@@ -81,7 +81,7 @@ def summarize_counters(fetch_csv: str, write_csv: str, workload: str, out_path: 
         return acc
 
     f, w = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
-    copy_name = next(k for k in f if "copy_blocks_kernel" in k)
+    copy_name = next(k for k in f if "move_blocks_kernel" in k)
     # The calibration copy reads and writes 256 MiB (K and V halves).
     true_bytes = 256.0 * (1 << 20)
     f_scale = true_bytes / statistics.mean(f[copy_name])
