@@ -185,8 +185,9 @@ int32_t pa_swap_blocks(const void* src_k, const void* src_v, int32_t src_num_blo
 /*
  * Workspace bytes pa_decode needs for split-K partials: 0 when
  * partition_size == 0 or one partition covers max_seq_len; for
- * PA_PARTITION_BALANCED two partial states per wavefront of the largest
- * balanced grid plus a two-word cut record per (sequence, KV head).
+ * PA_PARTITION_BALANCED two partial states and a two-word merge task per
+ * wavefront of the largest balanced grid, plus a two-word cut record per
+ * (sequence, KV head).
  */
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                                 int32_t head_size, int32_t max_seq_len, int32_t partition_size);

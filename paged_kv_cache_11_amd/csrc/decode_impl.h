@@ -702,7 +702,7 @@ __device__ __forceinline__ float merge_element(const float* acc, const float* ml
 template <typename KV, typename QT, int D, int BS, int G>
 __global__ __launch_bounds__(kMaxDecodeWaves * kWave) void decode_balanced_kernel(
     void* __restrict__ out, float* __restrict__ part_acc, float* __restrict__ part_ml,
-    int32_t* __restrict__ cuts, const void* __restrict__ query,
+    int32_t* __restrict__ merges, int32_t* __restrict__ cuts, const void* __restrict__ query,
     const void* __restrict__ k_cache, const void* __restrict__ v_cache,
     const int32_t* __restrict__ block_tables, const int32_t* __restrict__ seq_lens, int num_seqs,
     int max_blocks_per_seq, int num_kv_heads, int workers_per_head, float qk_scale_log2,
@@ -718,6 +718,8 @@ __global__ __launch_bounds__(kMaxDecodeWaves * kWave) void decode_balanced_kerne
 
   const int64_t T = total_blocks(seq_lens, num_seqs, BS, lane);
   const int W = effective_workers(T, workers_per_head, BS);
+  int32_t* merge = merges + 2 * (int64_t)worker;
+  if (lane == 0) merge[0] = -1;  // no merge task unless the last run sets one
   if (vw >= W) return;
   const int64_t start = worker_start(T, vw, W), end = worker_start(T, vw + 1, W);
   if (start >= end) return;
@@ -745,11 +747,16 @@ __global__ __launch_bounds__(kMaxDecodeWaves * kWave) void decode_balanced_kerne
       const int slot = pos == start ? 0 : 1;
       const int64_t hq0 = (int64_t)s * num_heads + (int64_t)g * G;
       if (b_lo == 0 && lane == 0) {
-        // The worker holding the sequence's first block describes its cut:
-        // first worker, number of pieces, and the first piece's slot.
-        const int np = whole ? 1 : worker_of(T, seg_end - 1, W) - vw + 1;
+        // The worker holding the sequence's first unit records how it is
+        // cut (first worker, 2 * pieces + first slot) per sequence, and, if
+        // it is cut, as this worker's merge task.
+        const int code = (whole ? 1 : worker_of(T, seg_end - 1, W) - vw + 1) * 2 + slot;
         cuts[2 * ((int64_t)s * num_kv_heads + g) + 0] = vw;
-        cuts[2 * ((int64_t)s * num_kv_heads + g) + 1] = np * 2 + slot;
+        cuts[2 * ((int64_t)s * num_kv_heads + g) + 1] = code;
+        if (!whole) {
+          merge[0] = s;
+          merge[1] = code;
+        }
       }
 #pragma unroll
       for (int h = 0; h < G; ++h) {
@@ -779,33 +786,64 @@ __global__ __launch_bounds__(kMaxDecodeWaves * kWave) void decode_balanced_kerne
   }
 }
 
-// Finishes what the balanced kernel left: one workgroup of D threads per
-// (query head, KV head, sequence), one output element per thread.  Empty
-// sequences get zeros; a sequence cut between workers is merged from its
-// pieces' (m, l, acc), found through the cut record its first worker
-// wrote; a whole sequence was finished by its worker.
+// Finishes what the balanced kernels left.  The worker holding a
+// sequence's first unit recorded how the sequence is cut: per sequence and
+// KV head {first worker, 2 * pieces + slot}, and for a cut sequence the
+// same as that worker's merge task {s, 2 * pieces + slot} (else -1).  A
+// cut sequence is merged from its pieces' (m, l, acc): the first worker's
+// (that slot) and slot 0 of each following worker.  A whole sequence was
+// finished by its worker.  Two grids do the same merges, one element per
+// thread: per (query head, KV head, sequence) when there are few
+// sequences, per (query head, worker, KV head) when there are many — what
+// a reduce costs is mostly the dispatch of its workgroups.
+
+template <typename OT, int D, int G>
+__device__ __forceinline__ void merge_cut(void* out, const float* part_acc, const float* part_ml,
+                                          int s, int va, int code, int h, int g, int d,
+                                          int num_kv_heads, float v_scale) {
+  const int np = code >> 1, slot0 = code & 1;
+  auto state = [&](int p, int hh) -> int64_t {
+    return ((int64_t)((va + p) * num_kv_heads + g) * 2 + (p == 0 ? slot0 : 0)) * G + hh;
+  };
+  const float o = merge_element<false>(part_acc, part_ml, np, D, h, d, state);
+  store_out<OT>(out, ((int64_t)s * num_kv_heads * G + g * G + h) * D + d, o * v_scale);
+}
+
+// Per (query head h, KV head g, sequence s); empty sequences get zeros.
 template <typename OT, int D, int G>
 __global__ __launch_bounds__(D) void balanced_reduce_kernel(
     void* __restrict__ out, const float* __restrict__ part_acc,
     const float* __restrict__ part_ml, const int32_t* __restrict__ cuts,
     const int32_t* __restrict__ seq_lens, int num_kv_heads, float v_scale) {
   const int h = blockIdx.x, g = blockIdx.y, s = blockIdx.z, d = threadIdx.x;
-  const int num_heads = num_kv_heads * G;
-  const int64_t row = (int64_t)s * num_heads + (int64_t)g * G + h;
   const int L = seq_lens[s];
   const int va = cuts[2 * ((int64_t)s * num_kv_heads + g) + 0];
   const int code = cuts[2 * ((int64_t)s * num_kv_heads + g) + 1];
   if (L == 0) {
-    store_out<OT>(out, row * D + d, 0.f);
+    store_out<OT>(out, ((int64_t)s * num_kv_heads * G + g * G + h) * D + d, 0.f);
     return;
   }
-  const int np = code >> 1, slot0 = code & 1;
-  if (np <= 1) return;
-  auto state = [&](int p, int hh) -> int64_t {
-    return ((int64_t)((va + p) * num_kv_heads + g) * 2 + (p == 0 ? slot0 : 0)) * G + hh;
-  };
-  const float o = merge_element<false>(part_acc, part_ml, np, D, h, d, state);
-  store_out<OT>(out, row * D + d, o * v_scale);
+  if ((code >> 1) <= 1) return;
+  merge_cut<OT, D, G>(out, part_acc, part_ml, s, va, code, h, g, d, num_kv_heads, v_scale);
+}
+
+// Per (query head h, worker vw, KV head g): the worker's merge task, and
+// zeros for the empty sequences among vw * D .. vw * D + D - 1 (+ the
+// grid's multiples), one sequence per thread.
+template <typename OT, int D, int G>
+__global__ __launch_bounds__(D) void balanced_reduce_tasks_kernel(
+    void* __restrict__ out, const float* __restrict__ part_acc,
+    const float* __restrict__ part_ml, const int32_t* __restrict__ merges,
+    const int32_t* __restrict__ seq_lens, int num_seqs, int num_kv_heads, float v_scale) {
+  const int h = blockIdx.x, vw = blockIdx.y, g = blockIdx.z, d = threadIdx.x;
+  const int32_t* task = merges + 2 * ((int64_t)vw * num_kv_heads + g);
+  const int s = task[0], code = task[1];
+  for (int e = vw * D + d; e < num_seqs; e += gridDim.y * D)
+    if (seq_lens[e] == 0)
+      for (int i = 0; i < D; ++i)
+        store_out<OT>(out, ((int64_t)e * num_kv_heads * G + g * G + h) * D + i, 0.f);
+  if (s < 0) return;
+  merge_cut<OT, D, G>(out, part_acc, part_ml, s, vw, code, h, g, d, num_kv_heads, v_scale);
 }
 
 // Log-sum-exp merge of the fixed partitions of one (query head, KV head,
@@ -873,21 +911,29 @@ hipError_t launch_decode(const DecodeArgs& a) {
       if (mfma)
         hipLaunchKernelGGL((decode_balanced_mfma_kernel<KV, QT, PBS, G>), dim3((unsigned)wg),
                            dim3(kMaxDecodeWaves * kWave), 0, a.stream, a.out, a.part_o, a.part_ml,
-                           a.cuts, a.query, a.k_cache, a.v_cache, a.block_tables, a.seq_lens,
+                           a.merges, a.cuts, a.query, a.k_cache, a.v_cache, a.block_tables,
+                           a.seq_lens,
                            a.num_seqs, a.max_blocks_per_seq, a.num_kv_heads, per_head, qk, v_scale);
     }
     if (!mfma)
       hipLaunchKernelGGL((decode_balanced_kernel<KV, QT, D, BS, G>), dim3((unsigned)wg),
                          dim3(kMaxDecodeWaves * kWave), 0, a.stream, a.out, a.part_o, a.part_ml,
-                         a.cuts, a.query, a.k_cache, a.v_cache, a.block_tables, a.seq_lens,
+                         a.merges, a.cuts, a.query, a.k_cache, a.v_cache, a.block_tables,
+                         a.seq_lens,
                          a.num_seqs, a.max_blocks_per_seq, a.num_kv_heads, per_head, qk, v_scale,
                          kSubShift);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((balanced_reduce_kernel<QT, D, G>),
-                       dim3((unsigned)G, (unsigned)a.num_kv_heads, (unsigned)a.num_seqs), dim3(D), 0,
-                       a.stream,
-                       a.out, a.part_o, a.part_ml, a.cuts, a.seq_lens, a.num_kv_heads, v_scale);
+    if (a.num_seqs <= per_head)
+      hipLaunchKernelGGL((balanced_reduce_kernel<QT, D, G>),
+                         dim3((unsigned)G, (unsigned)a.num_kv_heads, (unsigned)a.num_seqs), dim3(D),
+                         0, a.stream, a.out, a.part_o, a.part_ml, a.cuts, a.seq_lens,
+                         a.num_kv_heads, v_scale);
+    else
+      hipLaunchKernelGGL((balanced_reduce_tasks_kernel<QT, D, G>),
+                         dim3((unsigned)G, (unsigned)per_head, (unsigned)a.num_kv_heads), dim3(D),
+                         0, a.stream, a.out, a.part_o, a.part_ml, a.merges, a.seq_lens,
+                         a.num_seqs, a.num_kv_heads, v_scale);
     return hipGetLastError();
   }
   const int tiles_per_part = a.partition_blocks << kSubShift;  // 0: whole sequence

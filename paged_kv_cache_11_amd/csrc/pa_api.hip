@@ -245,6 +245,7 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num
   if (partition_size == PA_PARTITION_BALANCED) {
     const size_t n = (size_t)pa::kMaxBalancedWorkers * 2 * (num_heads / num_kv_heads);
     return align256(n * head_size * sizeof(float)) + align256(n * 2 * sizeof(float)) +
+           align256((size_t)pa::kMaxBalancedWorkers * 2 * sizeof(int32_t)) +
            align256((size_t)num_seqs * num_kv_heads * 2 * sizeof(int32_t));
   }
   const int64_t mp = decode_max_parts(max_seq_len, partition_size);
@@ -292,6 +293,7 @@ int32_t pa_decode(void* out, const void* query, int32_t q_dtype, int32_t num_seq
   float* part_o = nullptr;
   float* part_ml = nullptr;
   int32_t workers = 0;
+  int32_t* a_merges = nullptr;
   int32_t* a_cuts = nullptr;
   const int32_t engine = decode_engine(q_dtype, cache_dtype, head_size, num_heads / num_kv_heads);
   if (mp > 1 || balanced) {
@@ -305,7 +307,9 @@ int32_t pa_decode(void* out, const void* query, int32_t q_dtype, int32_t num_seq
     part_o = (float*)workspace;
     part_ml = (float*)((char*)workspace + align256(n * head_size * sizeof(float)));
     if (balanced) {
-      a_cuts = (int32_t*)((char*)part_ml + align256(n * 2 * sizeof(float)));
+      a_merges = (int32_t*)((char*)part_ml + align256(n * 2 * sizeof(float)));
+      a_cuts = (int32_t*)((char*)a_merges +
+                          align256((size_t)pa::kMaxBalancedWorkers * 2 * sizeof(int32_t)));
       const int32_t w = balanced_workers_for_device(engine);
       if (w <= 0) return fail(PA_ERR_HIP, "cannot query the device's compute units");
       workers = (w / num_kv_heads) * num_kv_heads;
@@ -325,6 +329,7 @@ int32_t pa_decode(void* out, const void* query, int32_t q_dtype, int32_t num_seq
   a.part_o = part_o; a.part_ml = part_ml;
   a.num_waves = decode_waves_override();
   a.balanced_workers = workers;
+  a.merges = a_merges;
   a.cuts = a_cuts;
   a.engine = engine;
   a.stream = (hipStream_t)stream;

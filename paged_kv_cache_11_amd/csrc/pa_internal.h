@@ -64,9 +64,10 @@ struct DecodeArgs {
   int32_t max_parts;         // grid extent over partitions
   float* part_o;             // [num_seqs][num_heads][max_parts][head_size]
   float* part_ml;            // [num_seqs][num_heads][max_parts][2]
+  int32_t* merges;           // balanced split: per wavefront {sequence or -1, 2*pieces+slot}
+  int32_t* cuts;             // balanced split: per (sequence, KV head) {first worker, 2*pieces+slot}
   int32_t num_waves;         // wavefronts per workgroup; 0 = chosen from the partition size
   int32_t balanced_workers;  // > 0: balanced split over this many wavefronts (multiple of Hkv)
-  int32_t* cuts;             // balanced split: per (sequence, KV head) {first worker, 2*pieces+slot}
   int32_t engine;            // balanced split: kEngineValu or kEngineMfma (where compiled)
   hipStream_t stream;
 };

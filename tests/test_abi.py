@@ -45,6 +45,7 @@ def test_pool_bytes_and_workspace_sizes():
     assert pa.pa_decode_workspace_size(8, 32, 8, 128, 32768, 512) == want
     nb = 4096 * 2 * 4  # two partial states of 4 heads per wavefront of the largest grid
     want_b = (((nb * 128 * 4 + 255) // 256) * 256 + ((nb * 2 * 4 + 255) // 256) * 256
+              + 4096 * 2 * 4    # + a two-word merge task per wavefront
               + ((64 * 8 * 8 + 255) // 256) * 256)   # + a two-word cut record per (seq, KV head)
     assert pa.pa_decode_workspace_size(64, 32, 8, 128, 4096, pa.PA_PARTITION_BALANCED) == want_b
     assert pa.pa_decode_workspace_size(64, 30, 8, 128, 4096, 0) == 0

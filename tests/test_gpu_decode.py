@@ -230,3 +230,26 @@ def test_decode_balanced_engines(engine, Hq, Hkv, bs, kv, monkeypatch):
     ref = G.oracle_decode(b, okp, ovp, G.query_f64(qt))
     got = G.run_decode(b, kp, vp, qt, partition_size=BAL)
     G.assert_close(got, ref, kv, f"{engine} engine {Hq}/{Hkv} bs{bs} {kv}")
+
+
+@pytest.mark.parametrize("engine", ["valu", "mfma"])
+@pytest.mark.parametrize("Hq,Hkv,bs,kv", [(32, 8, 16, "bf16"), (64, 8, 32, "fp8"), (16, 2, 64, "bf16")])
+def test_decode_balanced_many_sequences(engine, Hq, Hkv, bs, kv, monkeypatch):
+    """More sequences than workers per KV head (the reduce then works from
+    per-worker merge tasks): 600 sequences, mostly short, some empty, some
+    long enough to span several workers."""
+    monkeypatch.setenv("PA_DECODE_ENGINE", engine)
+    rng = np.random.default_rng(Hq + bs)
+    lens = rng.integers(1, 200, 600)
+    lens[rng.choice(600, 40, replace=False)] = 0
+    lens[rng.choice(600, 6, replace=False)] = rng.integers(3000, 9000, 6)
+    b = _shape_batch(Hq, Hkv, 128, bs, kv, lens, seed=Hq * 3 + bs)
+    G.say(f"[many {engine} {Hq}/{Hkv} bs{bs} {kv}] {len(lens)} seqs, {int(lens.sum())} tokens")
+    kp, vp = G.gpu_pool(b)
+    G.gpu_fill(b, kp, vp)
+    okp, ovp = G.oracle_pool(b)
+    qt = G.query_tensor(b)
+    got = G.run_decode(b, kp, vp, qt, partition_size=BAL)
+    ref = G.oracle_decode(b, okp, ovp, G.query_f64(qt))
+    assert np.all(got[lens == 0] == 0)
+    G.assert_close(got, ref, kv, f"balanced, {len(lens)} sequences, {engine}")
