@@ -605,15 +605,50 @@ constexpr int kBalancedMinTokens = 256;  // fewest tokens a worker is given
 
 __device__ __forceinline__ int nblocks_of(int L, int bs) { return (L + bs - 1) / bs; }
 
+// Sequence lengths are read kScanChunks chunks of 64 (one per lane) at a
+// time, all loads of a batch issued before any is used: a worker's start
+// then costs one memory round trip per 1024 sequences, not one per 64.
+constexpr int kScanChunks = 16;
+
+__device__ __forceinline__ void load_len_batch(const int32_t* seq_lens, int num_seqs, int c0,
+                                               int lane, int bs, int (&nb)[kScanChunks]) {
+#pragma unroll
+  for (int b = 0; b < kScanChunks; ++b) {
+    const int s = c0 + b * kWave + lane;
+    nb[b] = s < num_seqs ? seq_lens[s] : 0;
+  }
+#pragma unroll
+  for (int b = 0; b < kScanChunks; ++b) nb[b] = nblocks_of(nb[b], bs);
+}
+
+// Inclusive prefix sum over the wavefront's 64 lanes on DPP (row shifts
+// within each 16-lane row, then the rows' last lanes broadcast forward):
+// a few VALU cycles per step, where a lane shuffle is an LDS round trip.
+__device__ __forceinline__ int wave_scan_incl(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15 -> rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31 -> rows 2, 3
+  return v;
+}
+
+__device__ __forceinline__ int wave_sum(int v) {
+  return __builtin_amdgcn_readlane(wave_scan_incl(v), kWave - 1);
+}
+
 // Total blocks of all sequences (wavefront-uniform result).
 __device__ __forceinline__ int64_t total_blocks(const int32_t* seq_lens, int num_seqs, int bs,
                                                 int lane) {
-  int64_t t = 0;
-  for (int s = lane; s < num_seqs; s += kWave) t += nblocks_of(seq_lens[s], bs);
-  int32_t lo = (int32_t)t;  // per-lane partial sums stay far below 2^31
+  int t = 0;  // per-lane partial sums stay far below 2^31
+  for (int c0 = 0; c0 < num_seqs; c0 += kScanChunks * kWave) {
+    int nb[kScanChunks];
+    load_len_batch(seq_lens, num_seqs, c0, lane, bs, nb);
 #pragma unroll
-  for (int m = 1; m < kWave; m <<= 1) lo += __shfl_xor(lo, m, kWave);
-  return lo;
+    for (int b = 0; b < kScanChunks; ++b) t += nb[b];
+  }
+  return wave_sum(t);
 }
 
 // The sequence whose blocks hold flattened position x, and the flattened
@@ -621,24 +656,23 @@ __device__ __forceinline__ int64_t total_blocks(const int32_t* seq_lens, int num
 __device__ __forceinline__ void locate_block(const int32_t* seq_lens, int num_seqs, int bs,
                                              int64_t x, int lane, int& s_out, int64_t& base_out) {
   int64_t base = 0;
-  for (int c = 0; c < num_seqs; c += kWave) {
-    const int s = c + lane;
-    const int nb = s < num_seqs ? nblocks_of(seq_lens[s], bs) : 0;
-    int incl = nb;
+  for (int c0 = 0; c0 < num_seqs; c0 += kScanChunks * kWave) {
+    int nb[kScanChunks];
+    load_len_batch(seq_lens, num_seqs, c0, lane, bs, nb);
 #pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-      const int t = __shfl_up(incl, d, kWave);
-      if (lane >= d) incl += t;
+    for (int b = 0; b < kScanChunks; ++b) {
+      if (c0 + b * kWave >= num_seqs) break;
+      const int incl = wave_scan_incl(nb[b]);
+      const int chunk = __builtin_amdgcn_readlane(incl, kWave - 1);
+      if (base + chunk > x) {
+        const uint64_t found = __builtin_amdgcn_ballot_w64(base + incl > x);
+        const int k = __builtin_ctzll(found);
+        s_out = c0 + b * kWave + k;
+        base_out = base + __builtin_amdgcn_readlane(incl - nb[b], k);
+        return;
+      }
+      base += chunk;
     }
-    const int chunk = __shfl(incl, kWave - 1, kWave);
-    if (base + chunk > x) {
-      const uint64_t hit = __builtin_amdgcn_ballot_w64(base + incl > x);
-      const int k = __builtin_ctzll(hit);
-      s_out = c + k;
-      base_out = base + __shfl(incl - nb, k, kWave);
-      return;
-    }
-    base += chunk;
   }
   s_out = num_seqs;
   base_out = base;

@@ -233,16 +233,18 @@ def test_decode_balanced_engines(engine, Hq, Hkv, bs, kv, monkeypatch):
 
 
 @pytest.mark.parametrize("engine", ["valu", "mfma"])
-@pytest.mark.parametrize("Hq,Hkv,bs,kv", [(32, 8, 16, "bf16"), (64, 8, 32, "fp8"), (16, 2, 64, "bf16")])
-def test_decode_balanced_many_sequences(engine, Hq, Hkv, bs, kv, monkeypatch):
+@pytest.mark.parametrize("Hq,Hkv,bs,kv,S", [(32, 8, 16, "bf16", 600), (64, 8, 32, "fp8", 600),
+                                            (16, 2, 64, "bf16", 600), (32, 8, 16, "bf16", 1500)])
+def test_decode_balanced_many_sequences(engine, Hq, Hkv, bs, kv, S, monkeypatch):
     """More sequences than workers per KV head (the reduce then works from
-    per-worker merge tasks): 600 sequences, mostly short, some empty, some
-    long enough to span several workers."""
+    per-worker merge tasks), and more than one batch of the workers' length
+    scans (1024): mostly short sequences, some empty, some long enough to
+    span several workers."""
     monkeypatch.setenv("PA_DECODE_ENGINE", engine)
-    rng = np.random.default_rng(Hq + bs)
-    lens = rng.integers(1, 200, 600)
-    lens[rng.choice(600, 40, replace=False)] = 0
-    lens[rng.choice(600, 6, replace=False)] = rng.integers(3000, 9000, 6)
+    rng = np.random.default_rng(Hq + bs + S)
+    lens = rng.integers(1, 200, S)
+    lens[rng.choice(S, S // 15, replace=False)] = 0
+    lens[rng.choice(S, 6, replace=False)] = rng.integers(3000, 9000, 6)
     b = _shape_batch(Hq, Hkv, 128, bs, kv, lens, seed=Hq * 3 + bs)
     G.say(f"[many {engine} {Hq}/{Hkv} bs{bs} {kv}] {len(lens)} seqs, {int(lens.sum())} tokens")
     kp, vp = G.gpu_pool(b)
