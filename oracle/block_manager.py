@@ -22,7 +22,7 @@ What the pages describe and this models, step by step:
   one reference from each block and returns blocks that reach zero to the
   free list.
 
-Readings where the pages are silent or disagree (listed in the design doc):
+Readings where the pages are silent or disagree:
 
 * free-list order: blocks are taken from the front and returned to the back
   (first in, first out).  One page's code pops from the back, the other's
