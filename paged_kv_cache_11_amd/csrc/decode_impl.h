@@ -418,6 +418,8 @@ struct WaveAttn {
       return __builtin_amdgcn_readlane(bid_v, j & (kWave - 1));
     };
     auto blk_of = [&](int j) { return first + stride * j; };
+    // K/V lines are read once: non-temporal loads (evict first) keep the
+    // stream from churning the caches and lower its latency under load.
     auto load_tile = [&](int bid, int j, uint32_t (&kt)[NLOAD][LW], uint32_t (&vt)[NLOAD][LW]) {
       const int64_t off = (int64_t)bid * block_bytes + (int64_t)(blk_of(j) & sub_mask) * GM::TILE_BYTES;
       const uint8_t* kp = kbase + off;
@@ -425,20 +427,20 @@ struct WaveAttn {
 #pragma unroll
       for (int i = 0; i < NLOAD; ++i) {
         if constexpr (LW == 4) {
-          const u32x4 x = *(const u32x4*)(kp + i * kWave * GM::LB);
+          const u32x4 x = __builtin_nontemporal_load((const u32x4*)(kp + i * kWave * GM::LB));
           kt[i][0] = x.x; kt[i][1] = x.y; kt[i][2] = x.z; kt[i][3] = x.w;
         } else {
-          const u32x2 x = *(const u32x2*)(kp + i * kWave * GM::LB);
+          const u32x2 x = __builtin_nontemporal_load((const u32x2*)(kp + i * kWave * GM::LB));
           kt[i][0] = x.x; kt[i][1] = x.y;
         }
       }
 #pragma unroll
       for (int i = 0; i < NLOAD; ++i) {
         if constexpr (LW == 4) {
-          const u32x4 x = *(const u32x4*)(vp + i * kWave * GM::LB);
+          const u32x4 x = __builtin_nontemporal_load((const u32x4*)(vp + i * kWave * GM::LB));
           vt[i][0] = x.x; vt[i][1] = x.y; vt[i][2] = x.z; vt[i][3] = x.w;
         } else {
-          const u32x2 x = *(const u32x2*)(vp + i * kWave * GM::LB);
+          const u32x2 x = __builtin_nontemporal_load((const u32x2*)(vp + i * kWave * GM::LB));
           vt[i][0] = x.x; vt[i][1] = x.y;
         }
       }
