@@ -396,6 +396,8 @@ struct WaveAttn {
   // Blocks here are BS-token tiles: a pool block of 2^sub_shift x BS tokens
   // (64 or 128) holds 2^sub_shift consecutive ones (the (block, head) tile
   // of the pool is contiguous), found through table entry index >> sub_shift.
+  // NT: K/V lines are read once in this call (see kv_load).
+  template <bool NT>
   __device__ __forceinline__ void stream(const void* k_cache, const void* v_cache,
                                          const int32_t* tbl, int g, int num_kv_heads, int first,
                                          int count, int stride, int L, int sub_shift) {
@@ -418,8 +420,6 @@ struct WaveAttn {
       return __builtin_amdgcn_readlane(bid_v, j & (kWave - 1));
     };
     auto blk_of = [&](int j) { return first + stride * j; };
-    // K/V lines are read once: non-temporal loads (evict first) keep the
-    // stream from churning the caches and lower its latency under load.
     auto load_tile = [&](int bid, int j, uint32_t (&kt)[NLOAD][LW], uint32_t (&vt)[NLOAD][LW]) {
       const int64_t off = (int64_t)bid * block_bytes + (int64_t)(blk_of(j) & sub_mask) * GM::TILE_BYTES;
       const uint8_t* kp = kbase + off;
@@ -427,20 +427,20 @@ struct WaveAttn {
 #pragma unroll
       for (int i = 0; i < NLOAD; ++i) {
         if constexpr (LW == 4) {
-          const u32x4 x = __builtin_nontemporal_load((const u32x4*)(kp + i * kWave * GM::LB));
+          const u32x4 x = kv_load<NT>((const u32x4*)(kp + i * kWave * GM::LB));
           kt[i][0] = x.x; kt[i][1] = x.y; kt[i][2] = x.z; kt[i][3] = x.w;
         } else {
-          const u32x2 x = __builtin_nontemporal_load((const u32x2*)(kp + i * kWave * GM::LB));
+          const u32x2 x = kv_load<NT>((const u32x2*)(kp + i * kWave * GM::LB));
           kt[i][0] = x.x; kt[i][1] = x.y;
         }
       }
 #pragma unroll
       for (int i = 0; i < NLOAD; ++i) {
         if constexpr (LW == 4) {
-          const u32x4 x = __builtin_nontemporal_load((const u32x4*)(vp + i * kWave * GM::LB));
+          const u32x4 x = kv_load<NT>((const u32x4*)(vp + i * kWave * GM::LB));
           vt[i][0] = x.x; vt[i][1] = x.y; vt[i][2] = x.z; vt[i][3] = x.w;
         } else {
-          const u32x2 x = __builtin_nontemporal_load((const u32x2*)(vp + i * kWave * GM::LB));
+          const u32x2 x = kv_load<NT>((const u32x2*)(vp + i * kWave * GM::LB));
           vt[i][0] = x.x; vt[i][1] = x.y;
         }
       }
@@ -507,7 +507,8 @@ __global__ __launch_bounds__(kMaxDecodeWaves * kWave) void decode_kernel(
     const void* __restrict__ query, const void* __restrict__ k_cache,
     const void* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
     const int32_t* __restrict__ seq_lens, int max_blocks_per_seq, int num_kv_heads,
-    int partition_blocks, int max_parts, float qk_scale_log2, float v_scale, int sub_shift) {
+    int partition_blocks, int max_parts, float qk_scale_log2, float v_scale, int sub_shift,
+    int read_once) {
   using WA = WaveAttn<KV, QT, D, BS, G>;
   constexpr int EPL = WA::EPL, RPL = WA::RPL;
   using OT = QT;
@@ -531,8 +532,12 @@ __global__ __launch_bounds__(kMaxDecodeWaves * kWave) void decode_kernel(
   A.q.load(query, (int64_t)s * num_heads + (int64_t)g * G, D, A.col);
   const int span = b1 - b0;
   const int nmine = span > w ? (span - w + NW - 1) / NW : 0;
-  A.stream(k_cache, v_cache, block_tables + (int64_t)s * max_blocks_per_seq, g, num_kv_heads,
-           b0 + w, nmine, NW, L, sub_shift);
+  if (read_once)
+    A.template stream<true>(k_cache, v_cache, block_tables + (int64_t)s * max_blocks_per_seq, g,
+                            num_kv_heads, b0 + w, nmine, NW, L, sub_shift);
+  else
+    A.template stream<false>(k_cache, v_cache, block_tables + (int64_t)s * max_blocks_per_seq, g,
+                             num_kv_heads, b0 + w, nmine, NW, L, sub_shift);
   float l_h[G];
   A.merge_rows(l_h);
 
@@ -742,7 +747,7 @@ __global__ __launch_bounds__(kMaxDecodeWaves * kWave) void decode_balanced_kerne
     const void* __restrict__ k_cache, const void* __restrict__ v_cache,
     const int32_t* __restrict__ block_tables, const int32_t* __restrict__ seq_lens, int num_seqs,
     int max_blocks_per_seq, int num_kv_heads, int workers_per_head, float qk_scale_log2,
-    float v_scale, int sub_shift) {
+    float v_scale, int sub_shift, int64_t pool_tokens) {
   using WA = WaveAttn<KV, QT, D, BS, G>;
   constexpr int EPL = WA::EPL, RPL = WA::RPL;
   using OT = QT;
@@ -754,6 +759,9 @@ __global__ __launch_bounds__(kMaxDecodeWaves * kWave) void decode_balanced_kerne
 
   const int64_t T = total_blocks(seq_lens, num_seqs, BS, lane);
   const int W = effective_workers(T, workers_per_head, BS);
+  // More tokens referenced than the pool holds: blocks are shared, so
+  // their lines may be read again (ordinary loads); else non-temporal.
+  const bool read_once = T * BS <= pool_tokens;
   int32_t* merge = merges + 2 * (int64_t)worker;
   if (lane == 0) merge[0] = -1;  // no merge task unless the last run sets one
   if (vw >= W) return;
@@ -775,8 +783,12 @@ __global__ __launch_bounds__(kMaxDecodeWaves * kWave) void decode_balanced_kerne
       const int b_hi = (int)((end < seg_end ? end : seg_end) - base);
       A.reset();
       A.q.load(query, (int64_t)s * num_heads + (int64_t)g * G, D, A.col);
-      A.stream(k_cache, v_cache, block_tables + (int64_t)s * max_blocks_per_seq, g, num_kv_heads,
-               b_lo, b_hi - b_lo, 1, L, sub_shift);
+      if (read_once)
+        A.template stream<true>(k_cache, v_cache, block_tables + (int64_t)s * max_blocks_per_seq,
+                                g, num_kv_heads, b_lo, b_hi - b_lo, 1, L, sub_shift);
+      else
+        A.template stream<false>(k_cache, v_cache, block_tables + (int64_t)s * max_blocks_per_seq,
+                                 g, num_kv_heads, b_lo, b_hi - b_lo, 1, L, sub_shift);
       float l_h[G];
       A.merge_rows(l_h);
       const bool whole = b_lo == 0 && b_hi == nblk;
@@ -937,6 +949,7 @@ hipError_t launch_decode(const DecodeArgs& a) {
   const float k_scale = std::is_same<KV, FP8>::value ? a.k_scale : 1.0f;
   const float v_scale = std::is_same<KV, FP8>::value ? a.v_scale : 1.0f;
   const float qk = a.scale * k_scale * kLog2e;
+  const int64_t pool_tokens = (int64_t)a.num_blocks * PBS;
   if (a.balanced_workers > 0) {
     const int per_head = a.balanced_workers / a.num_kv_heads;
     const int workers = per_head * a.num_kv_heads;
@@ -949,7 +962,8 @@ hipError_t launch_decode(const DecodeArgs& a) {
                            dim3(kMaxDecodeWaves * kWave), 0, a.stream, a.out, a.part_o, a.part_ml,
                            a.merges, a.cuts, a.query, a.k_cache, a.v_cache, a.block_tables,
                            a.seq_lens,
-                           a.num_seqs, a.max_blocks_per_seq, a.num_kv_heads, per_head, qk, v_scale);
+                           a.num_seqs, a.max_blocks_per_seq, a.num_kv_heads, per_head, qk, v_scale,
+                           pool_tokens);
     }
     if (!mfma)
       hipLaunchKernelGGL((decode_balanced_kernel<KV, QT, D, BS, G>), dim3((unsigned)wg),
@@ -957,7 +971,7 @@ hipError_t launch_decode(const DecodeArgs& a) {
                          a.merges, a.cuts, a.query, a.k_cache, a.v_cache, a.block_tables,
                          a.seq_lens,
                          a.num_seqs, a.max_blocks_per_seq, a.num_kv_heads, per_head, qk, v_scale,
-                         kSubShift);
+                         kSubShift, pool_tokens);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.num_seqs <= per_head)
@@ -978,7 +992,10 @@ hipError_t launch_decode(const DecodeArgs& a) {
                      dim3((unsigned)a.max_parts, (unsigned)a.num_kv_heads, (unsigned)a.num_seqs),
                      dim3(nw * kWave), 0, a.stream, a.out, a.part_o, a.part_ml, a.query,
                      a.k_cache, a.v_cache, a.block_tables, a.seq_lens, a.max_blocks_per_seq,
-                     a.num_kv_heads, tiles_per_part, a.max_parts, qk, v_scale, kSubShift);
+                     a.num_kv_heads, tiles_per_part, a.max_parts, qk, v_scale, kSubShift,
+                     // every sequence at its longest still fits the pool: no
+                     // block can be shared, lines are read once
+                     (int64_t)a.num_seqs * a.max_seq_len <= pool_tokens ? 1 : 0);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.max_parts <= 1) return e;
   hipLaunchKernelGGL((lse_reduce_kernel<QT, D, G>),

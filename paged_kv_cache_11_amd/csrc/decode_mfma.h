@@ -141,11 +141,11 @@ struct MfmaAttn {
 
   // Loads the tile whose first key is k0 (a sequence position; a multiple
   // of 16, and of KEYS when blocks hold at least 32 tokens); bid(j) gives
-  // the physical id of the sequence's block j.  K/V lines are read once:
-  // non-temporal loads (evict first) keep the stream from churning the
-  // caches and lower its latency under load (about 10% on the bf16 and fp8
-  // decode workloads).
-  template <typename BidFn>
+  // the physical id of the sequence's block j.  NT: the lines are read once
+  // in this call, so they are loaded non-temporally (evict first), which
+  // keeps the stream from churning the caches and lowers its latency under
+  // load (about 10% on the bf16 and fp8 decode workloads).
+  template <bool NT, typename BidFn>
   __device__ __forceinline__ void load_tile(const uint8_t* kh, const uint8_t* vh, int64_t block_bytes,
                                             int k0, BidFn bid, Tile& T) const {
     int b[NBT];
@@ -157,7 +157,7 @@ struct MfmaAttn {
       const uint8_t* kb = kh + (int64_t)b[key / BS - k0 / BS] * block_bytes +
                           ((key % BS) + n) * kMD * EB + 16 * g4;
 #pragma unroll
-      for (int i = 0; i < KL; ++i) T.k[kg][i] = __builtin_nontemporal_load((const u32x4*)(kb + 64 * i));
+      for (int i = 0; i < KL; ++i) T.k[kg][i] = kv_load<NT>((const u32x4*)(kb + 64 * i));
     }
     // V: wavefront load i reads rows VRL*i .. +VRL of the tile, whole rows.
 #pragma unroll
@@ -165,7 +165,7 @@ struct MfmaAttn {
       const int key = k0 + vr + VRL * i;  // tile row vr + VRL*i
       const int u = key / BS - k0 / BS;
       const int bb = NBT == 1 ? b[0] : b[u < NBT ? u : NBT - 1];
-      T.v[i] = __builtin_nontemporal_load(
+      T.v[i] = kv_load<NT>(
           (const u32x4*)(vh + (int64_t)bb * block_bytes + (key % BS) * kMD * EB + 16 * vc));
     }
   }
@@ -297,6 +297,7 @@ struct MfmaAttn {
 
   // Units first .. first+count-1 (UBS tokens each) of a sequence of L
   // tokens, KV head g.
+  template <bool NT>
   __device__ __forceinline__ void stream(const void* k_cache, const void* v_cache, const int32_t* tbl,
                                          int g, int num_kv_heads, int first, int count, int L) {
     if (count <= 0) return;
@@ -330,12 +331,12 @@ struct MfmaAttn {
     };
     auto k0_of = [&](int t) { return key0 + t * KEYS; };
     Tile ta, tb;
-    load_tile(kh, vh, block_bytes, k0_of(0), bid, ta);
+    load_tile<NT>(kh, vh, block_bytes, k0_of(0), bid, ta);
     int t = 0;
     for (; t + 2 <= ntiles; t += 2) {
-      load_tile(kh, vh, block_bytes, k0_of(t + 1), bid, tb);
+      load_tile<NT>(kh, vh, block_bytes, k0_of(t + 1), bid, tb);
       tile(ta, limit(t));
-      load_tile(kh, vh, block_bytes, k0_of(t + 2 < ntiles ? t + 2 : t + 1), bid, ta);
+      load_tile<NT>(kh, vh, block_bytes, k0_of(t + 2 < ntiles ? t + 2 : t + 1), bid, ta);
       tile(tb, limit(t + 1));
     }
     if (t < ntiles) tile(ta, limit(t));
@@ -356,7 +357,7 @@ __global__ __launch_bounds__(kMaxDecodeWaves * kWave, 2) void decode_balanced_mf
     const void* __restrict__ k_cache, const void* __restrict__ v_cache,
     const int32_t* __restrict__ block_tables, const int32_t* __restrict__ seq_lens, int num_seqs,
     int max_blocks_per_seq, int num_kv_heads, int workers_per_head, float qk_scale_log2,
-    float v_scale) {
+    float v_scale, int64_t pool_tokens) {
   static_assert(std::is_same<QT, BF16>::value, "bf16 queries");
   using MA = MfmaAttn<KV, BS, G>;
   constexpr int D = kMD;
@@ -370,6 +371,9 @@ __global__ __launch_bounds__(kMaxDecodeWaves * kWave, 2) void decode_balanced_mf
 
   const int64_t T = total_blocks(seq_lens, num_seqs, MA::UBS, lane);
   const int W = effective_workers(T, workers_per_head, MA::UBS);
+  // More tokens referenced than the pool holds: blocks are shared, so
+  // their lines may be read again (ordinary loads); else non-temporal.
+  const bool read_once = T * MA::UBS <= pool_tokens;
   int32_t* merge = merges + 2 * (int64_t)worker;
   if (lane == 0) merge[0] = -1;  // no merge task unless the last run sets one
   if (vw >= W) return;
@@ -392,8 +396,12 @@ __global__ __launch_bounds__(kMaxDecodeWaves * kWave, 2) void decode_balanced_mf
       const int64_t hq0 = (int64_t)s * num_heads + (int64_t)g * G;
       A.reset();
       A.load_q(query, hq0);
-      A.stream(k_cache, v_cache, block_tables + (int64_t)s * max_blocks_per_seq, g, num_kv_heads,
-               b_lo, b_hi - b_lo, L);
+      if (read_once)
+        A.template stream<true>(k_cache, v_cache, block_tables + (int64_t)s * max_blocks_per_seq,
+                                g, num_kv_heads, b_lo, b_hi - b_lo, L);
+      else
+        A.template stream<false>(k_cache, v_cache, block_tables + (int64_t)s * max_blocks_per_seq,
+                                 g, num_kv_heads, b_lo, b_hi - b_lo, L);
       const float l_tot = A.l_total();
       const bool whole = b_lo == 0 && b_hi == nblk;
       const int slot = pos == start ? 0 : 1;

@@ -125,4 +125,13 @@ __device__ __forceinline__ float shfl_xor(float x, int m) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// A load of K/V words: non-temporal (evict first) when NT, for a stream that
+// reads every line once; an ordinary load when lines may be read again (a
+// block shared by several sequences).
+template <bool NT, typename V>
+__device__ __forceinline__ V kv_load(const V* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+
 }  // namespace pa
