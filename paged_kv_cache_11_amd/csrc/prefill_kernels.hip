@@ -37,6 +37,7 @@ namespace pa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kPD = 128;             // head size
 constexpr int kKB = 32;              // keys per wavefront tile
@@ -46,16 +47,18 @@ constexpr int kRowGroups = kRows / 32;
 constexpr int kPWaves = 2 * kRowGroups;
 constexpr int kPThreads = kPWaves * kWave;
 constexpr int kKStride = kPD + 8;    // LDS row stride of K (bf16 elements)
-constexpr int kVStride = kStep + 4;  // LDS row stride of V^T (bf16 elements)
+constexpr int kVStride = kPD + 32;   // LDS row stride of V (bf16 elements)
+constexpr int kBufs = 4;             // LDS step buffers in rotation
 constexpr float kPLog2e = 1.4426950408889634f;
 constexpr float kPSlack = 8.0f;
-static_assert(kPThreads / 8 == kStep && kPThreads / 16 * 2 == kStep,
-              "the staging maps cover one step exactly");
+static_assert(kPThreads / 8 == kStep, "the staging map covers one step exactly");
 constexpr int kKBytes = kStep * kKStride * 2;
-constexpr int kVBytes = kPD * kVStride * 2;
+constexpr int kVBytes = kStep * kVStride * 2;
 constexpr int kBufBytes = kKBytes + kVBytes;
 constexpr int kMergeFloats = kRowGroups * (kPD / 2) * kWave + 2 * kRowGroups * kWave;
-constexpr int kLdsBytes = 3 * kBufBytes > kMergeFloats * 4 ? 3 * kBufBytes : kMergeFloats * 4;
+constexpr int kLdsBytes =
+    kBufs * kBufBytes > kMergeFloats * 4 ? kBufs * kBufBytes : kMergeFloats * 4;
+static_assert(kLdsBytes <= 160 * 1024, "one workgroup's LDS fits a CU");
 
 // How the query enters: the kernel's score scale is always positive, so a
 // negative scale moves onto the query's sign and a zero scale zeroes the
@@ -79,6 +82,16 @@ __device__ __forceinline__ float xor32_max(float x) {
   return fmaxf(u2f(r[0]), u2f(r[1]));
 }
 
+// ds_read_b64_tr_b16 (gfx950): in each 16-lane group, lane t gives the
+// address of 4 consecutive bf16 F[t][0..3], and lane j receives
+// F[4k + j/4][j%4] for k = 0..3.
+__device__ __forceinline__ u32x2 lds_tr16(const __bf16* p) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+template <int N> struct Buf { static constexpr int value = N; };
+
 template <typename KV, int BS, int G>
 __global__ __launch_bounds__(kPThreads) void prefill_kernel(
     void* __restrict__ out, const void* __restrict__ query,
@@ -88,11 +101,11 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(
     float qk_scale_log2, int q_mode, float v_scale) {
   constexpr int EB = Elem<KV>::bytes;
   static_assert(kRows % G == 0, "rows hold whole queries");
-  // Three LDS buffers, each one step's K tile and V^T tile; after the key
-  // walk the same bytes hold the merge of the two key halves.
+  // Four LDS buffers, each one step's K tile and V tile (both key rows);
+  // after the key walk the same bytes hold the merge of the two key halves.
   __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
   auto k_lds = [&](int b) { return (__bf16*)(lds + b * kBufBytes); };
-  auto vt_lds = [&](int b) { return (__bf16*)(lds + b * kBufBytes + kKBytes); };
+  auto v_lds = [&](int b) { return (__bf16*)(lds + b * kBufBytes + kKBytes); };
 
   const int tile = blockIdx.x, g = blockIdx.y, c = blockIdx.z;
   const int t = threadIdx.x, lane = t & (kWave - 1), w = t / kWave;
@@ -139,31 +152,27 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(
     for (int i = 0; i < 16; ++i) oacc[mt][i] = 0.f;
   float m_ref = -INFINITY, l_part = 0.f;
 
-  // Staging: K — thread t covers key t/8, dims 16 (t%8) .. +16;
-  //          V — thread t covers keys 2 (t/16) and +1, dims 8 (t%16) .. +8.
+  // Staging: thread t covers key t/8, dims 16 (t%8) .. +16, of K and of V.
   // Each step's loads are issued two steps ahead (two register stages), and
   // the block-table entries they need one step before that.
   const int kk = t / 8, kd = (t % 8) * 16;
-  const int vk = 2 * (t / 16), vd = (t % 16) * 8;
-  constexpr int KVEC = 16 * EB / 16;  // 16-byte vectors per 16 K elements
-  constexpr int VW = 8 * EB / 4;      // dwords per 8 V elements
+  constexpr int KVEC = 16 * EB / 16;  // 16-byte vectors per 16 elements
   struct Stage {
     u32x4 k[KVEC];
-    uint32_t v[2][VW];
+    u32x4 v[KVEC];
   };
   const int64_t head_off = (int64_t)g * BS * kPD;  // element offset of head g in a block
   const int64_t block_elems = (int64_t)num_kv_heads * BS * kPD;
 
-  // A wavefront stages keys 8w .. 8w+7 of a step for K and for V, which lie
-  // in one block (blocks hold a multiple of 8 keys, and a step is whole
-  // blocks or a whole half or quarter of one): its physical block is one
-  // wave-uniform table entry, read with a scalar load so that waiting for
-  // it never waits for the vector loads in flight, and a thread's offset
-  // inside the block depends on the step only through the step's offset
-  // in a block larger than a step.  Past the last block the last one is
-  // re-read; keys at or past L are zeroed when stored, so every step
-  // issues the same loads unconditionally and the wait for a stage counts
-  // only later loads.
+  // A wavefront stages keys 8w .. 8w+7 of a step, which lie in one block
+  // (blocks hold a multiple of 8 keys, and a step is whole blocks or a
+  // whole half or quarter of one): its physical block is one wave-uniform
+  // table entry, read with a scalar load so that waiting for it never waits
+  // for the vector loads in flight, and a thread's offset inside the block
+  // depends on the step only through the step's offset in a block larger
+  // than a step.  Past the last block the last one is re-read; keys at or
+  // past L are zeroed when stored, so every step issues the same loads
+  // unconditionally and the wait for a stage counts only later loads.
   static_assert((kStep % BS == 0 || BS % kStep == 0) && BS % 8 == 0,
                 "steps and blocks nest, blocks are whole 8-key groups");
   const int wkey = __builtin_amdgcn_readfirstlane(8 * w);
@@ -171,90 +180,59 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(
   auto block_id = [&](int step) -> int { return tbl[min((step * kStep + wkey) / BS, last_blk)]; };
   const uint8_t* k_head = (const uint8_t*)k_cache + head_off * EB;
   const uint8_t* v_head = (const uint8_t*)v_cache + head_off * EB;
-  const int k_off = ((kk % BS) * kPD + kd) * EB;
-  const int v_off0 = ((vk % BS) * kPD + vd) * EB, v_off1 = v_off0 + kPD * EB;
+  const int kv_off = ((kk % BS) * kPD + kd) * EB;
   auto load_stage = [&](int bid, int step, Stage& S) {
     const int64_t base = (int64_t)bid * block_elems * EB +
                          (BS > kStep ? (int64_t)((step * kStep) % BS) * kPD * EB : 0);
-    const u32x4* kp = (const u32x4*)(k_head + base + k_off);
+    const u32x4* kp = (const u32x4*)(k_head + base + kv_off);
+    const u32x4* vp = (const u32x4*)(v_head + base + kv_off);
 #pragma unroll
     for (int v = 0; v < KVEC; ++v) S.k[v] = kp[v];
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const uint32_t* vp = (const uint32_t*)(v_head + base + (r ? v_off1 : v_off0));
-      if constexpr (VW == 4) {
-        const u32x4 x4 = *(const u32x4*)vp;
-        S.v[r][0] = x4.x; S.v[r][1] = x4.y; S.v[r][2] = x4.z; S.v[r][3] = x4.w;
-      } else {
-        const u32x2 x2 = *(const u32x2*)vp;
-        S.v[r][0] = x2.x; S.v[r][1] = x2.y;
-      }
-    }
+    for (int v = 0; v < KVEC; ++v) S.v[v] = vp[v];
   };
-  // LDS layout of a buffer.  K: key rows of kKStride bf16.  V^T: dim rows
-  // of kVStride bf16, keys in pairs (one dword per key pair); the key-pair
-  // column is XORed with 4 x (dim / 32), which spreads the staging writes
-  // of a wavefront (16 dims 8 apart) over distinct banks, and leaves each
-  // 32-dim MFMA tile reading its columns uniformly shifted.
-  // In chunks 4..7 of a K row (16 dims each) the two 8-dim halves are
-  // stored swapped: the first 16-byte write of the 8 threads of a row then
-  // lands on distinct banks also with 32 banks.  Readers undo the swap.
+  // LDS layout of a buffer: K and V both as key rows of bf16, strides
+  // kKStride and kVStride.  The two 8-dim halves of a 16-dim chunk are
+  // stored swapped in chunks 4..7 of a K row and in every chunk of an odd V
+  // row; either way the first 16-byte writes of a wavefront land on
+  // distinct banks.  The V stride puts the 4 key rows of a transposing read
+  // 16 banks apart.  Readers undo the swaps.
   const int k_wr_lo = kk * kKStride + kd + ((t % 8) >= 4 ? 8 : 0);  // bf16 elements
   const int k_wr_hi = kk * kKStride + kd + ((t % 8) >= 4 ? 0 : 8);
-  const int v_wr = vd * kVStride + 2 * ((vk / 2) ^ (4 * (vd / 32)));
+  const int v_wr_lo = kk * kVStride + kd + ((kk & 1) ? 8 : 0);
+  const int v_wr_hi = kk * kVStride + kd + ((kk & 1) ? 0 : 8);
+  auto widen = [&](const u32x4 (&x)[KVEC], uint32_t (&o)[8]) {
+    if constexpr (std::is_same<KV, BF16>::value) {
+      o[0] = x[0].x; o[1] = x[0].y; o[2] = x[0].z; o[3] = x[0].w;
+      o[4] = x[1].x; o[5] = x[1].y; o[6] = x[1].z; o[7] = x[1].w;
+    } else {
+      fp8x4_to_bf16x2x2(x[0].x, o[0], o[1]);
+      fp8x4_to_bf16x2x2(x[0].y, o[2], o[3]);
+      fp8x4_to_bf16x2x2(x[0].z, o[4], o[5]);
+      fp8x4_to_bf16x2x2(x[0].w, o[6], o[7]);
+    }
+  };
   // Zeroing keys past L happens here, where the stage is consumed, so the
   // wait for its loads stays two steps after their issue.
   auto store_stage = [&](int step, const Stage& S, int b) {
     const bool tail = step * kStep + kStep > L;  // some keys of the step are past L
-    const bool k_ok = step * kStep + kk < L;
-    const bool v_ok[2] = {step * kStep + vk < L, step * kStep + vk + 1 < L};
-    // K row: 16 bf16 at k_lds[kk][kd..].
-    uint32_t kw[8];
-    if constexpr (std::is_same<KV, BF16>::value) {
-      kw[0] = S.k[0].x; kw[1] = S.k[0].y; kw[2] = S.k[0].z; kw[3] = S.k[0].w;
-      kw[4] = S.k[1].x; kw[5] = S.k[1].y; kw[6] = S.k[1].z; kw[7] = S.k[1].w;
-    } else {
-      fp8x4_to_bf16x2x2(S.k[0].x, kw[0], kw[1]);
-      fp8x4_to_bf16x2x2(S.k[0].y, kw[2], kw[3]);
-      fp8x4_to_bf16x2x2(S.k[0].z, kw[4], kw[5]);
-      fp8x4_to_bf16x2x2(S.k[0].w, kw[6], kw[7]);
-    }
+    const bool ok = step * kStep + kk < L;
+    uint32_t kw[8], vw[8];
+    widen(S.k, kw);
+    widen(S.v, vw);
     if (tail) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) kw[i] = k_ok ? kw[i] : 0u;
+      for (int i = 0; i < 8; ++i) {
+        kw[i] = ok ? kw[i] : 0u;
+        vw[i] = ok ? vw[i] : 0u;
+      }
     }
     *(u32x4*)(k_lds(b) + k_wr_lo) = u32x4{kw[0], kw[1], kw[2], kw[3]};
     *(u32x4*)(k_lds(b) + k_wr_hi) = u32x4{kw[4], kw[5], kw[6], kw[7]};
-    // V^T: dims vd..vd+7, keys vk and vk+1 packed as one dword per dim.
-    uint32_t va[4], vb[4];  // bf16 pairs (dims 2x, 2x+1) of keys vk and vk+1
-    if constexpr (std::is_same<KV, BF16>::value) {
-#pragma unroll
-      for (int x = 0; x < 4; ++x) { va[x] = S.v[0][x]; vb[x] = S.v[1][x]; }
-    } else {
-#pragma unroll
-      for (int x = 0; x < 2; ++x) {
-        fp8x4_to_bf16x2x2(S.v[0][x], va[2 * x], va[2 * x + 1]);
-        fp8x4_to_bf16x2x2(S.v[1][x], vb[2 * x], vb[2 * x + 1]);
-      }
-    }
-    if (tail) {
-#pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        va[x] = v_ok[0] ? va[x] : 0u;
-        vb[x] = v_ok[1] ? vb[x] : 0u;
-      }
-    }
-#pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      // dim 2x: low halves of both keys; dim 2x+1: high halves.
-      *(uint32_t*)(vt_lds(b) + v_wr + (2 * x) * kVStride) = __builtin_amdgcn_perm(vb[x], va[x], 0x05040100u);
-      *(uint32_t*)(vt_lds(b) + v_wr + (2 * x + 1) * kVStride) = __builtin_amdgcn_perm(vb[x], va[x], 0x07060302u);
-    }
+    *(u32x4*)(v_lds(b) + v_wr_lo) = u32x4{vw[0], vw[1], vw[2], vw[3]};
+    *(u32x4*)(v_lds(b) + v_wr_hi) = u32x4{vw[4], vw[5], vw[6], vw[7]};
   };
 
-  // The math of a step on its LDS buffer b, for this wavefront's 32 keys,
-  // in two parts so that the next step's score MFMAs can be interleaved
-  // with this step's exponentials.
   auto active = [&](int step) { return step * kStep + kh * kKB <= wave_max_pos; };
 
   // S^T = K Q^T: lane holds keys m(i) = (i/4)*8 + 4 half + i%4 of its row.
@@ -298,32 +276,38 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(
     return fast_exp2(__builtin_fmaf(st[i], qk_scale_log2, neg_m));
   };
 
-  // O^T += V^T P^T over two 16-key steps (keys in the permuted order).
-  auto pv = [&](const uint32_t (&pw)[8], int b) {
+  // O^T += V^T P^T over two 16-key steps.  The A operand V^T (32 dims x 16
+  // keys, keys in the scores' permuted order: k-index 8 half + i is key
+  // 16 ks + 4 half + 8 (i/4) + i%4) comes from the key-row V tile with two
+  // transposing reads: lane t of 16-lane group q addresses key row
+  // 4 half + t/4 (+8 for the second read) and dims 16 (q%2) + 4 (t%4) .. +3.
+  const int q16 = lane / 16, t16 = lane % 16;
+  const int v_rd = (4 * half + t16 / 4) * kVStride +
+                   ((16 * (q16 & 1) + 4 * (t16 % 4)) ^ (((t16 / 4) & 1) ? 8 : 0));
+  auto pv = [&](const uint32_t (&pw)[8], const __bf16* vt) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const bf16x8 pb = __builtin_bit_cast(
           bf16x8, u32x4{pw[4 * ks + 0], pw[4 * ks + 1], pw[4 * ks + 2], pw[4 * ks + 3]});
 #pragma unroll
       for (int mt = 0; mt < kPD / 32; ++mt) {
-        // key pairs kh*16 + 8ks + 2half (+4), column-swizzled by 4 mt
-        const __bf16* vrow = vt_lds(b) + (32 * mt + (lane & 31)) * kVStride + kh * kKB + 4 * half;
-        const u32x2 lo = *(const u32x2*)(vrow + 2 * ((8 * ks) ^ (4 * mt)));
-        const u32x2 hi = *(const u32x2*)(vrow + 2 * ((8 * ks + 4) ^ (4 * mt)));
+        const __bf16* p = vt + (kh * kKB + 16 * ks) * kVStride + 32 * mt + v_rd;
+        const u32x2 lo = lds_tr16(p), hi = lds_tr16(p + 8 * kVStride);
         const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
         oacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, oacc[mt], 0, 0, 0);
       }
     }
   };
 
-  // Pipeline over steps j: buffer j%3 holds step j.  Iteration j: barrier
-  // (every wavefront is past iteration j-1, so buffer (j+2)%3, last read
-  // there, is free and buffer (j+1)%3, written there, is complete); store
-  // step j+2 from its register stage and issue that stage's loads for step
-  // j+4; then step j+1's score MFMAs interleaved with step j's softmax,
-  // then step j's P·V.  Register stages alternate (sa: even steps).
-  // (The scheduling barriers keep the stages' loads in issue order, which
-  // the waits for them count on.)
+  // Pipeline over steps j: buffer j%4 holds step j.  Iteration j: barrier
+  // (every wavefront is past iteration j-1, so buffer (j+2)%4, last read
+  // by step j-2's P·V, is free, and buffer (j+1)%4, written in iteration
+  // j-1, is complete); store step j+2 from its register stage and issue
+  // that stage's loads for step j+4; then step j+1's score MFMAs
+  // interleaved with step j's exponentials, then step j's P·V.  Register
+  // stages alternate (sa: even steps); the loop is unrolled by four so that
+  // every buffer offset is a constant.  (The scheduling barriers keep the
+  // stages' loads in issue order, which the waits for them count on.)
   Stage sa, sb;
   load_stage(block_id(0), 0, sa);
   __builtin_amdgcn_sched_barrier(0);
@@ -345,32 +329,36 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(
 #pragma unroll
   for (int s = 0; s < kPD / 16; ++s) score_mfma(st_a, 0, s);
 
-  int bj = 0;  // buffer of step j
-  auto iteration = [&](int j, Stage& S, f32x16& st_cur, f32x16& st_next) {
-    const int bj1 = bj == 2 ? 0 : bj + 1, bj2 = bj1 == 2 ? 0 : bj1 + 1;
+  auto iteration = [&](auto buf, int j, Stage& S, f32x16& st_cur, f32x16& st_next) {
+    constexpr int B = decltype(buf)::value;  // j % 4
     __syncthreads();
-    store_stage(j + 2, S, bj2);
+    store_stage(j + 2, S, (B + 2) % kBufs);
     load_stage(bid, j + 4, S);  // past the last step: harmless re-reads
     bid = block_id(j + 5);
     if (active(j)) {  // later steps are inactive too: nothing is left to do
       const float neg_m = softmax_head(j, st_cur);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) st_next[i] = 0.f;
       uint32_t pw[8];
 #pragma unroll
+      for (int i = 0; i < 16; ++i) st_next[i] = 0.f;
+#pragma unroll
       for (int s = 0; s < kPD / 16; ++s) {
-        score_mfma(st_next, bj1, s);  // step j+1 (unused if it is inactive)
+        score_mfma(st_next, (B + 1) % kBufs, s);  // step j+1 (unused if it is inactive)
         const float p0 = prob(st_cur, 2 * s, neg_m), p1 = prob(st_cur, 2 * s + 1, neg_m);
         l_part += p0 + p1;
         pw[s] = pk_bf16(p0, p1);
       }
-      pv(pw, bj);
+      pv(pw, v_lds(B));
     }
-    bj = bj1;
   };
-  for (int j = 0; j < nsteps; j += 2) {
-    iteration(j, sa, st_a, st_b);
-    iteration(j + 1, sb, st_b, st_a);
+  for (int j = 0;; j += kBufs) {
+    iteration(Buf<0>{}, j, sa, st_a, st_b);
+    if (j + 1 >= nsteps) break;
+    iteration(Buf<1>{}, j + 1, sb, st_b, st_a);
+    if (j + 2 >= nsteps) break;
+    iteration(Buf<2>{}, j + 2, sa, st_a, st_b);
+    if (j + 3 >= nsteps) break;
+    iteration(Buf<3>{}, j + 3, sb, st_b, st_a);
+    if (j + 4 >= nsteps) break;
   }
   __syncthreads();  // the buffers become the merge area
   float* mo_lds = (float*)lds;                             // [rg][kPD/2][kWave]
