@@ -101,6 +101,20 @@ def test_prefill_varlen_chunks(Hq, Hkv, bs, kv):
     G.assert_close(got, ref, kv, f"prefill {Hq}/{Hkv} bs{bs} {kv}", rows=rows)
 
 
+@pytest.mark.parametrize("Hq,Hkv,bs,kv", [(32, 8, 16, "bf16"), (64, 8, 32, "fp8")])
+def test_prefill_varlen_every_row(Hq, Hkv, bs, kv):
+    """The varlen chunk set with every query row and head compared, so that
+    each lane, row group, key half and staging slot of the kernel is seen."""
+    b, cq, qsl, lens, tables, max_q = _varlen_case(Hq, Hkv, bs, kv, seed=7 * Hq + bs)
+    kp, vp = G.gpu_pool(b)
+    G.gpu_fill(b, kp, vp)
+    okp, ovp = G.oracle_pool(b)
+    got, q64 = run_prefill(b, kp, vp, cq, qsl, lens, tables, max_q)
+    ref = opg.paged_prefill(q64, qsl, okp, ovp, tables, lens, b.scale, kv_dtype=kv,
+                            k_scale=b.k_scale, v_scale=b.v_scale)
+    G.assert_close(got, ref, kv, f"prefill every row {Hq}/{Hkv} bs{bs} {kv}")
+
+
 @pytest.mark.parametrize("scale", [-0.07, 0.0])
 def test_prefill_negative_and_zero_scale(scale):
     """The softmax scale enters only as scale * q·k: a negative scale flips
