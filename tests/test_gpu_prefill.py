@@ -52,11 +52,12 @@ def test_prefill_mixed_step_fp8_70b_shape():
     G.assert_close(got[pick], dec, "fp8", "prefill rows vs decode")
 
 
-def _varlen_case(Hq, Hkv, bs, kv, seed):
+def _varlen_case(Hq, Hkv, bs, kv, seed, chunks=None):
     rng = np.random.default_rng(seed)
     D = 128
     # (queries in the chunk, keys including the chunk)
-    chunks = [(1, 1), (37, 100), (300, 300), (129, 777), (64, 1024)]
+    if chunks is None:
+        chunks = [(1, 1), (37, 100), (300, 300), (129, 777), (64, 1024)]
     lens = np.array([L for _, L in chunks], dtype=np.int32)
     qsl = np.concatenate([[0], np.cumsum([n for n, _ in chunks])]).astype(np.int32)
     nblk = (lens + bs - 1) // bs
@@ -113,6 +114,20 @@ def test_prefill_varlen_every_row(Hq, Hkv, bs, kv):
     ref = opg.paged_prefill(q64, qsl, okp, ovp, tables, lens, b.scale, kv_dtype=kv,
                             k_scale=b.k_scale, v_scale=b.v_scale)
     G.assert_close(got, ref, kv, f"prefill every row {Hq}/{Hkv} bs{bs} {kv}")
+
+
+def test_prefill_empty_chunks():
+    """Chunks with no queries (one with no context at all) before, between
+    and after real ones: they write nothing and leave the others intact."""
+    chunks = [(0, 40), (17, 50), (0, 0), (5, 5), (0, 33)]
+    b, cq, qsl, lens, tables, max_q = _varlen_case(32, 8, 16, "bf16", seed=11, chunks=chunks)
+    kp, vp = G.gpu_pool(b)
+    G.gpu_fill(b, kp, vp)
+    okp, ovp = G.oracle_pool(b)
+    got, q64 = run_prefill(b, kp, vp, cq, qsl, lens, tables, max_q)
+    ref = opg.paged_prefill(q64, qsl, okp, ovp, tables, lens, b.scale, kv_dtype="bf16")
+    assert got.shape[0] == 22
+    G.assert_close(got, ref, "bf16", "prefill with empty chunks")
 
 
 @pytest.mark.parametrize("scale", [-0.07, 0.0])
