@@ -20,7 +20,9 @@ def build(lib_dir: str) -> str:
            "-isystem", os.path.join(ROCM, "include"), "-I", os.path.join(ROOT, "include"),
            os.path.join(HERE, "pa_device_client.c"), "-o", EXE, "-L", lib_dir, "-lpa",
            "-L", os.path.join(ROCM, "lib"), "-lamdhip64",
-           f"-Wl,-rpath,{lib_dir}", f"-Wl,-rpath,{os.path.join(ROCM, 'lib')}"]
+           # libpa.so found relative to the program, so the tree can move
+           "-Wl,-rpath,$ORIGIN/" + os.path.relpath(lib_dir, HERE),
+           f"-Wl,-rpath,{os.path.join(ROCM, 'lib')}"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"C client build failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
