@@ -255,3 +255,27 @@ def test_decode_balanced_many_sequences(engine, Hq, Hkv, bs, kv, S, monkeypatch)
     ref = G.oracle_decode(b, okp, ovp, G.query_f64(qt))
     assert np.all(got[lens == 0] == 0)
     G.assert_close(got, ref, kv, f"balanced, {len(lens)} sequences, {engine}")
+
+
+@pytest.fixture(scope="module")
+def one_long_sequence():
+    """One sequence of 50,003 tokens (ending inside a block), Llama-3-8B
+    head shape, bf16: the balanced split cuts it over every wavefront of a
+    KV head, and 512-token partitions over 98 partitions."""
+    b = _shape_batch(32, 8, 128, 16, "bf16", [50_003], seed=91)
+    G.say(f"[one long sequence] {int(b.seq_lens[0])} tokens, {b.num_blocks} blocks")
+    kp, vp = G.gpu_pool(b)
+    G.gpu_fill(b, kp, vp)
+    okp, ovp = G.oracle_pool(b)
+    qt = G.query_tensor(b)
+    ref = G.oracle_decode(b, okp, ovp, G.query_f64(qt))
+    return b, kp, vp, qt, ref
+
+
+@pytest.mark.parametrize("engine,ps", [("mfma", BAL), ("valu", BAL), (None, 512)])
+def test_decode_one_very_long_sequence(one_long_sequence, engine, ps, monkeypatch):
+    b, kp, vp, qt, ref = one_long_sequence
+    if engine is not None:
+        monkeypatch.setenv("PA_DECODE_ENGINE", engine)
+    got = G.run_decode(b, kp, vp, qt, partition_size=ps)
+    G.assert_close(got, ref, "bf16", f"one 50,003-token sequence, {engine or 'default'} engine, ps {ps}")
