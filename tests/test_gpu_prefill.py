@@ -130,6 +130,20 @@ def test_prefill_empty_chunks():
     G.assert_close(got, ref, "bf16", "prefill with empty chunks")
 
 
+def test_prefill_long_context():
+    """A 256-query chunk at the end of a 40,000-token context: 625 key steps
+    per tile.  Sampled rows, each against attention over all its keys."""
+    b, cq, qsl, lens, tables, max_q = _varlen_case(32, 8, 16, "bf16", seed=5, chunks=[(256, 40_000)])
+    G.say(f"[long prefill] {int(lens[0])} keys, {max_q} queries")
+    kp, vp = G.gpu_pool(b)
+    G.gpu_fill(b, kp, vp)
+    okp, ovp = G.oracle_pool(b)
+    got, q64 = run_prefill(b, kp, vp, cq, qsl, lens, tables, max_q)
+    rows = [0, 1, 31, 32, 100, 127, 128, 200, 254, 255]
+    ref = opg.paged_prefill(q64, qsl, okp, ovp, tables, lens, b.scale, kv_dtype="bf16", rows=rows)
+    G.assert_close(got, ref, "bf16", "prefill over a 40,000-token context", rows=rows)
+
+
 @pytest.mark.parametrize("scale", [-0.07, 0.0])
 def test_prefill_negative_and_zero_scale(scale):
     """The softmax scale enters only as scale * q·k: a negative scale flips
