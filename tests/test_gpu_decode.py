@@ -279,3 +279,22 @@ def test_decode_one_very_long_sequence(one_long_sequence, engine, ps, monkeypatc
         monkeypatch.setenv("PA_DECODE_ENGINE", engine)
     got = G.run_decode(b, kp, vp, qt, partition_size=ps)
     G.assert_close(got, ref, "bf16", f"one 50,003-token sequence, {engine or 'default'} engine, ps {ps}")
+
+
+@pytest.mark.parametrize("scale", [-0.07, 0.0])
+@pytest.mark.parametrize("engine,ps", [("mfma", BAL), ("valu", BAL), (None, 64), (None, 0)])
+def test_decode_negative_and_zero_scale(scale, engine, ps, monkeypatch):
+    """A negative score scale (the softmax then favours the smallest q·k) and
+    a zero one (every key weighs the same, the output is the mean of V), on
+    both balanced engines and the partitioned path, fp8 cache."""
+    if engine is not None:
+        monkeypatch.setenv("PA_DECODE_ENGINE", engine)
+    b = _shape_batch(32, 8, 128, 16, "fp8", [1, 17, 300, 1000, 64], seed=23)
+    b.scale = scale
+    kp, vp = G.gpu_pool(b)
+    G.gpu_fill(b, kp, vp)
+    okp, ovp = G.oracle_pool(b)
+    qt = G.query_tensor(b)
+    ref = G.oracle_decode(b, okp, ovp, G.query_f64(qt))
+    got = G.run_decode(b, kp, vp, qt, partition_size=ps)
+    G.assert_close(got, ref, "fp8", f"decode scale {scale}, {engine or 'default'} engine, ps {ps}")
