@@ -12,10 +12,13 @@ ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 EXE = os.path.join(HERE, "pa_device_client")
 
 
-def build(lib_dir: str) -> str:
+def build(lib_dir: str):
+    """Returns the program's path, or None (with a note) if there is no C
+    compiler; the GPU test then fails and says so."""
     cc = shutil.which("gcc") or shutil.which("cc")
     if cc is None:
-        raise RuntimeError("no C compiler for the C client")
+        print("note: no C compiler, the C client of the device calls is not built")
+        return None
     cmd = [cc, "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror", "-D__HIP_PLATFORM_AMD__",
            "-isystem", os.path.join(ROCM, "include"), "-I", os.path.join(ROOT, "include"),
            os.path.join(HERE, "pa_device_client.c"), "-o", EXE, "-L", lib_dir, "-lpa",
