@@ -16,8 +16,14 @@ Prints ONE JSON line (rank 0):
               against the 8 TB/s HBM3E peak
   cpu_baseline  the float64 CPU oracle on the same workload (test
               infrastructure, timed on the host cores)
+  rows        event timings of the other rows of the path (long-context
+              split-K, copy-on-write copy, shared prefix, fp8 decode and
+              cache write, fp8 prefill chunk, the mixed step, pool blocks of
+              64 and 128 tokens, chunked-prefill budget steps, the host block
+              manager, swap to pinned host memory, prefix caching)
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+       [--no-rows | --rows-only GROUP] [--cpu-budget SECONDS]
 """
 from __future__ import annotations
 
