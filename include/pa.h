@@ -388,7 +388,9 @@ int32_t pa_bm_is_swapped(const pa_block_manager* bm, int64_t seq_id);
  * Every full block gets a chained hash of the previous block's hash, the
  * block's token ids and an extra hash (e.g. an adapter id): 64-bit FNV-1a
  * over the little-endian bytes of parent_hash (8; 0 for a sequence's first
- * block), the token ids (4 each) and extra_hash (8) — pa_bm_block_hash.  A
+ * block), the token ids (4 each) and extra_hash (8) — pa_bm_block_hash
+ * (which returns 0 for a negative num_tokens or NULL tokens; 0 is also a
+ * possible hash, so callers validate their own input).  A
  * table maps hashes to device blocks.  Unreferenced cached blocks stay in
  * the free list, whose front block leaves the table when it is taken
  * (eviction): least recently released first and, since a freed sequence
