@@ -328,7 +328,8 @@ def row_measurements(dev, iters=20, groups=ROW_GROUPS):
                                                                 b.head_size, b.max_seq_len, ps)),
                              dtype=torch.uint8, device=dev)
             us = _time_us(lambda i: pa.pa_decode(out, q, sets[0][0], sets[0][1], tb, ln, b.max_seq_len,
-                                                 b.scale, partition_size=ps, workspace=ws), iters)
+                                                 b.scale, partition_size=ps, workspace=ws,
+                                                 flags=pa.PA_DECODE_READ_ONCE), iters)
             by = b.decode_kv_bytes()
             rows[name] = {"us": round(us, 2), "kv_bytes": by, "gbs": round(by / us / 1e3, 1),
                           "pct_hbm_peak": round(100 * by / us / 1e3 / HBM_PEAK_GBS, 2),
@@ -354,7 +355,8 @@ def row_measurements(dev, iters=20, groups=ROW_GROUPS):
                                                      b.head_size, b.max_seq_len, -1),
                          dtype=torch.uint8, device=dev)
         us = _time_us(lambda i: pa.pa_decode(out, q, sets[0][0], sets[0][1], tb, ln, b.max_seq_len,
-                                             b.scale, partition_size=-1, workspace=ws), iters)
+                                             b.scale, partition_size=-1, workspace=ws,
+                                             flags=pa.PA_DECODE_SHARED), iters)
         logical = b.decode_kv_bytes()
         unique = (int(np.unique(b.block_tables[b.block_tables >= 0]).size) * b.block_size
                   * b.kv_bytes_per_token())
@@ -397,7 +399,8 @@ def row_measurements(dev, iters=20, groups=ROW_GROUPS):
 
         def dec(i):
             kc, vc = sets[i % 2]
-            pa.pa_decode(out, q, kc, vc, tb, ln, b.max_seq_len, b.scale, b.k_scale, b.v_scale, -1, ws)
+            pa.pa_decode(out, q, kc, vc, tb, ln, b.max_seq_len, b.scale, b.k_scale, b.v_scale, -1, ws,
+                         flags=pa.PA_DECODE_READ_ONCE)
 
         def pre(i):
             kc, vc = sets[i % 2]
@@ -516,7 +519,7 @@ def row_measurements(dev, iters=20, groups=ROW_GROUPS):
                              dtype=torch.uint8, device=dev)
             us = _time_us(lambda i: pa.pa_decode(out, q, sets[i % N_SETS][0], sets[i % N_SETS][1],
                                                  tb, ln, b.max_seq_len, b.scale, partition_size=-1,
-                                                 workspace=ws), iters)
+                                                 workspace=ws, flags=pa.PA_DECODE_READ_ONCE), iters)
             by = b.decode_kv_bytes()
             rows[f"decode_llama3_8b_bs{bs}"] = {"us": round(us, 2), "kv_bytes": by,
                                                "gbs": round(by / us / 1e3, 1),
@@ -610,7 +613,7 @@ def main(argv=None):
         if ev is not None:
             ev[0].record(stream)
         pa.pa_decode(out, q, kc, vc, tables, lens, b.max_seq_len, b.scale, b.k_scale, b.v_scale,
-                     ps, ws, stream=stream)
+                     ps, ws, stream=stream, flags=pa.PA_DECODE_READ_ONCE)
         if ev is not None:
             ev[1].record(stream)
 

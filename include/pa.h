@@ -54,9 +54,18 @@
  *   and returns one of the PA_* codes below; on error nothing is enqueued.
  *   pa_strerror(code) names the code; pa_last_error() returns a message
  *   about the most recent failure on the calling thread.  Device-side
- *   data errors (a block id >= num_blocks, a slot past the pool) cannot be
- *   seen on the host and are undefined behaviour, like a bad page-table
- *   entry.
+ *   data errors (a block id >= num_blocks, a sequence length past its
+ *   table) cannot be seen by the device calls, which never read device
+ *   memory on the host; they are undefined behaviour, like a bad
+ *   page-table entry.  The pa_validate_* calls at the end of this header
+ *   check host copies of those arrays and name the first bad entry.  Slots
+ *   past the pool (cache write) and block pairs outside it (copy, swap)
+ *   are skipped by the kernels.
+ *
+ * Alignment.  Query, output, key and value arrays and the pools must be
+ *   16-byte aligned (the kernels move 16-byte vectors); int32 arrays 4-byte
+ *   and int64 arrays 8-byte aligned.  Misaligned pointers are refused with
+ *   PA_ERR_INVALID.
  */
 #ifndef PA_H_
 #define PA_H_
@@ -106,8 +115,9 @@ size_t pa_pool_bytes(int32_t num_blocks, int32_t num_kv_heads, int32_t block_siz
  * head h:
  *     k_cache[slot / block_size][h][slot % block_size][:] = enc(key[t][h][:])
  *     v_cache[...same...]                                  = enc(value[t][h][:])
- * A negative slot marks a padding token and is skipped.  Two tokens must not
- * share a slot.
+ * A negative slot marks a padding token and is skipped; so is a slot at or
+ * past num_blocks * block_size (no byte outside the pools is written).  Two
+ * tokens must not share a slot.
  *
  *   key, value     [num_tokens][num_kv_heads][head_size] of src_dtype, contiguous
  *   src_dtype      PA_F32 or PA_BF16 (or PA_FP8_E4M3 into an fp8 cache)
@@ -182,6 +192,12 @@ int32_t pa_swap_blocks(const void* src_k, const void* src_v, int32_t src_num_blo
 /* partition_size value selecting the balanced split of pa_decode. */
 #define PA_PARTITION_BALANCED (-1)
 
+/* pa_decode flags (see pa_decode). */
+#define PA_DECODE_READ_ONCE 0x1
+#define PA_DECODE_SHARED 0x2
+#define PA_DECODE_ENGINE_VALU 0x4
+#define PA_DECODE_ENGINE_MFMA 0x8
+
 /*
  * Workspace bytes pa_decode needs for split-K partials: 0 when
  * partition_size == 0 or one partition covers max_seq_len; for
@@ -231,11 +247,28 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num
  * Supported: head_size 64 or 128, block_size 16, 32, 64 or 128 (the range
  * [EVAL] gives for a physical block), num_heads / num_kv_heads in
  * {1, 2, 4, 8}, except f32 with head_size 128.
- * Engines (results agree within the bf16 rounding of P): with
+ * flags (a bitwise OR; 0 is always correct) tell the call how the K/V it
+ * reads is shared, which it cannot see itself ([DEEP] §3.1: forks and
+ * prefix sharing make several tables point at one physical block; the
+ * caller's block manager knows the reference counts, pa_bm_tables_shared):
+ *   PA_DECODE_READ_ONCE   no physical block appears twice among the blocks
+ *                         the call reads (no sharing in the batch): K/V
+ *                         lines are loaded evict-first, since none is read
+ *                         again.  Wrong only in speed if the batch does
+ *                         share blocks;
+ *   PA_DECODE_SHARED      the tables share blocks: ordinary loads, and the
+ *                         balanced split runs on the vector engine, whose
+ *                         whole-row loads suit lines served from the caches;
+ *   PA_DECODE_ENGINE_VALU pin the balanced split to the vector engine;
+ *   PA_DECODE_ENGINE_MFMA pin it to the matrix-core engine (PA_ERR_UNSUPPORTED
+ *                         where that engine is not built).
+ * READ_ONCE with SHARED, or both engine bits, is PA_ERR_INVALID.
+ * Engines (results agree within the bf16 rounding of P): by default, with
  * PA_PARTITION_BALANCED, head_size 128, groups of 4 or 8 and bf16 queries
- * run on the matrix cores; everything else on the vector ALUs.  The
- * environment variable PA_DECODE_ENGINE=valu pins the vector engine (read
- * on every call).
+ * run on the matrix cores; everything else on the vector ALUs.
+ * Limits: with fixed partitions (partition_size >= 0) num_seqs and the
+ * partition count are at most 65535; the balanced split has no limit on
+ * num_seqs.
  */
 int32_t pa_decode(void* out, const void* query, int32_t q_dtype,
                   int32_t num_seqs, int32_t num_heads, int32_t head_size,
@@ -244,8 +277,8 @@ int32_t pa_decode(void* out, const void* query, int32_t q_dtype,
                   const int32_t* block_tables, int32_t max_blocks_per_seq,
                   const int32_t* seq_lens, int32_t max_seq_len,
                   float scale, float k_scale, float v_scale,
-                  int32_t partition_size, void* workspace, size_t workspace_bytes,
-                  void* stream);
+                  int32_t partition_size, int32_t flags, void* workspace,
+                  size_t workspace_bytes, void* stream);
 
 /*
  * pa_prefill_chunk — causal attention for chunks of prompt tokens whose K/V
@@ -428,6 +461,47 @@ int32_t pa_bm_append_tokens(pa_block_manager* bm, int32_t num_seqs, const int64_
                             int32_t* num_cow);
 /* Blocks in the prefix cache's table (>= 0), or PA_ERR_INVALID. */
 int32_t pa_bm_num_cached_blocks(const pa_block_manager* bm);
+
+/* ---------------------------------------------------------------------------
+ * Host-side validation of the device calls' data arrays
+ * ---------------------------------------------------------------------------
+ * The device calls never read device memory on the host, so a block id past
+ * the pool or a length past its table reaches the kernels ([LIB] §4.2 item
+ * 2: the block table is the only map from logical to physical blocks, as a
+ * page table is).  These calls check HOST copies of those arrays before a
+ * launch.  Each returns PA_OK, or PA_ERR_INVALID with pa_last_error naming
+ * the first offending entry (array, index, value and the bound it breaks)
+ * and, if bad_index is not NULL, that entry's flat index in its array
+ * (-1 on PA_OK).  They touch no device state and cost O(entries read).
+ *
+ * pa_validate_decode: for every sequence s, 0 <= seq_lens[s] <=
+ *   max_seq_len, ceil(seq_lens[s] / block_size) <= max_blocks_per_seq, and
+ *   every table entry the sequence reads is a block of the pool
+ *   (0 <= id < num_blocks).  block_tables is [num_seqs][max_blocks_per_seq].
+ * pa_validate_prefill: query_start_loc[0] == 0, non-decreasing, ending at
+ *   num_tokens; every chunk's query count <= max_query_len and <= its
+ *   seq_lens entry; its table entries as for decode.
+ * pa_validate_slots: every slot is negative (padding) or inside the pool
+ *   (< num_blocks * block_size), and no slot repeats.
+ * pa_validate_block_pairs: every (src, dst) pair of block_mapping
+ *   [num_pairs][2] names blocks inside the source (src_num_blocks) and
+ *   destination (dst_num_blocks) pools, destinations are distinct, and, with
+ *   same_pool != 0 (pa_copy_blocks), no destination is the source of a pair.
+ */
+int32_t pa_validate_decode(const int32_t* block_tables, int32_t num_seqs,
+                           int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                           int32_t max_seq_len, int32_t num_blocks, int32_t block_size,
+                           int64_t* bad_index);
+int32_t pa_validate_prefill(const int32_t* query_start_loc, int32_t num_chunks,
+                            int32_t num_tokens, int32_t max_query_len,
+                            const int32_t* block_tables, int32_t max_blocks_per_seq,
+                            const int32_t* seq_lens, int32_t num_blocks, int32_t block_size,
+                            int64_t* bad_index);
+int32_t pa_validate_slots(const int64_t* slot_mapping, int32_t num_tokens, int32_t num_blocks,
+                          int32_t block_size, int64_t* bad_index);
+int32_t pa_validate_block_pairs(const int64_t* block_mapping, int32_t num_pairs,
+                                int32_t src_num_blocks, int32_t dst_num_blocks,
+                                int32_t same_pool, int64_t* bad_index);
 
 #ifdef __cplusplus
 }

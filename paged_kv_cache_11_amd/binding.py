@@ -23,6 +23,9 @@ from typing import Optional
 
 PA_F32, PA_BF16, PA_FP8_E4M3 = 0, 1, 2
 PA_PARTITION_BALANCED = -1
+# pa_decode flags (include/pa.h)
+PA_DECODE_READ_ONCE, PA_DECODE_SHARED = 0x1, 0x2
+PA_DECODE_ENGINE_VALU, PA_DECODE_ENGINE_MFMA = 0x4, 0x8
 PA_OK, PA_ERR_INVALID, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = 0, -1, -2, -3, -4
 PA_ERR_NO_BLOCKS = -5
 
@@ -43,11 +46,17 @@ _SIGNATURES = {
                         _c_p, _c_int, _c_p], _c_int),
     "pa_decode_workspace_size": ([_c_int, _c_int, _c_int, _c_int, _c_int, _c_int], _c_sz),
     "pa_decode": ([_c_p, _c_p, _c_int, _c_int, _c_int, _c_int, _c_p, _c_p, _c_int, _c_int, _c_int,
-                   _c_int, _c_p, _c_int, _c_p, _c_int, _c_f, _c_f, _c_f, _c_int, _c_p, _c_sz,
-                   _c_p], _c_int),
+                   _c_int, _c_p, _c_int, _c_p, _c_int, _c_f, _c_f, _c_f, _c_int, _c_int, _c_p,
+                   _c_sz, _c_p], _c_int),
     "pa_prefill_chunk": ([_c_p, _c_p, _c_int, _c_int, _c_int, _c_int, _c_p, _c_int, _c_int, _c_p,
                           _c_p, _c_int, _c_int, _c_int, _c_int, _c_p, _c_int, _c_p, _c_f, _c_f,
                           _c_f, _c_p], _c_int),
+    # host-side validation of the data arrays (host pointers)
+    "pa_validate_decode": ([_c_p, _c_int, _c_int, _c_p, _c_int, _c_int, _c_int, _c_p], _c_int),
+    "pa_validate_prefill": ([_c_p, _c_int, _c_int, _c_int, _c_p, _c_int, _c_p, _c_int, _c_int,
+                             _c_p], _c_int),
+    "pa_validate_slots": ([_c_p, _c_int, _c_int, _c_int, _c_p], _c_int),
+    "pa_validate_block_pairs": ([_c_p, _c_int, _c_int, _c_int, _c_int, _c_p], _c_int),
     # host block manager
     "pa_bm_create": ([_c_int, _c_int], _c_p),
     "pa_bm_destroy": ([_c_p], None),
@@ -159,6 +168,8 @@ def pa_cache_write(key, value, k_cache, v_cache, slot_mapping, k_scale: float = 
                    v_scale: float = 1.0, stream=None) -> None:
     """Write key/value [num_tokens, num_kv_heads, head_size] into their slots."""
     nb, hkv, bs, d = _pool_dims(k_cache, v_cache)
+    if _validating():
+        validate_slots(slot_mapping, nb, bs)
     _check(load().pa_cache_write(_ptr(key), _ptr(value), dtype_code(key), int(key.shape[0]),
                                  _ptr(k_cache), _ptr(v_cache), dtype_code(k_cache), nb, bs, hkv, d,
                                  _ptr(slot_mapping), float(k_scale), float(v_scale), _stream(stream)))
@@ -168,6 +179,8 @@ def pa_copy_blocks(k_cache, v_cache, block_mapping, stream=None) -> None:
     """Copy whole physical blocks (src, dst) in both pools."""
     nb, hkv, bs, d = _pool_dims(k_cache, v_cache)
     n = int(block_mapping.shape[0]) if block_mapping is not None else 0
+    if _validating() and n:
+        validate_block_pairs(block_mapping, nb, nb, True)
     _check(load().pa_copy_blocks(_ptr(k_cache), _ptr(v_cache), dtype_code(k_cache), nb, bs, hkv, d,
                                  _ptr(block_mapping) if n else None, n, _stream(stream)))
 
@@ -204,11 +217,13 @@ def pa_decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_size, max_s
 
 def pa_decode(out, query, k_cache, v_cache, block_tables, seq_lens, max_seq_len: int,
               scale: float, k_scale: float = 1.0, v_scale: float = 1.0,
-              partition_size: int = 0, workspace=None, stream=None) -> None:
+              partition_size: int = 0, workspace=None, stream=None, flags: int = 0) -> None:
     """Decode attention of query [num_seqs, num_heads, head_size] into out.
 
     partition_size: 0 (no split), a multiple of the block size (fixed
     partitions), or PA_PARTITION_BALANCED (equal block runs per wavefront).
+    flags: PA_DECODE_READ_ONCE / PA_DECODE_SHARED (how blocks are shared)
+    and PA_DECODE_ENGINE_VALU / _MFMA (engine pin), as in include/pa.h.
 
     With ``workspace=None`` and a split that needs one, a workspace tensor
     is taken from torch's allocator."""
@@ -216,6 +231,8 @@ def pa_decode(out, query, k_cache, v_cache, block_tables, seq_lens, max_seq_len:
 
     nb, hkv, bs, d = _pool_dims(k_cache, v_cache)
     S, H = int(query.shape[0]), int(query.shape[1])
+    if _validating():
+        validate_decode(block_tables, seq_lens, max_seq_len, nb, bs)
     need = pa_decode_workspace_size(S, H, hkv, d, max_seq_len, partition_size)
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=query.device)
@@ -224,7 +241,76 @@ def pa_decode(out, query, k_cache, v_cache, block_tables, seq_lens, max_seq_len:
                             _ptr(v_cache), dtype_code(k_cache), nb, bs, hkv, _ptr(block_tables),
                             int(block_tables.shape[1]), _ptr(seq_lens), int(max_seq_len),
                             float(scale), float(k_scale), float(v_scale), int(partition_size),
-                            _ptr(workspace), ws_bytes, _stream(stream)))
+                            int(flags), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+# --- host-side validation ---------------------------------------------------
+# PA_VALIDATE=1 in the environment makes every device call of this binding
+# copy its index arrays to the host and check them first (a debug mode: it
+# synchronises).  The validate_* functions can also be called directly on
+# numpy arrays or tensors.
+
+def _validating() -> bool:
+    return os.environ.get("PA_VALIDATE", "0") not in ("", "0")
+
+
+def _host(a, dtype):
+    import numpy as np
+
+    if hasattr(a, "detach"):
+        a = a.detach().cpu().numpy()
+    return np.ascontiguousarray(np.asarray(a, dtype=dtype))
+
+
+def _validated(code):
+    if code != PA_OK:
+        raise PagedAttentionError(code, load().pa_last_error().decode())
+
+
+def validate_decode(block_tables, seq_lens, max_seq_len: int, num_blocks: int,
+                    block_size: int) -> None:
+    """Raise PagedAttentionError naming the first table entry or length a
+    pa_decode call with these arrays would read out of bounds."""
+    import numpy as np
+
+    t = _host(block_tables, np.int32)
+    ln = _host(seq_lens, np.int32).reshape(-1)
+    if t.ndim != 2 or t.shape[0] != ln.size:
+        raise PagedAttentionError(PA_ERR_INVALID, "block_tables must be [num_seqs, max_blocks]")
+    _validated(load().pa_validate_decode(t.ctypes.data, ln.size, t.shape[1], ln.ctypes.data,
+                                         int(max_seq_len), int(num_blocks), int(block_size), None))
+
+
+def validate_prefill(query_start_loc, num_tokens: int, max_query_len: int, block_tables,
+                     seq_lens, num_blocks: int, block_size: int) -> None:
+    import numpy as np
+
+    q = _host(query_start_loc, np.int32).reshape(-1)
+    t = _host(block_tables, np.int32)
+    ln = _host(seq_lens, np.int32).reshape(-1)
+    if q.size != ln.size + 1 or t.ndim != 2 or t.shape[0] != ln.size:
+        raise PagedAttentionError(PA_ERR_INVALID, "query_start_loc / block_tables / seq_lens "
+                                  "disagree on the number of chunks")
+    _validated(load().pa_validate_prefill(q.ctypes.data, ln.size, int(num_tokens),
+                                          int(max_query_len), t.ctypes.data, t.shape[1],
+                                          ln.ctypes.data, int(num_blocks), int(block_size), None))
+
+
+def validate_slots(slot_mapping, num_blocks: int, block_size: int) -> None:
+    import numpy as np
+
+    s = _host(slot_mapping, np.int64).reshape(-1)
+    _validated(load().pa_validate_slots(s.ctypes.data, s.size, int(num_blocks), int(block_size),
+                                        None))
+
+
+def validate_block_pairs(block_mapping, src_num_blocks: int, dst_num_blocks: int,
+                         same_pool: bool) -> None:
+    import numpy as np
+
+    m = _host(block_mapping, np.int64).reshape(-1, 2)
+    _validated(load().pa_validate_block_pairs(m.ctypes.data, m.shape[0], int(src_num_blocks),
+                                              int(dst_num_blocks), int(bool(same_pool)), None))
 
 
 def pa_prefill_chunk(out, query, query_start_loc, max_query_len: int, k_cache, v_cache,
@@ -233,6 +319,8 @@ def pa_prefill_chunk(out, query, query_start_loc, max_query_len: int, k_cache, v
     """Causal attention of chunk queries [num_tokens, num_heads, head_size]."""
     nb, hkv, bs, d = _pool_dims(k_cache, v_cache)
     T, H = int(query.shape[0]), int(query.shape[1])
+    if _validating():
+        validate_prefill(query_start_loc, T, max_query_len, block_tables, seq_lens, nb, bs)
     _check(load().pa_prefill_chunk(_ptr(out), _ptr(query), dtype_code(query), T, H, d,
                                    _ptr(query_start_loc), int(seq_lens.shape[0]),
                                    int(max_query_len), _ptr(k_cache), _ptr(v_cache),

@@ -22,7 +22,7 @@ template <typename SRC, typename DST>
 __global__ __launch_bounds__(256) void cache_write_kernel(
     const uint8_t* __restrict__ key, const uint8_t* __restrict__ value,
     uint8_t* __restrict__ k_cache, uint8_t* __restrict__ v_cache,
-    const int64_t* __restrict__ slot_mapping, int64_t total_chunks,
+    const int64_t* __restrict__ slot_mapping, int64_t total_chunks, int64_t pool_slots,
     int chunks_per_row, int num_kv_heads, int block_size, int head_size,
     float k_scale, float v_scale) {
   constexpr int SB = Elem<SRC>::bytes, DB = Elem<DST>::bytes;
@@ -44,7 +44,9 @@ __global__ __launch_bounds__(256) void cache_write_kernel(
     ks[j] = ((const u32x4*)(key + src_elem * SB))[j];
     vs[j] = ((const u32x4*)(value + src_elem * SB))[j];
   }
-  if (slot < 0) return;
+  // A negative slot is a padding token; one past the pool is a caller's
+  // error that must not write outside it.  Both are skipped.
+  if (slot < 0 || slot >= pool_slots) return;
   const int64_t blk = slot / block_size;
   const int off = (int)(slot % block_size);
   const int64_t dst_elem =
@@ -82,7 +84,7 @@ static hipError_t launch_cache_write(const CacheWriteArgs& a) {
   hipLaunchKernelGGL((cache_write_kernel<SRC, DST>), dim3((unsigned)nblocks), dim3(256), 0,
                      a.stream, (const uint8_t*)a.key, (const uint8_t*)a.value,
                      (uint8_t*)a.k_cache, (uint8_t*)a.v_cache, a.slot_mapping, total,
-                     chunks_per_row, a.num_kv_heads, a.block_size, a.head_size, a.k_scale,
+                     (int64_t)a.num_blocks * a.block_size, chunks_per_row, a.num_kv_heads, a.block_size, a.head_size, a.k_scale,
                      a.v_scale);
   return hipGetLastError();
 }

@@ -5,7 +5,7 @@
 namespace pa {
 
 hipError_t decode_f32(const DecodeArgs& a) {
-  if (a.head_size != 64) return hipErrorInvalidValue;
+  if (a.head_size != 64) return kNotInstantiated;
   return dispatch_block<F32, F32, 64>(a);
 }
 

@@ -8,7 +8,7 @@ hipError_t decode_fp8(const DecodeArgs& a) {
   switch (a.head_size) {
     case 64: return dispatch_block<FP8, BF16, 64>(a);
     case 128: return dispatch_block<FP8, BF16, 128>(a);
-    default: return hipErrorInvalidValue;
+    default: return kNotInstantiated;
   }
 }
 

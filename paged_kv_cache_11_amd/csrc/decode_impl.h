@@ -747,7 +747,7 @@ __global__ __launch_bounds__(kMaxDecodeWaves * kWave) void decode_balanced_kerne
     const void* __restrict__ k_cache, const void* __restrict__ v_cache,
     const int32_t* __restrict__ block_tables, const int32_t* __restrict__ seq_lens, int num_seqs,
     int max_blocks_per_seq, int num_kv_heads, int workers_per_head, float qk_scale_log2,
-    float v_scale, int sub_shift, int64_t pool_tokens) {
+    float v_scale, int sub_shift, int read_once_hint) {
   using WA = WaveAttn<KV, QT, D, BS, G>;
   constexpr int EPL = WA::EPL, RPL = WA::RPL;
   using OT = QT;
@@ -759,9 +759,8 @@ __global__ __launch_bounds__(kMaxDecodeWaves * kWave) void decode_balanced_kerne
 
   const int64_t T = total_blocks(seq_lens, num_seqs, BS, lane);
   const int W = effective_workers(T, workers_per_head, BS);
-  // More tokens referenced than the pool holds: blocks are shared, so
-  // their lines may be read again (ordinary loads); else non-temporal.
-  const bool read_once = T * BS <= pool_tokens;
+  // The caller declared that no block is read twice: evict-first loads.
+  const bool read_once = read_once_hint != 0;
   int32_t* merge = merges + 2 * (int64_t)worker;
   if (lane == 0) merge[0] = -1;  // no merge task unless the last run sets one
   if (vw >= W) return;
@@ -949,7 +948,6 @@ hipError_t launch_decode(const DecodeArgs& a) {
   const float k_scale = std::is_same<KV, FP8>::value ? a.k_scale : 1.0f;
   const float v_scale = std::is_same<KV, FP8>::value ? a.v_scale : 1.0f;
   const float qk = a.scale * k_scale * kLog2e;
-  const int64_t pool_tokens = (int64_t)a.num_blocks * PBS;
   if (a.balanced_workers > 0) {
     const int per_head = a.balanced_workers / a.num_kv_heads;
     const int workers = per_head * a.num_kv_heads;
@@ -963,7 +961,7 @@ hipError_t launch_decode(const DecodeArgs& a) {
                            a.merges, a.cuts, a.query, a.k_cache, a.v_cache, a.block_tables,
                            a.seq_lens,
                            a.num_seqs, a.max_blocks_per_seq, a.num_kv_heads, per_head, qk, v_scale,
-                           pool_tokens);
+                           a.read_once);
     }
     if (!mfma)
       hipLaunchKernelGGL((decode_balanced_kernel<KV, QT, D, BS, G>), dim3((unsigned)wg),
@@ -971,7 +969,7 @@ hipError_t launch_decode(const DecodeArgs& a) {
                          a.merges, a.cuts, a.query, a.k_cache, a.v_cache, a.block_tables,
                          a.seq_lens,
                          a.num_seqs, a.max_blocks_per_seq, a.num_kv_heads, per_head, qk, v_scale,
-                         kSubShift, pool_tokens);
+                         kSubShift, a.read_once);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.num_seqs <= per_head)
@@ -993,9 +991,7 @@ hipError_t launch_decode(const DecodeArgs& a) {
                      dim3(nw * kWave), 0, a.stream, a.out, a.part_o, a.part_ml, a.query,
                      a.k_cache, a.v_cache, a.block_tables, a.seq_lens, a.max_blocks_per_seq,
                      a.num_kv_heads, tiles_per_part, a.max_parts, qk, v_scale, kSubShift,
-                     // every sequence at its longest still fits the pool: no
-                     // block can be shared, lines are read once
-                     (int64_t)a.num_seqs * a.max_seq_len <= pool_tokens ? 1 : 0);
+                     a.read_once);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.max_parts <= 1) return e;
   hipLaunchKernelGGL((lse_reduce_kernel<QT, D, G>),
@@ -1013,7 +1009,7 @@ hipError_t dispatch_group(const DecodeArgs& a) {
     case 2: return launch_decode<KV, QT, D, BS, 2>(a);
     case 4: return launch_decode<KV, QT, D, BS, 4>(a);
     case 8: return launch_decode<KV, QT, D, BS, 8>(a);
-    default: return hipErrorInvalidValue;
+    default: return kNotInstantiated;
   }
 }
 
@@ -1024,7 +1020,7 @@ hipError_t dispatch_block(const DecodeArgs& a) {
     case 32: return dispatch_group<KV, QT, D, 32>(a);
     case 64: return dispatch_group<KV, QT, D, 64>(a);
     case 128: return dispatch_group<KV, QT, D, 128>(a);
-    default: return hipErrorInvalidValue;
+    default: return kNotInstantiated;
   }
 }
 

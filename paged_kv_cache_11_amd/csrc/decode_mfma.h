@@ -357,7 +357,7 @@ __global__ __launch_bounds__(kMaxDecodeWaves * kWave, 2) void decode_balanced_mf
     const void* __restrict__ k_cache, const void* __restrict__ v_cache,
     const int32_t* __restrict__ block_tables, const int32_t* __restrict__ seq_lens, int num_seqs,
     int max_blocks_per_seq, int num_kv_heads, int workers_per_head, float qk_scale_log2,
-    float v_scale, int64_t pool_tokens) {
+    float v_scale, int read_once_hint) {
   static_assert(std::is_same<QT, BF16>::value, "bf16 queries");
   using MA = MfmaAttn<KV, BS, G>;
   constexpr int D = kMD;
@@ -371,9 +371,8 @@ __global__ __launch_bounds__(kMaxDecodeWaves * kWave, 2) void decode_balanced_mf
 
   const int64_t T = total_blocks(seq_lens, num_seqs, MA::UBS, lane);
   const int W = effective_workers(T, workers_per_head, MA::UBS);
-  // More tokens referenced than the pool holds: blocks are shared, so
-  // their lines may be read again (ordinary loads); else non-temporal.
-  const bool read_once = T * MA::UBS <= pool_tokens;
+  // The caller declared that no block is read twice: evict-first loads.
+  const bool read_once = read_once_hint != 0;
   int32_t* merge = merges + 2 * (int64_t)worker;
   if (lane == 0) merge[0] = -1;  // no merge task unless the last run sets one
   if (vw >= W) return;

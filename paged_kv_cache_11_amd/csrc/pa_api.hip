@@ -6,6 +6,7 @@
 #include <stdio.h>
 #include <stdlib.h>
 
+#include <atomic>
 #include <string>
 
 #include <string.h>
@@ -53,10 +54,21 @@ int32_t check_pool(const void* k_cache, const void* v_cache, int32_t cache_dtype
 
 int32_t hip_result(hipError_t e, const char* what) {
   if (e == hipSuccess) return ok();
-  if (e == hipErrorInvalidValue)
+  if (e == pa::kNotInstantiated)
     return fail(PA_ERR_UNSUPPORTED, "%s: shape not instantiated", what);
   return fail(PA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
+
+// A pointer argument must be aligned to `align` bytes (NULL passes; the
+// callers check for it where it matters).
+int32_t check_align(const void* p, size_t align, const char* name) {
+  if ((uintptr_t)p % align != 0)
+    return fail(PA_ERR_INVALID, "%s must be %zu-byte aligned", name, align);
+  return PA_OK;
+}
+
+// Grid y and z extents are at most 65535 workgroups.
+constexpr int64_t kMaxGridYZ = 65535;
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -69,7 +81,7 @@ int64_t decode_max_parts(int32_t max_seq_len, int32_t partition_size) {
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // PA_DECODE_WAVES=1|2|4 pins the wavefronts per decode workgroup (a tuning
-// knob); otherwise the library picks from the partition size.
+// knob, read once); otherwise the library picks from the partition size.
 int32_t decode_waves_override() {
   static const int32_t v = [] {
     const char* e = getenv("PA_DECODE_WAVES");
@@ -79,27 +91,52 @@ int32_t decode_waves_override() {
   return v;
 }
 
-// The balanced decode's engine: PA_DECODE_ENGINE=valu|mfma pins it (a
-// tuning knob); by default the matrix cores, wherever that engine is
-// compiled (head size 128, groups of 4 or 8, bf16 queries; elsewhere the
-// launch falls back to the vector engine).  Read on every call (a few
-// hundred nanoseconds), so that a process can compare the engines.
-int32_t decode_engine(int32_t q_dtype, int32_t cache_dtype, int32_t head_size, int32_t group) {
-  const bool has_mfma = head_size == 128 && (group == 4 || group == 8) && q_dtype == PA_BF16 &&
-                        cache_dtype != PA_F32;
-  const char* e = getenv("PA_DECODE_ENGINE");
-  if (!has_mfma || (e && !strcmp(e, "valu"))) return pa::kEngineValu;
+bool has_mfma_engine(int32_t q_dtype, int32_t cache_dtype, int32_t head_size, int32_t group) {
+  return head_size == 128 && (group == 4 || group == 8) && q_dtype == PA_BF16 &&
+         cache_dtype != PA_F32;
+}
+
+// The balanced decode's engine from the call's flags: a pinned engine if
+// asked for; the vector engine when the tables share blocks (its 1 KiB row
+// loads take fewer cache-line requests than the matrix-core operand loads
+// when lines come from L2 and MALL rather than HBM); else the matrix cores
+// where that engine is built.  Returns -1 for a pinned engine that is not
+// built for the shape.
+int32_t decode_engine(int32_t flags, int32_t q_dtype, int32_t cache_dtype, int32_t head_size,
+                      int32_t group) {
+  const bool has_mfma = has_mfma_engine(q_dtype, cache_dtype, head_size, group);
+  if (flags & PA_DECODE_ENGINE_VALU) return pa::kEngineValu;
+  if (flags & PA_DECODE_ENGINE_MFMA) return has_mfma ? pa::kEngineMfma : -1;
+  if ((flags & PA_DECODE_SHARED) || !has_mfma) return pa::kEngineValu;
   return pa::kEngineMfma;
+}
+
+// Compute units of the current device, queried once per device.
+using pa::kMaxDevices;
+std::atomic<int32_t> g_device_cus[kMaxDevices];
+
+int32_t device_cus() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < kMaxDevices) {
+    const int32_t c = g_device_cus[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  if (dev < kMaxDevices) g_device_cus[dev].store(cus, std::memory_order_relaxed);
+  return cus;
 }
 
 // Wavefronts of the balanced split per compute unit of the current device,
 // capped by the workspace layout: PA_BALANCED_WAVES_PER_CU pins it (a
-// tuning knob); by default 4 (one workgroup per CU) for the matrix-core
-// engine, whose wavefronts keep two tiles in flight with little arithmetic
-// between them, and 8 (two per SIMD, so that one's loads hide the other's
-// score and softmax arithmetic) for the vector engine.  Whole workgroups
-// per CU matter: a fraction leaves some CUs with one more workgroup than
-// others for the whole kernel.
+// tuning knob, read once); by default 4 (one workgroup per CU) for the
+// matrix-core engine, whose wavefronts keep two tiles in flight with little
+// arithmetic between them, and 8 (two per SIMD, so that one's loads hide
+// the other's score and softmax arithmetic) for the vector engine.  Whole
+// workgroups per CU matter: a fraction leaves some CUs with one more
+// workgroup than others for the whole kernel.
 int32_t balanced_workers_for_device(int32_t engine) {
   static const int pinned = [] {
     const char* e = getenv("PA_BALANCED_WAVES_PER_CU");
@@ -107,10 +144,8 @@ int32_t balanced_workers_for_device(int32_t engine) {
     return (x >= 1 && x <= 32) ? x : 0;
   }();
   const int per_cu = pinned ? pinned : (engine == pa::kEngineMfma ? 4 : 8);
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    return 0;
+  const int cus = device_cus();
+  if (cus <= 0) return 0;
   const int64_t w = (int64_t)cus * per_cu;
   return (int32_t)(w < pa::kMaxBalancedWorkers ? w : pa::kMaxBalancedWorkers);
 }
@@ -143,6 +178,115 @@ int32_t pa::record_error(int32_t code, const char* msg) {
   if (code == PA_OK) g_last_error.clear();
   else g_last_error = msg;
   return code;
+}
+
+// Validation and launch of a decode call, shared by pa_decode (caller's
+// workspace) and pa_decode_no_alloc (the library's static scratch).
+int32_t pa::decode_call(void* out, const void* query, int32_t q_dtype, int32_t num_seqs,
+                           int32_t num_heads, int32_t head_size, const void* k_cache,
+                           const void* v_cache, int32_t cache_dtype, int32_t num_blocks,
+                           int32_t block_size, int32_t num_kv_heads, const int32_t* block_tables,
+                           int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                           int32_t max_seq_len, float scale, float k_scale, float v_scale,
+                           int32_t partition_size, int32_t flags, void* workspace,
+                           size_t workspace_bytes, void* stream, const char* who) {
+  if (int32_t r = check_pool(k_cache, v_cache, cache_dtype, num_blocks, block_size, num_kv_heads,
+                             head_size))
+    return r;
+  if (num_seqs < 0) return fail(PA_ERR_INVALID, "num_seqs %d < 0", num_seqs);
+  if (num_heads <= 0 || num_heads % num_kv_heads != 0)
+    return fail(PA_ERR_INVALID, "num_heads %d must be a positive multiple of num_kv_heads %d",
+                num_heads, num_kv_heads);
+  if (!valid_dtype(q_dtype)) return fail(PA_ERR_INVALID, "unknown query dtype %d", q_dtype);
+  if (max_blocks_per_seq <= 0) return fail(PA_ERR_INVALID, "max_blocks_per_seq must be > 0");
+  if (max_seq_len < 0 || (int64_t)max_seq_len > (int64_t)max_blocks_per_seq * block_size)
+    return fail(PA_ERR_INVALID, "max_seq_len %d does not fit %d blocks of %d tokens", max_seq_len,
+                max_blocks_per_seq, block_size);
+  const bool balanced = partition_size == PA_PARTITION_BALANCED;
+  if (!balanced && (partition_size < 0 || partition_size % block_size != 0))
+    return fail(PA_ERR_INVALID,
+                "partition_size %d must be PA_PARTITION_BALANCED, 0 or a multiple of block_size %d",
+                partition_size, block_size);
+  if (!(scale == scale) || !(k_scale == k_scale) || !(v_scale == v_scale))
+    return fail(PA_ERR_INVALID, "scales must not be NaN");
+  const int32_t known = PA_DECODE_READ_ONCE | PA_DECODE_SHARED | PA_DECODE_ENGINE_VALU |
+                        PA_DECODE_ENGINE_MFMA;
+  if ((flags & ~known) != 0) return fail(PA_ERR_INVALID, "unknown decode flags %#x", flags);
+  if ((flags & PA_DECODE_READ_ONCE) && (flags & PA_DECODE_SHARED))
+    return fail(PA_ERR_INVALID, "PA_DECODE_READ_ONCE and PA_DECODE_SHARED exclude each other");
+  if ((flags & PA_DECODE_ENGINE_VALU) && (flags & PA_DECODE_ENGINE_MFMA))
+    return fail(PA_ERR_INVALID, "two engines pinned");
+  const int group = num_heads / num_kv_heads;
+  if (!pa::decode_supported(q_dtype, cache_dtype, head_size, block_size, group))
+    return fail(PA_ERR_UNSUPPORTED,
+                "decode not built for q dtype %d, cache dtype %d, head_size %d, block_size %d, "
+                "group %d", q_dtype, cache_dtype, head_size, block_size, group);
+  const int32_t engine = decode_engine(flags, q_dtype, cache_dtype, head_size, group);
+  if (engine < 0)
+    return fail(PA_ERR_UNSUPPORTED, "the matrix-core decode engine is not built for this shape");
+  if (num_seqs == 0) return ok();
+  if (!out || !query || !block_tables || !seq_lens)
+    return fail(PA_ERR_INVALID, "out / query / block_tables / seq_lens is NULL");
+  if (int32_t r = check_align(out, 16, "out")) return r;
+  if (int32_t r = check_align(query, 16, "query")) return r;
+  if (int32_t r = check_align(block_tables, 4, "block_tables")) return r;
+  if (int32_t r = check_align(seq_lens, 4, "seq_lens")) return r;
+  const int64_t mp = balanced ? 1 : decode_max_parts(max_seq_len, partition_size);
+  if (!balanced && (num_seqs > kMaxGridYZ || num_kv_heads > kMaxGridYZ))
+    return fail(PA_ERR_INVALID,
+                "%d sequences / %d KV heads exceed the %lld a partitioned decode grid takes "
+                "(the balanced split takes any number of sequences)",
+                num_seqs, num_kv_heads, (long long)kMaxGridYZ);
+  if (mp > kMaxGridYZ) return fail(PA_ERR_INVALID, "too many partitions (%lld)", (long long)mp);
+  float* part_o = nullptr;
+  float* part_ml = nullptr;
+  int32_t workers = 0;
+  int32_t* a_merges = nullptr;
+  int32_t* a_cuts = nullptr;
+  if (mp > 1 || balanced) {
+    const size_t need = pa_decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_size,
+                                                 max_seq_len, partition_size);
+    if (!workspace || workspace_bytes < need)
+      return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                  workspace ? workspace_bytes : (size_t)0);
+    if (int32_t r = check_align(workspace, 16, "workspace")) return r;
+    const size_t n = balanced ? (size_t)pa::kMaxBalancedWorkers * 2 * (num_heads / num_kv_heads)
+                              : (size_t)num_seqs * num_heads * mp;
+    part_o = (float*)workspace;
+    part_ml = (float*)((char*)workspace + align256(n * head_size * sizeof(float)));
+    if (balanced) {
+      a_merges = (int32_t*)((char*)part_ml + align256(n * 2 * sizeof(float)));
+      a_cuts = (int32_t*)((char*)a_merges +
+                          align256((size_t)pa::kMaxBalancedWorkers * 2 * sizeof(int32_t)));
+      const int32_t w = balanced_workers_for_device(engine);
+      if (w <= 0) return fail(PA_ERR_HIP, "cannot query the device's compute units");
+      workers = (w / num_kv_heads) * num_kv_heads;
+      if (workers < num_kv_heads) workers = num_kv_heads;
+    }
+  }
+  pa::DecodeArgs a{};
+  a.out = out; a.query = query; a.q_dtype = q_dtype;
+  a.num_seqs = num_seqs; a.num_heads = num_heads; a.head_size = head_size;
+  a.k_cache = k_cache; a.v_cache = v_cache; a.cache_dtype = cache_dtype;
+  a.num_blocks = num_blocks; a.block_size = block_size; a.num_kv_heads = num_kv_heads;
+  a.block_tables = block_tables; a.max_blocks_per_seq = max_blocks_per_seq;
+  a.seq_lens = seq_lens; a.max_seq_len = max_seq_len;
+  a.scale = scale; a.k_scale = k_scale; a.v_scale = v_scale;
+  a.partition_blocks = mp > 1 ? partition_size / block_size : 0;
+  a.max_parts = (int32_t)mp;
+  a.part_o = part_o; a.part_ml = part_ml;
+  a.num_waves = decode_waves_override();
+  a.balanced_workers = workers;
+  a.merges = a_merges;
+  a.cuts = a_cuts;
+  a.engine = engine;
+  a.read_once = (flags & PA_DECODE_READ_ONCE) ? 1 : 0;
+  a.stream = (hipStream_t)stream;
+  hipError_t e;
+  if (cache_dtype == PA_F32) e = pa::decode_f32(a);
+  else if (cache_dtype == PA_BF16) e = pa::decode_bf16(a);
+  else e = pa::decode_fp8(a);
+  return hip_result(e, who);
 }
 
 extern "C" {
@@ -190,6 +334,11 @@ int32_t pa_cache_write(const void* key, const void* value, int32_t src_dtype, in
   if (num_tokens == 0) return ok();
   if (!key || !value || !slot_mapping)
     return fail(PA_ERR_INVALID, "key / value / slot_mapping is NULL");
+  if (int32_t r = check_align(key, 16, "key")) return r;
+  if (int32_t r = check_align(value, 16, "value")) return r;
+  if (int32_t r = check_align(slot_mapping, 8, "slot_mapping")) return r;
+  if ((head_size * pa::dtype_bytes(src_dtype)) % 16 != 0)
+    return fail(PA_ERR_UNSUPPORTED, "a source head row must be a multiple of 16 bytes");
   pa::CacheWriteArgs a{key, value, src_dtype, num_tokens, k_cache, v_cache, cache_dtype,
                        num_blocks, block_size, num_kv_heads, head_size, slot_mapping, k_scale,
                        v_scale, (hipStream_t)stream};
@@ -205,6 +354,7 @@ int32_t pa_copy_blocks(void* k_cache, void* v_cache, int32_t cache_dtype, int32_
   if (num_pairs < 0) return fail(PA_ERR_INVALID, "num_pairs %d < 0", num_pairs);
   if (num_pairs == 0) return ok();
   if (!block_mapping) return fail(PA_ERR_INVALID, "block_mapping is NULL");
+  if (int32_t r = check_align(block_mapping, 8, "block_mapping")) return r;
   pa::MoveBlocksArgs a{k_cache,    v_cache,      k_cache,      v_cache,
                        cache_dtype, num_blocks,  num_blocks,   block_size,
                        num_kv_heads, head_size,  block_mapping, num_pairs,
@@ -230,6 +380,7 @@ int32_t pa_swap_blocks(const void* src_k, const void* src_v, int32_t src_num_blo
   if (int32_t r = device_view(dst_v, "dst_v", &dv)) return r;
   if (num_pairs == 0) return ok();
   if (!block_mapping) return fail(PA_ERR_INVALID, "block_mapping is NULL");
+  if (int32_t r = check_align(block_mapping, 8, "block_mapping")) return r;
   if (int32_t r = device_view(block_mapping, "block_mapping", &map)) return r;
   pa::MoveBlocksArgs a{sk, sv, (void*)dk, (void*)dv, cache_dtype, src_num_blocks, dst_num_blocks,
                        block_size, num_kv_heads, head_size, (const int64_t*)map, num_pairs,
@@ -259,85 +410,12 @@ int32_t pa_decode(void* out, const void* query, int32_t q_dtype, int32_t num_seq
                   int32_t cache_dtype, int32_t num_blocks, int32_t block_size,
                   int32_t num_kv_heads, const int32_t* block_tables, int32_t max_blocks_per_seq,
                   const int32_t* seq_lens, int32_t max_seq_len, float scale, float k_scale,
-                  float v_scale, int32_t partition_size, void* workspace, size_t workspace_bytes,
-                  void* stream) {
-  if (int32_t r = check_pool(k_cache, v_cache, cache_dtype, num_blocks, block_size, num_kv_heads,
-                             head_size))
-    return r;
-  if (num_seqs < 0) return fail(PA_ERR_INVALID, "num_seqs %d < 0", num_seqs);
-  if (num_heads <= 0 || num_heads % num_kv_heads != 0)
-    return fail(PA_ERR_INVALID, "num_heads %d must be a positive multiple of num_kv_heads %d",
-                num_heads, num_kv_heads);
-  if (!valid_dtype(q_dtype)) return fail(PA_ERR_INVALID, "unknown query dtype %d", q_dtype);
-  if (max_blocks_per_seq <= 0) return fail(PA_ERR_INVALID, "max_blocks_per_seq must be > 0");
-  if (max_seq_len < 0 || (int64_t)max_seq_len > (int64_t)max_blocks_per_seq * block_size)
-    return fail(PA_ERR_INVALID, "max_seq_len %d does not fit %d blocks of %d tokens", max_seq_len,
-                max_blocks_per_seq, block_size);
-  const bool balanced = partition_size == PA_PARTITION_BALANCED;
-  if (!balanced && (partition_size < 0 || partition_size % block_size != 0))
-    return fail(PA_ERR_INVALID,
-                "partition_size %d must be PA_PARTITION_BALANCED, 0 or a multiple of block_size %d",
-                partition_size, block_size);
-  if (!(scale == scale) || !(k_scale == k_scale) || !(v_scale == v_scale))
-    return fail(PA_ERR_INVALID, "scales must not be NaN");
-  const int group = num_heads / num_kv_heads;
-  if (!pa::decode_supported(q_dtype, cache_dtype, head_size, block_size, group))
-    return fail(PA_ERR_UNSUPPORTED,
-                "decode not built for q dtype %d, cache dtype %d, head_size %d, block_size %d, "
-                "group %d", q_dtype, cache_dtype, head_size, block_size, group);
-  if (num_seqs == 0) return ok();
-  if (!out || !query || !block_tables || !seq_lens)
-    return fail(PA_ERR_INVALID, "out / query / block_tables / seq_lens is NULL");
-  const int64_t mp = balanced ? 1 : decode_max_parts(max_seq_len, partition_size);
-  if (mp > 65535) return fail(PA_ERR_INVALID, "too many partitions (%lld)", (long long)mp);
-  float* part_o = nullptr;
-  float* part_ml = nullptr;
-  int32_t workers = 0;
-  int32_t* a_merges = nullptr;
-  int32_t* a_cuts = nullptr;
-  const int32_t engine = decode_engine(q_dtype, cache_dtype, head_size, num_heads / num_kv_heads);
-  if (mp > 1 || balanced) {
-    const size_t need = pa_decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_size,
-                                                 max_seq_len, partition_size);
-    if (!workspace || workspace_bytes < need)
-      return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
-                  workspace ? workspace_bytes : (size_t)0);
-    const size_t n = balanced ? (size_t)pa::kMaxBalancedWorkers * 2 * (num_heads / num_kv_heads)
-                              : (size_t)num_seqs * num_heads * mp;
-    part_o = (float*)workspace;
-    part_ml = (float*)((char*)workspace + align256(n * head_size * sizeof(float)));
-    if (balanced) {
-      a_merges = (int32_t*)((char*)part_ml + align256(n * 2 * sizeof(float)));
-      a_cuts = (int32_t*)((char*)a_merges +
-                          align256((size_t)pa::kMaxBalancedWorkers * 2 * sizeof(int32_t)));
-      const int32_t w = balanced_workers_for_device(engine);
-      if (w <= 0) return fail(PA_ERR_HIP, "cannot query the device's compute units");
-      workers = (w / num_kv_heads) * num_kv_heads;
-      if (workers < num_kv_heads) workers = num_kv_heads;
-    }
-  }
-  pa::DecodeArgs a{};
-  a.out = out; a.query = query; a.q_dtype = q_dtype;
-  a.num_seqs = num_seqs; a.num_heads = num_heads; a.head_size = head_size;
-  a.k_cache = k_cache; a.v_cache = v_cache; a.cache_dtype = cache_dtype;
-  a.num_blocks = num_blocks; a.block_size = block_size; a.num_kv_heads = num_kv_heads;
-  a.block_tables = block_tables; a.max_blocks_per_seq = max_blocks_per_seq;
-  a.seq_lens = seq_lens; a.max_seq_len = max_seq_len;
-  a.scale = scale; a.k_scale = k_scale; a.v_scale = v_scale;
-  a.partition_blocks = mp > 1 ? partition_size / block_size : 0;
-  a.max_parts = (int32_t)mp;
-  a.part_o = part_o; a.part_ml = part_ml;
-  a.num_waves = decode_waves_override();
-  a.balanced_workers = workers;
-  a.merges = a_merges;
-  a.cuts = a_cuts;
-  a.engine = engine;
-  a.stream = (hipStream_t)stream;
-  hipError_t e;
-  if (cache_dtype == PA_F32) e = pa::decode_f32(a);
-  else if (cache_dtype == PA_BF16) e = pa::decode_bf16(a);
-  else e = pa::decode_fp8(a);
-  return hip_result(e, "pa_decode");
+                  float v_scale, int32_t partition_size, int32_t flags, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+  return pa::decode_call(out, query, q_dtype, num_seqs, num_heads, head_size, k_cache, v_cache,
+                     cache_dtype, num_blocks, block_size, num_kv_heads, block_tables,
+                     max_blocks_per_seq, seq_lens, max_seq_len, scale, k_scale, v_scale,
+                     partition_size, flags, workspace, workspace_bytes, stream, "pa_decode");
 }
 
 int32_t pa_prefill_chunk(void* out, const void* query, int32_t q_dtype, int32_t num_tokens,
@@ -367,6 +445,14 @@ int32_t pa_prefill_chunk(void* out, const void* query, int32_t q_dtype, int32_t 
   if (num_tokens == 0 || num_chunks == 0) return ok();
   if (!out || !query || !query_start_loc || !block_tables || !seq_lens)
     return fail(PA_ERR_INVALID, "a device array argument is NULL");
+  if (int32_t r = check_align(out, 16, "out")) return r;
+  if (int32_t r = check_align(query, 16, "query")) return r;
+  if (int32_t r = check_align(query_start_loc, 4, "query_start_loc")) return r;
+  if (int32_t r = check_align(block_tables, 4, "block_tables")) return r;
+  if (int32_t r = check_align(seq_lens, 4, "seq_lens")) return r;
+  if (num_chunks > kMaxGridYZ || num_kv_heads > kMaxGridYZ)
+    return fail(PA_ERR_INVALID, "%d chunks / %d KV heads exceed the grid's %lld", num_chunks,
+                num_kv_heads, (long long)kMaxGridYZ);
   pa::PrefillArgs a{};
   a.out = out; a.query = query; a.q_dtype = q_dtype;
   a.num_tokens = num_tokens; a.num_heads = num_heads; a.head_size = head_size;

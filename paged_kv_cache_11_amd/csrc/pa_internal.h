@@ -18,6 +18,10 @@ inline int dtype_bytes(int32_t dt) { return dt == PA_F32 ? 4 : dt == PA_BF16 ? 2
 // balanced decode holds two partial states per wavefront.
 constexpr int kMaxBalancedWorkers = 4096;
 
+// What a launcher returns for a shape it has no kernel for (the C ABI maps
+// it, and only it, to PA_ERR_UNSUPPORTED).
+constexpr hipError_t kNotInstantiated = hipErrorNotSupported;
+
 struct CacheWriteArgs {
   const void* key;
   const void* value;
@@ -69,6 +73,7 @@ struct DecodeArgs {
   int32_t num_waves;         // wavefronts per workgroup; 0 = chosen from the partition size
   int32_t balanced_workers;  // > 0: balanced split over this many wavefronts (multiple of Hkv)
   int32_t engine;            // balanced split: kEngineValu or kEngineMfma (where compiled)
+  int32_t read_once;         // 1: no block is read twice in the call (evict-first loads)
   hipStream_t stream;
 };
 
@@ -98,7 +103,7 @@ hipError_t cache_write(const CacheWriteArgs& a);
 hipError_t move_blocks(const MoveBlocksArgs& a);
 
 // Decode launchers, one per (query, cache) dtype pair; each dispatches on
-// head_size, block_size and group size.  Return hipErrorInvalidValue for a
+// head_size, block_size and group size.  Return kNotInstantiated for a
 // shape that was not instantiated.
 hipError_t decode_f32(const DecodeArgs& a);
 hipError_t decode_bf16(const DecodeArgs& a);
@@ -107,6 +112,20 @@ bool decode_supported(int32_t q_dtype, int32_t cache_dtype, int head_size, int b
                       int group);
 
 hipError_t prefill(const PrefillArgs& a);
+
+// Devices the library keeps per-device state for (ids 0 .. kMaxDevices-1).
+constexpr int kMaxDevices = 64;
+
+// Host validation, workspace carving and launch of a decode call (the body
+// of pa_decode; `who` names the entry point in error messages).
+int32_t decode_call(void* out, const void* query, int32_t q_dtype, int32_t num_seqs,
+                    int32_t num_heads, int32_t head_size, const void* k_cache,
+                    const void* v_cache, int32_t cache_dtype, int32_t num_blocks,
+                    int32_t block_size, int32_t num_kv_heads, const int32_t* block_tables,
+                    int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t max_seq_len,
+                    float scale, float k_scale, float v_scale, int32_t partition_size,
+                    int32_t flags, void* workspace, size_t workspace_bytes, void* stream,
+                    const char* who);
 bool prefill_supported(int32_t q_dtype, int32_t cache_dtype, int head_size, int block_size,
                        int group);
 

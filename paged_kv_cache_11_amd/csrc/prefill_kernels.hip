@@ -429,7 +429,7 @@ static hipError_t prefill_group(const PrefillArgs& a) {
     case 2: return launch_prefill<KV, BS, 2>(a);
     case 4: return launch_prefill<KV, BS, 4>(a);
     case 8: return launch_prefill<KV, BS, 8>(a);
-    default: return hipErrorInvalidValue;
+    default: return kNotInstantiated;
   }
 }
 
@@ -440,7 +440,7 @@ static hipError_t prefill_block(const PrefillArgs& a) {
     case 32: return prefill_group<KV, 32>(a);
     case 64: return prefill_group<KV, 64>(a);
     case 128: return prefill_group<KV, 128>(a);
-    default: return hipErrorInvalidValue;
+    default: return kNotInstantiated;
   }
 }
 

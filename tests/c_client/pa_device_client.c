@@ -124,7 +124,8 @@ int main(void) {
   ws_bytes = pa_decode_workspace_size(3, HQ, HKV, D, 100, 32);
   if (ws_bytes > 0 && !hip_ok(hipMalloc(&ws, ws_bytes), "hipMalloc")) return 1;
   if (!pa_ok(pa_decode(dout, dq, PA_F32, 3, HQ, D, kpool, vpool, PA_F32, NB, BS, HKV, dtables, MAXB,
-                       dlens, 100, 0.125f, 1.0f, 1.0f, 32, ws, ws_bytes, NULL), "pa_decode split-K"))
+                       dlens, 100, 0.125f, 1.0f, 1.0f, 32, PA_DECODE_READ_ONCE, ws, ws_bytes, NULL),
+             "pa_decode split-K"))
     return 1;
   if (!hip_ok(hipMemcpy(out1, dout, sizeof(float) * 3 * HQ * D, hipMemcpyDeviceToHost), "hipMemcpy"))
     return 1;
@@ -155,7 +156,8 @@ int main(void) {
         !hip_ok(hipMemcpy(dq, q2, sizeof(q2), hipMemcpyHostToDevice), "hipMemcpy"))
       return 1;
     if (!pa_ok(pa_decode(dout, dq, PA_F32, 2, HQ, D, kpool, vpool, PA_F32, NB, BS, HKV, dtables, MAXB,
-                         dlens, 101, 0.125f, 1.0f, 1.0f, 0, NULL, 0, NULL), "pa_decode"))
+                         dlens, 101, 0.125f, 1.0f, 1.0f, 0, PA_DECODE_SHARED, NULL, 0, NULL),
+               "pa_decode"))
       return 1;
     if (!hip_ok(hipMemcpy(out2, dout, sizeof(out2), hipMemcpyDeviceToHost), "hipMemcpy")) return 1;
     hipFree(dcow);

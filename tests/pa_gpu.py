@@ -34,8 +34,10 @@ def gpu_pool(b: wl.PagedBatch):
 
 
 def gpu_fill(b: wl.PagedBatch, kp, vp, sel=slice(None), chunk=1 << 16):
-    """Write the batch's tokens (optionally a selection) with pa_cache_write."""
+    """Write the batch's tokens (optionally a selection) with pa_cache_write,
+    after the host check of their slots."""
     k_all, v_all, s_all = b.k[sel], b.v[sel], b.slot_mapping[sel]
+    pa.validate_slots(s_all, int(kp.shape[0]), int(kp.shape[2]))
     for a in range(0, len(s_all), chunk):
         k = wl.storage_tensor(k_all[a:a + chunk], b.kv_src_dtype).to(DEV)
         v = wl.storage_tensor(v_all[a:a + chunk], b.kv_src_dtype).to(DEV)
@@ -84,16 +86,22 @@ def query_f64(qt) -> np.ndarray:
     return qt.float().cpu().numpy().astype(np.float64)
 
 
+ENGINE_FLAG = {None: 0, "valu": pa.PA_DECODE_ENGINE_VALU, "mfma": pa.PA_DECODE_ENGINE_MFMA}
+
+
 def run_decode(b: wl.PagedBatch, kp, vp, qt, partition_size=None, seq_lens=None, tables=None,
-               max_seq_len=None):
+               max_seq_len=None, flags=0):
+    """pa_decode on the batch (or other lengths / tables), after the host
+    check of every table entry and length the call will read."""
     lens = b.seq_lens if seq_lens is None else seq_lens
     tab = b.block_tables if tables is None else tables
+    msl = int(lens.max()) if max_seq_len is None else max_seq_len
+    pa.validate_decode(tab, lens, msl, int(kp.shape[0]), int(kp.shape[2]))
     out = torch.empty_like(qt)
     ps = b.partition_size if partition_size is None else partition_size
     pa.pa_decode(out, qt, kp, vp, torch.from_numpy(np.ascontiguousarray(tab)).to(DEV),
-                 torch.from_numpy(np.ascontiguousarray(lens)).to(DEV),
-                 int(lens.max()) if max_seq_len is None else max_seq_len,
-                 b.scale, b.k_scale, b.v_scale, ps)
+                 torch.from_numpy(np.ascontiguousarray(lens)).to(DEV), msl,
+                 b.scale, b.k_scale, b.v_scale, ps, flags=flags)
     torch.cuda.synchronize()
     return out.float().cpu().numpy().astype(np.float64)
 

@@ -58,7 +58,7 @@ def _decode(**kw):
     a = dict(out=P, query=P, q_dtype=pa.PA_BF16, num_seqs=4, num_heads=32, head_size=128,
              k_cache=P, v_cache=P, cache_dtype=pa.PA_BF16, num_blocks=100, block_size=16,
              num_kv_heads=8, block_tables=P, max_blocks_per_seq=8, seq_lens=P, max_seq_len=128,
-             scale=0.1, k_scale=1.0, v_scale=1.0, partition_size=0, workspace=None,
+             scale=0.1, k_scale=1.0, v_scale=1.0, partition_size=0, flags=0, workspace=None,
              workspace_bytes=0, stream=None)
     a.update(kw)
     return pa.load().pa_decode(*a.values())
@@ -81,6 +81,18 @@ def _decode(**kw):
     (dict(partition_size=pa.PA_PARTITION_BALANCED), pa.PA_ERR_WORKSPACE),
     (dict(partition_size=-2), pa.PA_ERR_INVALID),
     (dict(out=None), pa.PA_ERR_INVALID),
+    # flags: unknown bits, contradictory hints, two engines, an engine not built
+    (dict(flags=0x10), pa.PA_ERR_INVALID),
+    (dict(flags=pa.PA_DECODE_READ_ONCE | pa.PA_DECODE_SHARED), pa.PA_ERR_INVALID),
+    (dict(flags=pa.PA_DECODE_ENGINE_VALU | pa.PA_DECODE_ENGINE_MFMA), pa.PA_ERR_INVALID),
+    (dict(flags=pa.PA_DECODE_ENGINE_MFMA, head_size=64, max_seq_len=128), pa.PA_ERR_UNSUPPORTED),
+    # misaligned arrays (the kernels move 16-byte vectors)
+    (dict(query=ctypes.c_void_p(24)), pa.PA_ERR_INVALID),
+    (dict(out=ctypes.c_void_p(40)), pa.PA_ERR_INVALID),
+    (dict(block_tables=ctypes.c_void_p(18)), pa.PA_ERR_INVALID),
+    (dict(k_cache=ctypes.c_void_p(8)), pa.PA_ERR_INVALID),
+    # fixed partitions put sequences on a grid axis of at most 65535
+    (dict(num_seqs=70000), pa.PA_ERR_INVALID),
 ])
 def test_decode_rejects_bad_host_arguments(kw, code):
     assert _decode(**kw) == code
@@ -108,6 +120,15 @@ def test_cache_write_and_copy_validation():
     assert lib.pa_copy_blocks(P, P, pa.PA_BF16, 10, 16, 8, 128, None, 0, None) == pa.PA_OK
     assert lib.pa_copy_blocks(P, P, pa.PA_BF16, 10, 16, 8, 128, None, 3, None) == pa.PA_ERR_INVALID
     assert lib.pa_copy_blocks(None, P, pa.PA_BF16, 10, 16, 8, 128, P, 3, None) == pa.PA_ERR_INVALID
+    # misaligned key / value / slot_mapping / block_mapping
+    assert lib.pa_cache_write(ctypes.c_void_p(8), P, pa.PA_BF16, 2, P, P, pa.PA_BF16, 10, 16, 8,
+                              128, P, 1.0, 1.0, None) == pa.PA_ERR_INVALID
+    assert lib.pa_cache_write(P, ctypes.c_void_p(20), pa.PA_BF16, 2, P, P, pa.PA_BF16, 10, 16, 8,
+                              128, P, 1.0, 1.0, None) == pa.PA_ERR_INVALID
+    assert lib.pa_cache_write(P, P, pa.PA_BF16, 2, P, P, pa.PA_BF16, 10, 16, 8, 128,
+                              ctypes.c_void_p(12), 1.0, 1.0, None) == pa.PA_ERR_INVALID
+    assert lib.pa_copy_blocks(P, P, pa.PA_BF16, 10, 16, 8, 128, ctypes.c_void_p(4), 3,
+                              None) == pa.PA_ERR_INVALID
 
 
 def test_prefill_validation():
@@ -120,3 +141,9 @@ def test_prefill_validation():
     bad = list(args)
     bad[5] = 96
     assert lib.pa_prefill_chunk(*bad) == pa.PA_ERR_UNSUPPORTED
+    bad = list(args)
+    bad[1] = ctypes.c_void_p(8)  # misaligned query
+    assert lib.pa_prefill_chunk(*bad) == pa.PA_ERR_INVALID
+    bad = list(args)
+    bad[7] = 70000  # chunks on a grid axis of at most 65535
+    assert lib.pa_prefill_chunk(*bad) == pa.PA_ERR_INVALID

@@ -83,6 +83,35 @@ def test_cache_write_fp8_quantise_edges_and_padding(src):
     assert ok_k and ok_v
 
 
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_cache_write_skips_slots_past_the_pool(kv):
+    """Slots at or past num_blocks * block_size are skipped like padding:
+    the whole NaN-poisoned pool equals the oracle's write of the other
+    tokens, so no byte inside the pools changes for them (and the kernel
+    forms no address past them).  The host check names the first one."""
+    rng = np.random.default_rng(5)
+    nb, Hkv, bs, D = 6, 2, 16, 128
+    T = 30
+    k = rng.standard_normal((T, Hkv, D)).astype(np.float32)
+    v = rng.standard_normal((T, Hkv, D)).astype(np.float32)
+    slots = rng.permutation(nb * bs)[:T].astype(np.int64)
+    past = [2, 11, 29]
+    slots[past] = [nb * bs, nb * bs + 5, 1 << 40]
+    scale = 0.02 if kv == "fp8" else 1.0
+    b = wl.PagedBatch("past_pool", Hkv, Hkv, D, bs, nb, "bf16", "bf16", kv, 0.1, k[:1], k, v,
+                      slots, np.array([1], np.int32), np.zeros((1, 1), np.int32),
+                      k_scale=scale, v_scale=scale)
+    with pytest.raises(pa.PagedAttentionError, match=r"slot_mapping\[2\]"):
+        pa.validate_slots(slots, nb, bs)
+    kp, vp = G.gpu_pool(b)
+    pa.pa_cache_write(wl.storage_tensor(k, "bf16").to(G.DEV), wl.storage_tensor(v, "bf16").to(G.DEV),
+                      kp, vp, torch.from_numpy(slots).to(G.DEV), scale, scale)
+    torch.cuda.synchronize()
+    inside = np.setdiff1d(np.arange(T), past)
+    okp, ovp = G.oracle_pool(b, sel=inside)
+    assert G.raw_equal(kp, okp) and G.raw_equal(vp, ovp)
+
+
 def test_cache_write_zero_tokens_is_noop():
     b = wl.tiny_decode()
     kp, vp = G.gpu_pool(b)

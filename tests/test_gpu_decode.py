@@ -45,13 +45,26 @@ def test_decode_tiny_fp32():
         assert np.array_equal(got[0, h], v0[h // 4].astype(np.float64))
 
 
+_refs = {}
+
+
+def _full_ref(name, b, okp, ovp, q64):
+    """The oracle over every sequence of a workload, computed once."""
+    if name not in _refs:
+        _refs.clear()
+        _refs[name] = G.oracle_decode(b, okp, ovp, q64)
+    return _refs[name]
+
+
+@pytest.mark.parametrize("flags", [pa.PA_DECODE_READ_ONCE, 0])
 @pytest.mark.parametrize("ps", [BAL, 512, 0, 256])
-def test_decode_llama3_8b_shape_bf16(ps):
+def test_decode_llama3_8b_shape_bf16(ps, flags):
+    """Every sequence and head of the Llama-3-8B-shape workload, in every
+    partition mode, with and without the read-once hint."""
     b, kp, vp, okp, ovp, qt, q64 = _setup("llama3_8b_decode_bf16")
-    got = G.run_decode(b, kp, vp, qt, partition_size=ps)
-    seqs = range(b.num_seqs) if ps in (BAL, 512) else range(0, b.num_seqs, 8)
-    ref = G.oracle_decode(b, okp, ovp, q64, seqs=seqs)
-    G.assert_close(got, ref, "bf16", f"llama3-8b decode, partition {ps}", rows=list(seqs))
+    got = G.run_decode(b, kp, vp, qt, partition_size=ps, flags=flags)
+    ref = _full_ref("llama3", b, okp, ovp, q64)
+    G.assert_close(got, ref, "bf16", f"llama3-8b decode, partition {ps}, flags {flags}")
 
 
 def test_decode_long_context_split_k():
@@ -67,13 +80,14 @@ def test_decode_long_context_split_k():
     G.assert_close(bal, ref, "bf16", "long-context, balanced split")
 
 
-@pytest.mark.parametrize("ps", [512, BAL])
-def test_decode_shared_prefix_matches_private_copies(ps):
+@pytest.mark.parametrize("ps,flags", [(512, pa.PA_DECODE_SHARED), (BAL, pa.PA_DECODE_SHARED),
+                                      (BAL, 0)])
+def test_decode_shared_prefix_matches_private_copies(ps, flags):
+    """All 256 forks of the 2048-token shared prefix against the oracle."""
     b, kp, vp, okp, ovp, qt, q64 = _setup("shared_prefix_bf16")
-    got = G.run_decode(b, kp, vp, qt, partition_size=ps)
-    seqs = list(range(0, b.num_seqs, 16))
-    ref = G.oracle_decode(b, okp, ovp, q64, seqs=seqs)
-    G.assert_close(got, ref, "bf16", "shared-prefix decode", rows=seqs)
+    got = G.run_decode(b, kp, vp, qt, partition_size=ps, flags=flags)
+    ref = _full_ref("shared_prefix", b, okp, ovp, q64)
+    G.assert_close(got, ref, "bf16", f"shared-prefix decode, partition {ps}, flags {flags}")
     # Give sequences 0..3 private copies of the shared prefix blocks: outputs
     # are bit-identical (arithmetic order depends on logical positions only).
     free = np.setdiff1d(np.arange(b.num_blocks), b.block_tables[b.block_tables >= 0])
@@ -86,7 +100,7 @@ def test_decode_shared_prefix_matches_private_copies(ps):
         tables[s, :n_pref] = new
     pa.pa_copy_blocks(kp, vp, torch.tensor(pairs, dtype=torch.int64, device=G.DEV))
     torch.cuda.synchronize()
-    priv = G.run_decode(b, kp, vp, qt, partition_size=ps, tables=tables)
+    priv = G.run_decode(b, kp, vp, qt, partition_size=ps, tables=tables, flags=flags)
     assert np.array_equal(priv[:4], got[:4])
 
 
@@ -216,11 +230,10 @@ def _shape_batch(Hq, Hkv, D, bs, kv, lens, seed):
     (32, 8, 16, "fp8"), (16, 2, 32, "fp8"), (32, 8, 64, "bf16"), (64, 8, 128, "fp8"),
     (32, 8, 128, "bf16"),
 ])
-def test_decode_balanced_engines(engine, Hq, Hkv, bs, kv, monkeypatch):
+def test_decode_balanced_engines(engine, Hq, Hkv, bs, kv):
     """Both engines of the balanced split (vector ALU and matrix cores) on
     head size 128, groups of 4 and 8, with lengths that end inside blocks,
     inside 16-key groups and on block edges, and a one-token sequence."""
-    monkeypatch.setenv("PA_DECODE_ENGINE", engine)
     lens = [1, 15, 16, 17, 31, 33, 47, 500, 1000, 2049, 63, 64]
     b = _shape_batch(Hq, Hkv, 128, bs, kv, lens, seed=Hq + 7 * bs + (kv == "fp8"))
     kp, vp = G.gpu_pool(b)
@@ -228,19 +241,22 @@ def test_decode_balanced_engines(engine, Hq, Hkv, bs, kv, monkeypatch):
     okp, ovp = G.oracle_pool(b)
     qt = G.query_tensor(b)
     ref = G.oracle_decode(b, okp, ovp, G.query_f64(qt))
-    got = G.run_decode(b, kp, vp, qt, partition_size=BAL)
+    got = G.run_decode(b, kp, vp, qt, partition_size=BAL, flags=G.ENGINE_FLAG[engine])
     G.assert_close(got, ref, kv, f"{engine} engine {Hq}/{Hkv} bs{bs} {kv}")
+    # The read-once hint changes the loads' cache policy only.
+    once = G.run_decode(b, kp, vp, qt, partition_size=BAL,
+                        flags=G.ENGINE_FLAG[engine] | pa.PA_DECODE_READ_ONCE)
+    assert np.array_equal(once, got)
 
 
 @pytest.mark.parametrize("engine", ["valu", "mfma"])
 @pytest.mark.parametrize("Hq,Hkv,bs,kv,S", [(32, 8, 16, "bf16", 600), (64, 8, 32, "fp8", 600),
                                             (16, 2, 64, "bf16", 600), (32, 8, 16, "bf16", 1500)])
-def test_decode_balanced_many_sequences(engine, Hq, Hkv, bs, kv, S, monkeypatch):
+def test_decode_balanced_many_sequences(engine, Hq, Hkv, bs, kv, S):
     """More sequences than workers per KV head (the reduce then works from
     per-worker merge tasks), and more than one batch of the workers' length
     scans (1024): mostly short sequences, some empty, some long enough to
     span several workers."""
-    monkeypatch.setenv("PA_DECODE_ENGINE", engine)
     rng = np.random.default_rng(Hq + bs + S)
     lens = rng.integers(1, 200, S)
     lens[rng.choice(S, S // 15, replace=False)] = 0
@@ -251,7 +267,8 @@ def test_decode_balanced_many_sequences(engine, Hq, Hkv, bs, kv, S, monkeypatch)
     G.gpu_fill(b, kp, vp)
     okp, ovp = G.oracle_pool(b)
     qt = G.query_tensor(b)
-    got = G.run_decode(b, kp, vp, qt, partition_size=BAL)
+    got = G.run_decode(b, kp, vp, qt, partition_size=BAL,
+                       flags=G.ENGINE_FLAG[engine] | pa.PA_DECODE_READ_ONCE)
     ref = G.oracle_decode(b, okp, ovp, G.query_f64(qt))
     assert np.all(got[lens == 0] == 0)
     G.assert_close(got, ref, kv, f"balanced, {len(lens)} sequences, {engine}")
@@ -273,22 +290,19 @@ def one_long_sequence():
 
 
 @pytest.mark.parametrize("engine,ps", [("mfma", BAL), ("valu", BAL), (None, 512)])
-def test_decode_one_very_long_sequence(one_long_sequence, engine, ps, monkeypatch):
+def test_decode_one_very_long_sequence(one_long_sequence, engine, ps):
     b, kp, vp, qt, ref = one_long_sequence
-    if engine is not None:
-        monkeypatch.setenv("PA_DECODE_ENGINE", engine)
-    got = G.run_decode(b, kp, vp, qt, partition_size=ps)
+    got = G.run_decode(b, kp, vp, qt, partition_size=ps,
+                       flags=G.ENGINE_FLAG[engine] | pa.PA_DECODE_READ_ONCE)
     G.assert_close(got, ref, "bf16", f"one 50,003-token sequence, {engine or 'default'} engine, ps {ps}")
 
 
 @pytest.mark.parametrize("scale", [-0.07, 0.0])
 @pytest.mark.parametrize("engine,ps", [("mfma", BAL), ("valu", BAL), (None, 64), (None, 0)])
-def test_decode_negative_and_zero_scale(scale, engine, ps, monkeypatch):
+def test_decode_negative_and_zero_scale(scale, engine, ps):
     """A negative score scale (the softmax then favours the smallest q·k) and
     a zero one (every key weighs the same, the output is the mean of V), on
     both balanced engines and the partitioned path, fp8 cache."""
-    if engine is not None:
-        monkeypatch.setenv("PA_DECODE_ENGINE", engine)
     b = _shape_batch(32, 8, 128, 16, "fp8", [1, 17, 300, 1000, 64], seed=23)
     b.scale = scale
     kp, vp = G.gpu_pool(b)
@@ -296,5 +310,5 @@ def test_decode_negative_and_zero_scale(scale, engine, ps, monkeypatch):
     okp, ovp = G.oracle_pool(b)
     qt = G.query_tensor(b)
     ref = G.oracle_decode(b, okp, ovp, G.query_f64(qt))
-    got = G.run_decode(b, kp, vp, qt, partition_size=ps)
+    got = G.run_decode(b, kp, vp, qt, partition_size=ps, flags=G.ENGINE_FLAG[engine])
     G.assert_close(got, ref, "fp8", f"decode scale {scale}, {engine or 'default'} engine, ps {ps}")
