@@ -281,6 +281,28 @@ int32_t pa_decode(void* out, const void* query, int32_t q_dtype,
                   size_t workspace_bytes, void* stream);
 
 /*
+ * pa_decode_no_alloc — pa_decode for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same arguments, meaning and results as pa_decode
+ * without workspace / workspace_bytes: the split-K partials live in a
+ * static device array of PA_DECODE_NO_ALLOC_SCRATCH_BYTES that every GPU the
+ * library runs on holds until the process ends.  A split that needs more
+ * (pa_decode_workspace_size) is refused with PA_ERR_WORKSPACE before
+ * anything is enqueued.  No call allocates or frees memory.  All calls on
+ * one GPU share its array: calls that overlap on one GPU (other streams,
+ * other threads) race and must be serialised by the caller.
+ */
+#define PA_DECODE_NO_ALLOC_SCRATCH_BYTES (48u * 1024u * 1024u)
+int32_t pa_decode_no_alloc(void* out, const void* query, int32_t q_dtype,
+                           int32_t num_seqs, int32_t num_heads, int32_t head_size,
+                           const void* k_cache, const void* v_cache, int32_t cache_dtype,
+                           int32_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                           const int32_t* block_tables, int32_t max_blocks_per_seq,
+                           const int32_t* seq_lens, int32_t max_seq_len,
+                           float scale, float k_scale, float v_scale,
+                           int32_t partition_size, int32_t flags, void* stream);
+
+/*
  * pa_prefill_chunk — causal attention for chunks of prompt tokens whose K/V
  * are already in the paged cache.
  *

@@ -51,6 +51,9 @@ _SIGNATURES = {
     "pa_prefill_chunk": ([_c_p, _c_p, _c_int, _c_int, _c_int, _c_int, _c_p, _c_int, _c_int, _c_p,
                           _c_p, _c_int, _c_int, _c_int, _c_int, _c_p, _c_int, _c_p, _c_f, _c_f,
                           _c_f, _c_p], _c_int),
+    "pa_decode_no_alloc": ([_c_p, _c_p, _c_int, _c_int, _c_int, _c_int, _c_p, _c_p, _c_int, _c_int,
+                            _c_int, _c_int, _c_p, _c_int, _c_p, _c_int, _c_f, _c_f, _c_f, _c_int,
+                            _c_int, _c_p], _c_int),
     # host-side validation of the data arrays (host pointers)
     "pa_validate_decode": ([_c_p, _c_int, _c_int, _c_p, _c_int, _c_int, _c_int, _c_p], _c_int),
     "pa_validate_prefill": ([_c_p, _c_int, _c_int, _c_int, _c_p, _c_int, _c_p, _c_int, _c_int,
@@ -242,6 +245,24 @@ def pa_decode(out, query, k_cache, v_cache, block_tables, seq_lens, max_seq_len:
                             int(block_tables.shape[1]), _ptr(seq_lens), int(max_seq_len),
                             float(scale), float(k_scale), float(v_scale), int(partition_size),
                             int(flags), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def pa_decode_no_alloc(out, query, k_cache, v_cache, block_tables, seq_lens, max_seq_len: int,
+                       scale: float, k_scale: float = 1.0, v_scale: float = 1.0,
+                       partition_size: int = 0, stream=None, flags: int = 0) -> None:
+    """pa_decode whose split-K partials live in the library's static
+    per-device scratch (no workspace, no allocation); calls on one GPU must
+    not overlap."""
+    nb, hkv, bs, d = _pool_dims(k_cache, v_cache)
+    S, H = int(query.shape[0]), int(query.shape[1])
+    if _validating():
+        validate_decode(block_tables, seq_lens, max_seq_len, nb, bs)
+    _check(load().pa_decode_no_alloc(_ptr(out), _ptr(query), dtype_code(query), S, H, d,
+                                     _ptr(k_cache), _ptr(v_cache), dtype_code(k_cache), nb, bs,
+                                     hkv, _ptr(block_tables), int(block_tables.shape[1]),
+                                     _ptr(seq_lens), int(max_seq_len), float(scale),
+                                     float(k_scale), float(v_scale), int(partition_size),
+                                     int(flags), _stream(stream)))
 
 
 # --- host-side validation ---------------------------------------------------
