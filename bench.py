@@ -338,35 +338,68 @@ def row_measurements(dev, iters=20, groups=ROW_GROUPS):
         torch.cuda.empty_cache()
 
     if "shared_prefix" in groups:
-        # Shared prefix: 256 forks of a 2040-token prefix -> 256 copy-on-write
-        # block copies, then decode.
-        b = wl.shared_prefix_decode(prefix_len=2040)
-        sets = _gpu_pools(b, dev)
-        pairs = torch.from_numpy(b.copy_pairs).to(dev)
-        blk_bytes = 2 * b.num_kv_heads * b.block_size * b.head_size * 2
-        us = _time_us(lambda i: pa.pa_copy_blocks(sets[0][0], sets[0][1], pairs), iters)
-        rows["copy_blocks_cow_256"] = {"us": round(us, 2), "pairs": len(b.copy_pairs),
-                                       "bytes_read_written": 2 * len(b.copy_pairs) * blk_bytes,
-                                       "gbs": round(2 * len(b.copy_pairs) * blk_bytes / us / 1e3, 1)}
-        q = wl.storage_tensor(b.q, b.q_dtype).to(dev)
-        out = torch.empty_like(q)
-        tb, ln = torch.from_numpy(b.block_tables).to(dev), torch.from_numpy(b.seq_lens).to(dev)
-        ws = torch.empty(pa.pa_decode_workspace_size(b.num_seqs, b.num_heads, b.num_kv_heads,
-                                                     b.head_size, b.max_seq_len, -1),
-                         dtype=torch.uint8, device=dev)
-        us = _time_us(lambda i: pa.pa_decode(out, q, sets[0][0], sets[0][1], tb, ln, b.max_seq_len,
-                                             b.scale, partition_size=-1, workspace=ws,
-                                             flags=pa.PA_DECODE_SHARED), iters)
-        logical = b.decode_kv_bytes()
-        unique = (int(np.unique(b.block_tables[b.block_tables >= 0]).size) * b.block_size
-                  * b.kv_bytes_per_token())
-        rows["shared_prefix_decode"] = {"us": round(us, 2), "logical_kv_bytes": logical,
-                                        "unique_kv_bytes": unique,
-                                        "effective_gbs_logical": round(logical / us / 1e3, 1),
-                                        "gbs_unique": round(unique / us / 1e3, 1),
-                                        "tokens_per_s": round(b.num_seqs / us * 1e6, 1)}
-        del sets
-        torch.cuda.empty_cache()
+        # Shared prefix: 256 forks of one prefix (config 4): the literal
+        # 2048-token prefix (no copy-on-write), the 2040-token variant whose
+        # partly filled last prefix block every fork copies first (256
+        # pairs; 127 blocks stay shared), and the 2048-token prefix in a
+        # pool 4x the blocks in use (a serving pool sized to memory).  Three
+        # copies of the pools are rotated so calls read HBM, not the 256 MB
+        # last-level cache.  Each row times pa_decode_shared_prefix (prefix
+        # once per KV head on the matrix cores + suffixes + merge) beside
+        # pa_decode on the same tables with the sharing hint.
+        for tag, prefix_len, pool_factor in (("c4", 2048, 1.25), ("c4_cow", 2040, 1.25),
+                                             ("c4_pool4x", 2048, 4.0)):
+            b = wl.shared_prefix_decode(prefix_len=prefix_len, pool_factor=pool_factor)
+            sets = _gpu_pools(b, dev, copies=N_SETS)
+            pairs = torch.from_numpy(b.copy_pairs).to(dev)
+            blk_bytes = 2 * b.num_kv_heads * b.block_size * b.head_size * 2
+            us_copy = _time_us(lambda i: pa.pa_copy_blocks(sets[i % N_SETS][0], sets[i % N_SETS][1],
+                                                           pairs), iters)
+            q = wl.storage_tensor(b.q, b.q_dtype).to(dev)
+            out = torch.empty_like(q)
+            tb, ln = torch.from_numpy(b.block_tables).to(dev), torch.from_numpy(b.seq_lens).to(dev)
+            shared = (prefix_len // b.block_size) * b.block_size
+            ws_sp = torch.empty(pa.pa_decode_shared_prefix_workspace_size(
+                b.num_seqs, b.num_heads, b.num_kv_heads, b.head_size, shared),
+                dtype=torch.uint8, device=dev)
+            ws = torch.empty(pa.pa_decode_workspace_size(b.num_seqs, b.num_heads, b.num_kv_heads,
+                                                         b.head_size, b.max_seq_len, -1),
+                             dtype=torch.uint8, device=dev)
+
+            def sp(i):
+                kc, vc = sets[i % N_SETS]
+                pa.pa_decode_shared_prefix(out, q, kc, vc, tb, ln, b.max_seq_len, shared, b.scale,
+                                           workspace=ws_sp, flags=pa.PA_DECODE_READ_ONCE)
+
+            def dec(flags):
+                return lambda i: pa.pa_decode(out, q, sets[i % N_SETS][0], sets[i % N_SETS][1], tb,
+                                              ln, b.max_seq_len, b.scale, partition_size=-1,
+                                              workspace=ws, flags=flags)
+
+            us_sp = _time_us(sp, iters)
+            us_dec = _time_us(dec(pa.PA_DECODE_SHARED), iters)
+            logical = b.decode_kv_bytes()
+            unique = (int(np.unique(b.block_tables[b.block_tables >= 0]).size) * b.block_size
+                      * b.kv_bytes_per_token())
+            row = {"us": round(us_sp, 2), "prefix_len": prefix_len, "shared_tokens": shared,
+                   "forks": b.num_seqs, "pool_blocks": b.num_blocks,
+                   "unique_kv_bytes": unique, "logical_kv_bytes": logical,
+                   "gbs_unique": round(unique / us_sp / 1e3, 1),
+                   "pct_hbm_peak_unique": round(100 * unique / us_sp / 1e3 / HBM_PEAK_GBS, 2),
+                   "effective_gbs_logical": round(logical / us_sp / 1e3, 1),
+                   "tokens_per_s": round(b.num_seqs / us_sp * 1e6, 1),
+                   "pa_decode_shared_hint_us": round(us_dec, 2),
+                   "copy_on_write": {"pairs": len(b.copy_pairs), "us": round(us_copy, 2),
+                                     "bytes_read_written": 2 * len(b.copy_pairs) * blk_bytes}}
+            if tag == "c4_pool4x":
+                # The hints on shared tables: none (ordinary loads), and the
+                # read-once hint misapplied (evict-first loads of shared lines).
+                row["pa_decode_no_hint_us"] = round(_time_us(dec(0), iters), 2)
+                row["pa_decode_read_once_hint_us"] = round(
+                    _time_us(dec(pa.PA_DECODE_READ_ONCE), iters), 2)
+            rows[f"shared_prefix_{tag}"] = row
+            del sets, ws, ws_sp
+            torch.cuda.empty_cache()
 
     if "mixed_fp8" in groups:
         # Mixed fp8 step (70B shape): cache write of the step's new tokens,

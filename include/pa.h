@@ -281,6 +281,49 @@ int32_t pa_decode(void* out, const void* query, int32_t q_dtype,
                   size_t workspace_bytes, void* stream);
 
 /*
+ * pa_decode_shared_prefix — pa_decode for a batch whose sequences all begin
+ * with the same prefix_len tokens held in the same physical blocks.
+ *
+ * [LIB] §4.2 item 2 and [DEEP] §3.1: parallel samples forked from one
+ * prompt share the prompt's physical blocks (prefix sharing; copy-on-write
+ * only for a block that changes).  pa_decode reads those blocks once per
+ * sequence; here the attention to the shared prefix is computed once per
+ * KV head for all the sequences' query heads together, as a dense product
+ * on the matrix cores (S^T = K Q^T and O^T = V^T P^T over the prefix keys,
+ * cut into splits across the chip), each sequence's own tokens past the
+ * prefix run through the balanced split (from token prefix_len, with the
+ * K/V reuse hints of `flags` as in pa_decode), and a log-sum-exp merge joins
+ * the two.  The result is the same attention as pa_decode on the same
+ * arguments (within the bf16 rounding of the probabilities).
+ *
+ * Arguments as pa_decode, plus
+ *   prefix_len   tokens every sequence shares: a multiple of block_size,
+ *                0 <= prefix_len <= every seq_lens[s]; the shared blocks are
+ *                read from row 0 of block_tables, and every row must hold
+ *                the same ids in its first prefix_len / block_size entries
+ *                (pa_validate_shared_prefix checks a host copy)
+ *   flags        PA_DECODE_* hints for the suffix part (usually
+ *                PA_DECODE_READ_ONCE: the suffixes are private blocks)
+ *   workspace    >= pa_decode_shared_prefix_workspace_size(...) bytes; needs
+ *                no initialisation
+ * Supported: bf16 queries, bf16 or fp8 cache, head_size 128, groups of 1,
+ * 2, 4 or 8 (a prefix_len of 0 reduces to the balanced pa_decode and takes
+ * its shapes); num_seqs <= 65535.
+ */
+size_t pa_decode_shared_prefix_workspace_size(int32_t num_seqs, int32_t num_heads,
+                                              int32_t num_kv_heads, int32_t head_size,
+                                              int32_t prefix_len);
+int32_t pa_decode_shared_prefix(void* out, const void* query, int32_t q_dtype,
+                                int32_t num_seqs, int32_t num_heads, int32_t head_size,
+                                const void* k_cache, const void* v_cache, int32_t cache_dtype,
+                                int32_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                                const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                const int32_t* seq_lens, int32_t max_seq_len,
+                                int32_t prefix_len, float scale, float k_scale, float v_scale,
+                                int32_t flags, void* workspace, size_t workspace_bytes,
+                                void* stream);
+
+/*
  * pa_decode_no_alloc — pa_decode for callers that cannot allocate device
  * memory (code under HIP graph capture, tight serving loops, harnesses that
  * forbid hipMalloc).  Same arguments, meaning and results as pa_decode
@@ -505,6 +548,9 @@ int32_t pa_bm_num_cached_blocks(const pa_block_manager* bm);
  *   seq_lens entry; its table entries as for decode.
  * pa_validate_slots: every slot is negative (padding) or inside the pool
  *   (< num_blocks * block_size), and no slot repeats.
+ * pa_validate_shared_prefix: every sequence holds at least prefix_len
+ *   tokens (a multiple of block_size) and its first prefix_len / block_size
+ *   table entries equal those of row 0, which are pool blocks.
  * pa_validate_block_pairs: every (src, dst) pair of block_mapping
  *   [num_pairs][2] names blocks inside the source (src_num_blocks) and
  *   destination (dst_num_blocks) pools, destinations are distinct, and, with
@@ -521,6 +567,10 @@ int32_t pa_validate_prefill(const int32_t* query_start_loc, int32_t num_chunks,
                             int64_t* bad_index);
 int32_t pa_validate_slots(const int64_t* slot_mapping, int32_t num_tokens, int32_t num_blocks,
                           int32_t block_size, int64_t* bad_index);
+int32_t pa_validate_shared_prefix(const int32_t* block_tables, int32_t num_seqs,
+                                  int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                  int32_t prefix_len, int32_t num_blocks, int32_t block_size,
+                                  int64_t* bad_index);
 int32_t pa_validate_block_pairs(const int64_t* block_mapping, int32_t num_pairs,
                                 int32_t src_num_blocks, int32_t dst_num_blocks,
                                 int32_t same_pool, int64_t* bad_index);

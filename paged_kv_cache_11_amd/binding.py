@@ -54,12 +54,18 @@ _SIGNATURES = {
     "pa_decode_no_alloc": ([_c_p, _c_p, _c_int, _c_int, _c_int, _c_int, _c_p, _c_p, _c_int, _c_int,
                             _c_int, _c_int, _c_p, _c_int, _c_p, _c_int, _c_f, _c_f, _c_f, _c_int,
                             _c_int, _c_p], _c_int),
+    "pa_decode_shared_prefix_workspace_size": ([_c_int, _c_int, _c_int, _c_int, _c_int], _c_sz),
+    "pa_decode_shared_prefix": ([_c_p, _c_p, _c_int, _c_int, _c_int, _c_int, _c_p, _c_p, _c_int,
+                                 _c_int, _c_int, _c_int, _c_p, _c_int, _c_p, _c_int, _c_int, _c_f,
+                                 _c_f, _c_f, _c_int, _c_p, _c_sz, _c_p], _c_int),
     # host-side validation of the data arrays (host pointers)
     "pa_validate_decode": ([_c_p, _c_int, _c_int, _c_p, _c_int, _c_int, _c_int, _c_p], _c_int),
     "pa_validate_prefill": ([_c_p, _c_int, _c_int, _c_int, _c_p, _c_int, _c_p, _c_int, _c_int,
                              _c_p], _c_int),
     "pa_validate_slots": ([_c_p, _c_int, _c_int, _c_int, _c_p], _c_int),
     "pa_validate_block_pairs": ([_c_p, _c_int, _c_int, _c_int, _c_int, _c_p], _c_int),
+    "pa_validate_shared_prefix": ([_c_p, _c_int, _c_int, _c_p, _c_int, _c_int, _c_int, _c_p],
+                                  _c_int),
     # host block manager
     "pa_bm_create": ([_c_int, _c_int], _c_p),
     "pa_bm_destroy": ([_c_p], None),
@@ -265,6 +271,38 @@ def pa_decode_no_alloc(out, query, k_cache, v_cache, block_tables, seq_lens, max
                                      int(flags), _stream(stream)))
 
 
+def pa_decode_shared_prefix_workspace_size(num_seqs, num_heads, num_kv_heads, head_size,
+                                           prefix_len) -> int:
+    return int(load().pa_decode_shared_prefix_workspace_size(num_seqs, num_heads, num_kv_heads,
+                                                             head_size, prefix_len))
+
+
+def pa_decode_shared_prefix(out, query, k_cache, v_cache, block_tables, seq_lens,
+                            max_seq_len: int, prefix_len: int, scale: float, k_scale: float = 1.0,
+                            v_scale: float = 1.0, workspace=None, stream=None,
+                            flags: int = PA_DECODE_READ_ONCE) -> None:
+    """pa_decode for sequences that share their first prefix_len tokens
+    (the same blocks, read from table row 0): the prefix attention once per
+    KV head for all sequences on the matrix cores, the suffixes through the
+    balanced split, a log-sum-exp merge of the two."""
+    import torch
+
+    nb, hkv, bs, d = _pool_dims(k_cache, v_cache)
+    S, H = int(query.shape[0]), int(query.shape[1])
+    if _validating():
+        validate_decode(block_tables, seq_lens, max_seq_len, nb, bs)
+        validate_shared_prefix(block_tables, seq_lens, prefix_len, nb, bs)
+    need = pa_decode_shared_prefix_workspace_size(S, H, hkv, d, prefix_len)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=query.device)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(load().pa_decode_shared_prefix(
+        _ptr(out), _ptr(query), dtype_code(query), S, H, d, _ptr(k_cache), _ptr(v_cache),
+        dtype_code(k_cache), nb, bs, hkv, _ptr(block_tables), int(block_tables.shape[1]),
+        _ptr(seq_lens), int(max_seq_len), int(prefix_len), float(scale), float(k_scale),
+        float(v_scale), int(flags), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
 # --- host-side validation ---------------------------------------------------
 # PA_VALIDATE=1 in the environment makes every device call of this binding
 # copy its index arrays to the host and check them first (a debug mode: it
@@ -323,6 +361,17 @@ def validate_slots(slot_mapping, num_blocks: int, block_size: int) -> None:
     s = _host(slot_mapping, np.int64).reshape(-1)
     _validated(load().pa_validate_slots(s.ctypes.data, s.size, int(num_blocks), int(block_size),
                                         None))
+
+
+def validate_shared_prefix(block_tables, seq_lens, prefix_len: int, num_blocks: int,
+                           block_size: int) -> None:
+    import numpy as np
+
+    t = _host(block_tables, np.int32)
+    ln = _host(seq_lens, np.int32).reshape(-1)
+    _validated(load().pa_validate_shared_prefix(t.ctypes.data, ln.size, t.shape[1],
+                                                ln.ctypes.data, int(prefix_len), int(num_blocks),
+                                                int(block_size), None))
 
 
 def validate_block_pairs(block_mapping, src_num_blocks: int, dst_num_blocks: int,

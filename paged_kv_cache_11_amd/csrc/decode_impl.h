@@ -610,6 +610,7 @@ __global__ __launch_bounds__(kMaxDecodeWaves * kWave) void decode_kernel(
 constexpr int kBalancedMinTokens = 256;  // fewest tokens a worker is given
 
 
+
 __device__ __forceinline__ int nblocks_of(int L, int bs) { return (L + bs - 1) / bs; }
 
 // Sequence lengths are read kScanChunks chunks of 64 (one per lane) at a
@@ -617,12 +618,16 @@ __device__ __forceinline__ int nblocks_of(int L, int bs) { return (L + bs - 1) /
 // then costs one memory round trip per 1024 sequences, not one per 64.
 constexpr int kScanChunks = 16;
 
+// Lengths count from token `skip` of each sequence (0: the whole sequence;
+// the suffix past a shared prefix otherwise).
 __device__ __forceinline__ void load_len_batch(const int32_t* seq_lens, int num_seqs, int c0,
-                                               int lane, int bs, int (&nb)[kScanChunks]) {
+                                               int lane, int bs, int skip,
+                                               int (&nb)[kScanChunks]) {
 #pragma unroll
   for (int b = 0; b < kScanChunks; ++b) {
     const int s = c0 + b * kWave + lane;
-    nb[b] = s < num_seqs ? seq_lens[s] : 0;
+    nb[b] = s < num_seqs ? seq_lens[s] - skip : 0;
+    nb[b] = nb[b] > 0 ? nb[b] : 0;
   }
 #pragma unroll
   for (int b = 0; b < kScanChunks; ++b) nb[b] = nblocks_of(nb[b], bs);
@@ -647,11 +652,11 @@ __device__ __forceinline__ int wave_sum(int v) {
 
 // Total blocks of all sequences (wavefront-uniform result).
 __device__ __forceinline__ int64_t total_blocks(const int32_t* seq_lens, int num_seqs, int bs,
-                                                int lane) {
+                                                int skip, int lane) {
   int t = 0;  // per-lane partial sums stay far below 2^31
   for (int c0 = 0; c0 < num_seqs; c0 += kScanChunks * kWave) {
     int nb[kScanChunks];
-    load_len_batch(seq_lens, num_seqs, c0, lane, bs, nb);
+    load_len_batch(seq_lens, num_seqs, c0, lane, bs, skip, nb);
 #pragma unroll
     for (int b = 0; b < kScanChunks; ++b) t += nb[b];
   }
@@ -661,11 +666,12 @@ __device__ __forceinline__ int64_t total_blocks(const int32_t* seq_lens, int num
 // The sequence whose blocks hold flattened position x, and the flattened
 // position of its first block (wavefront-uniform).
 __device__ __forceinline__ void locate_block(const int32_t* seq_lens, int num_seqs, int bs,
-                                             int64_t x, int lane, int& s_out, int64_t& base_out) {
+                                             int skip, int64_t x, int lane, int& s_out,
+                                             int64_t& base_out) {
   int64_t base = 0;
   for (int c0 = 0; c0 < num_seqs; c0 += kScanChunks * kWave) {
     int nb[kScanChunks];
-    load_len_batch(seq_lens, num_seqs, c0, lane, bs, nb);
+    load_len_batch(seq_lens, num_seqs, c0, lane, bs, skip, nb);
 #pragma unroll
     for (int b = 0; b < kScanChunks; ++b) {
       if (c0 + b * kWave >= num_seqs) break;
@@ -747,7 +753,7 @@ __global__ __launch_bounds__(kMaxDecodeWaves * kWave) void decode_balanced_kerne
     const void* __restrict__ k_cache, const void* __restrict__ v_cache,
     const int32_t* __restrict__ block_tables, const int32_t* __restrict__ seq_lens, int num_seqs,
     int max_blocks_per_seq, int num_kv_heads, int workers_per_head, float qk_scale_log2,
-    float v_scale, int sub_shift, int read_once_hint) {
+    float v_scale, int sub_shift, int read_once_hint, SuffixStates sx) {
   using WA = WaveAttn<KV, QT, D, BS, G>;
   constexpr int EPL = WA::EPL, RPL = WA::RPL;
   using OT = QT;
@@ -757,7 +763,7 @@ __global__ __launch_bounds__(kMaxDecodeWaves * kWave) void decode_balanced_kerne
   if (vw >= workers_per_head) return;
   const int num_heads = num_kv_heads * G;
 
-  const int64_t T = total_blocks(seq_lens, num_seqs, BS, lane);
+  const int64_t T = total_blocks(seq_lens, num_seqs, BS, sx.skip, lane);
   const int W = effective_workers(T, workers_per_head, BS);
   // The caller declared that no block is read twice: evict-first loads.
   const bool read_once = read_once_hint != 0;
@@ -768,13 +774,15 @@ __global__ __launch_bounds__(kMaxDecodeWaves * kWave) void decode_balanced_kerne
   if (start >= end) return;
   int s;
   int64_t base;
-  locate_block(seq_lens, num_seqs, BS, start, lane, s, base);
+  locate_block(seq_lens, num_seqs, BS, sx.skip, start, lane, s, base);
+  // With a skip, the table row starts at the first block past it.
+  const int tbl_skip = sx.skip / (BS << sub_shift);
 
   WA A;
   A.init(lane, qk_scale_log2);
   int64_t pos = start;
   while (pos < end && s < num_seqs) {
-    const int L = seq_lens[s];
+    const int L = max(seq_lens[s] - sx.skip, 0);
     const int nblk = nblocks_of(L, BS);
     const int64_t seg_end = base + nblk;
     if (nblk > 0) {
@@ -782,12 +790,13 @@ __global__ __launch_bounds__(kMaxDecodeWaves * kWave) void decode_balanced_kerne
       const int b_hi = (int)((end < seg_end ? end : seg_end) - base);
       A.reset();
       A.q.load(query, (int64_t)s * num_heads + (int64_t)g * G, D, A.col);
+      const int32_t* row = block_tables + (int64_t)s * max_blocks_per_seq + tbl_skip;
       if (read_once)
-        A.template stream<true>(k_cache, v_cache, block_tables + (int64_t)s * max_blocks_per_seq,
-                                g, num_kv_heads, b_lo, b_hi - b_lo, 1, L, sub_shift);
+        A.template stream<true>(k_cache, v_cache, row, g, num_kv_heads, b_lo, b_hi - b_lo, 1, L,
+                                sub_shift);
       else
-        A.template stream<false>(k_cache, v_cache, block_tables + (int64_t)s * max_blocks_per_seq,
-                                 g, num_kv_heads, b_lo, b_hi - b_lo, 1, L, sub_shift);
+        A.template stream<false>(k_cache, v_cache, row, g, num_kv_heads, b_lo, b_hi - b_lo, 1, L,
+                                 sub_shift);
       float l_h[G];
       A.merge_rows(l_h);
       const bool whole = b_lo == 0 && b_hi == nblk;
@@ -808,19 +817,22 @@ __global__ __launch_bounds__(kMaxDecodeWaves * kWave) void decode_balanced_kerne
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         if (h % RPL != A.row) continue;
-        if (whole) {
+        if (whole && !sx.acc) {
 #pragma unroll
           for (int e = 0; e < EPL; ++e) {
             const float o = l_h[h] > 0.f ? A.acc[h][e] / l_h[h] * v_scale : 0.f;
             store_out<OT>(out, (hq0 + h) * D + A.col * EPL + e, o);
           }
         } else {
-          const int64_t pslot = ((int64_t)worker * 2 + slot) * G + h;
+          // A piece of a cut sequence, or (suffix states kept) a whole one.
+          const int64_t pslot = whole ? hq0 + h : ((int64_t)worker * 2 + slot) * G + h;
+          float* dacc = whole ? sx.acc : part_acc;
+          float* dml = whole ? sx.ml : part_ml;
 #pragma unroll
-          for (int e = 0; e < EPL; ++e) part_acc[pslot * D + A.col * EPL + e] = A.acc[h][e];
+          for (int e = 0; e < EPL; ++e) dacc[pslot * D + A.col * EPL + e] = A.acc[h][e];
           if (A.col == 0) {
-            part_ml[pslot * 2 + 0] = A.m_ref[h];
-            part_ml[pslot * 2 + 1] = l_h[h];
+            dml[pslot * 2 + 0] = A.m_ref[h];
+            dml[pslot * 2 + 1] = l_h[h];
           }
         }
       }
@@ -893,6 +905,56 @@ __global__ __launch_bounds__(D) void balanced_reduce_tasks_kernel(
   merge_cut<OT, D, G>(out, part_acc, part_ml, s, vw, code, h, g, d, num_kv_heads, v_scale);
 }
 
+// The last step of a shared-prefix decode, per (query head h, KV head g,
+// sequence s), one output element per thread: the log-sum-exp merge of the
+// sequence's suffix (its pieces when the balanced split cut it, else the
+// whole-sequence state the suffix mode kept) with the prefix's splits.
+// Every state is unnormalised with its own reference maximum (log2
+// domain); a state with no keys has m = -inf and is skipped.
+template <typename OT, int D, int G>
+__global__ __launch_bounds__(D) void prefix_merge_kernel(
+    void* __restrict__ out, const float* __restrict__ part_acc,
+    const float* __restrict__ part_ml, const int32_t* __restrict__ cuts,
+    const int32_t* __restrict__ seq_lens, int num_seqs, int num_kv_heads, float v_scale,
+    SuffixStates sx, const float* __restrict__ prefix_acc, const float* __restrict__ prefix_ml,
+    int prefix_splits) {
+  const int h = blockIdx.x, g = blockIdx.y, s = blockIdx.z, d = threadIdx.x;
+  const int num_heads = num_kv_heads * G;
+  const int64_t hq = (int64_t)s * num_heads + g * G + h;
+  float M = -INFINITY, num = 0.f, den = 0.f;
+  auto add = [&](float m, float l, float a) {
+    if (m == -INFINITY) return;
+    if (m > M) {
+      const float f = M == -INFINITY ? 0.f : fast_exp2(M - m);
+      num *= f;
+      den *= f;
+      M = m;
+    }
+    const float e = fast_exp2(m - M);
+    num = __builtin_fmaf(e, a, num);
+    den = __builtin_fmaf(e, l, den);
+  };
+  if (seq_lens[s] > sx.skip) {
+    const int va = cuts[2 * ((int64_t)s * num_kv_heads + g) + 0];
+    const int code = cuts[2 * ((int64_t)s * num_kv_heads + g) + 1];
+    const int np = code >> 1, slot0 = code & 1;
+    if (np <= 1) {
+      add(sx.ml[2 * hq], sx.ml[2 * hq + 1], sx.acc[hq * D + d]);
+    } else {
+      for (int p = 0; p < np; ++p) {
+        const int64_t st =
+            ((int64_t)((va + p) * num_kv_heads + g) * 2 + (p == 0 ? slot0 : 0)) * G + h;
+        add(part_ml[2 * st], part_ml[2 * st + 1], part_acc[st * D + d]);
+      }
+    }
+  }
+  for (int c = 0; c < prefix_splits; ++c) {
+    const int64_t st = (int64_t)c * num_seqs * num_heads + hq;
+    add(prefix_ml[2 * st], prefix_ml[2 * st + 1], prefix_acc[st * D + d]);
+  }
+  store_out<OT>(out, hq * D + d, den > 0.f ? num / den * v_scale : 0.f);
+}
+
 // Log-sum-exp merge of the fixed partitions of one (query head, KV head,
 // sequence), one output element per thread: partition p of query head h
 // left (m_p, l_p, o_p) with o_p normalised;
@@ -961,7 +1023,7 @@ hipError_t launch_decode(const DecodeArgs& a) {
                            a.merges, a.cuts, a.query, a.k_cache, a.v_cache, a.block_tables,
                            a.seq_lens,
                            a.num_seqs, a.max_blocks_per_seq, a.num_kv_heads, per_head, qk, v_scale,
-                           a.read_once);
+                           a.read_once, a.suffix);
     }
     if (!mfma)
       hipLaunchKernelGGL((decode_balanced_kernel<KV, QT, D, BS, G>), dim3((unsigned)wg),
@@ -969,10 +1031,16 @@ hipError_t launch_decode(const DecodeArgs& a) {
                          a.merges, a.cuts, a.query, a.k_cache, a.v_cache, a.block_tables,
                          a.seq_lens,
                          a.num_seqs, a.max_blocks_per_seq, a.num_kv_heads, per_head, qk, v_scale,
-                         kSubShift, a.read_once);
+                         kSubShift, a.read_once, a.suffix);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (a.num_seqs <= per_head)
+    if (a.prefix_acc)
+      hipLaunchKernelGGL((prefix_merge_kernel<QT, D, G>),
+                         dim3((unsigned)G, (unsigned)a.num_kv_heads, (unsigned)a.num_seqs), dim3(D),
+                         0, a.stream, a.out, a.part_o, a.part_ml, a.cuts, a.seq_lens, a.num_seqs,
+                         a.num_kv_heads, v_scale, a.suffix, a.prefix_acc, a.prefix_ml,
+                         a.prefix_splits);
+    else if (a.num_seqs <= per_head)
       hipLaunchKernelGGL((balanced_reduce_kernel<QT, D, G>),
                          dim3((unsigned)G, (unsigned)a.num_kv_heads, (unsigned)a.num_seqs), dim3(D),
                          0, a.stream, a.out, a.part_o, a.part_ml, a.cuts, a.seq_lens,

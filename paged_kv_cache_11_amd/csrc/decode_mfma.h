@@ -357,7 +357,7 @@ __global__ __launch_bounds__(kMaxDecodeWaves * kWave, 2) void decode_balanced_mf
     const void* __restrict__ k_cache, const void* __restrict__ v_cache,
     const int32_t* __restrict__ block_tables, const int32_t* __restrict__ seq_lens, int num_seqs,
     int max_blocks_per_seq, int num_kv_heads, int workers_per_head, float qk_scale_log2,
-    float v_scale, int read_once_hint) {
+    float v_scale, int read_once_hint, SuffixStates sx) {
   static_assert(std::is_same<QT, BF16>::value, "bf16 queries");
   using MA = MfmaAttn<KV, BS, G>;
   constexpr int D = kMD;
@@ -369,7 +369,7 @@ __global__ __launch_bounds__(kMaxDecodeWaves * kWave, 2) void decode_balanced_mf
   if (vw >= workers_per_head) return;
   const int num_heads = num_kv_heads * G;
 
-  const int64_t T = total_blocks(seq_lens, num_seqs, MA::UBS, lane);
+  const int64_t T = total_blocks(seq_lens, num_seqs, MA::UBS, sx.skip, lane);
   const int W = effective_workers(T, workers_per_head, MA::UBS);
   // The caller declared that no block is read twice: evict-first loads.
   const bool read_once = read_once_hint != 0;
@@ -380,13 +380,14 @@ __global__ __launch_bounds__(kMaxDecodeWaves * kWave, 2) void decode_balanced_mf
   if (start >= end) return;
   int s;
   int64_t base;
-  locate_block(seq_lens, num_seqs, MA::UBS, start, lane, s, base);
+  locate_block(seq_lens, num_seqs, MA::UBS, sx.skip, start, lane, s, base);
+  const int tbl_skip = sx.skip / BS;  // table entries of the skipped tokens
 
   MA A;
   A.init(lane, qk_scale_log2, vt_lds[wv]);
   int64_t pos = start;
   while (pos < end && s < num_seqs) {
-    const int L = seq_lens[s];
+    const int L = max(seq_lens[s] - sx.skip, 0);
     const int nblk = nblocks_of(L, MA::UBS);  // units of the split
     const int64_t seg_end = base + nblk;
     if (nblk > 0) {
@@ -395,12 +396,11 @@ __global__ __launch_bounds__(kMaxDecodeWaves * kWave, 2) void decode_balanced_mf
       const int64_t hq0 = (int64_t)s * num_heads + (int64_t)g * G;
       A.reset();
       A.load_q(query, hq0);
+      const int32_t* row = block_tables + (int64_t)s * max_blocks_per_seq + tbl_skip;
       if (read_once)
-        A.template stream<true>(k_cache, v_cache, block_tables + (int64_t)s * max_blocks_per_seq,
-                                g, num_kv_heads, b_lo, b_hi - b_lo, L);
+        A.template stream<true>(k_cache, v_cache, row, g, num_kv_heads, b_lo, b_hi - b_lo, L);
       else
-        A.template stream<false>(k_cache, v_cache, block_tables + (int64_t)s * max_blocks_per_seq,
-                                 g, num_kv_heads, b_lo, b_hi - b_lo, L);
+        A.template stream<false>(k_cache, v_cache, row, g, num_kv_heads, b_lo, b_hi - b_lo, L);
       const float l_tot = A.l_total();
       const bool whole = b_lo == 0 && b_hi == nblk;
       const int slot = pos == start ? 0 : 1;
@@ -417,7 +417,7 @@ __global__ __launch_bounds__(kMaxDecodeWaves * kWave, 2) void decode_balanced_mf
       }
       if (A.n < G) {
         const int h = A.n;
-        if (whole) {
+        if (whole && !sx.acc) {
           const float inv = l_tot > 0.f ? v_scale / l_tot : 0.f;
 #pragma unroll
           for (int mb = 0; mb < D / 16; ++mb) {
@@ -427,13 +427,16 @@ __global__ __launch_bounds__(kMaxDecodeWaves * kWave, 2) void decode_balanced_mf
             *(u32x2*)((uint16_t*)out + (hq0 + h) * D + d0) = u32x2{w0, w1};
           }
         } else {
-          const int64_t pslot = ((int64_t)worker * 2 + slot) * G + h;
+          // A piece of a cut sequence, or (suffix states kept) a whole one.
+          const int64_t pslot = whole ? hq0 + h : ((int64_t)worker * 2 + slot) * G + h;
+          float* dacc = whole ? sx.acc : part_acc;
+          float* dml = whole ? sx.ml : part_ml;
 #pragma unroll
           for (int mb = 0; mb < D / 16; ++mb)
-            *(f32x4*)(part_acc + pslot * D + 16 * mb + 4 * A.g4) = A.acc[mb];
+            *(f32x4*)(dacc + pslot * D + 16 * mb + 4 * A.g4) = A.acc[mb];
           if (A.g4 == 0) {
-            part_ml[pslot * 2 + 0] = A.m_ref;
-            part_ml[pslot * 2 + 1] = l_tot;
+            dml[pslot * 2 + 0] = A.m_ref;
+            dml[pslot * 2 + 1] = l_tot;
           }
         }
       }

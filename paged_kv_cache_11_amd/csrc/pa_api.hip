@@ -189,7 +189,8 @@ int32_t pa::decode_call(void* out, const void* query, int32_t q_dtype, int32_t n
                            int32_t max_blocks_per_seq, const int32_t* seq_lens,
                            int32_t max_seq_len, float scale, float k_scale, float v_scale,
                            int32_t partition_size, int32_t flags, void* workspace,
-                           size_t workspace_bytes, void* stream, const char* who) {
+                           size_t workspace_bytes, void* stream, const char* who,
+                           const pa::DecodeExtras* extra) {
   if (int32_t r = check_pool(k_cache, v_cache, cache_dtype, num_blocks, block_size, num_kv_heads,
                              head_size))
     return r;
@@ -281,6 +282,16 @@ int32_t pa::decode_call(void* out, const void* query, int32_t q_dtype, int32_t n
   a.cuts = a_cuts;
   a.engine = engine;
   a.read_once = (flags & PA_DECODE_READ_ONCE) ? 1 : 0;
+  if (extra) {
+    if (!balanced) return fail(PA_ERR_INVALID, "%s: the suffix runs in the balanced split", who);
+    a.suffix = extra->suffix;
+    a.prefix_acc = extra->prefix_acc;
+    a.prefix_ml = extra->prefix_ml;
+    a.prefix_splits = extra->prefix_splits;
+    if (extra->before_launch) {
+      if (int32_t r = extra->before_launch(extra->ctx)) return r;
+    }
+  }
   a.stream = (hipStream_t)stream;
   hipError_t e;
   if (cache_dtype == PA_F32) e = pa::decode_f32(a);
@@ -416,6 +427,127 @@ int32_t pa_decode(void* out, const void* query, int32_t q_dtype, int32_t num_seq
                      cache_dtype, num_blocks, block_size, num_kv_heads, block_tables,
                      max_blocks_per_seq, seq_lens, max_seq_len, scale, k_scale, v_scale,
                      partition_size, flags, workspace, workspace_bytes, stream, "pa_decode");
+}
+
+// Splits of a shared prefix: enough (query tile, KV head, split) workgroups
+// to give every compute unit one, each split a multiple of 128 keys (whole
+// blocks and whole 64-key steps), at most kMaxPrefixSplits.
+constexpr int32_t kMaxPrefixSplits = 16;
+constexpr int32_t kPrefixSplitQuantum = 128;
+
+static int32_t prefix_split_len(int32_t prefix_len, int32_t num_seqs, int32_t group,
+                                int32_t num_kv_heads, int32_t cus) {
+  const int64_t tiles = ceil_div((int64_t)num_seqs * group, 128) * num_kv_heads;
+  const int64_t quanta = ceil_div(prefix_len, kPrefixSplitQuantum);
+  int64_t want = tiles > 0 ? ceil_div(cus > 0 ? cus : 256, tiles) : 1;
+  if (want > kMaxPrefixSplits) want = kMaxPrefixSplits;
+  if (want > quanta) want = quanta;
+  if (want < 1) want = 1;
+  return (int32_t)(ceil_div(quanta, want) * kPrefixSplitQuantum);
+}
+
+size_t pa_decode_shared_prefix_workspace_size(int32_t num_seqs, int32_t num_heads,
+                                              int32_t num_kv_heads, int32_t head_size,
+                                              int32_t prefix_len) {
+  if (num_seqs <= 0 || num_heads <= 0 || num_kv_heads <= 0 || head_size <= 0 ||
+      num_heads % num_kv_heads != 0 || prefix_len < 0)
+    return 0;
+  const size_t bal = pa_decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_size, 0,
+                                              PA_PARTITION_BALANCED);
+  const size_t rows = (size_t)num_seqs * num_heads;
+  int64_t splits = ceil_div(prefix_len, kPrefixSplitQuantum);
+  if (splits > kMaxPrefixSplits) splits = kMaxPrefixSplits;
+  return bal + align256(rows * head_size * 4) + align256(rows * 2 * 4) +
+         align256((size_t)splits * rows * head_size * 4) + align256((size_t)splits * rows * 2 * 4);
+}
+
+int32_t pa_decode_shared_prefix(void* out, const void* query, int32_t q_dtype, int32_t num_seqs,
+                                int32_t num_heads, int32_t head_size, const void* k_cache,
+                                const void* v_cache, int32_t cache_dtype, int32_t num_blocks,
+                                int32_t block_size, int32_t num_kv_heads,
+                                const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                const int32_t* seq_lens, int32_t max_seq_len, int32_t prefix_len,
+                                float scale, float k_scale, float v_scale, int32_t flags,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  if (int32_t r = check_pool(k_cache, v_cache, cache_dtype, num_blocks, block_size, num_kv_heads,
+                             head_size))
+    return r;
+  if (num_seqs < 0) return fail(PA_ERR_INVALID, "num_seqs %d < 0", num_seqs);
+  if (num_heads <= 0 || num_heads % num_kv_heads != 0)
+    return fail(PA_ERR_INVALID, "num_heads %d must be a positive multiple of num_kv_heads %d",
+                num_heads, num_kv_heads);
+  if (prefix_len < 0 || prefix_len % block_size != 0 || prefix_len > max_seq_len)
+    return fail(PA_ERR_INVALID,
+                "prefix_len %d must be a multiple of block_size %d in [0, max_seq_len %d]",
+                prefix_len, block_size, max_seq_len);
+  if (num_seqs > kMaxGridYZ)
+    return fail(PA_ERR_INVALID, "%d sequences exceed the merge grid's %lld", num_seqs,
+                (long long)kMaxGridYZ);
+  const int group = num_heads / num_kv_heads;
+  if (prefix_len > 0 && !pa::prefill_supported(q_dtype, cache_dtype, head_size, block_size, group))
+    return fail(PA_ERR_UNSUPPORTED,
+                "the shared-prefix product is not built for q dtype %d, cache dtype %d, "
+                "head_size %d, block_size %d, group %d",
+                q_dtype, cache_dtype, head_size, block_size, group);
+  if (num_seqs == 0) return ok();
+  const size_t need = pa_decode_shared_prefix_workspace_size(num_seqs, num_heads, num_kv_heads,
+                                                             head_size, prefix_len);
+  if (!workspace || workspace_bytes < need)
+    return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (int32_t r = check_align(workspace, 16, "workspace")) return r;
+  if (!query || !block_tables) return fail(PA_ERR_INVALID, "query / block_tables is NULL");
+  if (int32_t r = check_align(query, 16, "query")) return r;
+  if (int32_t r = check_align(block_tables, 4, "block_tables")) return r;
+  // Carve: the balanced split's workspace, the suffix states, the prefix states.
+  const size_t bal = pa_decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_size, 0,
+                                              PA_PARTITION_BALANCED);
+  const size_t rows = (size_t)num_seqs * num_heads;
+  char* p = (char*)workspace + bal;
+  pa::DecodeExtras ex{};
+  ex.suffix.skip = prefix_len;
+  ex.suffix.acc = (float*)p;
+  p += align256(rows * head_size * 4);
+  ex.suffix.ml = (float*)p;
+  p += align256(rows * 2 * 4);
+  float* pre_acc = (float*)p;
+  int32_t splits = 0;
+  int32_t split_len = 0;
+  if (prefix_len > 0) {
+    split_len = prefix_split_len(prefix_len, num_seqs, group, num_kv_heads, device_cus());
+    splits = (int32_t)ceil_div(prefix_len, split_len);
+  }
+  p += align256((size_t)splits * rows * head_size * 4);
+  float* pre_ml = (float*)p;
+  ex.prefix_acc = pre_acc;
+  ex.prefix_ml = pre_ml;
+  ex.prefix_splits = splits;
+  // The prefix: every sequence's query against the shared blocks of row 0,
+  // enqueued by decode_call once all its checks have passed.
+  pa::PrefillArgs a{};
+  if (splits > 0) {
+    a.query = query; a.q_dtype = q_dtype;
+    a.num_tokens = num_seqs; a.num_heads = num_heads; a.head_size = head_size;
+    a.k_cache = k_cache; a.v_cache = v_cache; a.cache_dtype = cache_dtype;
+    a.num_blocks = num_blocks; a.block_size = block_size; a.num_kv_heads = num_kv_heads;
+    a.block_tables = block_tables; a.max_blocks_per_seq = max_blocks_per_seq;
+    a.scale = scale; a.k_scale = k_scale; a.v_scale = v_scale;
+    a.prefix.acc = pre_acc;
+    a.prefix.ml = pre_ml;
+    a.prefix.split_len = split_len;
+    a.prefix.prefix_len = prefix_len;
+    a.stream = (hipStream_t)stream;
+    ex.before_launch = [](const void* ctx) -> int32_t {
+      return hip_result(pa::prefill(*(const pa::PrefillArgs*)ctx), "pa_decode_shared_prefix");
+    };
+    ex.ctx = &a;
+  }
+  // The suffixes through the balanced split, then the merge.
+  return pa::decode_call(out, query, q_dtype, num_seqs, num_heads, head_size, k_cache, v_cache,
+                         cache_dtype, num_blocks, block_size, num_kv_heads, block_tables,
+                         max_blocks_per_seq, seq_lens, max_seq_len, scale, k_scale, v_scale,
+                         PA_PARTITION_BALANCED, flags, workspace, bal, stream,
+                         "pa_decode_shared_prefix", &ex);
 }
 
 int32_t pa_prefill_chunk(void* out, const void* query, int32_t q_dtype, int32_t num_tokens,

@@ -50,6 +50,19 @@ struct MoveBlocksArgs {
   hipStream_t stream;
 };
 
+// Suffix mode of the balanced kernels (the part of a shared-prefix decode
+// past the prefix): every sequence is walked from token `skip` (a multiple
+// of the pool block size; its table row from entry skip / block size), and
+// when `acc` is set, a sequence a worker holds whole leaves its
+// unnormalised state in acc[s * num_heads + h][D], ml[...][2] instead of
+// its output (cut sequences leave their pieces as usual), for a merge with
+// the prefix's states.
+struct SuffixStates {
+  int skip;
+  float* acc;
+  float* ml;
+};
+
 struct DecodeArgs {
   void* out;
   const void* query;
@@ -74,6 +87,14 @@ struct DecodeArgs {
   int32_t balanced_workers;  // > 0: balanced split over this many wavefronts (multiple of Hkv)
   int32_t engine;            // balanced split: kEngineValu or kEngineMfma (where compiled)
   int32_t read_once;         // 1: no block is read twice in the call (evict-first loads)
+  // Shared-prefix decode: the balanced split runs in suffix mode, and a
+  // merge kernel joins each sequence's suffix state with prefix_splits
+  // prefix states ([(split * num_seqs + s) * num_heads + h][head_size] and
+  // [...][2]) into the output.
+  SuffixStates suffix;
+  const float* prefix_acc;
+  const float* prefix_ml;
+  int32_t prefix_splits;
   hipStream_t stream;
 };
 
@@ -96,6 +117,14 @@ struct PrefillArgs {
   int32_t max_blocks_per_seq;
   const int32_t* seq_lens;
   float scale, k_scale, v_scale;
+  // Prefix mode (acc != nullptr): num_tokens decode queries against the
+  // first prefix_len keys of block_tables row 0, non-causal, in splits of
+  // split_len keys; the splits' states go to acc / ml (see prefill_kernels).
+  struct {
+    float* acc;
+    float* ml;
+    int32_t split_len, prefix_len;
+  } prefix;
   hipStream_t stream;
 };
 
@@ -125,7 +154,19 @@ int32_t decode_call(void* out, const void* query, int32_t q_dtype, int32_t num_s
                     int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t max_seq_len,
                     float scale, float k_scale, float v_scale, int32_t partition_size,
                     int32_t flags, void* workspace, size_t workspace_bytes, void* stream,
-                    const char* who);
+                    const char* who, const struct DecodeExtras* extra = nullptr);
+
+// What a shared-prefix decode adds to the balanced split (see DecodeArgs).
+struct DecodeExtras {
+  SuffixStates suffix;
+  const float* prefix_acc;
+  const float* prefix_ml;
+  int32_t prefix_splits;
+  // Called after every host check passed, before the decode kernels are
+  // enqueued (the shared-prefix product goes first on the stream).
+  int32_t (*before_launch)(const void* ctx);
+  const void* ctx;
+};
 bool prefill_supported(int32_t q_dtype, int32_t cache_dtype, int head_size, int block_size,
                        int group);
 

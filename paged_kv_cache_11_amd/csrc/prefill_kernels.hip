@@ -92,13 +92,29 @@ __device__ __forceinline__ u32x2 lds_tr16(const __bf16* p) {
 
 template <int N> struct Buf { static constexpr int value = N; };
 
-template <typename KV, int BS, int G>
+// The prefix mode of the kernel (attention of many decode queries to one
+// shared prefix): the rows are num_q queries (one per sequence), every row
+// sees every key of the prefix (no causal mask), and the keys are cut into
+// splits of split_len (grid z): split c covers keys c * split_len ..
+// min(prefix_len, (c + 1) * split_len) - 1 of table row 0.  Each split
+// leaves, per (query, head), its unnormalised accumulator and (reference
+// maximum, exponent sum), log2 domain, for a log-sum-exp merge:
+// acc[(c * num_q + q) * num_heads + h][head dim], ml[...][2].
+struct PrefixStates {
+  float* acc;
+  float* ml;
+  int num_q;
+  int split_len;   // a multiple of 128 keys: whole blocks and whole steps
+  int prefix_len;
+};
+
+template <typename KV, int BS, int G, bool kPrefix>
 __global__ __launch_bounds__(kPThreads) void prefill_kernel(
     void* __restrict__ out, const void* __restrict__ query,
     const int32_t* __restrict__ query_start_loc, const void* __restrict__ k_cache,
     const void* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
     int max_blocks_per_seq, const int32_t* __restrict__ seq_lens, int num_kv_heads,
-    float qk_scale_log2, int q_mode, float v_scale) {
+    float qk_scale_log2, int q_mode, float v_scale, PrefixStates ps) {
   constexpr int EB = Elem<KV>::bytes;
   static_assert(kRows % G == 0, "rows hold whole queries");
   // Four LDS buffers, each one step's K tile and V tile (both key rows);
@@ -111,25 +127,42 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(
   const int t = threadIdx.x, lane = t & (kWave - 1), w = t / kWave;
   const int rg = w % kRowGroups, kh = w / kRowGroups;
   const int half = lane / 32;
-  const int qs = query_start_loc[c], n = query_start_loc[c + 1] - qs;
-  const int L = seq_lens[c];
+  // Chunk c: queries qs .. qs+n-1 over its L keys, query i at position
+  // L - n + i.  Prefix mode: split c's L keys (positions relative to the
+  // split's first key, whose table entries start at tbl), every query at
+  // position L - 1.
+  int qs, n, L;
+  const int32_t* tbl;
+  if constexpr (kPrefix) {
+    qs = 0;
+    n = ps.num_q;
+    const int k_lo = c * ps.split_len;
+    L = min(ps.prefix_len - k_lo, ps.split_len);
+    tbl = block_tables + k_lo / BS;
+  } else {
+    qs = query_start_loc[c];
+    n = query_start_loc[c + 1] - qs;
+    L = seq_lens[c];
+    tbl = block_tables + (int64_t)c * max_blocks_per_seq;
+  }
   if (tile * kRows >= n * G) return;
+  const int pos_shift = kPrefix ? L - 1 : L - n;  // position of query i: pos_shift + (kPrefix ? 0 : i)
+  auto position = [&](int i) { return kPrefix ? pos_shift : pos_shift + i; };
   const int q_first = tile * kRows / G;
   const int q_last = min(q_first + kRows / G, n) - 1;
-  const int min_pos = L - n + q_first, max_pos = L - n + q_last;
+  const int min_pos = position(q_first), max_pos = position(q_last);
   const int nsteps = (max_pos + kStep) / kStep;
   const int nblk = (L + BS - 1) / BS;
   const int num_heads = num_kv_heads * G;
-  const int32_t* tbl = block_tables + (int64_t)c * max_blocks_per_seq;
 
   // This lane's row: query qi, head hq.
   const int row = 32 * rg + (lane & 31);
   const int qi = q_first + row / G;
   const int hq = g * G + row % G;
   const bool row_ok = qi < n;
-  const int pos = L - n + qi;
+  const int pos = position(qi);
   // Last position among this wavefront's rows: later tiles are all masked.
-  const int wave_max_pos = L - n + min(q_first + (32 * rg + 31) / G, q_last);
+  const int wave_max_pos = position(min(q_first + (32 * rg + 31) / G, q_last));
 
   // Q^T operand: k-step s holds dims 16 s + 8 half .. +8 of the row.
   bf16x8 qreg[kPD / 16];
@@ -376,6 +409,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(
   }
   __syncthreads();
   if (kh == 1) return;
+  float m_tot;  // the reference the merged state is relative to (-inf: no key)
   {
     const float m1 = mm_lds[rg * kWave + lane], l1 = ml_lds[rg * kWave + lane];
     const float M = fmaxf(m_ref, m1);
@@ -387,11 +421,30 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(
 #pragma unroll
       for (int i = 0; i < 16; ++i)
         oacc[mt][i] = oacc[mt][i] * f0 + mo_lds[(rg * (kPD / 2) + 16 * mt + i) * kWave + lane] * f1;
+    m_tot = M;
   }
 
   // Finish: the two halves of the wave hold the same rows' other keys.
   const float l_tot = l_part + __shfl_xor(l_part, 32, kWave);
   if (!row_ok) return;
+  if constexpr (kPrefix) {
+    // The split's state of this row, unnormalised, for the merge.
+    const int64_t st = ((int64_t)c * n + qi) * num_heads + hq;
+    float* arow = ps.acc + st * kPD;
+#pragma unroll
+    for (int mt = 0; mt < kPD / 32; ++mt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d0 = 32 * mt + q4 * 8 + 4 * half;
+        *(f32x4*)(arow + d0) = f32x4{oacc[mt][4 * q4 + 0], oacc[mt][4 * q4 + 1],
+                                     oacc[mt][4 * q4 + 2], oacc[mt][4 * q4 + 3]};
+      }
+    if (half == 0) {
+      ps.ml[2 * st + 0] = m_tot;
+      ps.ml[2 * st + 1] = l_tot;
+    }
+    return;
+  }
   const float inv = l_tot > 0.f ? v_scale / l_tot : 0.f;
   uint16_t* orow = (uint16_t*)out + ((int64_t)(qs + qi) * num_heads + hq) * kPD;
 #pragma unroll
@@ -405,20 +458,42 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(
     }
 }
 
+// The prefix mode: a.num_tokens queries (one per sequence) against
+// a.prefix.prefix_len keys of table row 0, in a.prefix splits.
+template <typename KV, int BS, int G>
+static hipError_t launch_prefix(const PrefillArgs& a) {
+  const float k_scale = std::is_same<KV, FP8>::value ? a.k_scale : 1.0f;
+  const float qk = a.scale * k_scale * kPLog2e;
+  const int tiles = (a.num_tokens * G + kRows - 1) / kRows;
+  const int splits = (a.prefix.prefix_len + a.prefix.split_len - 1) / a.prefix.split_len;
+  if (tiles == 0 || splits == 0) return hipSuccess;
+  hipLaunchKernelGGL((prefill_kernel<KV, BS, G, true>),
+                     dim3((unsigned)tiles, (unsigned)a.num_kv_heads, (unsigned)splits),
+                     dim3(kPThreads), 0, a.stream, a.out, a.query, a.query_start_loc,
+                     a.k_cache, a.v_cache, a.block_tables, a.max_blocks_per_seq, a.seq_lens,
+                     a.num_kv_heads, qk == 0.f ? 1.f : fabsf(qk),
+                     qk == 0.f ? kQZero : (qk < 0.f ? kQNegate : kQAsIs), 1.0f,
+                     PrefixStates{a.prefix.acc, a.prefix.ml, a.num_tokens, a.prefix.split_len,
+                                  a.prefix.prefix_len});
+  return hipGetLastError();
+}
+
 template <typename KV, int BS, int G>
 static hipError_t launch_prefill(const PrefillArgs& a) {
+  if (a.prefix.acc) return launch_prefix<KV, BS, G>(a);
   const float k_scale = std::is_same<KV, FP8>::value ? a.k_scale : 1.0f;
   const float v_scale = std::is_same<KV, FP8>::value ? a.v_scale : 1.0f;
   // The kernel takes a positive score scale (see kQNegate, kQZero).
   const float qk = a.scale * k_scale * kPLog2e;
   const int tiles = (a.max_query_len * G + kRows - 1) / kRows;
   if (tiles == 0) return hipSuccess;
-  hipLaunchKernelGGL((prefill_kernel<KV, BS, G>),
+  hipLaunchKernelGGL((prefill_kernel<KV, BS, G, false>),
                      dim3((unsigned)tiles, (unsigned)a.num_kv_heads, (unsigned)a.num_chunks),
                      dim3(kPThreads), 0, a.stream, a.out, a.query, a.query_start_loc,
                      a.k_cache, a.v_cache, a.block_tables, a.max_blocks_per_seq, a.seq_lens,
                      a.num_kv_heads, qk == 0.f ? 1.f : fabsf(qk),
-                     qk == 0.f ? kQZero : (qk < 0.f ? kQNegate : kQAsIs), v_scale);
+                     qk == 0.f ? kQZero : (qk < 0.f ? kQNegate : kQAsIs), v_scale,
+                     PrefixStates{});
   return hipGetLastError();
 }
 

@@ -136,6 +136,39 @@ int32_t pa_validate_slots(const int64_t* slot_mapping, int32_t num_tokens, int32
   return good(bad_index);
 }
 
+int32_t pa_validate_shared_prefix(const int32_t* block_tables, int32_t num_seqs,
+                                  int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                  int32_t prefix_len, int32_t num_blocks, int32_t block_size,
+                                  int64_t* bad_index) {
+  if (num_seqs < 0 || max_blocks_per_seq <= 0 || prefix_len < 0 || !pool_ok(num_blocks, block_size))
+    return bad(bad_index, -1, "pa_validate_shared_prefix: bad sizes");
+  if (prefix_len % block_size != 0)
+    return bad(bad_index, -1, "prefix_len %d is not a multiple of block_size %d", prefix_len,
+               block_size);
+  const int64_t np = prefix_len / block_size;
+  if (np > max_blocks_per_seq)
+    return bad(bad_index, -1, "prefix_len %d needs %lld blocks, more than max_blocks_per_seq %d",
+               prefix_len, (long long)np, max_blocks_per_seq);
+  if (num_seqs > 0 && (!block_tables || !seq_lens))
+    return bad(bad_index, -1, "pa_validate_shared_prefix: NULL array");
+  for (int64_t j = 0; j < (num_seqs > 0 ? np : 0); ++j)
+    if (block_tables[j] < 0 || block_tables[j] >= num_blocks)
+      return bad(bad_index, j, "block_tables[0][%lld] = %d is not a block of the %d-block pool",
+                 (long long)j, block_tables[j], num_blocks);
+  for (int64_t s = 0; s < num_seqs; ++s) {
+    if (seq_lens[s] < prefix_len)
+      return bad(bad_index, s, "seq_lens[%lld] = %d is shorter than the shared prefix (%d)",
+                 (long long)s, seq_lens[s], prefix_len);
+    const int32_t* r = block_tables + s * max_blocks_per_seq;
+    for (int64_t j = 0; j < np; ++j)
+      if (r[j] != block_tables[j])
+        return bad(bad_index, s * max_blocks_per_seq + j,
+                   "block_tables[%lld][%lld] = %d differs from row 0's shared block %d",
+                   (long long)s, (long long)j, r[j], block_tables[j]);
+  }
+  return good(bad_index);
+}
+
 int32_t pa_validate_block_pairs(const int64_t* block_mapping, int32_t num_pairs,
                                 int32_t src_num_blocks, int32_t dst_num_blocks,
                                 int32_t same_pool, int64_t* bad_index) {

@@ -207,7 +207,7 @@ def long_context_decode(seed: int = 1237, num_seqs: int = 8, seq_len: int = 3276
 
 
 def shared_prefix_decode(seed: int = 1238, num_forks: int = 256, prefix_len: int = 2048,
-                         max_suffix: int = 512) -> PagedBatch:
+                         max_suffix: int = 512, pool_factor: float = 1.25) -> PagedBatch:
     """Parallel sampling from one shared prefix: 256 sequences forked from a
     2048-token prefix whose blocks every fork shares, then distinct suffixes
     of uniform [0, 512] tokens plus one new decode token each.
@@ -220,6 +220,8 @@ def shared_prefix_decode(seed: int = 1238, num_forks: int = 256, prefix_len: int
     ``copy_pairs`` as (shared block, private block).  With a 2048-token prefix
     at block 16 no prefix block is partial and ``copy_pairs`` is empty; pass
     ``prefix_len=2040`` for the variant where all 256 forks copy.
+    ``pool_factor`` sizes the pool against the blocks in use (1.25 by
+    default; a serving pool sized to memory is several times larger).
     """
     rng = np.random.default_rng(seed)
     Hq, Hkv, D, bs = 32, 8, 128, 16
@@ -231,7 +233,7 @@ def shared_prefix_decode(seed: int = 1238, num_forks: int = 256, prefix_len: int
     # Blocks each fork owns privately: everything past the full prefix blocks.
     own = [(int(L) + bs - 1) // bs - full_prefix for L in seq_lens]
     needed = n_prefix_blocks + sum(own)
-    nb = _pool_blocks(needed)
+    nb = _pool_blocks(needed, pool_factor)
     perm = rng.permutation(nb).astype(np.int32)
     prefix_blocks = perm[:n_prefix_blocks]
     cur = n_prefix_blocks

@@ -147,3 +147,40 @@ def test_prefill_validation():
     bad = list(args)
     bad[7] = 70000  # chunks on a grid axis of at most 65535
     assert lib.pa_prefill_chunk(*bad) == pa.PA_ERR_INVALID
+
+
+def _shared(**kw):
+    a = dict(out=P, query=P, q_dtype=pa.PA_BF16, num_seqs=4, num_heads=32, head_size=128,
+             k_cache=P, v_cache=P, cache_dtype=pa.PA_BF16, num_blocks=100, block_size=16,
+             num_kv_heads=8, block_tables=P, max_blocks_per_seq=8, seq_lens=P, max_seq_len=128,
+             prefix_len=64, scale=0.1, k_scale=1.0, v_scale=1.0, flags=0, workspace=None,
+             workspace_bytes=0, stream=None)
+    a.update(kw)
+    return pa.load().pa_decode_shared_prefix(*a.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(prefix_len=40), pa.PA_ERR_INVALID),          # not whole blocks
+    (dict(prefix_len=144), pa.PA_ERR_INVALID),         # past max_seq_len
+    (dict(prefix_len=-16), pa.PA_ERR_INVALID),
+    (dict(head_size=64), pa.PA_ERR_UNSUPPORTED),        # the prefix product takes head size 128
+    (dict(q_dtype=pa.PA_F32, cache_dtype=pa.PA_F32), pa.PA_ERR_UNSUPPORTED),
+    (dict(num_seqs=70000), pa.PA_ERR_INVALID),
+    (dict(), pa.PA_ERR_WORKSPACE),
+    (dict(workspace=P, workspace_bytes=1000), pa.PA_ERR_WORKSPACE),
+])
+def test_shared_prefix_rejects_bad_host_arguments(kw, code):
+    assert _shared(**kw) == code
+    assert pa.load().pa_last_error()
+
+
+def test_shared_prefix_checks_decode_arguments_before_any_launch():
+    # With a large enough (never touched) workspace, the decode checks still
+    # run before the prefix product is enqueued: contradictory flags fail.
+    need = pa.pa_decode_shared_prefix_workspace_size(4, 32, 8, 128, 64)
+    assert need > pa.pa_decode_workspace_size(4, 32, 8, 128, 128, pa.PA_PARTITION_BALANCED)
+    rc = _shared(workspace=P, workspace_bytes=need,
+                 flags=pa.PA_DECODE_READ_ONCE | pa.PA_DECODE_SHARED)
+    assert rc == pa.PA_ERR_INVALID
+    assert _shared(workspace=P, workspace_bytes=need, out=None) == pa.PA_ERR_INVALID
+    assert _shared(num_seqs=0) == pa.PA_OK

@@ -138,3 +138,22 @@ def test_binding_debug_mode_validates_before_launch(monkeypatch):
     slots = torch.from_numpy(np.array([0, 1, 1], dtype=np.int64))
     with pytest.raises(pa.PagedAttentionError, match=r"slot_mapping\[2\] = 1 repeats"):
         pa.pa_cache_write(torch.zeros((3, 2, 64)), torch.zeros((3, 2, 64)), kp, kp, slots)
+
+
+def test_shared_prefix_tables():
+    b = wl.shared_prefix_decode(prefix_len=2040)
+    shared = 2032  # the partly filled block 127 is each fork's own copy
+    pa.validate_shared_prefix(b.block_tables, b.seq_lens, shared, b.num_blocks, 16)
+    # The copied block differs between forks: 2048 tokens are not shared.
+    assert "differs from row 0" in _err(pa.validate_shared_prefix, b.block_tables, b.seq_lens,
+                                        2048, b.num_blocks, 16)
+    assert "not a multiple" in _err(pa.validate_shared_prefix, b.block_tables, b.seq_lens, 2040,
+                                    b.num_blocks, 16)
+    lens = b.seq_lens.copy()
+    lens[7] = 2000
+    assert "seq_lens[7] = 2000 is shorter" in _err(pa.validate_shared_prefix, b.block_tables,
+                                                   lens, shared, b.num_blocks, 16)
+    t = b.block_tables.copy()
+    t[:, 5] = b.num_blocks + 1
+    assert "block_tables[0][5]" in _err(pa.validate_shared_prefix, t, b.seq_lens, shared,
+                                        b.num_blocks, 16)
