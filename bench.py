@@ -128,7 +128,7 @@ def cpu_baseline(b, budget_s: float = 12.0):
     opg.cache_write(kp, vp, b.kv_dtype, ks, vs, b.kv_src_dtype, b.slot_mapping, b.k_scale,
                     b.v_scale)
     q64 = wl.storage_tensor(b.q, b.q_dtype).float().numpy().astype(np.float64)
-    seqs_done, tokens_read, t0 = 0, 0, time.perf_counter()
+    seqs_done, tokens_read, t0, c0 = 0, 0, time.perf_counter(), time.process_time()
     while seqs_done < b.num_seqs or time.perf_counter() - t0 < budget_s:
         s = seqs_done % b.num_seqs
         opg.paged_decode(q64, kp, vp, b.block_tables, b.seq_lens, b.scale, kv_dtype=b.kv_dtype,
@@ -138,12 +138,70 @@ def cpu_baseline(b, budget_s: float = 12.0):
         if time.perf_counter() - t0 > budget_s:
             break
     dt = time.perf_counter() - t0
+    cpu = time.process_time() - c0
     return {
-        "value": seqs_done / dt, "unit": "tokens/s", "cores": int(blas_threads), "kind": "oracle",
-        "gbs": tokens_read * b.kv_bytes_per_token() / dt / 1e9,
+        "value": seqs_done / dt, "unit": "tokens/s", "cores": round(cpu / dt, 1),
+        "kind": "oracle", "gbs": tokens_read * b.kv_bytes_per_token() / dt / 1e9,
         "sample": f"{seqs_done} sequence decodes of the same workload ({tokens_read} cached tokens "
-                  f"read) in {dt:.1f} s; host has {os.cpu_count()} logical cpus",
+                  f"read) in {dt:.1f} s; cores = process CPU time / wall time ({cpu:.1f} s / "
+                  f"{dt:.1f} s), numpy BLAS pool {blas_threads} threads, host has "
+                  f"{os.cpu_count()} logical cpus",
     }
+
+
+def oracle_rows(budget_s: float = 2.5):
+    """The oracle (test infrastructure) timed on each workload of the path,
+    on a bounded sample of it (about budget_s seconds each): decode of a few
+    sequences of the tiny, Llama-3-8B-shape, long-context, shared-prefix and
+    fp8 70B-shape workloads, and prefill of a slice of the fp8 chunk's
+    queries.  Rates are per sampled unit; cores = CPU time / wall time."""
+    from oracle import paged as opg
+    from paged_kv_cache_11_amd import workloads as wl
+
+    rows = {}
+
+    def pools(b):
+        kp = wl.poisoned_pool(b.num_blocks, b.num_kv_heads, b.block_size, b.head_size, b.kv_dtype)
+        vp = wl.poisoned_pool(b.num_blocks, b.num_kv_heads, b.block_size, b.head_size, b.kv_dtype)
+        ks = wl.storage_bits(wl.storage_tensor(b.k, b.kv_src_dtype))
+        vs = wl.storage_bits(wl.storage_tensor(b.v, b.kv_src_dtype))
+        opg.cache_write(kp, vp, b.kv_dtype, ks, vs, b.kv_src_dtype, b.slot_mapping, b.k_scale,
+                        b.v_scale)
+        return kp, vp
+
+    for name in ("tiny_fp32", "llama3_8b_decode_bf16", "long_context_splitk_bf16",
+                 "shared_prefix_bf16", "mixed_prefill_decode_fp8"):
+        b = wl.make(name)
+        kp, vp = pools(b)
+        q64 = wl.storage_tensor(b.q, b.q_dtype).float().numpy().astype(np.float64)
+        done, toks, t0, c0 = 0, 0, time.perf_counter(), time.process_time()
+        while done < b.num_seqs and (done == 0 or time.perf_counter() - t0 < budget_s):
+            opg.paged_decode(q64, kp, vp, b.block_tables, b.seq_lens, b.scale,
+                             kv_dtype=b.kv_dtype, k_scale=b.k_scale, v_scale=b.v_scale,
+                             seqs=[done])
+            toks += int(b.seq_lens[done])
+            done += 1
+        dt, cpu = time.perf_counter() - t0, time.process_time() - c0
+        rows[name] = {"kind": "oracle", "op": "paged_decode", "sample_seqs": done,
+                      "of_seqs": b.num_seqs, "s": round(dt, 3),
+                      "tokens_per_s": round(done / dt, 2),
+                      "gbs": round(toks * b.kv_bytes_per_token() / dt / 1e9, 4),
+                      "cores": round(cpu / dt, 1)}
+        if name == "mixed_prefill_decode_fp8":
+            # Prefill of the first queries of the 512-query chunk.
+            n = 16
+            qc = wl.storage_tensor(b.chunk_q, "bf16").float().numpy().astype(np.float64)
+            t0, c0 = time.perf_counter(), time.process_time()
+            L = int(b.chunk_seq_lens[0])
+            opg.paged_prefill(qc[:n], np.array([0, n], np.int32), kp, vp, b.chunk_block_tables,
+                              np.array([L - len(qc) + n], np.int32), b.scale, kv_dtype=b.kv_dtype,
+                              k_scale=b.k_scale, v_scale=b.v_scale)
+            dt, cpu = time.perf_counter() - t0, time.process_time() - c0
+            rows[name + "_prefill"] = {"kind": "oracle", "op": "paged_prefill",
+                                       "sample_queries": n, "of_queries": len(qc),
+                                       "s": round(dt, 3), "queries_per_s": round(n / dt, 2),
+                                       "cores": round(cpu / dt, 1)}
+    return rows
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 # PCIe 5.0 x16, one direction: 32 GT/s x 16 lanes, 128b/130b coding.
@@ -186,8 +244,31 @@ def _time_us(fn, iters, warmup=3):
     return a.elapsed_time(b) / iters * 1e3
 
 
+def _kernel_us(fn, iters, warmup=3):
+    """Mean duration of the main decode kernel of fn(i) (one decode call),
+    from HIP events the library records right around that kernel
+    (pa_profile_next_decode)."""
+    import torch
+
+    from paged_kv_cache_11_amd import binding as pa
+
+    for i in range(warmup):
+        fn(i)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(iters)]
+    for e0, e1 in evs:
+        e0.record()
+        e1.record()
+    torch.cuda.synchronize()
+    for i in range(iters):
+        pa.pa_profile_next_decode(*evs[i])
+        fn(i)
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(c) for a, c in evs])) * 1e3
+
+
 ROW_GROUPS = ("long_context", "shared_prefix", "mixed_fp8", "block_sizes", "block_manager",
-              "chunked_prefill", "swap", "prefix_cache")
+              "chunked_prefill", "swap", "prefix_cache", "continuous_batching", "ceiling")
 
 
 def _manager_trace(mgr, lens, samples: int, steps: int, budget_s: float = 1e9):
@@ -446,10 +527,13 @@ def row_measurements(dev, iters=20, groups=ROW_GROUPS):
                                               "bytes_moved": cw_bytes,
                                               "gbs": round(cw_bytes / us_cw / 1e3, 1)}
         us_dec = _time_us(dec, iters)
+        kern_dec = _kernel_us(dec, iters)
         by = b.decode_kv_bytes()
         rows["decode_fp8_70b_shape"] = {"us": round(us_dec, 2), "kv_bytes": by,
                                         "gbs": round(by / us_dec / 1e3, 1),
                                         "pct_hbm_peak": round(100 * by / us_dec / 1e3 / HBM_PEAK_GBS, 2),
+                                        "kernel_us": round(kern_dec, 2),
+                                        "kernel_pct_hbm_peak": round(100 * by / kern_dec / 1e3 / HBM_PEAK_GBS, 2),
                                         "tokens_per_s": round(b.num_seqs / us_dec * 1e6, 1)}
         us_pre = _time_us(pre, iters)
         L, n = int(b.chunk_seq_lens[0]), nq
@@ -534,6 +618,57 @@ def row_measurements(dev, iters=20, groups=ROW_GROUPS):
             "host_link_peak_gbs": link}
         del kd, vd, hk, hv, flat_d, flat_h
         torch.cuda.empty_cache()
+    if "continuous_batching" in groups:
+        # A continuous-batching decode step: 768 sequences of lengths
+        # U[64, 1024], Llama-3-8B shape, balanced split, read-once hint,
+        # three pool copies rotated.  The decode kernel is also timed alone
+        # (library-recorded events around it).
+        b = wl.continuous_batching_decode()
+        sets = _gpu_pools(b, dev, copies=N_SETS)
+        q = wl.storage_tensor(b.q, b.q_dtype).to(dev)
+        out = torch.empty_like(q)
+        tb, ln = torch.from_numpy(b.block_tables).to(dev), torch.from_numpy(b.seq_lens).to(dev)
+        ws = torch.empty(pa.pa_decode_workspace_size(b.num_seqs, b.num_heads, b.num_kv_heads,
+                                                     b.head_size, b.max_seq_len, -1),
+                         dtype=torch.uint8, device=dev)
+
+        def dec(i):
+            pa.pa_decode(out, q, sets[i % N_SETS][0], sets[i % N_SETS][1], tb, ln, b.max_seq_len,
+                         b.scale, partition_size=-1, workspace=ws, flags=pa.PA_DECODE_READ_ONCE)
+
+        us = _time_us(dec, iters)
+        kern = _kernel_us(dec, iters)
+        by = b.decode_kv_bytes()
+        rows["continuous_batching_768"] = {
+            "us": round(us, 2), "kernel_us": round(kern, 2), "seqs": b.num_seqs,
+            "seq_lens": f"U[{int(b.seq_lens.min())}, {int(b.seq_lens.max())}]",
+            "kv_bytes": by, "gbs": round(by / us / 1e3, 1),
+            "pct_hbm_peak": round(100 * by / us / 1e3 / HBM_PEAK_GBS, 2),
+            "kernel_gbs": round(by / kern / 1e3, 1),
+            "tokens_per_s": round(b.num_seqs / us * 1e6, 1)}
+        del sets
+        torch.cuda.empty_cache()
+    if "ceiling" in groups:
+        # The practical HBM ceiling of this access pattern: pa_copy_blocks
+        # over 16384 scattered whole blocks of the headline pool geometry
+        # (bf16, 8 KV heads, block 16: 64 KiB per block for K and V), 1 GiB
+        # read and 1 GiB written per call.
+        Hkv, bs, D = 8, 16, 128
+        nb = 2 * 16384 + 64
+        kp = torch.empty((nb, Hkv, bs, D), dtype=torch.bfloat16, device=dev)
+        vp = torch.empty_like(kp)
+        perm = np.random.default_rng(9).permutation(nb)
+        pairs = torch.from_numpy(np.stack([perm[:16384], perm[16384:32768]], 1)
+                                 .astype(np.int64)).to(dev)
+        us = _time_us(lambda i: pa.pa_copy_blocks(kp, vp, pairs), iters)
+        moved = 16384 * 2 * Hkv * bs * D * 2
+        rows["ceiling_copy_blocks_1gib"] = {
+            "us": round(us, 2), "bytes_read": moved, "bytes_written": moved,
+            "read_gbs": round(moved / us / 1e3, 1),
+            "read_plus_write_gbs": round(2 * moved / us / 1e3, 1),
+            "pct_hbm_peak_read_plus_write": round(100 * 2 * moved / us / 1e3 / HBM_PEAK_GBS, 2)}
+        del kp, vp
+        torch.cuda.empty_cache()
     if "block_manager" in groups:
         rows.update(block_manager_rows())
     if "prefix_cache" in groups:
@@ -572,6 +707,9 @@ def main(argv=None):
     ap.add_argument("--partition-size", type=int, default=-1,
                     help="pa_decode partition_size: -1 balanced split (default), 0 none, or tokens")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--oracle-budget", type=float, default=2.0,
+                    help="seconds of oracle time per workload for cpu_baseline_per_workload "
+                         "(0 skips it)")
     ap.add_argument("--no-rows", action="store_true",
                     help="skip the per-row measurements of the other workloads")
     ap.add_argument("--rows-only", choices=ROW_GROUPS,
@@ -640,15 +778,11 @@ def main(argv=None):
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
-    def step(i, ev=None):
+    def step(i, stream=stream):
         kc, vc = sets[i % N_SETS]
         pa.pa_cache_write(k_new, v_new, kc, vc, slots_new, b.k_scale, b.v_scale, stream=stream)
-        if ev is not None:
-            ev[0].record(stream)
         pa.pa_decode(out, q, kc, vc, tables, lens, b.max_seq_len, b.scale, b.k_scale, b.v_scale,
                      ps, ws, stream=stream, flags=pa.PA_DECODE_READ_ONCE)
-        if ev is not None:
-            ev[1].record(stream)
 
     for i in range(args.warmup):
         step(i)
@@ -660,22 +794,64 @@ def main(argv=None):
     wall = time.perf_counter() - t0
     ms_per_step = wall / args.steps * 1e3
 
-    # Per-call decode durations with HIP events on the launch stream.
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        step(i, evs[i])
-    torch.cuda.synchronize()
-    dec_ms = np.array([a.elapsed_time(c) for a, c in evs])
-    dec_avg_s = float(dec_ms.mean()) / 1e3
-
     kv_bytes = b.decode_kv_bytes()
+    n_calls = max(args.steps, 200)
+
+    # The pa_decode call alone (decode kernel + reduce kernel), back to
+    # back over n_calls calls, HIP events on its stream around the run.
+    def dec_call(i):
+        kc, vc = sets[i % N_SETS]
+        pa.pa_decode(out, q, kc, vc, tables, lens, b.max_seq_len, b.scale, b.k_scale, b.v_scale,
+                     ps, ws, stream=stream, flags=pa.PA_DECODE_READ_ONCE)
+
+    call_us = _time_us(dec_call, n_calls)
+
+    # The dominant kernel alone: pa_profile_next_decode makes the library
+    # record a pair of HIP events right around the decode kernel's launch
+    # (hipExtLaunchKernelGGL, same stream), call after call.
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n_calls)]
+    for e0, e1 in evs:  # create the events
+        e0.record(stream)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    for i in range(n_calls):
+        pa.pa_profile_next_decode(*evs[i])
+        dec_call(i)
+    torch.cuda.synchronize()
+    kern_ms = np.array([a.elapsed_time(c) for a, c in evs])
+    kern_us = float(kern_ms.mean()) * 1e3
+
+    # The same step captured in HIP graphs (one per pool copy; cache write
+    # + decode kernel + reduce kernel), replayed in rotation.
+    graph_ms = None
+    try:
+        graphs = []
+        gs = torch.cuda.Stream()
+        for k in range(N_SETS):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=gs):
+                step(k, stream=torch.cuda.current_stream())
+            graphs.append(g)
+        for i in range(args.warmup):
+            graphs[i % N_SETS].replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            graphs[i % N_SETS].replay()
+        torch.cuda.synchronize()
+        graph_ms = (time.perf_counter() - t0) / args.steps * 1e3
+        del graphs
+    except Exception as e:  # pragma: no cover - reported, not fatal
+        print(f"[bench] graph capture failed: {e}", file=sys.stderr, flush=True)
+
     gbs = kv_bytes / (ms_per_step / 1e3) / 1e9
-    achieved = kv_bytes / dec_avg_s / 1e9
-    print(f"[bench] step {ms_per_step * 1e3:.1f} us, decode call {dec_avg_s * 1e6:.1f} us "
-          f"(p10 {np.percentile(dec_ms, 10) * 1e3:.1f}, p90 {np.percentile(dec_ms, 90) * 1e3:.1f}), "
-          f"{achieved:.0f} GB/s in decode", file=sys.stderr, flush=True)
+    achieved = kv_bytes / (kern_us / 1e6) / 1e9
+    call_gbs = kv_bytes / (call_us / 1e6) / 1e9
+    print(f"[bench] step {ms_per_step * 1e3:.1f} us (graph {graph_ms * 1e3 if graph_ms else -1:.1f}),"
+          f" decode call {call_us:.1f} us, decode kernel {kern_us:.1f} us "
+          f"(p10 {np.percentile(kern_ms, 10) * 1e3:.1f}, p90 {np.percentile(kern_ms, 90) * 1e3:.1f}),"
+          f" {achieved:.0f} GB/s in the kernel", file=sys.stderr, flush=True)
 
     calib = None
     if args.copy_calibration_mib:
@@ -694,6 +870,7 @@ def main(argv=None):
         torch.cuda.empty_cache()
         rows = row_measurements(dev)
     cpu = cpu_baseline(b, args.cpu_budget)
+    oracle_per_workload = oracle_rows(args.oracle_budget) if args.oracle_budget > 0 else None
     tokens_per_s = b.num_seqs / (ms_per_step / 1e3)
     res = {
         "metric": METRIC,
@@ -720,13 +897,22 @@ def main(argv=None):
         "tokens_per_s": round(tokens_per_s, 1),
         "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "roofline": {
-            "kernel": "pa_decode (balanced decode kernel + split-K reduce kernel)",
+            "kernel": "decode_balanced_mfma_kernel (the dominant kernel of pa_decode)",
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": traffic, "avg_us": round(dec_avg_s * 1e6, 2),
+            "traffic": traffic, "avg_us": round(kern_us, 2),
+            "timing": f"mean over {n_calls} launches of HIP events the library records right "
+                      "around the kernel (pa_profile_next_decode, hipExtLaunchKernelGGL) on its "
+                      "stream; achieved = algorithmic K/V bytes / avg_us",
+            "call": {"what": "pa_decode call = decode kernel + reduce kernel, back to back",
+                     "avg_us": round(call_us, 2), "achieved": round(call_gbs, 1),
+                     "frac": round(call_gbs / HBM_PEAK_GBS, 4)},
         },
+        "graph_ms_per_step": round(graph_ms, 5) if graph_ms else None,
         "cpu_baseline": cpu,
     }
+    if oracle_per_workload:
+        res["cpu_baseline_per_workload"] = oracle_per_workload
     if rows:
         res["rows"] = rows
     if calib:

@@ -308,7 +308,7 @@ int32_t pa_decode(void* out, const void* query, int32_t q_dtype,
  *                no initialisation
  * Supported: bf16 queries, bf16 or fp8 cache, head_size 128, groups of 1,
  * 2, 4 or 8 (a prefix_len of 0 reduces to the balanced pa_decode and takes
- * its shapes); num_seqs <= 65535.
+ * its shapes).
  */
 size_t pa_decode_shared_prefix_workspace_size(int32_t num_seqs, int32_t num_heads,
                                               int32_t num_kv_heads, int32_t head_size,
@@ -344,6 +344,18 @@ int32_t pa_decode_no_alloc(void* out, const void* query, int32_t q_dtype,
                            const int32_t* seq_lens, int32_t max_seq_len,
                            float scale, float k_scale, float v_scale,
                            int32_t partition_size, int32_t flags, void* stream);
+
+/*
+ * pa_profile_next_decode — measurement: the next decode call on the calling
+ * thread (pa_decode, pa_decode_no_alloc or pa_decode_shared_prefix) records
+ * start_event immediately before and stop_event immediately after its main
+ * decode kernel on the call's stream (hipExtLaunchKernelGGL), so that the
+ * kernel's own duration can be read with hipEventElapsedTime apart from
+ * the reduce and merge kernels around it.  The events are hipEvent_t
+ * created with timing enabled; they are used once and forgotten, also when
+ * that call fails.  Passing NULL, NULL cancels; one NULL is PA_ERR_INVALID.
+ */
+int32_t pa_profile_next_decode(void* start_event, void* stop_event);
 
 /*
  * pa_prefill_chunk — causal attention for chunks of prompt tokens whose K/V

@@ -58,6 +58,7 @@ _SIGNATURES = {
     "pa_decode_shared_prefix": ([_c_p, _c_p, _c_int, _c_int, _c_int, _c_int, _c_p, _c_p, _c_int,
                                  _c_int, _c_int, _c_int, _c_p, _c_int, _c_p, _c_int, _c_int, _c_f,
                                  _c_f, _c_f, _c_int, _c_p, _c_sz, _c_p], _c_int),
+    "pa_profile_next_decode": ([_c_p, _c_p], _c_int),
     # host-side validation of the data arrays (host pointers)
     "pa_validate_decode": ([_c_p, _c_int, _c_int, _c_p, _c_int, _c_int, _c_int, _c_p], _c_int),
     "pa_validate_prefill": ([_c_p, _c_int, _c_int, _c_int, _c_p, _c_int, _c_p, _c_int, _c_int,
@@ -301,6 +302,15 @@ def pa_decode_shared_prefix(out, query, k_cache, v_cache, block_tables, seq_lens
         dtype_code(k_cache), nb, bs, hkv, _ptr(block_tables), int(block_tables.shape[1]),
         _ptr(seq_lens), int(max_seq_len), int(prefix_len), float(scale), float(k_scale),
         float(v_scale), int(flags), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def pa_profile_next_decode(start_event, stop_event) -> None:
+    """Record these torch.cuda.Event objects (timing enabled, already
+    created by one record()) around the main kernel of the next decode call
+    on this thread; None, None cancels."""
+    h = [ctypes.c_void_p(e.cuda_event) if e is not None else None
+         for e in (start_event, stop_event)]
+    _check(load().pa_profile_next_decode(*h))
 
 
 # --- host-side validation ---------------------------------------------------

@@ -905,20 +905,25 @@ __global__ __launch_bounds__(D) void balanced_reduce_tasks_kernel(
   merge_cut<OT, D, G>(out, part_acc, part_ml, s, vw, code, h, g, d, num_kv_heads, v_scale);
 }
 
-// The last step of a shared-prefix decode, per (query head h, KV head g,
-// sequence s), one output element per thread: the log-sum-exp merge of the
-// sequence's suffix (its pieces when the balanced split cut it, else the
-// whole-sequence state the suffix mode kept) with the prefix's splits.
-// Every state is unnormalised with its own reference maximum (log2
-// domain); a state with no keys has m = -inf and is skipped.
+// The last step of a shared-prefix decode, per (sequence s, KV head g),
+// one output element of one of the G query heads per thread: the
+// log-sum-exp merge of the sequence's suffix (its pieces when the balanced
+// split cut it, else the whole-sequence state the suffix mode kept) with
+// the prefix's splits.  Every state is unnormalised with its own reference
+// maximum (log2 domain); a state with no keys has m = -inf and is skipped.
+// The prefix states, the cut record and the whole-sequence state do not
+// depend on each other, so their loads are issued together; only the
+// pieces of a cut sequence wait for the cut record.
 template <typename OT, int D, int G>
-__global__ __launch_bounds__(D) void prefix_merge_kernel(
+__global__ __launch_bounds__(G * D) void prefix_merge_kernel(
     void* __restrict__ out, const float* __restrict__ part_acc,
     const float* __restrict__ part_ml, const int32_t* __restrict__ cuts,
     const int32_t* __restrict__ seq_lens, int num_seqs, int num_kv_heads, float v_scale,
     SuffixStates sx, const float* __restrict__ prefix_acc, const float* __restrict__ prefix_ml,
     int prefix_splits) {
-  const int h = blockIdx.x, g = blockIdx.y, s = blockIdx.z, d = threadIdx.x;
+  constexpr int kBatch = 4;
+  const int s = blockIdx.x, g = blockIdx.y;
+  const int h = threadIdx.x / D, d = threadIdx.x % D;
   const int num_heads = num_kv_heads * G;
   const int64_t hq = (int64_t)s * num_heads + g * G + h;
   float M = -INFINITY, num = 0.f, den = 0.f;
@@ -934,12 +939,34 @@ __global__ __launch_bounds__(D) void prefix_merge_kernel(
     num = __builtin_fmaf(e, a, num);
     den = __builtin_fmaf(e, l, den);
   };
-  if (seq_lens[s] > sx.skip) {
-    const int va = cuts[2 * ((int64_t)s * num_kv_heads + g) + 0];
-    const int code = cuts[2 * ((int64_t)s * num_kv_heads + g) + 1];
+  const bool has_suffix = seq_lens[s] > sx.skip;
+  int va = 0, code = 0;
+  float wm = -INFINITY, wl = 0.f, wa = 0.f;
+  if (has_suffix) {
+    va = cuts[2 * ((int64_t)s * num_kv_heads + g) + 0];
+    code = cuts[2 * ((int64_t)s * num_kv_heads + g) + 1];
+    wm = sx.ml[2 * hq];  // the whole-sequence state (used if not cut)
+    wl = sx.ml[2 * hq + 1];
+    wa = sx.acc[hq * D + d];
+  }
+  for (int c0 = 0; c0 < prefix_splits; c0 += kBatch) {
+    float m[kBatch], l[kBatch], a[kBatch];
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      const int c = c0 + b < prefix_splits ? c0 + b : prefix_splits - 1;
+      const int64_t st = (int64_t)c * num_seqs * num_heads + hq;
+      m[b] = prefix_ml[2 * st];
+      l[b] = prefix_ml[2 * st + 1];
+      a[b] = prefix_acc[st * D + d];
+    }
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b)
+      if (c0 + b < prefix_splits) add(m[b], l[b], a[b]);
+  }
+  if (has_suffix) {
     const int np = code >> 1, slot0 = code & 1;
     if (np <= 1) {
-      add(sx.ml[2 * hq], sx.ml[2 * hq + 1], sx.acc[hq * D + d]);
+      add(wm, wl, wa);
     } else {
       for (int p = 0; p < np; ++p) {
         const int64_t st =
@@ -947,10 +974,6 @@ __global__ __launch_bounds__(D) void prefix_merge_kernel(
         add(part_ml[2 * st], part_ml[2 * st + 1], part_acc[st * D + d]);
       }
     }
-  }
-  for (int c = 0; c < prefix_splits; ++c) {
-    const int64_t st = (int64_t)c * num_seqs * num_heads + hq;
-    add(prefix_ml[2 * st], prefix_ml[2 * st + 1], prefix_acc[st * D + d]);
   }
   store_out<OT>(out, hq * D + d, den > 0.f ? num / den * v_scale : 0.f);
 }
@@ -1018,16 +1041,16 @@ hipError_t launch_decode(const DecodeArgs& a) {
     if constexpr (kHasMfma<KV, QT, D, G>) mfma = a.engine == kEngineMfma;
     if constexpr (kHasMfma<KV, QT, D, G>) {
       if (mfma)
-        hipLaunchKernelGGL((decode_balanced_mfma_kernel<KV, QT, PBS, G>), dim3((unsigned)wg),
-                           dim3(kMaxDecodeWaves * kWave), 0, a.stream, a.out, a.part_o, a.part_ml,
+        launch_main(a, decode_balanced_mfma_kernel<KV, QT, PBS, G>, dim3((unsigned)wg),
+                           dim3(kMaxDecodeWaves * kWave), a.out, a.part_o, a.part_ml,
                            a.merges, a.cuts, a.query, a.k_cache, a.v_cache, a.block_tables,
                            a.seq_lens,
                            a.num_seqs, a.max_blocks_per_seq, a.num_kv_heads, per_head, qk, v_scale,
                            a.read_once, a.suffix);
     }
     if (!mfma)
-      hipLaunchKernelGGL((decode_balanced_kernel<KV, QT, D, BS, G>), dim3((unsigned)wg),
-                         dim3(kMaxDecodeWaves * kWave), 0, a.stream, a.out, a.part_o, a.part_ml,
+      launch_main(a, decode_balanced_kernel<KV, QT, D, BS, G>, dim3((unsigned)wg),
+                         dim3(kMaxDecodeWaves * kWave), a.out, a.part_o, a.part_ml,
                          a.merges, a.cuts, a.query, a.k_cache, a.v_cache, a.block_tables,
                          a.seq_lens,
                          a.num_seqs, a.max_blocks_per_seq, a.num_kv_heads, per_head, qk, v_scale,
@@ -1036,7 +1059,7 @@ hipError_t launch_decode(const DecodeArgs& a) {
     if (e != hipSuccess) return e;
     if (a.prefix_acc)
       hipLaunchKernelGGL((prefix_merge_kernel<QT, D, G>),
-                         dim3((unsigned)G, (unsigned)a.num_kv_heads, (unsigned)a.num_seqs), dim3(D),
+                         dim3((unsigned)a.num_seqs, (unsigned)a.num_kv_heads), dim3(G * D),
                          0, a.stream, a.out, a.part_o, a.part_ml, a.cuts, a.seq_lens, a.num_seqs,
                          a.num_kv_heads, v_scale, a.suffix, a.prefix_acc, a.prefix_ml,
                          a.prefix_splits);
@@ -1054,9 +1077,9 @@ hipError_t launch_decode(const DecodeArgs& a) {
   }
   const int tiles_per_part = a.partition_blocks << kSubShift;  // 0: whole sequence
   const int nw = a.num_waves > 0 ? a.num_waves : decode_waves(tiles_per_part, a.max_seq_len, BS);
-  hipLaunchKernelGGL((decode_kernel<KV, QT, D, BS, G>),
+  launch_main(a, decode_kernel<KV, QT, D, BS, G>,
                      dim3((unsigned)a.max_parts, (unsigned)a.num_kv_heads, (unsigned)a.num_seqs),
-                     dim3(nw * kWave), 0, a.stream, a.out, a.part_o, a.part_ml, a.query,
+                     dim3(nw * kWave), a.out, a.part_o, a.part_ml, a.query,
                      a.k_cache, a.v_cache, a.block_tables, a.seq_lens, a.max_blocks_per_seq,
                      a.num_kv_heads, tiles_per_part, a.max_parts, qk, v_scale, kSubShift,
                      a.read_once);

@@ -18,6 +18,9 @@ namespace {
 
 thread_local std::string g_last_error;
 
+// Events for the next decode call's main kernel (pa_profile_next_decode).
+thread_local hipEvent_t g_prof_start = nullptr, g_prof_stop = nullptr;
+
 int32_t fail(int32_t code, const char* fmt, ...) {
   char buf[512];
   va_list ap;
@@ -282,6 +285,9 @@ int32_t pa::decode_call(void* out, const void* query, int32_t q_dtype, int32_t n
   a.cuts = a_cuts;
   a.engine = engine;
   a.read_once = (flags & PA_DECODE_READ_ONCE) ? 1 : 0;
+  a.prof_start = g_prof_start;
+  a.prof_stop = g_prof_stop;
+  g_prof_start = g_prof_stop = nullptr;
   if (extra) {
     if (!balanced) return fail(PA_ERR_INVALID, "%s: the suffix runs in the balanced split", who);
     a.suffix = extra->suffix;
@@ -416,6 +422,14 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num
   return align256(n * head_size * sizeof(float)) + align256(n * 2 * sizeof(float));
 }
 
+int32_t pa_profile_next_decode(void* start_event, void* stop_event) {
+  if ((start_event == nullptr) != (stop_event == nullptr))
+    return fail(PA_ERR_INVALID, "pa_profile_next_decode: give both events or neither");
+  g_prof_start = (hipEvent_t)start_event;
+  g_prof_stop = (hipEvent_t)stop_event;
+  return ok();
+}
+
 int32_t pa_decode(void* out, const void* query, int32_t q_dtype, int32_t num_seqs,
                   int32_t num_heads, int32_t head_size, const void* k_cache, const void* v_cache,
                   int32_t cache_dtype, int32_t num_blocks, int32_t block_size,
@@ -480,8 +494,8 @@ int32_t pa_decode_shared_prefix(void* out, const void* query, int32_t q_dtype, i
     return fail(PA_ERR_INVALID,
                 "prefix_len %d must be a multiple of block_size %d in [0, max_seq_len %d]",
                 prefix_len, block_size, max_seq_len);
-  if (num_seqs > kMaxGridYZ)
-    return fail(PA_ERR_INVALID, "%d sequences exceed the merge grid's %lld", num_seqs,
+  if (num_kv_heads > kMaxGridYZ)
+    return fail(PA_ERR_INVALID, "%d KV heads exceed the grid's %lld", num_kv_heads,
                 (long long)kMaxGridYZ);
   const int group = num_heads / num_kv_heads;
   if (prefix_len > 0 && !pa::prefill_supported(q_dtype, cache_dtype, head_size, block_size, group))

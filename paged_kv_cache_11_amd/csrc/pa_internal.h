@@ -2,6 +2,7 @@
 // shared between the C ABI (pa_api.hip) and the kernel translation units.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -95,8 +96,24 @@ struct DecodeArgs {
   const float* prefix_acc;
   const float* prefix_ml;
   int32_t prefix_splits;
+  // Measurement (pa_profile_next_decode): events recorded right before and
+  // after the main decode kernel, or null.
+  hipEvent_t prof_start, prof_stop;
   hipStream_t stream;
 };
+
+// Launches the main decode kernel of a call, between the call's profiling
+// events when it has them (hipExtLaunchKernelGGL records them on the
+// stream immediately around this one dispatch).
+template <typename... KArgs, typename... Args>
+inline void launch_main(const DecodeArgs& a, void (*kernel)(KArgs...), dim3 grid, dim3 block,
+                        Args... args) {
+  if (a.prof_start)
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, a.stream, a.prof_start, a.prof_stop, 0,
+                          args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, 0, a.stream, args...);
+}
 
 // Engines of the balanced decode: the wavefront (vector ALU) engine, or the
 // matrix-core engine for head size 128 with groups of 4 or 8.

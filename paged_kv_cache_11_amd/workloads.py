@@ -179,6 +179,20 @@ def llama3_8b_decode(seed: int = 1236, num_seqs: int = 64, min_len: int = 512,
                       1.0 / math.sqrt(D), q, k, v, slots, seq_lens, tables)
 
 
+def continuous_batching_decode(seed: int = 1241, num_seqs: int = 768, min_len: int = 64,
+                               max_len: int = 1024, block_size: int = 16) -> PagedBatch:
+    """A continuous-batching decode step, Llama-3-8B shape: many sequences
+    at every stage of generation in one batch ("vLLM：大语言模型推理与服务库"
+    §4.5: requests join and leave the running batch each step), here 768
+    sequences with lengths uniform in [64, 1024], 32 query heads over 8 KV
+    heads, head size 128, bf16, block 16, pool 1.25x the blocks needed,
+    tables from a shuffled pool."""
+    b = llama3_8b_decode(seed=seed, num_seqs=num_seqs, min_len=min_len, max_len=max_len,
+                         block_size=block_size)
+    b.name = "continuous_batching_decode_bf16"
+    return b
+
+
 def long_context_decode(seed: int = 1237, num_seqs: int = 8, seq_len: int = 32768,
                         partition_size: int = 512, outlier_frac: float = 0.01,
                         outlier_gain: float = 8.0) -> PagedBatch:
@@ -379,6 +393,7 @@ WORKLOADS = {
     "llama3_8b_decode_bf16": llama3_8b_decode,
     "long_context_splitk_bf16": long_context_decode,
     "shared_prefix_bf16": shared_prefix_decode,
+    "continuous_batching_decode_bf16": continuous_batching_decode,
     "mixed_prefill_decode_fp8": mixed_fp8_step,
     "chunked_prefill_budget2048_bf16": chunked_prefill_step,
     "chunked_prefill_budget512_bf16": lambda **kw: chunked_prefill_step(**{"budget": 512, **kw}),

@@ -165,7 +165,7 @@ def _shared(**kw):
     (dict(prefix_len=-16), pa.PA_ERR_INVALID),
     (dict(head_size=64), pa.PA_ERR_UNSUPPORTED),        # the prefix product takes head size 128
     (dict(q_dtype=pa.PA_F32, cache_dtype=pa.PA_F32), pa.PA_ERR_UNSUPPORTED),
-    (dict(num_seqs=70000), pa.PA_ERR_INVALID),
+    (dict(num_seqs=70000), pa.PA_ERR_WORKSPACE),       # any number of sequences
     (dict(), pa.PA_ERR_WORKSPACE),
     (dict(workspace=P, workspace_bytes=1000), pa.PA_ERR_WORKSPACE),
 ])

@@ -312,3 +312,15 @@ def test_decode_negative_and_zero_scale(scale, engine, ps):
     ref = G.oracle_decode(b, okp, ovp, G.query_f64(qt))
     got = G.run_decode(b, kp, vp, qt, partition_size=ps, flags=G.ENGINE_FLAG[engine])
     G.assert_close(got, ref, "fp8", f"decode scale {scale}, {engine or 'default'} engine, ps {ps}")
+
+
+def test_decode_continuous_batching_shape():
+    """The continuous-batching decode step (768 sequences of U[64, 1024]
+    tokens, Llama-3-8B shape): every sequence against the oracle, both
+    engines."""
+    b, kp, vp, okp, ovp, qt, q64 = _setup("continuous_batching_decode_bf16")
+    ref = _full_ref("continuous", b, okp, ovp, q64)
+    for engine in ("mfma", "valu"):
+        got = G.run_decode(b, kp, vp, qt, partition_size=BAL,
+                           flags=G.ENGINE_FLAG[engine] | pa.PA_DECODE_READ_ONCE)
+        G.assert_close(got, ref, "bf16", f"continuous batching, {engine} engine")

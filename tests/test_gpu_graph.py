@@ -1,0 +1,114 @@
+"""The decode step captured in a HIP graph: cache write + decode (balanced
+split: decode kernel + reduce kernel), the allocation-free decode, and the
+shared-prefix decode (prefix product + suffix decode + merge).  Each graph
+is replayed several times with eager library work and synchronisations
+between the replays, and every replay must equal the eager result bit for
+bit (the kernels are deterministic and enqueue no memset)."""
+import numpy as np
+import pytest
+import torch
+
+import pa_gpu as G
+from paged_kv_cache_11_amd import binding as pa
+from paged_kv_cache_11_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+BAL = pa.PA_PARTITION_BALANCED
+
+
+def _replays_equal(capture_fn, read_fn, eager_fn, disturb_fn, n=3):
+    """Capture capture_fn() on a side stream, replay it n times with
+    disturb_fn() (eager work that overwrites the outputs) between replays;
+    each replay's outputs (read_fn) must equal eager_fn()'s."""
+    eager_fn()
+    torch.cuda.synchronize()
+    want = read_fn()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    with torch.cuda.graph(g, stream=s):
+        capture_fn()
+    for r in range(n):
+        disturb_fn()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = read_fn()
+        for a, b in zip(got, want):
+            assert np.array_equal(a, b), f"replay {r} differs from the eager result"
+
+
+@pytest.fixture(scope="module")
+def llama():
+    b = wl.llama3_8b_decode()
+    G.say(f"[graph] {b.num_seqs} seqs, {b.num_blocks} blocks")
+    ends = np.cumsum(b.seq_lens.astype(np.int64))
+    new = ends - 1
+    kp, vp = G.gpu_pool(b)
+    G.gpu_fill(b, kp, vp, sel=np.setdiff1d(np.arange(ends[-1]), new))
+    return b, kp, vp, new
+
+
+def test_graph_cache_write_and_decode(llama):
+    b, kp, vp, new = llama
+    k_new = wl.storage_tensor(b.k[new], "bf16").to(G.DEV)
+    v_new = wl.storage_tensor(b.v[new], "bf16").to(G.DEV)
+    slots = torch.from_numpy(b.slot_mapping[new]).to(G.DEV)
+    q = G.query_tensor(b)
+    out = torch.empty_like(q)
+    tb, ln = torch.from_numpy(b.block_tables).to(G.DEV), torch.from_numpy(b.seq_lens).to(G.DEV)
+    ws = torch.empty(pa.pa_decode_workspace_size(b.num_seqs, b.num_heads, b.num_kv_heads,
+                                                 b.head_size, b.max_seq_len, BAL),
+                     dtype=torch.uint8, device=G.DEV)
+
+    def step():
+        pa.pa_cache_write(k_new, v_new, kp, vp, slots)
+        pa.pa_decode(out, q, kp, vp, tb, ln, b.max_seq_len, b.scale, partition_size=BAL,
+                     workspace=ws, flags=pa.PA_DECODE_READ_ONCE)
+
+    def disturb():
+        out.fill_(float("nan"))
+        # Other eager decodes through the same workspace in between.
+        pa.pa_decode(torch.empty_like(q), q, kp, vp, tb, (ln // 2).contiguous(), b.max_seq_len,
+                     b.scale, partition_size=BAL, workspace=ws)
+
+    _replays_equal(step, lambda: [out.float().cpu().numpy()], step, disturb)
+
+
+def test_graph_no_alloc_decode(llama):
+    b, kp, vp, _ = llama
+    q = G.query_tensor(b)
+    out = torch.empty_like(q)
+    tb, ln = torch.from_numpy(b.block_tables).to(G.DEV), torch.from_numpy(b.seq_lens).to(G.DEV)
+
+    def dec():
+        pa.pa_decode_no_alloc(out, q, kp, vp, tb, ln, b.max_seq_len, b.scale, partition_size=BAL,
+                              flags=pa.PA_DECODE_READ_ONCE)
+
+    def disturb():
+        out.fill_(float("nan"))
+        pa.pa_decode_no_alloc(torch.empty_like(q), q, kp, vp, tb, (ln // 3).contiguous(),
+                              b.max_seq_len, b.scale, partition_size=512)
+
+    _replays_equal(dec, lambda: [out.float().cpu().numpy()], dec, disturb)
+
+
+def test_graph_shared_prefix_decode():
+    b = wl.shared_prefix_decode()
+    kp, vp = G.gpu_pool(b)
+    G.gpu_fill(b, kp, vp)
+    q = G.query_tensor(b)
+    out = torch.empty_like(q)
+    tb, ln = torch.from_numpy(b.block_tables).to(G.DEV), torch.from_numpy(b.seq_lens).to(G.DEV)
+    ws = torch.empty(pa.pa_decode_shared_prefix_workspace_size(b.num_seqs, b.num_heads,
+                                                               b.num_kv_heads, b.head_size, 2048),
+                     dtype=torch.uint8, device=G.DEV)
+
+    def dec():
+        pa.pa_decode_shared_prefix(out, q, kp, vp, tb, ln, b.max_seq_len, 2048, b.scale,
+                                   workspace=ws)
+
+    def disturb():
+        out.fill_(float("nan"))
+        ws.fill_(0x55)
+
+    _replays_equal(dec, lambda: [out.float().cpu().numpy()], dec, disturb)

@@ -15,6 +15,8 @@ pytestmark = pytest.mark.gpu
 
 
 def run_prefill(b, kp, vp, cq, qsl, lens, tables, max_q):
+    pa.validate_prefill(qsl, int(cq.shape[0]), max_q, tables, lens, int(kp.shape[0]),
+                        int(kp.shape[2]))
     qt = wl.storage_tensor(cq, "bf16").to(G.DEV)
     out = torch.empty_like(qt)
     pa.pa_prefill_chunk(out, qt, torch.from_numpy(np.ascontiguousarray(qsl)).to(G.DEV), max_q, kp, vp,
@@ -36,11 +38,11 @@ def test_prefill_mixed_step_fp8_70b_shape():
     assert G.raw_equal(kp, okp) and G.raw_equal(vp, ovp)
     got, q64 = run_prefill(b, kp, vp, b.chunk_q, b.chunk_query_start, b.chunk_seq_lens,
                            b.chunk_block_tables, int(b.chunk_q.shape[0]))
-    rows = list(range(0, 512, 5)) + [511]
+    # Every one of the 512 queries and 64 heads.
     ref = opg.paged_prefill(q64, b.chunk_query_start, okp, ovp, b.chunk_block_tables,
                             b.chunk_seq_lens, b.scale, kv_dtype="fp8", k_scale=b.k_scale,
-                            v_scale=b.v_scale, rows=rows)
-    G.assert_close(got, ref, "fp8", "fp8 prefill chunk", rows=rows)
+                            v_scale=b.v_scale)
+    G.assert_close(got, ref, "fp8", "fp8 prefill chunk")
     # Cross-kernel: prefill row i equals a decode of the same query with the
     # context cut at its position.
     pick = [0, 100, 511]
@@ -178,3 +180,52 @@ def test_prefill_token_budget_step(budget):
     ref = opg.paged_prefill(q64, qsl, okp, ovp, b.chunk_block_tables, b.chunk_seq_lens, b.scale,
                             kv_dtype="bf16", rows=rows)
     G.assert_close(got, ref, "bf16", f"budget-{budget} prefill step", rows=rows)
+
+
+def test_mixed_step_end_to_end_one_stream():
+    """The whole mixed fp8 step on one stream with no host synchronisation
+    between its calls: the cache write of the step's 544 new tokens (the
+    last token of each of the 32 decode sequences and the 512 chunk tokens)
+    into a pool holding the rest of the history, then pa_decode of the 32
+    sequences, then pa_prefill_chunk of the 512 queries.  Pools, every
+    decode output and every prefill output against the oracle's same
+    sequence of steps."""
+    b = wl.mixed_fp8_step()
+    ends = np.cumsum(b.seq_lens.astype(np.int64))
+    dec_new = ends - 1
+    prompt0 = int(ends[-1])
+    chunk_new = np.arange(prompt0 + 1536, prompt0 + 2048)
+    new = np.concatenate([dec_new, chunk_new])
+    hist = np.setdiff1d(np.arange(len(b.slot_mapping)), new)
+    kp, vp = G.gpu_pool(b)
+    G.gpu_fill(b, kp, vp, sel=hist)
+    okp, ovp = G.oracle_pool(b, sel=hist)
+    # Inputs of the step, on the device before it starts.
+    k_new = wl.storage_tensor(b.k[new], b.kv_src_dtype).to(G.DEV)
+    v_new = wl.storage_tensor(b.v[new], b.kv_src_dtype).to(G.DEV)
+    s_new = torch.from_numpy(b.slot_mapping[new]).to(G.DEV)
+    pa.validate_slots(b.slot_mapping[new], b.num_blocks, b.block_size)
+    qt = G.query_tensor(b)
+    cq = wl.storage_tensor(b.chunk_q, "bf16").to(G.DEV)
+    out, cout = torch.empty_like(qt), torch.empty_like(cq)
+    tb, ln = torch.from_numpy(b.block_tables).to(G.DEV), torch.from_numpy(b.seq_lens).to(G.DEV)
+    cqs = torch.from_numpy(b.chunk_query_start).to(G.DEV)
+    ctb = torch.from_numpy(b.chunk_block_tables).to(G.DEV)
+    cln = torch.from_numpy(b.chunk_seq_lens).to(G.DEV)
+    torch.cuda.synchronize()
+    pa.pa_cache_write(k_new, v_new, kp, vp, s_new, b.k_scale, b.v_scale)
+    pa.pa_decode(out, qt, kp, vp, tb, ln, b.max_seq_len, b.scale, b.k_scale, b.v_scale,
+                 pa.PA_PARTITION_BALANCED, flags=pa.PA_DECODE_READ_ONCE)
+    pa.pa_prefill_chunk(cout, cq, cqs, 512, kp, vp, ctb, cln, b.scale, b.k_scale, b.v_scale)
+    torch.cuda.synchronize()
+    ks = wl.storage_bits(wl.storage_tensor(b.k[new], b.kv_src_dtype))
+    vs = wl.storage_bits(wl.storage_tensor(b.v[new], b.kv_src_dtype))
+    opg.cache_write(okp, ovp, "fp8", ks, vs, b.kv_src_dtype, b.slot_mapping[new], b.k_scale,
+                    b.v_scale)
+    assert G.raw_equal(kp, okp) and G.raw_equal(vp, ovp)
+    ref = G.oracle_decode(b, okp, ovp, G.query_f64(qt))
+    G.assert_close(out.float().cpu().numpy().astype(np.float64), ref, "fp8", "mixed step decode")
+    cref = opg.paged_prefill(G.query_f64(cq), b.chunk_query_start, okp, ovp, b.chunk_block_tables,
+                             b.chunk_seq_lens, b.scale, kv_dtype="fp8", k_scale=b.k_scale,
+                             v_scale=b.v_scale)
+    G.assert_close(cout.float().cpu().numpy().astype(np.float64), cref, "fp8", "mixed step prefill")
