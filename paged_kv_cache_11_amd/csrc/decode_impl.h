@@ -905,77 +905,96 @@ __global__ __launch_bounds__(D) void balanced_reduce_tasks_kernel(
   merge_cut<OT, D, G>(out, part_acc, part_ml, s, vw, code, h, g, d, num_kv_heads, v_scale);
 }
 
-// The last step of a shared-prefix decode, per (sequence s, KV head g),
-// one output element of one of the G query heads per thread: the
-// log-sum-exp merge of the sequence's suffix (its pieces when the balanced
-// split cut it, else the whole-sequence state the suffix mode kept) with
-// the prefix's splits.  Every state is unnormalised with its own reference
-// maximum (log2 domain); a state with no keys has m = -inf and is skipped.
-// The prefix states, the cut record and the whole-sequence state do not
-// depend on each other, so their loads are issued together; only the
-// pieces of a cut sequence wait for the cut record.
+// The last step of a shared-prefix decode: the log-sum-exp merge of each
+// sequence's suffix (its pieces when the balanced split cut it, else the
+// whole-sequence state the suffix mode kept) with the prefix's splits.
+// Every state is unnormalised with its own reference maximum (log2
+// domain); a state with no keys has m = -inf and is skipped.
+// Workgroups of kMergeThreads, grid (sequence, element block of
+// 4 kMergeThreads outputs); a thread owns 4 consecutive output elements of
+// one head (16-byte loads).  The prefix
+// states, the cut records and the whole-sequence states do not depend on
+// each other, so all their loads are issued before any is used; only the
+// pieces of a cut sequence wait for its cut record.
+constexpr int kMergeThreads = 256;
+
 template <typename OT, int D, int G>
-__global__ __launch_bounds__(G * D) void prefix_merge_kernel(
+__global__ __launch_bounds__(kMergeThreads) void prefix_merge_kernel(
     void* __restrict__ out, const float* __restrict__ part_acc,
     const float* __restrict__ part_ml, const int32_t* __restrict__ cuts,
     const int32_t* __restrict__ seq_lens, int num_seqs, int num_kv_heads, float v_scale,
     SuffixStates sx, const float* __restrict__ prefix_acc, const float* __restrict__ prefix_ml,
     int prefix_splits) {
-  constexpr int kBatch = 4;
-  const int s = blockIdx.x, g = blockIdx.y;
-  const int h = threadIdx.x / D, d = threadIdx.x % D;
+  constexpr int kMaxSplits = kMaxPrefixSplits;
+  const int s = blockIdx.x;
   const int num_heads = num_kv_heads * G;
-  const int64_t hq = (int64_t)s * num_heads + g * G + h;
-  float M = -INFINITY, num = 0.f, den = 0.f;
-  auto add = [&](float m, float l, float a) {
-    if (m == -INFINITY) return;
-    if (m > M) {
-      const float f = M == -INFINITY ? 0.f : fast_exp2(M - m);
-      num *= f;
-      den *= f;
-      M = m;
-    }
-    const float e = fast_exp2(m - M);
-    num = __builtin_fmaf(e, a, num);
-    den = __builtin_fmaf(e, l, den);
-  };
   const bool has_suffix = seq_lens[s] > sx.skip;
-  int va = 0, code = 0;
-  float wm = -INFINITY, wl = 0.f, wa = 0.f;
-  if (has_suffix) {
-    va = cuts[2 * ((int64_t)s * num_kv_heads + g) + 0];
-    code = cuts[2 * ((int64_t)s * num_kv_heads + g) + 1];
-    wm = sx.ml[2 * hq];  // the whole-sequence state (used if not cut)
-    wl = sx.ml[2 * hq + 1];
-    wa = sx.acc[hq * D + d];
-  }
-  for (int c0 = 0; c0 < prefix_splits; c0 += kBatch) {
-    float m[kBatch], l[kBatch], a[kBatch];
-#pragma unroll
-    for (int b = 0; b < kBatch; ++b) {
-      const int c = c0 + b < prefix_splits ? c0 + b : prefix_splits - 1;
-      const int64_t st = (int64_t)c * num_seqs * num_heads + hq;
-      m[b] = prefix_ml[2 * st];
-      l[b] = prefix_ml[2 * st + 1];
-      a[b] = prefix_acc[st * D + d];
+  for (int e0 = (blockIdx.y * kMergeThreads + threadIdx.x) * 4; e0 < num_heads * D;
+       e0 += gridDim.y * kMergeThreads * 4) {
+    const int h = e0 / D, d = e0 % D;  // query head (of all num_heads) and first dim
+    const int g = h / G, hg = h % G;
+    const int64_t hq = (int64_t)s * num_heads + h;
+    float M = -INFINITY, den = 0.f;
+    f32x4 num = {0.f, 0.f, 0.f, 0.f};
+    auto add = [&](float m, float l, f32x4 a) {
+      if (m == -INFINITY) return;
+      if (m > M) {
+        const float f = M == -INFINITY ? 0.f : fast_exp2(M - m);
+        num *= f;
+        den *= f;
+        M = m;
+      }
+      const float e = fast_exp2(m - M);
+      num += e * a;
+      den = __builtin_fmaf(e, l, den);
+    };
+    int va = 0, code = 0;
+    float wm = -INFINITY, wl = 0.f;
+    f32x4 wa = {0.f, 0.f, 0.f, 0.f};
+    if (has_suffix) {
+      va = cuts[2 * ((int64_t)s * num_kv_heads + g) + 0];
+      code = cuts[2 * ((int64_t)s * num_kv_heads + g) + 1];
+      wm = sx.ml[2 * hq];  // the whole-sequence state (used if not cut)
+      wl = sx.ml[2 * hq + 1];
+      wa = *(const f32x4*)(sx.acc + hq * D + d);
     }
+    float pm[kMaxSplits], pl[kMaxSplits];
+    f32x4 pa[kMaxSplits];
 #pragma unroll
-    for (int b = 0; b < kBatch; ++b)
-      if (c0 + b < prefix_splits) add(m[b], l[b], a[b]);
-  }
-  if (has_suffix) {
-    const int np = code >> 1, slot0 = code & 1;
-    if (np <= 1) {
-      add(wm, wl, wa);
-    } else {
-      for (int p = 0; p < np; ++p) {
-        const int64_t st =
-            ((int64_t)((va + p) * num_kv_heads + g) * 2 + (p == 0 ? slot0 : 0)) * G + h;
-        add(part_ml[2 * st], part_ml[2 * st + 1], part_acc[st * D + d]);
+    for (int c = 0; c < kMaxSplits; ++c) {
+      if (c < prefix_splits) {
+        const int64_t st = (int64_t)c * num_seqs * num_heads + hq;
+        pm[c] = prefix_ml[2 * st];
+        pl[c] = prefix_ml[2 * st + 1];
+        pa[c] = *(const f32x4*)(prefix_acc + st * D + d);
       }
     }
+#pragma unroll
+    for (int c = 0; c < kMaxSplits; ++c)
+      if (c < prefix_splits) add(pm[c], pl[c], pa[c]);
+    if (has_suffix) {
+      const int np = code >> 1, slot0 = code & 1;
+      if (np <= 1) {
+        add(wm, wl, wa);
+      } else {
+        for (int p = 0; p < np; ++p) {
+          const int64_t st =
+              ((int64_t)((va + p) * num_kv_heads + g) * 2 + (p == 0 ? slot0 : 0)) * G + hg;
+          add(part_ml[2 * st], part_ml[2 * st + 1], *(const f32x4*)(part_acc + st * D + d));
+        }
+      }
+    }
+    const float inv = den > 0.f ? v_scale / den : 0.f;
+    if constexpr (std::is_same<OT, F32>::value) {
+      *(f32x4*)((float*)out + hq * D + d) = num * inv;
+    } else {
+      const uint32_t w0 = (uint32_t)f32_to_bf16_rne(num[0] * inv) |
+                          ((uint32_t)f32_to_bf16_rne(num[1] * inv) << 16);
+      const uint32_t w1 = (uint32_t)f32_to_bf16_rne(num[2] * inv) |
+                          ((uint32_t)f32_to_bf16_rne(num[3] * inv) << 16);
+      *(u32x2*)((uint16_t*)out + hq * D + d) = u32x2{w0, w1};
+    }
   }
-  store_out<OT>(out, hq * D + d, den > 0.f ? num / den * v_scale : 0.f);
 }
 
 // Log-sum-exp merge of the fixed partitions of one (query head, KV head,
@@ -1059,7 +1078,10 @@ hipError_t launch_decode(const DecodeArgs& a) {
     if (e != hipSuccess) return e;
     if (a.prefix_acc)
       hipLaunchKernelGGL((prefix_merge_kernel<QT, D, G>),
-                         dim3((unsigned)a.num_seqs, (unsigned)a.num_kv_heads), dim3(G * D),
+                         dim3((unsigned)a.num_seqs,
+                              (unsigned)((a.num_heads * D + 4 * kMergeThreads - 1) /
+                                         (4 * kMergeThreads))),
+                         dim3(kMergeThreads),
                          0, a.stream, a.out, a.part_o, a.part_ml, a.cuts, a.seq_lens, a.num_seqs,
                          a.num_kv_heads, v_scale, a.suffix, a.prefix_acc, a.prefix_ml,
                          a.prefix_splits);

@@ -446,14 +446,21 @@ int32_t pa_decode(void* out, const void* query, int32_t q_dtype, int32_t num_seq
 // Splits of a shared prefix: enough (query tile, KV head, split) workgroups
 // to give every compute unit one, each split a multiple of 128 keys (whole
 // blocks and whole 64-key steps), at most kMaxPrefixSplits.
-constexpr int32_t kMaxPrefixSplits = 16;
+using pa::kMaxPrefixSplits;
 constexpr int32_t kPrefixSplitQuantum = 128;
 
 static int32_t prefix_split_len(int32_t prefix_len, int32_t num_seqs, int32_t group,
                                 int32_t num_kv_heads, int32_t cus) {
+  // PA_PREFIX_SPLITS pins the number of splits (a tuning knob, read once).
+  static const int pinned = [] {
+    const char* e = getenv("PA_PREFIX_SPLITS");
+    const int x = e ? atoi(e) : 0;
+    return (x >= 1 && x <= kMaxPrefixSplits) ? x : 0;
+  }();
   const int64_t tiles = ceil_div((int64_t)num_seqs * group, 128) * num_kv_heads;
   const int64_t quanta = ceil_div(prefix_len, kPrefixSplitQuantum);
   int64_t want = tiles > 0 ? ceil_div(cus > 0 ? cus : 256, tiles) : 1;
+  if (pinned) want = pinned;
   if (want > kMaxPrefixSplits) want = kMaxPrefixSplits;
   if (want > quanta) want = quanta;
   if (want < 1) want = 1;

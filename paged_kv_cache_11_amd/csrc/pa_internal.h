@@ -159,6 +159,10 @@ bool decode_supported(int32_t q_dtype, int32_t cache_dtype, int head_size, int b
 
 hipError_t prefill(const PrefillArgs& a);
 
+// Most splits the keys of a shared prefix are cut into (the merge kernel
+// holds one state per split in registers).
+constexpr int kMaxPrefixSplits = 16;
+
 // Devices the library keeps per-device state for (ids 0 .. kMaxDevices-1).
 constexpr int kMaxDevices = 64;
 
