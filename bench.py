@@ -55,9 +55,10 @@ def kernel_source_digest() -> str:
     return h.hexdigest()[:16]
 
 
-def stored_traffic(workload: str, launches_per_step: float):
-    """HBM bytes per decode launch from committed rocprofv3 counter runs,
-    or None if they were taken on other kernel sources."""
+def stored_traffic(workload: str):
+    """HBM bytes (read + written) per launch of the balanced decode kernel,
+    from committed rocprofv3 counter runs, or None if they were taken on
+    other kernel sources."""
     path = os.path.join(ROOT, "profiles", f"decode_kernel_{workload}_counters.json")
     if not os.path.exists(path):
         return None
@@ -65,7 +66,8 @@ def stored_traffic(workload: str, launches_per_step: float):
         d = json.load(f)
     if d.get("source_digest") != kernel_source_digest():
         return None
-    return d.get("hbm_bytes_per_launch")
+    k = d.get("kernels", {}).get("decode_balanced")
+    return round(k["fetch_bytes"] + k["write_bytes"]) if k else None
 
 
 def summarize_counters(fetch_csv: str, write_csv: str, workload: str, out_path: str) -> dict:
@@ -397,6 +399,12 @@ def row_measurements(dev, iters=20, groups=ROW_GROUPS):
     from paged_kv_cache_11_amd import workloads as wl
 
     rows = {}
+    t_start = time.perf_counter()
+
+    def done(group):
+        print(f"[bench] rows {group} done at {time.perf_counter() - t_start:.1f} s", file=sys.stderr,
+              flush=True)
+
     if "long_context" in groups:
         # Long-context split-K: 8 x 32768 tokens, 512-token partitions + LSE reduce.
         b = wl.long_context_decode()
@@ -418,6 +426,8 @@ def row_measurements(dev, iters=20, groups=ROW_GROUPS):
         del sets
         torch.cuda.empty_cache()
 
+    if "long_context" in groups:
+        done("long_context")
     if "shared_prefix" in groups:
         # Shared prefix: 256 forks of one prefix (config 4): the literal
         # 2048-token prefix (no copy-on-write), the 2040-token variant whose
@@ -482,6 +492,8 @@ def row_measurements(dev, iters=20, groups=ROW_GROUPS):
             del sets, ws, ws_sp
             torch.cuda.empty_cache()
 
+    if "shared_prefix" in groups:
+        done("shared_prefix")
     if "mixed_fp8" in groups:
         # Mixed fp8 step (70B shape): cache write of the step's new tokens,
         # decode of 32 sequences, prefill of a 512-query chunk.
@@ -546,6 +558,8 @@ def row_measurements(dev, iters=20, groups=ROW_GROUPS):
         us_step = _time_us(lambda i: (cw(i), dec(i), pre(i)), iters)
         rows["mixed_step_fp8"] = {"us": round(us_step, 2),
                                   "step": "cache_write(544 tokens) + decode(32 seqs) + prefill(512 queries)"}
+    if "mixed_fp8" in groups:
+        done("mixed_fp8")
     if "chunked_prefill" in groups:
         # One scheduler step of varlen chunked prefill under a 512- and a
         # 2048-token budget (Llama-3-8B shape, bf16 pool): one call per step.
@@ -569,6 +583,8 @@ def row_measurements(dev, iters=20, groups=ROW_GROUPS):
                 "tokens_per_s": round(budget / us * 1e6, 1)}
             del sets
             torch.cuda.empty_cache()
+    if "chunked_prefill" in groups:
+        done("chunked_prefill")
     if "swap" in groups:
         # SWAP preemption: the blocks of 8 sequences of the headline workload
         # (lengths U[512, 4096], bf16, 32 KiB per block and pool) moved to a
@@ -618,6 +634,8 @@ def row_measurements(dev, iters=20, groups=ROW_GROUPS):
             "host_link_peak_gbs": link}
         del kd, vd, hk, hv, flat_d, flat_h
         torch.cuda.empty_cache()
+    if "swap" in groups:
+        done("swap")
     if "continuous_batching" in groups:
         # A continuous-batching decode step: 768 sequences of lengths
         # U[64, 1024], Llama-3-8B shape, balanced split, read-once hint,
@@ -648,6 +666,8 @@ def row_measurements(dev, iters=20, groups=ROW_GROUPS):
             "tokens_per_s": round(b.num_seqs / us * 1e6, 1)}
         del sets
         torch.cuda.empty_cache()
+    if "continuous_batching" in groups:
+        done("continuous_batching")
     if "ceiling" in groups:
         # The practical HBM ceiling of this access pattern: pa_copy_blocks
         # over 16384 scattered whole blocks of the headline pool geometry
@@ -669,10 +689,16 @@ def row_measurements(dev, iters=20, groups=ROW_GROUPS):
             "pct_hbm_peak_read_plus_write": round(100 * 2 * moved / us / 1e3 / HBM_PEAK_GBS, 2)}
         del kp, vp
         torch.cuda.empty_cache()
+    if "ceiling" in groups:
+        done("ceiling")
     if "block_manager" in groups:
         rows.update(block_manager_rows())
+    if "block_manager" in groups:
+        done("block_manager")
     if "prefix_cache" in groups:
         rows.update(prefix_cache_rows())
+    if "prefix_cache" in groups:
+        done("prefix_cache")
     if "block_sizes" in groups:
         # The headline decode over pool blocks of 64 and 128 tokens (same
         # lengths and values), balanced split, three pool copies rotated.
@@ -694,6 +720,8 @@ def row_measurements(dev, iters=20, groups=ROW_GROUPS):
                                                "pct_hbm_peak": round(100 * by / us / 1e3 / HBM_PEAK_GBS, 2)}
             del sets
             torch.cuda.empty_cache()
+    if "block_sizes" in groups:
+        done("block_sizes")
     return rows
 
 
@@ -863,7 +891,7 @@ def main(argv=None):
         torch.cuda.synchronize()
         calib = {"copy_bytes_read": int(2 * nbk * k0[0].numel() * k0.element_size())}
 
-    traffic = stored_traffic(b.name, 1)
+    traffic = stored_traffic(b.name)
     rows = None
     if not args.no_rows:
         del sets
