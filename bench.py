@@ -556,8 +556,27 @@ def row_measurements(dev, iters=20, groups=ROW_GROUPS):
             "pct_mfma_bf16_peak": round(100 * flops / us_pre / 1e6 / MFMA_BF16_PEAK_TFLOPS, 2),
             "queries_per_s": round(n / us_pre * 1e6, 1)}
         us_step = _time_us(lambda i: (cw(i), dec(i), pre(i)), iters)
+        # The same step with decode and prefill on two streams after the
+        # cache write: whether the memory-bound and the compute-bound kernel
+        # gain from running side by side.
+        main = torch.cuda.current_stream()
+        s_dec, s_pre = torch.cuda.Stream(), torch.cuda.Stream()
+
+        def step_two_streams(i):
+            cw(i)
+            s_dec.wait_stream(main)
+            s_pre.wait_stream(main)
+            with torch.cuda.stream(s_dec):
+                dec(i)
+            with torch.cuda.stream(s_pre):
+                pre(i)
+            main.wait_stream(s_dec)
+            main.wait_stream(s_pre)
+
+        us_two = _time_us(step_two_streams, iters)
         rows["mixed_step_fp8"] = {"us": round(us_step, 2),
-                                  "step": "cache_write(544 tokens) + decode(32 seqs) + prefill(512 queries)"}
+                                  "step": "cache_write(544 tokens) + decode(32 seqs) + prefill(512 queries)",
+                                  "two_streams_us": round(us_two, 2)}
     if "mixed_fp8" in groups:
         done("mixed_fp8")
     if "chunked_prefill" in groups:
