@@ -55,9 +55,17 @@ static_assert(kPThreads / 8 == kStep, "the staging map covers one step exactly")
 constexpr int kKBytes = kStep * kKStride * 2;
 constexpr int kVBytes = kStep * kVStride * 2;
 constexpr int kBufBytes = kKBytes + kVBytes;
-constexpr int kMergeFloats = kRowGroups * (kPD / 2) * kWave + 2 * kRowGroups * kWave;
-constexpr int kLdsBytes =
-    kBufs * kBufBytes > kMergeFloats * 4 ? kBufs * kBufBytes : kMergeFloats * 4;
+// After the key walk: the two key halves trade half of their accumulators
+// (kMergeFloats), then the finished tile goes through LDS row by row
+// (kTileStride bytes per row: bf16 outputs, or fp32 states in prefix mode)
+// so that global stores cover whole rows.
+constexpr int kMergeFloats = 2 * kRowGroups * (kPD / 4) * kWave + 4 * kRowGroups * kWave;
+constexpr int kTileStride = kPD * 4 + 16;
+constexpr int kTileOff = kMergeFloats * 4;
+constexpr int kQStride = kPD * 2 + 16;  // LDS row stride of the query tile (bytes)
+constexpr int kLdsBytes = kBufs * kBufBytes;
+static_assert(kTileOff + kRows * kTileStride <= kLdsBytes, "the epilogue fits the step buffers");
+static_assert(kRows * kQStride <= kBufBytes, "the query tile fits one step buffer");
 static_assert(kLdsBytes <= 160 * 1024, "one workgroup's LDS fits a CU");
 
 // How the query enters: the kernel's score scale is always positive, so a
@@ -164,19 +172,23 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(
   // Last position among this wavefront's rows: later tiles are all masked.
   const int wave_max_pos = position(min(q_first + (32 * rg + 31) / G, q_last));
 
+  // The tile's query rows arrive with whole-row loads (16 lanes per 256-byte
+  // row, four rows per load instruction) and wait in the last step buffer,
+  // which is first written two steps into the key walk.
+  constexpr int kQPieces = kRows * kPD * 2 / 16 / kPThreads;  // 16-byte pieces per thread
+  u32x4 qraw[kQPieces];
+#pragma unroll
+  for (int k = 0; k < kQPieces; ++k) {
+    const int f = t + k * kPThreads, r = f / (kPD / 8), c = f % (kPD / 8);
+    const int rq = q_first + r / G;
+    qraw[k] = u32x4{0u, 0u, 0u, 0u};
+    if (rq < n)
+      qraw[k] = *(const u32x4*)((const uint16_t*)query +
+                                 ((int64_t)(qs + rq) * num_heads + g * G + r % G) * kPD + 8 * c);
+  }
+  uint8_t* q_lds = lds + (kBufs - 1) * kBufBytes;
   // Q^T operand: k-step s holds dims 16 s + 8 half .. +8 of the row.
   bf16x8 qreg[kPD / 16];
-  {
-    const uint16_t* qrow = (const uint16_t*)query + ((int64_t)(qs + qi) * num_heads + hq) * kPD;
-#pragma unroll
-    for (int s = 0; s < kPD / 16; ++s) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (row_ok) v = *(const u32x4*)(qrow + 16 * s + 8 * half);
-      if (q_mode == kQNegate) v ^= 0x80008000u;  // exact: -(q·k) = (-q)·k
-      if (q_mode == kQZero) v = u32x4{0u, 0u, 0u, 0u};  // every score is 0
-      qreg[s] = __builtin_bit_cast(bf16x8, v);
-    }
-  }
 
   f32x16 oacc[kPD / 32];
 #pragma unroll
@@ -354,7 +366,19 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(
   store_stage(1, sb, 1);
   load_stage(bid, 3, sb);
   bid = block_id(4);
+#pragma unroll
+  for (int k = 0; k < kQPieces; ++k) {
+    const int f = t + k * kPThreads;
+    *(u32x4*)(q_lds + (f / (kPD / 8)) * kQStride + (f % (kPD / 8)) * 16) = qraw[k];
+  }
   __syncthreads();
+#pragma unroll
+  for (int s = 0; s < kPD / 16; ++s) {
+    u32x4 v = *(const u32x4*)(q_lds + row * kQStride + (16 * s + 8 * half) * 2);
+    if (q_mode == kQNegate) v ^= 0x80008000u;  // exact: -(q·k) = (-q)·k
+    if (q_mode == kQZero) v = u32x4{0u, 0u, 0u, 0u};  // every score is 0
+    qreg[s] = __builtin_bit_cast(bf16x8, v);
+  }
   // Scores of even steps live in st_a, of odd steps in st_b.
   f32x16 st_a, st_b;
 #pragma unroll
@@ -394,68 +418,85 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(
     if (j + 4 >= nsteps) break;
   }
   __syncthreads();  // the buffers become the merge area
-  float* mo_lds = (float*)lds;                             // [rg][kPD/2][kWave]
-  float* mm_lds = mo_lds + kRowGroups * (kPD / 2) * kWave;  // [rg][kWave]
-  float* ml_lds = mm_lds + kRowGroups * kWave;              // [rg][kWave]
-
-  // Merge the key halves: the second half hands its state to the first.
-  if (kh == 1) {
-    mm_lds[rg * kWave + lane] = m_ref;
-    ml_lds[rg * kWave + lane] = l_part;
+  // Merge the key halves: half kh finishes output dims 64 kh .. 64 kh + 63
+  // (accumulator tiles 2 kh and 2 kh + 1) and hands the other half its
+  // other two tiles, with its reference and sum.
+  float* mo_lds = (float*)lds;                                  // [kh][rg][kPD/4][kWave]
+  float* mm_lds = mo_lds + 2 * kRowGroups * (kPD / 4) * kWave;  // [kh][rg][kWave]
+  float* ml_lds = mm_lds + 2 * kRowGroups * kWave;              // [kh][rg][kWave]
+  const int me = kh * kRowGroups + rg, other = (1 - kh) * kRowGroups + rg;
+  mm_lds[me * kWave + lane] = m_ref;
+  ml_lds[me * kWave + lane] = l_part;
+  f32x16 keep[2];
+  auto trade = [&](auto half_index) {
+    constexpr int K = decltype(half_index)::value;
 #pragma unroll
-    for (int mt = 0; mt < kPD / 32; ++mt)
+    for (int u = 0; u < 2; ++u) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mo_lds[(rg * (kPD / 2) + 16 * mt + i) * kWave + lane] = oacc[mt][i];
-  }
+      for (int i = 0; i < 16; ++i)
+        mo_lds[(me * (kPD / 4) + 16 * u + i) * kWave + lane] = oacc[2 * (1 - K) + u][i];
+      keep[u] = oacc[2 * K + u];
+    }
+  };
+  if (kh == 0) trade(Buf<0>{});
+  else trade(Buf<1>{});
   __syncthreads();
-  if (kh == 1) return;
   float m_tot;  // the reference the merged state is relative to (-inf: no key)
   {
-    const float m1 = mm_lds[rg * kWave + lane], l1 = ml_lds[rg * kWave + lane];
+    const float m1 = mm_lds[other * kWave + lane], l1 = ml_lds[other * kWave + lane];
     const float M = fmaxf(m_ref, m1);
     const float mu = M == -INFINITY ? 0.f : M;
     const float f0 = fast_exp2(m_ref - mu), f1 = fast_exp2(m1 - mu);
     l_part = l_part * f0 + l1 * f1;
 #pragma unroll
-    for (int mt = 0; mt < kPD / 32; ++mt)
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int i = 0; i < 16; ++i)
-        oacc[mt][i] = oacc[mt][i] * f0 + mo_lds[(rg * (kPD / 2) + 16 * mt + i) * kWave + lane] * f1;
+        keep[u][i] = keep[u][i] * f0 + mo_lds[(other * (kPD / 4) + 16 * u + i) * kWave + lane] * f1;
     m_tot = M;
   }
-
-  // Finish: the two halves of the wave hold the same rows' other keys.
+  // The two halves of the wave hold the same rows' other keys.
   const float l_tot = l_part + __shfl_xor(l_part, 32, kWave);
-  if (!row_ok) return;
-  if constexpr (kPrefix) {
-    // The split's state of this row, unnormalised, for the merge.
-    const int64_t st = ((int64_t)c * n + qi) * num_heads + hq;
-    float* arow = ps.acc + st * kPD;
+
+  // The finished tile goes to LDS as rows (row-major, kTileStride bytes per
+  // row), then every thread stores whole 16-byte pieces of rows.
+  uint8_t* tile_lds = lds + kTileOff;
+  const float inv = kPrefix ? 1.f : (l_tot > 0.f ? v_scale / l_tot : 0.f);
 #pragma unroll
-    for (int mt = 0; mt < kPD / 32; ++mt)
+  for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int d0 = 32 * mt + q4 * 8 + 4 * half;
-        *(f32x4*)(arow + d0) = f32x4{oacc[mt][4 * q4 + 0], oacc[mt][4 * q4 + 1],
-                                     oacc[mt][4 * q4 + 2], oacc[mt][4 * q4 + 3]};
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int d0 = 64 * kh + 32 * u + q4 * 8 + 4 * half;
+      const float x0 = keep[u][4 * q4 + 0], x1 = keep[u][4 * q4 + 1];
+      const float x2 = keep[u][4 * q4 + 2], x3 = keep[u][4 * q4 + 3];
+      if constexpr (kPrefix) {
+        *(f32x4*)(tile_lds + row * kTileStride + d0 * 4) = f32x4{x0, x1, x2, x3};
+      } else {
+        *(u32x2*)(tile_lds + row * kTileStride + d0 * 2) =
+            u32x2{pk_bf16(x0 * inv, x1 * inv), pk_bf16(x2 * inv, x3 * inv)};
       }
-    if (half == 0) {
+    }
+  if constexpr (kPrefix) {
+    if (kh == 0 && half == 0 && row_ok) {
+      const int64_t st = ((int64_t)c * n + qi) * num_heads + hq;
       ps.ml[2 * st + 0] = m_tot;
       ps.ml[2 * st + 1] = l_tot;
     }
-    return;
   }
-  const float inv = l_tot > 0.f ? v_scale / l_tot : 0.f;
-  uint16_t* orow = (uint16_t*)out + ((int64_t)(qs + qi) * num_heads + hq) * kPD;
+  __syncthreads();
+  constexpr int kRowPieces = kPD * (kPrefix ? 4 : 2) / 16;  // 16-byte pieces per row
 #pragma unroll
-  for (int mt = 0; mt < kPD / 32; ++mt)
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const int d0 = 32 * mt + q4 * 8 + 4 * half;
-      const u32x2 v = {pk_bf16(oacc[mt][4 * q4 + 0] * inv, oacc[mt][4 * q4 + 1] * inv),
-                       pk_bf16(oacc[mt][4 * q4 + 2] * inv, oacc[mt][4 * q4 + 3] * inv)};
-      *(u32x2*)(orow + d0) = v;
-    }
+  for (int k = 0; k < kRows * kRowPieces / kPThreads; ++k) {
+    const int f = t + k * kPThreads, r = f / kRowPieces, piece = f % kRowPieces;
+    const int rq = q_first + r / G;
+    if (rq >= n) continue;
+    const int64_t grow = (int64_t)(qs + rq) * num_heads + g * G + r % G;
+    const u32x4 v = *(const u32x4*)(tile_lds + r * kTileStride + piece * 16);
+    if constexpr (kPrefix)
+      *(u32x4*)(ps.acc + ((int64_t)c * n * num_heads + grow) * kPD + 4 * piece) = v;
+    else
+      *(u32x4*)((uint16_t*)out + grow * kPD + 8 * piece) = v;
+  }
 }
 
 // The prefix mode: a.num_tokens queries (one per sequence) against
