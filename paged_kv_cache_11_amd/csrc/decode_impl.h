@@ -948,16 +948,15 @@ __global__ __launch_bounds__(kMergeThreads) void prefix_merge_kernel(
       num += e * a;
       den = __builtin_fmaf(e, l, den);
     };
-    int va = 0, code = 0;
-    float wm = -INFINITY, wl = 0.f;
-    f32x4 wa = {0.f, 0.f, 0.f, 0.f};
-    if (has_suffix) {
-      va = cuts[2 * ((int64_t)s * num_kv_heads + g) + 0];
-      code = cuts[2 * ((int64_t)s * num_kv_heads + g) + 1];
-      wm = sx.ml[2 * hq];  // the whole-sequence state (used if not cut)
-      wl = sx.ml[2 * hq + 1];
-      wa = *(const f32x4*)(sx.acc + hq * D + d);
-    }
+    // Every load that does not depend on another is issued up front (the
+    // suffix words are read even for an empty suffix, whose slots hold
+    // stale values that are then ignored), so the merge waits for at most
+    // two rounds of memory latency: these, and the pieces of a cut suffix.
+    const int va = cuts[2 * ((int64_t)s * num_kv_heads + g) + 0];
+    const int code = cuts[2 * ((int64_t)s * num_kv_heads + g) + 1];
+    const float wm = sx.ml[2 * hq];  // the whole-sequence state (used if not cut)
+    const float wl = sx.ml[2 * hq + 1];
+    const f32x4 wa = *(const f32x4*)(sx.acc + hq * D + d);
     float pm[kMaxSplits], pl[kMaxSplits];
     f32x4 pa[kMaxSplits];
 #pragma unroll

@@ -322,6 +322,9 @@ struct MfmaAttn {
         const int jj = blk0 + chunk * kWave + lane;
         bid_v = tbl[jj < blk_last ? jj : blk_last];
         cached = chunk;
+        // Wait for the window here, where it is reloaded (once per 64
+        // blocks), so that the read below never waits for the tile loads.
+        asm volatile("" : "+v"(bid_v));
       }
       return __builtin_amdgcn_readlane(bid_v, j % kWave);
     };
