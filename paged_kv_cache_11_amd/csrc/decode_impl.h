@@ -416,6 +416,9 @@ struct WaveAttn {
       if ((j & (kWave - 1)) == 0) {
         const int jj = j + lane;
         bid_v = jj < count ? tbl[(first + stride * jj) >> sub_shift] : 0;
+        // Wait for the window here, where it is (re)loaded once per 64
+        // blocks, so that the read below never waits for the tile loads.
+        asm volatile("" : "+v"(bid_v));
       }
       return __builtin_amdgcn_readlane(bid_v, j & (kWave - 1));
     };
