@@ -2,18 +2,22 @@
 
 One step = the hot path over one batch of the Llama-3-8B-shape decode
 workload (64 sequences, lengths uniform in [512, 4096], 32 query / 8 KV
-heads, head size 128, block 16, bf16): ``pa_cache_write`` of each sequence's
-new token, then ``pa_decode`` (split-K decode kernel + log-sum-exp reduce
-kernel).  Inputs are resident in HBM before timing starts.  Three
+heads, head size 128, block 16, bf16): each sequence's new token written
+into its slot and the decode over every token.  By default that is one
+``pa_decode_append`` call (the write happens inside the split-K decode
+kernel, then the log-sum-exp reduce kernel); ``--two-calls`` times it as
+``pa_cache_write`` + ``pa_decode``, whose time is reported beside it either
+way.  Inputs are resident in HBM before timing starts.  Three
 independent copies of the K/V pools are rotated step by step so that each
 step streams its K/V from HBM rather than from the 256 MB last-level cache.
 
 Prints ONE JSON line (rank 0):
   value       effective decode K/V read rate, GB/s (algorithmic K/V bytes of
               the step / step time; bytes = sum(seq_lens) x 4096)
-  roofline    the pa_decode call (decode kernel + reduce kernel) timed with
-              HIP events on its stream: algorithmic bytes / average duration
-              against the 8 TB/s HBM3E peak
+  roofline    the step's decode kernel alone, timed with HIP events the
+              library records around its launch: algorithmic bytes / average
+              duration against the 8 TB/s HBM3E peak (and the same for the
+              whole call, decode kernel + reduce kernel)
   cpu_baseline  the float64 CPU oracle on the same workload (test
               infrastructure, timed on the host cores)
   rows        event timings of the other rows of the path (long-context
@@ -757,6 +761,9 @@ def main(argv=None):
     ap.add_argument("--oracle-budget", type=float, default=2.0,
                     help="seconds of oracle time per workload for cpu_baseline_per_workload "
                          "(0 skips it)")
+    ap.add_argument("--two-calls", action="store_true",
+                    help="time the headline step as pa_cache_write + pa_decode instead of one "
+                         "pa_decode_append call")
     ap.add_argument("--no-rows", action="store_true",
                     help="skip the per-row measurements of the other workloads")
     ap.add_argument("--rows-only", choices=ROW_GROUPS,
@@ -825,28 +832,48 @@ def main(argv=None):
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
-    def step(i, stream=stream):
+    # The step as two calls: the cache write of the new tokens, then the
+    # decode over every token.
+    def step_two_calls(i, stream=stream):
         kc, vc = sets[i % N_SETS]
         pa.pa_cache_write(k_new, v_new, kc, vc, slots_new, b.k_scale, b.v_scale, stream=stream)
         pa.pa_decode(out, q, kc, vc, tables, lens, b.max_seq_len, b.scale, b.k_scale, b.v_scale,
                      ps, ws, stream=stream, flags=pa.PA_DECODE_READ_ONCE)
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = wall / args.steps * 1e3
+    # The same step as one call: pa_decode_append writes each sequence's new
+    # token into its slot inside the decode kernel (balanced split only).
+    fused = ps == pa.PA_PARTITION_BALANCED and not args.two_calls
+
+    def step_fused(i, stream=stream):
+        kc, vc = sets[i % N_SETS]
+        pa.pa_decode_append(out, q, k_new, v_new, kc, vc, tables, lens, b.max_seq_len, b.scale,
+                            b.k_scale, b.v_scale, ws, stream=stream,
+                            flags=pa.PA_DECODE_READ_ONCE)
+
+    def time_steps(fn):
+        for i in range(args.warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            fn(i)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / args.steps * 1e3
+
+    two_call_ms = time_steps(step_two_calls)
+    step = step_fused if fused else step_two_calls
+    ms_per_step = time_steps(step) if fused else two_call_ms
 
     kv_bytes = b.decode_kv_bytes()
     n_calls = max(args.steps, 200)
 
-    # The pa_decode call alone (decode kernel + reduce kernel), back to
-    # back over n_calls calls, HIP events on its stream around the run.
+    # The step's decode call alone (decode kernel + reduce kernel; with the
+    # fused step, pa_decode_append), back to back over n_calls calls, HIP
+    # events on its stream around the run.
     def dec_call(i):
+        if fused:
+            step_fused(i)
+            return
         kc, vc = sets[i % N_SETS]
         pa.pa_decode(out, q, kc, vc, tables, lens, b.max_seq_len, b.scale, b.k_scale, b.v_scale,
                      ps, ws, stream=stream, flags=pa.PA_DECODE_READ_ONCE)
@@ -895,7 +922,8 @@ def main(argv=None):
     gbs = kv_bytes / (ms_per_step / 1e3) / 1e9
     achieved = kv_bytes / (kern_us / 1e6) / 1e9
     call_gbs = kv_bytes / (call_us / 1e6) / 1e9
-    print(f"[bench] step {ms_per_step * 1e3:.1f} us (graph {graph_ms * 1e3 if graph_ms else -1:.1f}),"
+    print(f"[bench] step {ms_per_step * 1e3:.1f} us (graph {graph_ms * 1e3 if graph_ms else -1:.1f};"
+          f" as two calls {two_call_ms * 1e3:.1f}),"
           f" decode call {call_us:.1f} us, decode kernel {kern_us:.1f} us "
           f"(p10 {np.percentile(kern_ms, 10) * 1e3:.1f}, p90 {np.percentile(kern_ms, 90) * 1e3:.1f}),"
           f" {achieved:.0f} GB/s in the kernel", file=sys.stderr, flush=True)
@@ -939,7 +967,9 @@ def main(argv=None):
             f"{int(b.seq_lens.max())}] (seeded)", "sum_seq_lens": int(b.seq_lens.sum()),
             "pool_blocks": b.num_blocks, "partition_size": ps,
             "kv_bytes_per_step": kv_bytes, "input_sets_rotated": N_SETS,
-            "step": "pa_cache_write(new token per sequence) + pa_decode (split-K + LSE reduce)",
+            "step": ("pa_decode_append: each sequence's new token written into its slot inside "
+                     "the decode kernel, then the LSE reduce (one call)") if fused else
+                    "pa_cache_write(new token per sequence) + pa_decode (split-K + LSE reduce)",
         },
         "tokens_per_s": round(tokens_per_s, 1),
         "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
@@ -951,11 +981,13 @@ def main(argv=None):
             "timing": f"mean over {n_calls} launches of HIP events the library records right "
                       "around the kernel (pa_profile_next_decode, hipExtLaunchKernelGGL) on its "
                       "stream; achieved = algorithmic K/V bytes / avg_us",
-            "call": {"what": "pa_decode call = decode kernel + reduce kernel, back to back",
+            "call": {"what": ("pa_decode_append call" if fused else "pa_decode call") +
+                             " = decode kernel + reduce kernel, back to back",
                      "avg_us": round(call_us, 2), "achieved": round(call_gbs, 1),
                      "frac": round(call_gbs / HBM_PEAK_GBS, 4)},
         },
         "graph_ms_per_step": round(graph_ms, 5) if graph_ms else None,
+        "two_call_ms_per_step": round(two_call_ms, 5),
         "cpu_baseline": cpu,
     }
     if oracle_per_workload:

@@ -281,6 +281,44 @@ int32_t pa_decode(void* out, const void* query, int32_t q_dtype,
                   size_t workspace_bytes, void* stream);
 
 /*
+ * pa_decode_append — a decode step's cache write and decode in one call:
+ * each sequence's newest token is written into the pool and attended to.
+ *
+ * [LIB] §4.3 item 2 (each new token's K/V goes into the sequence's current
+ * block, the slot the block table gives) followed by [LIB] §4.4 items 1
+ * and 3 (pa_decode): for every sequence s with L = seq_lens[s] > 0, token
+ * L - 1 is the new one.  Its K and V rows k_new[s] and v_new[s] (bf16,
+ * [num_kv_heads][head_size] each) are stored at slot
+ *     block_tables[s][(L - 1) / block_size] * block_size + (L - 1) % block_size
+ * (an fp8 pool: quantised code = e4m3(x / k_scale) as pa_cache_write does),
+ * and the attention over all L tokens is computed with them.  The pool
+ * afterwards holds exactly what pa_cache_write with those slots leaves, and
+ * `out` equals pa_cache_write followed by pa_decode with partition_size
+ * PA_PARTITION_BALANCED and the same flags: the decode kernel writes the
+ * token where it reads the sequence's last block and uses the new rows in
+ * place of the slot's old contents, so the step needs no separate launch.
+ *
+ * Arguments as pa_decode (balanced split implied), plus
+ *   k_new, v_new   bf16 [num_seqs][num_kv_heads][head_size], 16-byte aligned,
+ *                  device memory; read only
+ * Supported: the matrix-core engine's shapes (bf16 queries, bf16 or fp8 pool,
+ * head_size 128, num_heads / num_kv_heads 4 or 8); elsewhere, or with
+ * PA_DECODE_ENGINE_VALU, PA_ERR_UNSUPPORTED (use pa_cache_write and
+ * pa_decode).  fp8 pools need k_scale, v_scale > 0.  Workspace: as pa_decode
+ * with PA_PARTITION_BALANCED.  Two sequences whose last tokens map to one
+ * slot are the caller's error (the writes race), as in pa_cache_write.
+ */
+int32_t pa_decode_append(void* out, const void* query, int32_t q_dtype,
+                         int32_t num_seqs, int32_t num_heads, int32_t head_size,
+                         const void* k_new, const void* v_new,
+                         const void* k_cache, const void* v_cache, int32_t cache_dtype,
+                         int32_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                         const int32_t* block_tables, int32_t max_blocks_per_seq,
+                         const int32_t* seq_lens, int32_t max_seq_len,
+                         float scale, float k_scale, float v_scale,
+                         int32_t flags, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * pa_decode_shared_prefix — pa_decode for a batch whose sequences all begin
  * with the same prefix_len tokens held in the same physical blocks.
  *

@@ -48,6 +48,9 @@ _SIGNATURES = {
     "pa_decode": ([_c_p, _c_p, _c_int, _c_int, _c_int, _c_int, _c_p, _c_p, _c_int, _c_int, _c_int,
                    _c_int, _c_p, _c_int, _c_p, _c_int, _c_f, _c_f, _c_f, _c_int, _c_int, _c_p,
                    _c_sz, _c_p], _c_int),
+    "pa_decode_append": ([_c_p, _c_p, _c_int, _c_int, _c_int, _c_int, _c_p, _c_p, _c_p, _c_p,
+                          _c_int, _c_int, _c_int, _c_int, _c_p, _c_int, _c_p, _c_int, _c_f, _c_f,
+                          _c_f, _c_int, _c_p, _c_sz, _c_p], _c_int),
     "pa_prefill_chunk": ([_c_p, _c_p, _c_int, _c_int, _c_int, _c_int, _c_p, _c_int, _c_int, _c_p,
                           _c_p, _c_int, _c_int, _c_int, _c_int, _c_p, _c_int, _c_p, _c_f, _c_f,
                           _c_f, _c_p], _c_int),
@@ -252,6 +255,32 @@ def pa_decode(out, query, k_cache, v_cache, block_tables, seq_lens, max_seq_len:
                             int(block_tables.shape[1]), _ptr(seq_lens), int(max_seq_len),
                             float(scale), float(k_scale), float(v_scale), int(partition_size),
                             int(flags), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def pa_decode_append(out, query, k_new, v_new, k_cache, v_cache, block_tables, seq_lens,
+                     max_seq_len: int, scale: float, k_scale: float = 1.0, v_scale: float = 1.0,
+                     workspace=None, stream=None, flags: int = 0) -> None:
+    """One decode step in one call: each sequence's newest token (position
+    seq_len - 1), given as bf16 rows k_new / v_new [num_seqs, num_kv_heads,
+    head_size], is written into the slot its block table gives and attended
+    to with the rest (the balanced split, as pa_decode).  The same pool and
+    output as pa_cache_write with those slots followed by pa_decode."""
+    import torch
+
+    nb, hkv, bs, d = _pool_dims(k_cache, v_cache)
+    S, H = int(query.shape[0]), int(query.shape[1])
+    if _validating():
+        validate_decode(block_tables, seq_lens, max_seq_len, nb, bs)
+    need = pa_decode_workspace_size(S, H, hkv, d, max_seq_len, PA_PARTITION_BALANCED)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=query.device)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(load().pa_decode_append(_ptr(out), _ptr(query), dtype_code(query), S, H, d,
+                                   _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+                                   dtype_code(k_cache), nb, bs, hkv, _ptr(block_tables),
+                                   int(block_tables.shape[1]), _ptr(seq_lens), int(max_seq_len),
+                                   float(scale), float(k_scale), float(v_scale), int(flags),
+                                   _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def pa_decode_no_alloc(out, query, k_cache, v_cache, block_tables, seq_lens, max_seq_len: int,

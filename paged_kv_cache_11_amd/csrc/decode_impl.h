@@ -1067,7 +1067,7 @@ hipError_t launch_decode(const DecodeArgs& a) {
                            a.merges, a.cuts, a.query, a.k_cache, a.v_cache, a.block_tables,
                            a.seq_lens,
                            a.num_seqs, a.max_blocks_per_seq, a.num_kv_heads, per_head, qk, v_scale,
-                           a.read_once, a.suffix);
+                           a.read_once, a.suffix, a.append);
     }
     if (!mfma)
       launch_main(a, decode_balanced_kernel<KV, QT, D, BS, G>, dim3((unsigned)wg),

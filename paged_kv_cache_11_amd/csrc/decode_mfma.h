@@ -103,11 +103,16 @@ struct MfmaAttn {
   f32x4 acc[kMD / 16];    // O^T: dims 16mb + 4g4 + i, head n
   float m_ref, l_lane;
   __bf16* vt;             // this wavefront's V^T tile in LDS
+  const __bf16* newk;     // fused append: the new token's K and V as the tile uses them (LDS)
+  const __bf16* newv;
 
   static constexpr int kLdsElems = KEYS * kVRow;
 
-  __device__ __forceinline__ void init(int lane_, float qk, __bf16* vt_) {
+  __device__ __forceinline__ void init(int lane_, float qk, __bf16* vt_, const __bf16* newk_ = nullptr,
+                                       const __bf16* newv_ = nullptr) {
     lane = lane_;
+    newk = newk_;
+    newv = newv_;
     n = lane % 16;
     g4 = lane / 16;
     vr = lane / CPR;
@@ -217,8 +222,10 @@ struct MfmaAttn {
     }
   }
 
-  // One tile: lim valid keys (tile-relative, a prefix).
-  __device__ __forceinline__ void tile(const Tile& T, int lim) {
+  // One tile: lim valid keys (tile-relative, a prefix).  app >= 0: tile
+  // row app is the appended token, whose K and V come from newk / newv
+  // instead of T and the pool.
+  __device__ __forceinline__ void tile(const Tile& T, int lim, int app = -1) {
     // S^T per 16-key group: independent chains of 4 MFMAs.
     f32x4 c[KG];
 #pragma unroll
@@ -229,9 +236,22 @@ struct MfmaAttn {
       for (int kg = 0; kg < KG; ++kg) {
         uint32_t a[4];
         k_operand(T, kg, s, a);
+        if (app >= 0 && kg == app / 16) {
+          const u32x4 w = *(const u32x4*)(newk + kstep_dim0(s));
+          const bool mine = n == app % 16;
+          a[0] = mine ? w.x : a[0];
+          a[1] = mine ? w.y : a[1];
+          a[2] = mine ? w.z : a[2];
+          a[3] = mine ? w.w : a[3];
+        }
         c[kg] = mfma16(a, q[s], c[kg]);
       }
     stage_v(T, lim);
+    if (app >= 0 && lane < 16) {
+      // Row app of the V tile (bf16 dims in order, as stage_v leaves every
+      // row), written again from the new token: 8 dims (16 bytes) per lane.
+      *(u32x4*)(vt + app * kVRow + 8 * lane) = *(const u32x4*)(newv + 8 * lane);
+    }
 
     float x[KG][4];
 #pragma unroll
@@ -297,9 +317,12 @@ struct MfmaAttn {
 
   // Units first .. first+count-1 (UBS tokens each) of a sequence of L
   // tokens, KV head g.
+  // app >= 0: the run ends at the sequence's end and its last key is the
+  // appended token (row app of the last tile).
   template <bool NT>
   __device__ __forceinline__ void stream(const void* k_cache, const void* v_cache, const int32_t* tbl,
-                                         int g, int num_kv_heads, int first, int count, int L) {
+                                         int g, int num_kv_heads, int first, int count, int L,
+                                         int app = -1) {
     if (count <= 0) return;
     const int64_t tile_bytes = (int64_t)BS * kMD * EB;
     const int64_t block_bytes = (int64_t)num_kv_heads * tile_bytes;
@@ -340,9 +363,9 @@ struct MfmaAttn {
       load_tile<NT>(kh, vh, block_bytes, k0_of(t + 1), bid, tb);
       tile(ta, limit(t));
       load_tile<NT>(kh, vh, block_bytes, k0_of(t + 2 < ntiles ? t + 2 : t + 1), bid, ta);
-      tile(tb, limit(t + 1));
+      tile(tb, limit(t + 1), t + 2 == ntiles ? app : -1);
     }
-    if (t < ntiles) tile(ta, limit(t));
+    if (t < ntiles) tile(ta, limit(t), app);
   }
 
   // Sum of the head's probabilities over its 4 lanes.
@@ -360,11 +383,13 @@ __global__ __launch_bounds__(kMaxDecodeWaves * kWave, 2) void decode_balanced_mf
     const void* __restrict__ k_cache, const void* __restrict__ v_cache,
     const int32_t* __restrict__ block_tables, const int32_t* __restrict__ seq_lens, int num_seqs,
     int max_blocks_per_seq, int num_kv_heads, int workers_per_head, float qk_scale_log2,
-    float v_scale, int read_once_hint, SuffixStates sx) {
+    float v_scale, int read_once_hint, SuffixStates sx, AppendTokens ap) {
   static_assert(std::is_same<QT, BF16>::value, "bf16 queries");
   using MA = MfmaAttn<KV, BS, G>;
   constexpr int D = kMD;
+  constexpr int EB = Elem<KV>::bytes;
   __shared__ __attribute__((aligned(16))) __bf16 vt_lds[kMaxDecodeWaves][MA::kLdsElems];
+  __shared__ __attribute__((aligned(16))) __bf16 new_lds[kMaxDecodeWaves][2][D];
   const int lane = threadIdx.x & (kWave - 1);
   const int wv = threadIdx.x / kWave;
   const int worker = blockIdx.x * (blockDim.x / kWave) + wv;
@@ -387,7 +412,47 @@ __global__ __launch_bounds__(kMaxDecodeWaves * kWave, 2) void decode_balanced_mf
   const int tbl_skip = sx.skip / BS;  // table entries of the skipped tokens
 
   MA A;
-  A.init(lane, qk_scale_log2, vt_lds[wv]);
+  A.init(lane, qk_scale_log2, vt_lds[wv], new_lds[wv][0], new_lds[wv][1]);
+
+  // Fused append: the run that reaches a sequence's end writes that
+  // sequence's new token (position L-1) for this KV head into its pool slot
+  // and keeps it in LDS as the tiles see it (an fp8 pool: quantised exactly
+  // as the cache write does, then widened back), so its last tile uses it
+  // instead of the slot's old contents.  Lanes 0..15 take 8 dims each.
+  auto append_token = [&](int q, int L, const int32_t* row) {
+    const int pos = L - 1;
+    const int64_t bid = row[pos / BS];
+    const int64_t slot_elem = ((bid * num_kv_heads + g) * BS + pos % BS) * (int64_t)D;
+    if (lane < 16) {
+      const int64_t src = ((int64_t)q * num_kv_heads + g) * D + 8 * lane;
+#pragma unroll
+      for (int kv = 0; kv < 2; ++kv) {
+        const u32x4 w = *(const u32x4*)((const uint16_t*)(kv ? ap.v : ap.k) + src);
+        uint8_t* pool = (uint8_t*)(kv ? v_cache : k_cache) + (slot_elem + 8 * lane) * EB;
+        u32x4 tw = w;  // the 8 dims as the tiles see them (bf16)
+        if constexpr (EB == 1) {
+          const float sc = kv ? ap.v_scale : ap.k_scale;
+          const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+          uint32_t b[2] = {0u, 0u};
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const float x = u2f((wd[j / 2] >> (16 * (j % 2))) << 16);
+            b[j / 4] |= f32_to_e4m3fn(x / sc) << (8 * (j % 4));
+          }
+          *(u32x2*)pool = u32x2{b[0], b[1]};
+          uint32_t lo0, hi0, lo1, hi1;
+          lo0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(b[0], 1.0f, false));
+          hi0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(b[0], 1.0f, true));
+          lo1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(b[1], 1.0f, false));
+          hi1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(b[1], 1.0f, true));
+          tw = u32x4{lo0, hi0, lo1, hi1};
+        } else {
+          *(u32x4*)pool = w;
+        }
+        *(u32x4*)(new_lds[wv][kv] + 8 * lane) = tw;
+      }
+    }
+  };
   int64_t pos = start;
   while (pos < end && s < num_seqs) {
     const int L = max(seq_lens[s] - sx.skip, 0);
@@ -400,10 +465,18 @@ __global__ __launch_bounds__(kMaxDecodeWaves * kWave, 2) void decode_balanced_mf
       A.reset();
       A.load_q(query, hq0);
       const int32_t* row = block_tables + (int64_t)s * max_blocks_per_seq + tbl_skip;
+      // The appended token's row in the run's last tile, if this run ends
+      // the sequence.
+      int app = -1;
+      if (ap.k && b_hi == nblk) {
+        append_token(s, L, row);
+        app = (L - 1) - (b_lo * MA::UBS + ((b_hi - b_lo) * MA::UBS + MA::KEYS - 1) / MA::KEYS * MA::KEYS -
+                         MA::KEYS);
+      }
       if (read_once)
-        A.template stream<true>(k_cache, v_cache, row, g, num_kv_heads, b_lo, b_hi - b_lo, L);
+        A.template stream<true>(k_cache, v_cache, row, g, num_kv_heads, b_lo, b_hi - b_lo, L, app);
       else
-        A.template stream<false>(k_cache, v_cache, row, g, num_kv_heads, b_lo, b_hi - b_lo, L);
+        A.template stream<false>(k_cache, v_cache, row, g, num_kv_heads, b_lo, b_hi - b_lo, L, app);
       const float l_tot = A.l_total();
       const bool whole = b_lo == 0 && b_hi == nblk;
       const int slot = pos == start ? 0 : 1;

@@ -225,9 +225,16 @@ int32_t pa::decode_call(void* out, const void* query, int32_t q_dtype, int32_t n
     return fail(PA_ERR_UNSUPPORTED,
                 "decode not built for q dtype %d, cache dtype %d, head_size %d, block_size %d, "
                 "group %d", q_dtype, cache_dtype, head_size, block_size, group);
-  const int32_t engine = decode_engine(flags, q_dtype, cache_dtype, head_size, group);
+  const bool append = extra && extra->append.k;
+  // The fused append runs on the matrix-core engine only.
+  const int32_t engine =
+      append ? ((flags & PA_DECODE_ENGINE_VALU) ? -1
+                                                : decode_engine(PA_DECODE_ENGINE_MFMA, q_dtype,
+                                                                cache_dtype, head_size, group))
+             : decode_engine(flags, q_dtype, cache_dtype, head_size, group);
   if (engine < 0)
-    return fail(PA_ERR_UNSUPPORTED, "the matrix-core decode engine is not built for this shape");
+    return fail(PA_ERR_UNSUPPORTED, "%s: the matrix-core decode engine is not built for this "
+                "shape%s", who, append ? " (the fused append needs it)" : "");
   if (num_seqs == 0) return ok();
   if (!out || !query || !block_tables || !seq_lens)
     return fail(PA_ERR_INVALID, "out / query / block_tables / seq_lens is NULL");
@@ -235,6 +242,13 @@ int32_t pa::decode_call(void* out, const void* query, int32_t q_dtype, int32_t n
   if (int32_t r = check_align(query, 16, "query")) return r;
   if (int32_t r = check_align(block_tables, 4, "block_tables")) return r;
   if (int32_t r = check_align(seq_lens, 4, "seq_lens")) return r;
+  if (append) {
+    if (!extra->append.v) return fail(PA_ERR_INVALID, "%s: v_new is NULL", who);
+    if (int32_t r = check_align(extra->append.k, 16, "k_new")) return r;
+    if (int32_t r = check_align(extra->append.v, 16, "v_new")) return r;
+    if (cache_dtype == PA_FP8_E4M3 && (!(k_scale > 0.f) || !(v_scale > 0.f)))
+      return fail(PA_ERR_INVALID, "%s: fp8 scales must be > 0", who);
+  }
   const int64_t mp = balanced ? 1 : decode_max_parts(max_seq_len, partition_size);
   if (!balanced && (num_seqs > kMaxGridYZ || num_kv_heads > kMaxGridYZ))
     return fail(PA_ERR_INVALID,
@@ -289,7 +303,12 @@ int32_t pa::decode_call(void* out, const void* query, int32_t q_dtype, int32_t n
   a.prof_stop = g_prof_stop;
   g_prof_start = g_prof_stop = nullptr;
   if (extra) {
-    if (!balanced) return fail(PA_ERR_INVALID, "%s: the suffix runs in the balanced split", who);
+    if (!balanced) return fail(PA_ERR_INVALID, "%s: runs in the balanced split", who);
+    if (append) {
+      a.append = extra->append;
+      a.append.k_scale = k_scale;
+      a.append.v_scale = v_scale;
+    }
     a.suffix = extra->suffix;
     a.prefix_acc = extra->prefix_acc;
     a.prefix_ml = extra->prefix_ml;
@@ -441,6 +460,25 @@ int32_t pa_decode(void* out, const void* query, int32_t q_dtype, int32_t num_seq
                      cache_dtype, num_blocks, block_size, num_kv_heads, block_tables,
                      max_blocks_per_seq, seq_lens, max_seq_len, scale, k_scale, v_scale,
                      partition_size, flags, workspace, workspace_bytes, stream, "pa_decode");
+}
+
+int32_t pa_decode_append(void* out, const void* query, int32_t q_dtype, int32_t num_seqs,
+                         int32_t num_heads, int32_t head_size, const void* k_new,
+                         const void* v_new, const void* k_cache, const void* v_cache,
+                         int32_t cache_dtype, int32_t num_blocks, int32_t block_size,
+                         int32_t num_kv_heads, const int32_t* block_tables,
+                         int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                         int32_t max_seq_len, float scale, float k_scale, float v_scale,
+                         int32_t flags, void* workspace, size_t workspace_bytes, void* stream) {
+  if (num_seqs > 0 && !k_new) return fail(PA_ERR_INVALID, "pa_decode_append: k_new is NULL");
+  pa::DecodeExtras x{};
+  x.append.k = num_seqs > 0 ? k_new : nullptr;
+  x.append.v = v_new;
+  return pa::decode_call(out, query, q_dtype, num_seqs, num_heads, head_size, k_cache, v_cache,
+                         cache_dtype, num_blocks, block_size, num_kv_heads, block_tables,
+                         max_blocks_per_seq, seq_lens, max_seq_len, scale, k_scale, v_scale,
+                         PA_PARTITION_BALANCED, flags, workspace, workspace_bytes, stream,
+                         "pa_decode_append", num_seqs > 0 ? &x : nullptr);
 }
 
 // Splits of a shared prefix: enough (query tile, KV head, split) workgroups

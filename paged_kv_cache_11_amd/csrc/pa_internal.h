@@ -58,6 +58,18 @@ struct MoveBlocksArgs {
 // unnormalised state in acc[s * num_heads + h][D], ml[...][2] instead of
 // its output (cut sequences leave their pieces as usual), for a merge with
 // the prefix's states.
+// Fused append (pa_decode_append): each sequence's newest token (position
+// seq_len - 1) arrives as bf16 K and V rows [num_seqs][num_kv_heads][head
+// size]; the decode kernel writes them into the pool slot the table gives
+// (quantised with k_scale / v_scale for an fp8 pool, as the cache write
+// does) and attends to them in place of the slot's old contents.  Null k:
+// a plain decode.
+struct AppendTokens {
+  const void* k;
+  const void* v;
+  float k_scale, v_scale;
+};
+
 struct SuffixStates {
   int skip;
   float* acc;
@@ -93,6 +105,7 @@ struct DecodeArgs {
   // prefix states ([(split * num_seqs + s) * num_heads + h][head_size] and
   // [...][2]) into the output.
   SuffixStates suffix;
+  AppendTokens append;
   const float* prefix_acc;
   const float* prefix_ml;
   int32_t prefix_splits;
@@ -180,6 +193,7 @@ int32_t decode_call(void* out, const void* query, int32_t q_dtype, int32_t num_s
 // What a shared-prefix decode adds to the balanced split (see DecodeArgs).
 struct DecodeExtras {
   SuffixStates suffix;
+  AppendTokens append;
   const float* prefix_acc;
   const float* prefix_ml;
   int32_t prefix_splits;

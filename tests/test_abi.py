@@ -99,6 +99,38 @@ def test_decode_rejects_bad_host_arguments(kw, code):
     assert pa.load().pa_last_error()
 
 
+def _append(**kw):
+    a = dict(out=P, query=P, q_dtype=pa.PA_BF16, num_seqs=4, num_heads=32, head_size=128,
+             k_new=P, v_new=P, k_cache=P, v_cache=P, cache_dtype=pa.PA_BF16, num_blocks=100,
+             block_size=16, num_kv_heads=8, block_tables=P, max_blocks_per_seq=8, seq_lens=P,
+             max_seq_len=128, scale=0.1, k_scale=1.0, v_scale=1.0, flags=0, workspace=None,
+             workspace_bytes=0, stream=None)
+    a.update(kw)
+    return pa.load().pa_decode_append(*a.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(k_new=None), pa.PA_ERR_INVALID),
+    (dict(v_new=None), pa.PA_ERR_INVALID),
+    (dict(k_new=ctypes.c_void_p(24)), pa.PA_ERR_INVALID),
+    # the fused append runs on the matrix-core engine only
+    (dict(flags=pa.PA_DECODE_ENGINE_VALU), pa.PA_ERR_UNSUPPORTED),
+    (dict(head_size=64), pa.PA_ERR_UNSUPPORTED),
+    (dict(num_heads=16), pa.PA_ERR_UNSUPPORTED),
+    (dict(q_dtype=pa.PA_F32, cache_dtype=pa.PA_F32, head_size=64), pa.PA_ERR_UNSUPPORTED),
+    (dict(cache_dtype=pa.PA_FP8_E4M3, k_scale=0.0),
+     pa.PA_ERR_INVALID),
+    (dict(), pa.PA_ERR_WORKSPACE),
+])
+def test_decode_append_rejects_bad_host_arguments(kw, code):
+    assert _append(**kw) == code
+    assert pa.load().pa_last_error()
+
+
+def test_decode_append_with_no_sequences_is_a_noop():
+    assert _append(num_seqs=0, out=None, query=None, k_new=None, v_new=None) == pa.PA_OK
+
+
 def test_decode_with_no_sequences_is_a_noop():
     assert _decode(num_seqs=0, out=None, query=None) == pa.PA_OK
 
