@@ -1,6 +1,6 @@
 """The decode step captured in a HIP graph: cache write + decode (balanced
-split: decode kernel + reduce kernel), the allocation-free decode, and the
-shared-prefix decode (prefix product + suffix decode + merge).  Each graph
+split: decode kernel + reduce kernel), the fused append, the allocation-free
+decode, and the shared-prefix decode (prefix product + suffix decode + merge).  Each graph
 is replayed several times with eager library work and synchronisations
 between the replays, and every replay must equal the eager result bit for
 bit (the kernels are deterministic and enqueue no memset)."""
@@ -72,6 +72,32 @@ def test_graph_cache_write_and_decode(llama):
                      b.scale, partition_size=BAL, workspace=ws)
 
     _replays_equal(step, lambda: [out.float().cpu().numpy()], step, disturb)
+
+
+def test_graph_decode_append(llama):
+    """The fused step (new tokens written inside the decode kernel) captured
+    and replayed; the pool is rewritten with the same tokens each replay."""
+    b, kp, vp, new = llama
+    k_new = wl.storage_tensor(b.k[new], "bf16").to(G.DEV)
+    v_new = wl.storage_tensor(b.v[new], "bf16").to(G.DEV)
+    q = G.query_tensor(b)
+    out = torch.empty_like(q)
+    tb, ln = torch.from_numpy(b.block_tables).to(G.DEV), torch.from_numpy(b.seq_lens).to(G.DEV)
+    ws = torch.empty(pa.pa_decode_workspace_size(b.num_seqs, b.num_heads, b.num_kv_heads,
+                                                 b.head_size, b.max_seq_len, BAL),
+                     dtype=torch.uint8, device=G.DEV)
+
+    def step():
+        pa.pa_decode_append(out, q, k_new, v_new, kp, vp, tb, ln, b.max_seq_len, b.scale,
+                            workspace=ws, flags=pa.PA_DECODE_READ_ONCE)
+
+    def disturb():
+        out.fill_(float("nan"))
+        pa.pa_decode(torch.empty_like(q), q, kp, vp, tb, (ln // 2).contiguous(), b.max_seq_len,
+                     b.scale, partition_size=BAL, workspace=ws)
+
+    _replays_equal(step, lambda: [out.float().cpu().numpy(), kp.view(torch.uint8).cpu().numpy()],
+                   step, disturb)
 
 
 def test_graph_no_alloc_decode(llama):
