@@ -860,9 +860,9 @@ def main(argv=None):
         torch.cuda.synchronize()
         return (time.perf_counter() - t0) / args.steps * 1e3
 
-    two_call_ms = time_steps(step_two_calls)
     step = step_fused if fused else step_two_calls
-    ms_per_step = time_steps(step) if fused else two_call_ms
+    ms_per_step = time_steps(step)
+    two_call_ms = time_steps(step_two_calls) if fused else ms_per_step
 
     kv_bytes = b.decode_kv_bytes()
     n_calls = max(args.steps, 200)
