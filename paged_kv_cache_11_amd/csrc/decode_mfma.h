@@ -319,11 +319,18 @@ struct MfmaAttn {
   // tokens, KV head g.
   // app >= 0: the run ends at the sequence's end and its last key is the
   // appended token (row app of the last tile).
+  // win_ok: win_v already holds the run's first block-id window (blocks
+  // 0..63; the run starts at the sequence's first unit).  nxt_v: a window
+  // load for the next run, in flight; the stream waits for it once its own
+  // first two tiles are requested, so it is never waited for later.
   template <bool NT>
   __device__ __forceinline__ void stream(const void* k_cache, const void* v_cache, const int32_t* tbl,
                                          int g, int num_kv_heads, int first, int count, int L,
-                                         int app = -1) {
-    if (count <= 0) return;
+                                         int app, int& nxt_v, int win_v, bool win_ok) {
+    if (count <= 0) {
+      asm volatile("" ::"v"(nxt_v));
+      return;
+    }
     const int64_t tile_bytes = (int64_t)BS * kMD * EB;
     const int64_t block_bytes = (int64_t)num_kv_heads * tile_bytes;
     const uint8_t* kh = (const uint8_t*)k_cache + (int64_t)g * tile_bytes;
@@ -337,7 +344,7 @@ struct MfmaAttn {
     // Block ids of the run, 64 at a time, one per lane (the requests come
     // in non-decreasing order); past the run the last block is repeated
     // (its keys are masked).
-    int bid_v = 0, cached = -1;
+    int bid_v = win_v, cached = win_ok ? 0 : -1;
     auto bid = [&](int blk) -> int {
       const int j = (blk < blk_last ? blk : blk_last) - blk0;
       const int chunk = j / kWave;
@@ -356,16 +363,28 @@ struct MfmaAttn {
       return lim < KEYS ? lim : KEYS;
     };
     auto k0_of = [&](int t) { return key0 + t * KEYS; };
+    // Two tiles per pass, each loaded one tile ahead; the last one or two
+    // tiles are taken after the loop, so every load is used and none is in
+    // flight when the run ends.
     Tile ta, tb;
     load_tile<NT>(kh, vh, block_bytes, k0_of(0), bid, ta);
     int t = 0;
-    for (; t + 2 <= ntiles; t += 2) {
+    for (; t + 3 <= ntiles; t += 2) {
       load_tile<NT>(kh, vh, block_bytes, k0_of(t + 1), bid, tb);
+      asm volatile("" ::"v"(nxt_v));  // (no wait after the first pass)
       tile(ta, limit(t));
-      load_tile<NT>(kh, vh, block_bytes, k0_of(t + 2 < ntiles ? t + 2 : t + 1), bid, ta);
-      tile(tb, limit(t + 1), t + 2 == ntiles ? app : -1);
+      load_tile<NT>(kh, vh, block_bytes, k0_of(t + 2), bid, ta);
+      tile(tb, limit(t + 1));
     }
-    if (t < ntiles) tile(ta, limit(t), app);
+    if (t + 2 == ntiles) {
+      load_tile<NT>(kh, vh, block_bytes, k0_of(t + 1), bid, tb);
+      asm volatile("" ::"v"(nxt_v));
+      tile(ta, limit(t));
+      tile(tb, limit(t + 1), app);
+    } else {
+      asm volatile("" ::"v"(nxt_v));
+      tile(ta, limit(t), app);
+    }
   }
 
   // Sum of the head's probabilities over its 4 lanes.
@@ -453,9 +472,25 @@ __global__ __launch_bounds__(kMaxDecodeWaves * kWave, 2) void decode_balanced_mf
       }
     }
   };
+  // Lengths of sequences len_base .. len_base + 63, one per lane (the last
+  // sequence's repeated past the end), so that a run's start does not wait
+  // for a load of its length.
+  int len_base = s, len_v = seq_lens[min(s + lane, num_seqs - 1)];
+  asm volatile("" : "+v"(len_v));
+  auto len_at = [&](int q) -> int {  // q >= len_base, wavefront-uniform
+    if (q - len_base >= kWave) {
+      len_base = q;
+      len_v = seq_lens[min(q + lane, num_seqs - 1)];
+      asm volatile("" : "+v"(len_v));
+    }
+    return __builtin_amdgcn_readlane(len_v, q - len_base);
+  };
+  // The block-id window (blocks 0..63) of the sequence win_s, loaded while
+  // the previous run streamed; the next run uses it if it is that sequence.
+  int win_v = 0, win_s = -1;
   int64_t pos = start;
   while (pos < end && s < num_seqs) {
-    const int L = max(seq_lens[s] - sx.skip, 0);
+    const int L = max(len_at(s) - sx.skip, 0);
     const int nblk = nblocks_of(L, MA::UBS);  // units of the split
     const int64_t seg_end = base + nblk;
     if (nblk > 0) {
@@ -473,10 +508,34 @@ __global__ __launch_bounds__(kMaxDecodeWaves * kWave, 2) void decode_balanced_mf
         app = (L - 1) - (b_lo * MA::UBS + ((b_hi - b_lo) * MA::UBS + MA::KEYS - 1) / MA::KEYS * MA::KEYS -
                          MA::KEYS);
       }
+      // The next run's sequence: the next one with keys among the lengths at
+      // hand (else none is prefetched).  Its window is requested now, one
+      // load whatever the case (a harmless table read when there is none).
+      int sn = -1, ln = 0;
+      {
+        const int rel = s + 1 - len_base;
+        if (rel < kWave) {
+          const uint64_t more = __builtin_amdgcn_ballot_w64(len_base + lane < num_seqs &&
+                                                            len_v > sx.skip) &
+                                (~0ull << rel);
+          if (more) {
+            sn = len_base + __builtin_ctzll(more);
+            ln = __builtin_amdgcn_readlane(len_v, sn - len_base) - sx.skip;
+          }
+        }
+      }
+      const int last_n = ln > 0 ? (ln - 1) / BS : 0;
+      int nxt_v = block_tables[(int64_t)(sn >= 0 ? sn : s) * max_blocks_per_seq + tbl_skip +
+                               (lane < last_n ? lane : last_n)];
+      const bool win_ok = win_s == s && b_lo == 0;
       if (read_once)
-        A.template stream<true>(k_cache, v_cache, row, g, num_kv_heads, b_lo, b_hi - b_lo, L, app);
+        A.template stream<true>(k_cache, v_cache, row, g, num_kv_heads, b_lo, b_hi - b_lo, L, app,
+                                nxt_v, win_v, win_ok);
       else
-        A.template stream<false>(k_cache, v_cache, row, g, num_kv_heads, b_lo, b_hi - b_lo, L, app);
+        A.template stream<false>(k_cache, v_cache, row, g, num_kv_heads, b_lo, b_hi - b_lo, L, app,
+                                 nxt_v, win_v, win_ok);
+      win_v = nxt_v;
+      win_s = sn;
       const float l_tot = A.l_total();
       const bool whole = b_lo == 0 && b_hi == nblk;
       const int slot = pos == start ? 0 : 1;
