@@ -908,6 +908,91 @@ __global__ __launch_bounds__(D) void balanced_reduce_tasks_kernel(
   merge_cut<OT, D, G>(out, part_acc, part_ml, s, vw, code, h, g, d, num_kv_heads, v_scale);
 }
 
+// The same merges with one wavefront per (sequence, KV head), for
+// D G >= 256: lane l merges D G / 64 consecutive outputs of head
+// l / (64 / G) from 16-byte state loads, the states of eight pieces loaded
+// together (one reference raise per eight), and writes them; empty
+// sequences get zeros, whole ones were finished by their worker.  A
+// quarter as many workgroups as sequences x KV heads, where the kernels
+// above take G D-thread workgroups per sequence and KV head.
+constexpr int kReduceWaves = 4;
+
+template <typename OT, int D, int G>
+__global__ __launch_bounds__(kReduceWaves * kWave) void balanced_reduce_wave_kernel(
+    void* __restrict__ out, const float* __restrict__ part_acc,
+    const float* __restrict__ part_ml, const int32_t* __restrict__ cuts,
+    const int32_t* __restrict__ seq_lens, int num_seqs, int num_kv_heads, float v_scale) {
+  constexpr int kLanesPerHead = kWave / G, kDims = D / kLanesPerHead, kVecs = kDims / 4;
+  constexpr int kBatch = 8;
+  static_assert(kDims % 4 == 0, "whole 4-element groups per lane");
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t item = (int64_t)blockIdx.x * kReduceWaves +
+                       __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+  if (item >= (int64_t)num_seqs * num_kv_heads) return;
+  const int s = (int)(item / num_kv_heads), g = (int)(item % num_kv_heads);
+  const int h = lane / kLanesPerHead, d0 = (lane % kLanesPerHead) * kDims;
+  const int L = seq_lens[s];
+  const int va = cuts[2 * item + 0], code = cuts[2 * item + 1];
+  const int np = code >> 1, slot0 = code & 1;
+  if (L > 0 && np <= 1) return;  // a whole sequence: finished by its worker
+  float num[kVecs][4], den = 0.f, M = -INFINITY;
+#pragma unroll
+  for (int v = 0; v < kVecs; ++v)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) num[v][i] = 0.f;
+  for (int p0 = 0; L > 0 && p0 < np; p0 += kBatch) {
+    float m[kBatch], l[kBatch];
+    f32x4 a[kBatch][kVecs];
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q) {
+      const int p = p0 + q < np ? p0 + q : np - 1;
+      const int64_t st =
+          ((int64_t)((va + p) * num_kv_heads + g) * 2 + (p == 0 ? slot0 : 0)) * G + h;
+      m[q] = part_ml[2 * st];
+      l[q] = part_ml[2 * st + 1];
+#pragma unroll
+      for (int v = 0; v < kVecs; ++v) a[q][v] = *(const f32x4*)(part_acc + st * D + d0 + 4 * v);
+    }
+    float bm = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q) bm = p0 + q < np ? fmaxf(bm, m[q]) : bm;
+    if (bm > M) {
+      const float f = M == -INFINITY ? 0.f : fast_exp2(M - bm);
+#pragma unroll
+      for (int v = 0; v < kVecs; ++v)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) num[v][i] *= f;
+      den *= f;
+      M = bm;
+    }
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q) {
+      const float e = (p0 + q >= np || M == -INFINITY) ? 0.f : fast_exp2(m[q] - M);
+#pragma unroll
+      for (int v = 0; v < kVecs; ++v)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) num[v][i] = __builtin_fmaf(e, a[q][v][i], num[v][i]);
+      den = __builtin_fmaf(e, l[q], den);
+    }
+  }
+  // As merge_cut: num / den (0 when den is 0, as for an empty sequence)
+  // times v_scale, rounded once.
+  const int64_t o = ((int64_t)s * num_kv_heads * G + g * G + h) * D + d0;
+#pragma unroll
+  for (int v = 0; v < kVecs; ++v) {
+    float x[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = (den > 0.f ? num[v][i] / den : 0.f) * v_scale;
+    if constexpr (std::is_same<OT, F32>::value) {
+      *(f32x4*)((float*)out + o + 4 * v) = f32x4{x[0], x[1], x[2], x[3]};
+    } else {
+      const uint32_t w0 = (uint32_t)f32_to_bf16_rne(x[0]) | ((uint32_t)f32_to_bf16_rne(x[1]) << 16);
+      const uint32_t w1 = (uint32_t)f32_to_bf16_rne(x[2]) | ((uint32_t)f32_to_bf16_rne(x[3]) << 16);
+      *(u32x2*)((uint16_t*)out + o + 4 * v) = u32x2{w0, w1};
+    }
+  }
+}
+
 // The last step of a shared-prefix decode: the log-sum-exp merge of each
 // sequence's suffix (its pieces when the balanced split cut it, else the
 // whole-sequence state the suffix mode kept) with the prefix's splits.
@@ -999,6 +1084,123 @@ __global__ __launch_bounds__(kMergeThreads) void prefix_merge_kernel(
   }
 }
 
+// prefix_merge_kernel with one wavefront per (sequence, KV head), for
+// D G >= 256 (the layout of balanced_reduce_wave_kernel): the cut record,
+// the prefix splits' states and the suffix's states (its whole-sequence
+// state, or the pieces of a cut suffix, which wait for the cut record only)
+// are requested four at a time, the prefix's and the suffix's first four
+// together, before any is used.
+template <int D, int G>
+struct MergeBatch {
+  static constexpr int kLanesPerHead = kWave / G, kDims = D / kLanesPerHead, kVecs = kDims / 4;
+  static constexpr int kN = 4;
+  float m[kN], l[kN];
+  f32x4 a[kN][kVecs];
+  // States idx(0 .. n-1) from q0 on (at most kN; the rest repeat the last).
+  template <typename IndexFn>
+  __device__ __forceinline__ void load(const float* ml, const float* acc, int q0, int n, int d0,
+                                       IndexFn idx) {
+#pragma unroll
+    for (int q = 0; q < kN; ++q) {
+      const int64_t st = idx(q0 + q < n ? q0 + q : n - 1);
+      m[q] = ml[2 * st];
+      l[q] = ml[2 * st + 1];
+#pragma unroll
+      for (int v = 0; v < kVecs; ++v) a[q][v] = *(const f32x4*)(acc + st * D + d0 + 4 * v);
+    }
+  }
+  // Adds states q0 .. min(n, q0 + kN) - 1 (states with m = -inf hold no
+  // keys and are skipped) to the running (M, den, num).
+  __device__ __forceinline__ void absorb(int q0, int n, float& M, float& den,
+                                         float (&num)[kVecs][4]) const {
+    float bm = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < kN; ++q) bm = q0 + q < n ? fmaxf(bm, m[q]) : bm;
+    if (bm > M) {
+      const float f = M == -INFINITY ? 0.f : fast_exp2(M - bm);
+#pragma unroll
+      for (int v = 0; v < kVecs; ++v)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) num[v][i] *= f;
+      den *= f;
+      M = bm;
+    }
+#pragma unroll
+    for (int q = 0; q < kN; ++q) {
+      const float e = (q0 + q >= n || m[q] == -INFINITY) ? 0.f : fast_exp2(m[q] - M);
+#pragma unroll
+      for (int v = 0; v < kVecs; ++v)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) num[v][i] = __builtin_fmaf(e, a[q][v][i], num[v][i]);
+      den = __builtin_fmaf(e, l[q], den);
+    }
+  }
+};
+
+template <typename OT, int D, int G>
+__global__ __launch_bounds__(kReduceWaves * kWave) void prefix_merge_wave_kernel(
+    void* __restrict__ out, const float* __restrict__ part_acc,
+    const float* __restrict__ part_ml, const int32_t* __restrict__ cuts,
+    const int32_t* __restrict__ seq_lens, int num_seqs, int num_kv_heads, float v_scale,
+    SuffixStates sx, const float* __restrict__ prefix_acc, const float* __restrict__ prefix_ml,
+    int prefix_splits) {
+  using MB = MergeBatch<D, G>;
+  constexpr int kVecs = MB::kVecs;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t item = (int64_t)blockIdx.x * kReduceWaves +
+                       __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+  if (item >= (int64_t)num_seqs * num_kv_heads) return;
+  const int s = (int)(item / num_kv_heads), g = (int)(item % num_kv_heads);
+  const int h = lane / MB::kLanesPerHead, d0 = (lane % MB::kLanesPerHead) * MB::kDims;
+  const int num_heads = num_kv_heads * G;
+  const int64_t hq = (int64_t)s * num_heads + g * G + h;
+  const bool has_suffix = seq_lens[s] > sx.skip;
+  const int va = cuts[2 * item + 0], code = cuts[2 * item + 1];
+  const int np = code >> 1, slot0 = code & 1;
+  // The suffix's states: the whole-sequence state (np <= 1) or the pieces.
+  const int ns = has_suffix ? (np <= 1 ? 1 : np) : 0;
+  auto prefix_idx = [&](int c) -> int64_t { return (int64_t)c * num_seqs * num_heads + hq; };
+  auto piece_idx = [&](int p) -> int64_t {
+    return ((int64_t)((va + p) * num_kv_heads + g) * 2 + (p == 0 ? slot0 : 0)) * G + h;
+  };
+  const bool whole = np <= 1;
+  const float* s_ml = whole ? sx.ml : part_ml;
+  const float* s_acc = whole ? sx.acc : part_acc;
+  auto suffix_idx = [&](int p) -> int64_t { return whole ? hq : piece_idx(p); };
+  float M = -INFINITY, den = 0.f, num[kVecs][4];
+#pragma unroll
+  for (int v = 0; v < kVecs; ++v)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) num[v][i] = 0.f;
+  MB pb, sb;
+  if (prefix_splits > 0) pb.load(prefix_ml, prefix_acc, 0, prefix_splits, d0, prefix_idx);
+  if (ns > 0) sb.load(s_ml, s_acc, 0, ns, d0, suffix_idx);
+  if (prefix_splits > 0) pb.absorb(0, prefix_splits, M, den, num);
+  for (int c0 = MB::kN; c0 < prefix_splits; c0 += MB::kN) {
+    pb.load(prefix_ml, prefix_acc, c0, prefix_splits, d0, prefix_idx);
+    pb.absorb(c0, prefix_splits, M, den, num);
+  }
+  if (ns > 0) sb.absorb(0, ns, M, den, num);
+  for (int p0 = MB::kN; p0 < ns; p0 += MB::kN) {
+    sb.load(s_ml, s_acc, p0, ns, d0, suffix_idx);
+    sb.absorb(p0, ns, M, den, num);
+  }
+  const float inv = den > 0.f ? v_scale / den : 0.f;
+  const int64_t o = hq * D + d0;
+#pragma unroll
+  for (int v = 0; v < kVecs; ++v) {
+    const float x0 = num[v][0] * inv, x1 = num[v][1] * inv;
+    const float x2 = num[v][2] * inv, x3 = num[v][3] * inv;
+    if constexpr (std::is_same<OT, F32>::value) {
+      *(f32x4*)((float*)out + o + 4 * v) = f32x4{x0, x1, x2, x3};
+    } else {
+      const uint32_t w0 = (uint32_t)f32_to_bf16_rne(x0) | ((uint32_t)f32_to_bf16_rne(x1) << 16);
+      const uint32_t w1 = (uint32_t)f32_to_bf16_rne(x2) | ((uint32_t)f32_to_bf16_rne(x3) << 16);
+      *(u32x2*)((uint16_t*)out + o + 4 * v) = u32x2{w0, w1};
+    }
+  }
+}
+
 // Log-sum-exp merge of the fixed partitions of one (query head, KV head,
 // sequence), one output element per thread: partition p of query head h
 // left (m_p, l_p, o_p) with o_p normalised;
@@ -1078,8 +1280,16 @@ hipError_t launch_decode(const DecodeArgs& a) {
                          kSubShift, a.read_once, a.suffix);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (a.prefix_acc)
-      hipLaunchKernelGGL((prefix_merge_kernel<QT, D, G>),
+    if (a.prefix_acc) {
+      if constexpr (D * G >= 4 * kWave)
+        hipLaunchKernelGGL((prefix_merge_wave_kernel<QT, D, G>),
+                         dim3((unsigned)(((int64_t)a.num_seqs * a.num_kv_heads + kReduceWaves - 1) /
+                                         kReduceWaves)),
+                         dim3(kReduceWaves * kWave), 0, a.stream, a.out, a.part_o, a.part_ml,
+                         a.cuts, a.seq_lens, a.num_seqs, a.num_kv_heads, v_scale, a.suffix,
+                         a.prefix_acc, a.prefix_ml, a.prefix_splits);
+      else
+        hipLaunchKernelGGL((prefix_merge_kernel<QT, D, G>),
                          dim3((unsigned)a.num_seqs,
                               (unsigned)((a.num_heads * D + 4 * kMergeThreads - 1) /
                                          (4 * kMergeThreads))),
@@ -1087,6 +1297,12 @@ hipError_t launch_decode(const DecodeArgs& a) {
                          0, a.stream, a.out, a.part_o, a.part_ml, a.cuts, a.seq_lens, a.num_seqs,
                          a.num_kv_heads, v_scale, a.suffix, a.prefix_acc, a.prefix_ml,
                          a.prefix_splits);
+    } else if constexpr (D * G >= 4 * kWave)
+      hipLaunchKernelGGL((balanced_reduce_wave_kernel<QT, D, G>),
+                         dim3((unsigned)(((int64_t)a.num_seqs * a.num_kv_heads + kReduceWaves - 1) /
+                                         kReduceWaves)),
+                         dim3(kReduceWaves * kWave), 0, a.stream, a.out, a.part_o, a.part_ml,
+                         a.cuts, a.seq_lens, a.num_seqs, a.num_kv_heads, v_scale);
     else if (a.num_seqs <= per_head)
       hipLaunchKernelGGL((balanced_reduce_kernel<QT, D, G>),
                          dim3((unsigned)G, (unsigned)a.num_kv_heads, (unsigned)a.num_seqs), dim3(D),
