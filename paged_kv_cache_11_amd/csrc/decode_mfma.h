@@ -321,14 +321,16 @@ struct MfmaAttn {
   // appended token (row app of the last tile).
   // win_ok: win_v already holds the run's first block-id window (blocks
   // 0..63; the run starts at the sequence's first unit).  nxt_v: a window
-  // load for the next run, in flight; the stream waits for it once its own
-  // first two tiles are requested, so it is never waited for later.
+  // load for the next run, in flight; once the run's first two tiles are
+  // requested the stream waits for it and parks it in this lane's slot of
+  // nxt_lds, where the next run finds it (kept out of the registers that
+  // outlive the run, so that nothing loaded is waited for between runs).
   template <bool NT>
   __device__ __forceinline__ void stream(const void* k_cache, const void* v_cache, const int32_t* tbl,
                                          int g, int num_kv_heads, int first, int count, int L,
-                                         int app, int& nxt_v, int win_v, bool win_ok) {
+                                         int app, int nxt_v, int* nxt_lds, int win_v, bool win_ok) {
     if (count <= 0) {
-      asm volatile("" ::"v"(nxt_v));
+      nxt_lds[lane] = nxt_v;
       return;
     }
     const int64_t tile_bytes = (int64_t)BS * kMD * EB;
@@ -371,18 +373,18 @@ struct MfmaAttn {
     int t = 0;
     for (; t + 3 <= ntiles; t += 2) {
       load_tile<NT>(kh, vh, block_bytes, k0_of(t + 1), bid, tb);
-      asm volatile("" ::"v"(nxt_v));  // (no wait after the first pass)
+      nxt_lds[lane] = nxt_v;  // (no wait after the first pass)
       tile(ta, limit(t));
       load_tile<NT>(kh, vh, block_bytes, k0_of(t + 2), bid, ta);
       tile(tb, limit(t + 1));
     }
     if (t + 2 == ntiles) {
       load_tile<NT>(kh, vh, block_bytes, k0_of(t + 1), bid, tb);
-      asm volatile("" ::"v"(nxt_v));
+      nxt_lds[lane] = nxt_v;
       tile(ta, limit(t));
       tile(tb, limit(t + 1), app);
     } else {
-      asm volatile("" ::"v"(nxt_v));
+      nxt_lds[lane] = nxt_v;
       tile(ta, limit(t), app);
     }
   }
@@ -409,6 +411,7 @@ __global__ __launch_bounds__(kMaxDecodeWaves * kWave, 2) void decode_balanced_mf
   constexpr int EB = Elem<KV>::bytes;
   __shared__ __attribute__((aligned(16))) __bf16 vt_lds[kMaxDecodeWaves][MA::kLdsElems];
   __shared__ __attribute__((aligned(16))) __bf16 new_lds[kMaxDecodeWaves][2][D];
+  __shared__ int win_lds[kMaxDecodeWaves][kWave];  // the next run's block-id window
   const int lane = threadIdx.x & (kWave - 1);
   const int wv = threadIdx.x / kWave;
   const int worker = blockIdx.x * (blockDim.x / kWave) + wv;
@@ -486,8 +489,9 @@ __global__ __launch_bounds__(kMaxDecodeWaves * kWave, 2) void decode_balanced_mf
     return __builtin_amdgcn_readlane(len_v, q - len_base);
   };
   // The block-id window (blocks 0..63) of the sequence win_s, loaded while
-  // the previous run streamed; the next run uses it if it is that sequence.
-  int win_v = 0, win_s = -1;
+  // the previous run streamed and parked in win_lds; the next run uses it if
+  // it is that sequence.
+  int win_s = -1;
   int64_t pos = start;
   while (pos < end && s < num_seqs) {
     const int L = max(len_at(s) - sx.skip, 0);
@@ -528,13 +532,13 @@ __global__ __launch_bounds__(kMaxDecodeWaves * kWave, 2) void decode_balanced_mf
       int nxt_v = block_tables[(int64_t)(sn >= 0 ? sn : s) * max_blocks_per_seq + tbl_skip +
                                (lane < last_n ? lane : last_n)];
       const bool win_ok = win_s == s && b_lo == 0;
+      const int win_v = win_ok ? win_lds[wv][lane] : 0;
       if (read_once)
         A.template stream<true>(k_cache, v_cache, row, g, num_kv_heads, b_lo, b_hi - b_lo, L, app,
-                                nxt_v, win_v, win_ok);
+                                nxt_v, win_lds[wv], win_v, win_ok);
       else
         A.template stream<false>(k_cache, v_cache, row, g, num_kv_heads, b_lo, b_hi - b_lo, L, app,
-                                 nxt_v, win_v, win_ok);
-      win_v = nxt_v;
+                                 nxt_v, win_lds[wv], win_v, win_ok);
       win_s = sn;
       const float l_tot = A.l_total();
       const bool whole = b_lo == 0 && b_hi == nblk;
