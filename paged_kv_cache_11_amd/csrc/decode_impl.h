@@ -626,11 +626,18 @@ constexpr int kScanChunks = 16;
 __device__ __forceinline__ void load_len_batch(const int32_t* seq_lens, int num_seqs, int c0,
                                                int lane, int bs, int skip,
                                                int (&nb)[kScanChunks]) {
+  // Every load is issued unconditionally (past the end it reads the last
+  // length again, then ignores it): a load under a condition gets its own
+  // wait, which would serialise the batch.
 #pragma unroll
   for (int b = 0; b < kScanChunks; ++b) {
     const int s = c0 + b * kWave + lane;
-    nb[b] = s < num_seqs ? seq_lens[s] - skip : 0;
-    nb[b] = nb[b] > 0 ? nb[b] : 0;
+    nb[b] = seq_lens[s < num_seqs ? s : num_seqs - 1];
+  }
+#pragma unroll
+  for (int b = 0; b < kScanChunks; ++b) {
+    const int s = c0 + b * kWave + lane;
+    nb[b] = s < num_seqs && nb[b] > skip ? nb[b] - skip : 0;
   }
 #pragma unroll
   for (int b = 0; b < kScanChunks; ++b) nb[b] = nblocks_of(nb[b], bs);
@@ -692,6 +699,56 @@ __device__ __forceinline__ void locate_block(const int32_t* seq_lens, int num_se
   }
   s_out = num_seqs;
   base_out = base;
+}
+
+// The same two questions from one load of every length, where they fit one
+// batch (num_seqs <= kScanChunks * 64): raw[b] holds seq_lens[64 b + lane]
+// (0 past num_seqs), from which the total and the located sequence follow
+// with no second pass over memory.
+__device__ __forceinline__ void load_all_lens(const int32_t* seq_lens, int num_seqs, int lane,
+                                              int (&raw)[kScanChunks]) {
+#pragma unroll
+  for (int b = 0; b < kScanChunks; ++b) raw[b] = seq_lens[min(b * kWave + lane, num_seqs - 1)];
+#pragma unroll
+  for (int b = 0; b < kScanChunks; ++b) raw[b] = b * kWave + lane < num_seqs ? raw[b] : 0;
+}
+
+__device__ __forceinline__ int64_t total_blocks_of(const int (&raw)[kScanChunks], int bs, int skip) {
+  int t = 0;
+#pragma unroll
+  for (int b = 0; b < kScanChunks; ++b) t += nblocks_of(raw[b] > skip ? raw[b] - skip : 0, bs);
+  return wave_sum(t);
+}
+
+__device__ __forceinline__ void locate_block_of(const int (&raw)[kScanChunks], int num_seqs, int bs,
+                                                int skip, int64_t x, int& s_out,
+                                                int64_t& base_out) {
+  int64_t base = 0;
+#pragma unroll
+  for (int b = 0; b < kScanChunks; ++b) {
+    if (b * kWave >= num_seqs) break;
+    const int nb = nblocks_of(raw[b] > skip ? raw[b] - skip : 0, bs);
+    const int incl = wave_scan_incl(nb);
+    const int chunk = __builtin_amdgcn_readlane(incl, kWave - 1);
+    if (base + chunk > x) {
+      const uint64_t found = __builtin_amdgcn_ballot_w64(base + incl > x);
+      const int k = __builtin_ctzll(found);
+      s_out = b * kWave + k;
+      base_out = base + __builtin_amdgcn_readlane(incl - nb, k);
+      return;
+    }
+    base += chunk;
+  }
+  s_out = num_seqs;
+  base_out = base;
+}
+
+// raw[b] for a wavefront-uniform b.
+__device__ __forceinline__ int lens_chunk(const int (&raw)[kScanChunks], int b) {
+  int v = 0;
+#pragma unroll
+  for (int i = 0; i < kScanChunks; ++i) v = i == b ? raw[i] : v;
+  return v;
 }
 
 __device__ __forceinline__ int64_t worker_start(int64_t T, int v, int W) { return T * v / W; }

@@ -419,7 +419,13 @@ __global__ __launch_bounds__(kMaxDecodeWaves * kWave, 2) void decode_balanced_mf
   if (vw >= workers_per_head) return;
   const int num_heads = num_kv_heads * G;
 
-  const int64_t T = total_blocks(seq_lens, num_seqs, MA::UBS, sx.skip, lane);
+  // Every length in one load where they fit one batch (the total, the
+  // worker's first sequence and its window of lengths all come from it).
+  const bool one_load = num_seqs <= kScanChunks * kWave;
+  int raw[kScanChunks];
+  if (one_load) load_all_lens(seq_lens, num_seqs, lane, raw);
+  const int64_t T = one_load ? total_blocks_of(raw, MA::UBS, sx.skip)
+                             : total_blocks(seq_lens, num_seqs, MA::UBS, sx.skip, lane);
   const int W = effective_workers(T, workers_per_head, MA::UBS);
   // The caller declared that no block is read twice: evict-first loads.
   const bool read_once = read_once_hint != 0;
@@ -430,7 +436,8 @@ __global__ __launch_bounds__(kMaxDecodeWaves * kWave, 2) void decode_balanced_mf
   if (start >= end) return;
   int s;
   int64_t base;
-  locate_block(seq_lens, num_seqs, MA::UBS, sx.skip, start, lane, s, base);
+  if (one_load) locate_block_of(raw, num_seqs, MA::UBS, sx.skip, start, s, base);
+  else locate_block(seq_lens, num_seqs, MA::UBS, sx.skip, start, lane, s, base);
   const int tbl_skip = sx.skip / BS;  // table entries of the skipped tokens
 
   MA A;
@@ -475,11 +482,18 @@ __global__ __launch_bounds__(kMaxDecodeWaves * kWave, 2) void decode_balanced_mf
       }
     }
   };
-  // Lengths of sequences len_base .. len_base + 63, one per lane (the last
-  // sequence's repeated past the end), so that a run's start does not wait
-  // for a load of its length.
-  int len_base = s, len_v = seq_lens[min(s + lane, num_seqs - 1)];
-  asm volatile("" : "+v"(len_v));
+  // Lengths of sequences len_base .. len_base + 63, one per lane (past the
+  // end: 0, or the last sequence's repeated), so that a run's start does not
+  // wait for a load of its length.
+  int len_base, len_v;
+  if (one_load) {
+    len_base = s & ~(kWave - 1);
+    len_v = lens_chunk(raw, s / kWave);
+  } else {
+    len_base = s;
+    len_v = seq_lens[min(s + lane, num_seqs - 1)];
+    asm volatile("" : "+v"(len_v));
+  }
   auto len_at = [&](int q) -> int {  // q >= len_base, wavefront-uniform
     if (q - len_base >= kWave) {
       len_base = q;
