@@ -965,31 +965,40 @@ __global__ __launch_bounds__(D) void balanced_reduce_tasks_kernel(
   merge_cut<OT, D, G>(out, part_acc, part_ml, s, vw, code, h, g, d, num_kv_heads, v_scale);
 }
 
-// The same merges with one wavefront per (sequence, KV head), for
-// D G >= 256: lane l merges D G / 64 consecutive outputs of head
-// l / (64 / G) from 16-byte state loads, the states of eight pieces loaded
-// together (one reference raise per eight), and writes them; empty
-// sequences get zeros, whole ones were finished by their worker.  A
-// quarter as many workgroups as sequences x KV heads, where the kernels
-// above take G D-thread workgroups per sequence and KV head.
+// The same merges with one wavefront per (sequence, KV head, group of H =
+// min(G, 512 / D) heads), for D G >= 256: lane l merges D H / 64 consecutive
+// outputs of head l / (64 / H) of the group from 16-byte state loads, the
+// states of sixteen pieces (G = 8) or eight loaded together (one reference
+// raise per batch), and writes them; empty sequences get zeros, whole ones were
+// finished by their worker.  Far fewer workgroups than the kernels above,
+// which take G D-thread workgroups per sequence and KV head.
 constexpr int kReduceWaves = 4;
+
+template <int D, int G>
+struct ReduceShape {
+  static constexpr int H = G * D > 512 ? 512 / D : G;  // heads per wavefront
+  static constexpr int kGroups = G / H;                // wavefronts per (sequence, KV head)
+};
 
 template <typename OT, int D, int G>
 __global__ __launch_bounds__(kReduceWaves * kWave) void balanced_reduce_wave_kernel(
     void* __restrict__ out, const float* __restrict__ part_acc,
     const float* __restrict__ part_ml, const int32_t* __restrict__ cuts,
     const int32_t* __restrict__ seq_lens, int num_seqs, int num_kv_heads, float v_scale) {
-  constexpr int kLanesPerHead = kWave / G, kDims = D / kLanesPerHead, kVecs = kDims / 4;
-  constexpr int kBatch = 8;
+  constexpr int H = ReduceShape<D, G>::H, kGroups = ReduceShape<D, G>::kGroups;
+  constexpr int kLanesPerHead = kWave / H, kDims = D / kLanesPerHead, kVecs = kDims / 4;
+  constexpr int kBatch = G >= 8 ? 16 : 8;
   static_assert(kDims % 4 == 0, "whole 4-element groups per lane");
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t item = (int64_t)blockIdx.x * kReduceWaves +
                        __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
-  if (item >= (int64_t)num_seqs * num_kv_heads) return;
-  const int s = (int)(item / num_kv_heads), g = (int)(item % num_kv_heads);
-  const int h = lane / kLanesPerHead, d0 = (lane % kLanesPerHead) * kDims;
+  if (item >= (int64_t)num_seqs * num_kv_heads * kGroups) return;
+  const int64_t sg = item / kGroups;  // (sequence, KV head)
+  const int s = (int)(sg / num_kv_heads), g = (int)(sg % num_kv_heads);
+  const int h = (int)(item % kGroups) * H + lane / kLanesPerHead;  // head within the group of G
+  const int d0 = (lane % kLanesPerHead) * kDims;
   const int L = seq_lens[s];
-  const int va = cuts[2 * item + 0], code = cuts[2 * item + 1];
+  const int va = cuts[2 * sg + 0], code = cuts[2 * sg + 1];
   const int np = code >> 1, slot0 = code & 1;
   if (L > 0 && np <= 1) return;  // a whole sequence: finished by its worker
   float num[kVecs][4], den = 0.f, M = -INFINITY;
@@ -1356,7 +1365,9 @@ hipError_t launch_decode(const DecodeArgs& a) {
                          a.prefix_splits);
     } else if constexpr (D * G >= 4 * kWave)
       hipLaunchKernelGGL((balanced_reduce_wave_kernel<QT, D, G>),
-                         dim3((unsigned)(((int64_t)a.num_seqs * a.num_kv_heads + kReduceWaves - 1) /
+                         dim3((unsigned)(((int64_t)a.num_seqs * a.num_kv_heads *
+                                              ReduceShape<D, G>::kGroups +
+                                          kReduceWaves - 1) /
                                          kReduceWaves)),
                          dim3(kReduceWaves * kWave), 0, a.stream, a.out, a.part_o, a.part_ml,
                          a.cuts, a.seq_lens, a.num_seqs, a.num_kv_heads, v_scale);
