@@ -99,7 +99,7 @@ def summarize_counters(fetch_csv: str, write_csv: str, workload: str, out_path: 
     f_scale = true_bytes / statistics.mean(f[copy_name])
     w_scale = true_bytes / statistics.mean(w[copy_name])
     parts = {}
-    for tag in ("decode_balanced", "balanced_reduce_kernel"):
+    for tag in ("decode_balanced", "balanced_reduce"):
         kf = next(k for k in f if tag in k)
         kw = next(k for k in w if tag in k)
         parts[tag] = {"fetch_bytes": statistics.median(f[kf]) * f_scale,
