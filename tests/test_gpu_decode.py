@@ -274,6 +274,53 @@ def test_decode_balanced_many_sequences(engine, Hq, Hkv, bs, kv, S):
     G.assert_close(got, ref, kv, f"balanced, {len(lens)} sequences, {engine}")
 
 
+@pytest.mark.parametrize("engine", ["valu", "mfma"])
+def test_decode_balanced_runs_of_empty_sequences(engine):
+    """Long stretches of empty sequences between ones with keys (1000
+    sequences, so every length is read in one batch): a worker walks past
+    more than 64 sequences, so its window of lengths is reloaded, and the
+    next sequence with keys can lie beyond the window it holds."""
+    rng = np.random.default_rng(77)
+    lens = np.zeros(1000, dtype=np.int64)
+    live = np.concatenate([np.arange(0, 5), np.arange(150, 153), [400], np.arange(640, 700, 7),
+                           [998, 999]])
+    lens[live] = rng.integers(1, 900, len(live))
+    lens[live[::4]] = rng.integers(2000, 5000, len(live[::4]))
+    b = _shape_batch(32, 8, 128, 16, "bf16", lens, seed=78)
+    G.say(f"[empty runs {engine}] {len(lens)} seqs, {int((lens > 0).sum())} with keys")
+    kp, vp = G.gpu_pool(b)
+    G.gpu_fill(b, kp, vp)
+    okp, ovp = G.oracle_pool(b)
+    qt = G.query_tensor(b)
+    got = G.run_decode(b, kp, vp, qt, partition_size=BAL,
+                       flags=G.ENGINE_FLAG[engine] | pa.PA_DECODE_READ_ONCE)
+    assert np.all(got[lens == 0] == 0)
+    seqs = np.flatnonzero(lens)
+    ref = G.oracle_decode(b, okp, ovp, G.query_f64(qt), seqs=seqs)
+    G.assert_close(got, ref, "bf16", f"runs of empty sequences, {engine}", rows=seqs)
+
+
+def test_decode_balanced_more_than_64_sequences_per_worker():
+    """17,000 one-block sequences (some empty): every worker of a KV head
+    walks about 66 of them, past its first window of 64 lengths, and the
+    lengths take more than one batch to read."""
+    rng = np.random.default_rng(79)
+    lens = rng.integers(1, 17, 17000)
+    lens[rng.choice(len(lens), 700, replace=False)] = 0
+    b = _shape_batch(32, 8, 128, 16, "bf16", lens, seed=80)
+    G.say(f"[17000 sequences] {int(lens.sum())} tokens")
+    kp, vp = G.gpu_pool(b)
+    G.gpu_fill(b, kp, vp)
+    okp, ovp = G.oracle_pool(b)
+    qt = G.query_tensor(b)
+    got = G.run_decode(b, kp, vp, qt, partition_size=BAL, flags=pa.PA_DECODE_READ_ONCE)
+    assert np.all(got[lens == 0] == 0)
+    seqs = np.unique(np.concatenate([np.arange(0, 17000, 41), np.arange(16930, 17000)]))
+    seqs = seqs[lens[seqs] > 0]
+    ref = G.oracle_decode(b, okp, ovp, G.query_f64(qt), seqs=seqs)
+    G.assert_close(got, ref, "bf16", "17,000 one-block sequences", rows=seqs)
+
+
 @pytest.fixture(scope="module")
 def one_long_sequence():
     """One sequence of 50,003 tokens (ending inside a block), Llama-3-8B
