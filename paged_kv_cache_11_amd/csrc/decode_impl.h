@@ -1328,11 +1328,13 @@ hipError_t launch_decode(const DecodeArgs& a) {
     const int wg = (workers + kMaxDecodeWaves - 1) / kMaxDecodeWaves;
     bool mfma = false;
     if constexpr (kHasMfma<KV, QT, D, G>) mfma = a.engine == kEngineMfma;
+    static_assert(!kHasMfma<KV, QT, D, G> || D * G >= 4 * kWave,
+                  "the matrix-core engine writes no merge tasks: its reduce is the wavefront one");
     if constexpr (kHasMfma<KV, QT, D, G>) {
       if (mfma)
         launch_main(a, decode_balanced_mfma_kernel<KV, QT, PBS, G>, dim3((unsigned)wg),
                            dim3(kMaxDecodeWaves * kWave), a.out, a.part_o, a.part_ml,
-                           a.merges, a.cuts, a.query, a.k_cache, a.v_cache, a.block_tables,
+                           a.cuts, a.query, a.k_cache, a.v_cache, a.block_tables,
                            a.seq_lens,
                            a.num_seqs, a.max_blocks_per_seq, a.num_kv_heads, per_head, qk, v_scale,
                            a.read_once, a.suffix, a.append);

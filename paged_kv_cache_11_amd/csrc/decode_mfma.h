@@ -400,7 +400,7 @@ struct MfmaAttn {
 template <typename KV, typename QT, int BS, int G>
 __global__ __launch_bounds__(kMaxDecodeWaves * kWave, 2) void decode_balanced_mfma_kernel(
     void* __restrict__ out, float* __restrict__ part_acc, float* __restrict__ part_ml,
-    int32_t* __restrict__ merges, int32_t* __restrict__ cuts, const void* __restrict__ query,
+    int32_t* __restrict__ cuts, const void* __restrict__ query,
     const void* __restrict__ k_cache, const void* __restrict__ v_cache,
     const int32_t* __restrict__ block_tables, const int32_t* __restrict__ seq_lens, int num_seqs,
     int max_blocks_per_seq, int num_kv_heads, int workers_per_head, float qk_scale_log2,
@@ -429,8 +429,6 @@ __global__ __launch_bounds__(kMaxDecodeWaves * kWave, 2) void decode_balanced_mf
   const int W = effective_workers(T, workers_per_head, MA::UBS);
   // The caller declared that no block is read twice: evict-first loads.
   const bool read_once = read_once_hint != 0;
-  int32_t* merge = merges + 2 * (int64_t)worker;
-  if (lane == 0) merge[0] = -1;  // no merge task unless the last run sets one
   if (vw >= W) return;
   const int64_t start = worker_start(T, vw, W), end = worker_start(T, vw + 1, W);
   if (start >= end) return;
@@ -558,15 +556,12 @@ __global__ __launch_bounds__(kMaxDecodeWaves * kWave, 2) void decode_balanced_mf
       const bool whole = b_lo == 0 && b_hi == nblk;
       const int slot = pos == start ? 0 : 1;
       if (b_lo == 0 && lane == 0) {
-        // The sequence's cut record and, if it is cut, this worker's merge
-        // task (as in the vector path).
+        // The sequence's cut record, which the reduce and merge kernels read
+        // (every shape of this engine takes the wavefront reduce, which needs
+        // no per-worker merge tasks).
         const int code = (whole ? 1 : worker_of(T, seg_end - 1, W) - vw + 1) * 2 + slot;
         cuts[2 * ((int64_t)s * num_kv_heads + g) + 0] = vw;
         cuts[2 * ((int64_t)s * num_kv_heads + g) + 1] = code;
-        if (!whole) {
-          merge[0] = s;
-          merge[1] = code;
-        }
       }
       if (A.n < G) {
         const int h = A.n;
