@@ -625,7 +625,7 @@ constexpr int kScanChunks = 16;
 // the suffix past a shared prefix otherwise).
 __device__ __forceinline__ void load_len_batch(const int32_t* seq_lens, int num_seqs, int c0,
                                                int lane, int bs, int skip,
-                                               int (&nb)[kScanChunks]) {
+                                               int (&nb)[kScanChunks], int extra = 0) {
   // Every load is issued unconditionally (past the end it reads the last
   // length again, then ignores it): a load under a condition gets its own
   // wait, which would serialise the batch.
@@ -640,7 +640,7 @@ __device__ __forceinline__ void load_len_batch(const int32_t* seq_lens, int num_
     nb[b] = s < num_seqs && nb[b] > skip ? nb[b] - skip : 0;
   }
 #pragma unroll
-  for (int b = 0; b < kScanChunks; ++b) nb[b] = nblocks_of(nb[b], bs);
+  for (int b = 0; b < kScanChunks; ++b) nb[b] = nb[b] > 0 ? nblocks_of(nb[b], bs) + extra : 0;
 }
 
 // Inclusive prefix sum over the wavefront's 64 lanes on DPP (row shifts
@@ -662,11 +662,11 @@ __device__ __forceinline__ int wave_sum(int v) {
 
 // Total blocks of all sequences (wavefront-uniform result).
 __device__ __forceinline__ int64_t total_blocks(const int32_t* seq_lens, int num_seqs, int bs,
-                                                int skip, int lane) {
+                                                int skip, int lane, int extra = 0) {
   int t = 0;  // per-lane partial sums stay far below 2^31
   for (int c0 = 0; c0 < num_seqs; c0 += kScanChunks * kWave) {
     int nb[kScanChunks];
-    load_len_batch(seq_lens, num_seqs, c0, lane, bs, skip, nb);
+    load_len_batch(seq_lens, num_seqs, c0, lane, bs, skip, nb, extra);
 #pragma unroll
     for (int b = 0; b < kScanChunks; ++b) t += nb[b];
   }
@@ -677,11 +677,11 @@ __device__ __forceinline__ int64_t total_blocks(const int32_t* seq_lens, int num
 // position of its first block (wavefront-uniform).
 __device__ __forceinline__ void locate_block(const int32_t* seq_lens, int num_seqs, int bs,
                                              int skip, int64_t x, int lane, int& s_out,
-                                             int64_t& base_out) {
+                                             int64_t& base_out, int extra = 0) {
   int64_t base = 0;
   for (int c0 = 0; c0 < num_seqs; c0 += kScanChunks * kWave) {
     int nb[kScanChunks];
-    load_len_batch(seq_lens, num_seqs, c0, lane, bs, skip, nb);
+    load_len_batch(seq_lens, num_seqs, c0, lane, bs, skip, nb, extra);
 #pragma unroll
     for (int b = 0; b < kScanChunks; ++b) {
       if (c0 + b * kWave >= num_seqs) break;
@@ -713,21 +713,26 @@ __device__ __forceinline__ void load_all_lens(const int32_t* seq_lens, int num_s
   for (int b = 0; b < kScanChunks; ++b) raw[b] = b * kWave + lane < num_seqs ? raw[b] : 0;
 }
 
-__device__ __forceinline__ int64_t total_blocks_of(const int (&raw)[kScanChunks], int bs, int skip) {
+__device__ __forceinline__ int units_of(int len, int bs, int skip, int extra) {
+  return len > skip ? nblocks_of(len - skip, bs) + extra : 0;
+}
+
+__device__ __forceinline__ int64_t total_blocks_of(const int (&raw)[kScanChunks], int bs, int skip,
+                                                   int extra = 0) {
   int t = 0;
 #pragma unroll
-  for (int b = 0; b < kScanChunks; ++b) t += nblocks_of(raw[b] > skip ? raw[b] - skip : 0, bs);
+  for (int b = 0; b < kScanChunks; ++b) t += units_of(raw[b], bs, skip, extra);
   return wave_sum(t);
 }
 
 __device__ __forceinline__ void locate_block_of(const int (&raw)[kScanChunks], int num_seqs, int bs,
                                                 int skip, int64_t x, int& s_out,
-                                                int64_t& base_out) {
+                                                int64_t& base_out, int extra = 0) {
   int64_t base = 0;
 #pragma unroll
   for (int b = 0; b < kScanChunks; ++b) {
     if (b * kWave >= num_seqs) break;
-    const int nb = nblocks_of(raw[b] > skip ? raw[b] - skip : 0, bs);
+    const int nb = units_of(raw[b], bs, skip, extra);
     const int incl = wave_scan_incl(nb);
     const int chunk = __builtin_amdgcn_readlane(incl, kWave - 1);
     if (base + chunk > x) {

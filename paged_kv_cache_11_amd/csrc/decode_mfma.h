@@ -419,13 +419,18 @@ __global__ __launch_bounds__(kMaxDecodeWaves * kWave, 2) void decode_balanced_mf
   if (vw >= workers_per_head) return;
   const int num_heads = num_kv_heads * G;
 
+  // The split's units: each sequence with keys counts its units of UBS
+  // tokens plus kRunCost more that hold no keys (at its end), the cost of a
+  // run's start, so that a worker whose range starts more runs is given
+  // fewer keys.
+  constexpr int kRunCost = 1;
   // Every length in one load where they fit one batch (the total, the
   // worker's first sequence and its window of lengths all come from it).
   const bool one_load = num_seqs <= kScanChunks * kWave;
   int raw[kScanChunks];
   if (one_load) load_all_lens(seq_lens, num_seqs, lane, raw);
-  const int64_t T = one_load ? total_blocks_of(raw, MA::UBS, sx.skip)
-                             : total_blocks(seq_lens, num_seqs, MA::UBS, sx.skip, lane);
+  const int64_t T = one_load ? total_blocks_of(raw, MA::UBS, sx.skip, kRunCost)
+                             : total_blocks(seq_lens, num_seqs, MA::UBS, sx.skip, lane, kRunCost);
   const int W = effective_workers(T, workers_per_head, MA::UBS);
   // The caller declared that no block is read twice: evict-first loads.
   const bool read_once = read_once_hint != 0;
@@ -434,8 +439,8 @@ __global__ __launch_bounds__(kMaxDecodeWaves * kWave, 2) void decode_balanced_mf
   if (start >= end) return;
   int s;
   int64_t base;
-  if (one_load) locate_block_of(raw, num_seqs, MA::UBS, sx.skip, start, s, base);
-  else locate_block(seq_lens, num_seqs, MA::UBS, sx.skip, start, lane, s, base);
+  if (one_load) locate_block_of(raw, num_seqs, MA::UBS, sx.skip, start, s, base, kRunCost);
+  else locate_block(seq_lens, num_seqs, MA::UBS, sx.skip, start, lane, s, base, kRunCost);
   const int tbl_skip = sx.skip / BS;  // table entries of the skipped tokens
 
   MA A;
@@ -507,11 +512,12 @@ __global__ __launch_bounds__(kMaxDecodeWaves * kWave, 2) void decode_balanced_mf
   int64_t pos = start;
   while (pos < end && s < num_seqs) {
     const int L = max(len_at(s) - sx.skip, 0);
-    const int nblk = nblocks_of(L, MA::UBS);  // units of the split
-    const int64_t seg_end = base + nblk;
-    if (nblk > 0) {
+    const int nblk = nblocks_of(L, MA::UBS);  // units of the split with keys
+    const int64_t seg_end = base + (nblk > 0 ? nblk + kRunCost : 0);
+    const int64_t vend = end < seg_end ? end : seg_end;  // this worker's end in the sequence
+    if (nblk > 0 && pos - base < nblk) {
       const int b_lo = (int)(pos - base);
-      const int b_hi = (int)((end < seg_end ? end : seg_end) - base);
+      const int b_hi = (int)(vend - base < nblk ? vend - base : nblk);
       const int64_t hq0 = (int64_t)s * num_heads + (int64_t)g * G;
       A.reset();
       A.load_q(query, hq0);
@@ -559,7 +565,7 @@ __global__ __launch_bounds__(kMaxDecodeWaves * kWave, 2) void decode_balanced_mf
         // The sequence's cut record, which the reduce and merge kernels read
         // (every shape of this engine takes the wavefront reduce, which needs
         // no per-worker merge tasks).
-        const int code = (whole ? 1 : worker_of(T, seg_end - 1, W) - vw + 1) * 2 + slot;
+        const int code = (whole ? 1 : worker_of(T, base + nblk - 1, W) - vw + 1) * 2 + slot;
         cuts[2 * ((int64_t)s * num_kv_heads + g) + 0] = vw;
         cuts[2 * ((int64_t)s * num_kv_heads + g) + 1] = code;
       }
@@ -588,8 +594,8 @@ __global__ __launch_bounds__(kMaxDecodeWaves * kWave, 2) void decode_balanced_mf
           }
         }
       }
-      pos = base + b_hi;
     }
+    if (nblk > 0) pos = vend;
     if (pos >= seg_end) {
       base = seg_end;
       ++s;
