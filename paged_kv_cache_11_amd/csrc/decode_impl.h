@@ -1294,6 +1294,117 @@ __global__ __launch_bounds__(D) void lse_reduce_kernel(
   store_out<OT>(out, (hq0 + h) * D + d, merge_element<true>(part_o, part_ml, nparts, D, h, d, state));
 }
 
+// The same merge by one workgroup of kLseWaves wavefronts per (sequence,
+// KV head, group of ReduceShape heads), for D G >= 256: wavefront w merges
+// partitions w, w + kLseWaves, ... sixteen at a time (16-byte state loads,
+// D H / 64 consecutive outputs of one head per lane, H = ReduceShape::H),
+// the partial merges meet in LDS and wavefront 0 writes the outputs.  A
+// sequence of 64 partitions then takes one round of state loads per
+// wavefront, where lse_reduce_kernel takes four.  (Sixteen wavefronts of
+// four partitions each measured the same: the kernel's fixed cost, not its
+// loads, sets its time.)
+constexpr int kLseWaves = 4;
+
+template <typename OT, int D, int G>
+__global__ __launch_bounds__(kLseWaves * kWave) void lse_reduce_wg_kernel(
+    void* __restrict__ out, const float* __restrict__ part_o,
+    const float* __restrict__ part_ml, const int32_t* __restrict__ seq_lens, int num_kv_heads,
+    int block_size, int partition_blocks, int max_parts) {
+  constexpr int H = ReduceShape<D, G>::H, kGroups = ReduceShape<D, G>::kGroups;
+  constexpr int kLanesPerHead = kWave / H, kDims = D / kLanesPerHead, kVecs = kDims / 4;
+  constexpr int kBatch = 16;
+  static_assert(kDims % 4 == 0, "whole 4-element groups per lane");
+  __shared__ float red[kLseWaves][2 + kDims][kWave];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+  const int64_t sg = blockIdx.x / kGroups;  // (sequence, KV head)
+  const int s = (int)(sg / num_kv_heads), g = (int)(sg % num_kv_heads);
+  const int h = (int)(blockIdx.x % kGroups) * H + lane / kLanesPerHead;  // head within G
+  const int d0 = (lane % kLanesPerHead) * kDims;
+  const int L = seq_lens[s];
+  const int nblk = (L + block_size - 1) / block_size;
+  const int nparts = nblk > partition_blocks ? (nblk + partition_blocks - 1) / partition_blocks : 1;
+  if (nparts <= 1) return;  // the decode kernel wrote the output
+  const int64_t hq = (int64_t)s * num_kv_heads * G + (int64_t)g * G + h;
+  float M = -INFINITY, den = 0.f, num[kVecs][4];
+#pragma unroll
+  for (int v = 0; v < kVecs; ++v)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) num[v][i] = 0.f;
+  // This wavefront's partitions w, w + kLseWaves, ...: n_mine of them.
+  const int n_mine = nparts > w ? (nparts - w + kLseWaves - 1) / kLseWaves : 0;
+  for (int q0 = 0; q0 < n_mine; q0 += kBatch) {
+    float m[kBatch], l[kBatch];
+    f32x4 a[kBatch][kVecs];
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q) {
+      const int p = w + kLseWaves * (q0 + q < n_mine ? q0 + q : n_mine - 1);
+      const int64_t st = hq * max_parts + p;
+      m[q] = part_ml[2 * st];
+      l[q] = part_ml[2 * st + 1];
+#pragma unroll
+      for (int v = 0; v < kVecs; ++v) a[q][v] = *(const f32x4*)(part_o + st * D + d0 + 4 * v);
+    }
+    float bm = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q) bm = q0 + q < n_mine ? fmaxf(bm, m[q]) : bm;
+    if (bm > M) {
+      const float f = M == -INFINITY ? 0.f : fast_exp2(M - bm);
+#pragma unroll
+      for (int v = 0; v < kVecs; ++v)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) num[v][i] *= f;
+      den *= f;
+      M = bm;
+    }
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q) {
+      // Normalised states: each adds e l o to the numerator, e l to the sum.
+      const float el = (q0 + q >= n_mine || M == -INFINITY) ? 0.f : fast_exp2(m[q] - M) * l[q];
+#pragma unroll
+      for (int v = 0; v < kVecs; ++v)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) num[v][i] = __builtin_fmaf(el, a[q][v][i], num[v][i]);
+      den += el;
+    }
+  }
+  red[w][0][lane] = M;
+  red[w][1][lane] = den;
+#pragma unroll
+  for (int v = 0; v < kVecs; ++v)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[w][2 + 4 * v + i][lane] = num[v][i];
+  __syncthreads();
+  if (w != 0) return;
+  float Mt = -INFINITY;
+  for (int x = 0; x < kLseWaves; ++x) Mt = fmaxf(Mt, red[x][0][lane]);
+  float dt = 0.f, nt[kDims];
+#pragma unroll
+  for (int i = 0; i < kDims; ++i) nt[i] = 0.f;
+#pragma unroll 2
+  for (int x = 0; x < kLseWaves; ++x) {
+    const float mx = red[x][0][lane];
+    const float f = mx == -INFINITY ? 0.f : fast_exp2(mx - Mt);
+    dt = __builtin_fmaf(f, red[x][1][lane], dt);
+#pragma unroll
+    for (int i = 0; i < kDims; ++i) nt[i] = __builtin_fmaf(f, red[x][2 + i][lane], nt[i]);
+  }
+  const int64_t o = hq * D + d0;
+#pragma unroll
+  for (int v = 0; v < kVecs; ++v) {
+    float x[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = dt > 0.f ? nt[4 * v + i] / dt : 0.f;
+    if constexpr (std::is_same<OT, F32>::value) {
+      *(f32x4*)((float*)out + o + 4 * v) = f32x4{x[0], x[1], x[2], x[3]};
+    } else {
+      const uint32_t w0 = (uint32_t)f32_to_bf16_rne(x[0]) | ((uint32_t)f32_to_bf16_rne(x[1]) << 16);
+      const uint32_t w1 = (uint32_t)f32_to_bf16_rne(x[2]) | ((uint32_t)f32_to_bf16_rne(x[3]) << 16);
+      *(u32x2*)((uint16_t*)out + o + 4 * v) = u32x2{w0, w1};
+    }
+  }
+}
+
 // Wavefronts per workgroup: enough blocks per wavefront to keep its
 // one-tile-ahead pipeline busy, at most four.
 }  // namespace pa
@@ -1391,20 +1502,43 @@ hipError_t launch_decode(const DecodeArgs& a) {
     return hipGetLastError();
   }
   const int tiles_per_part = a.partition_blocks << kSubShift;  // 0: whole sequence
-  const int nw = a.num_waves > 0 ? a.num_waves : decode_waves(tiles_per_part, a.max_seq_len, BS);
-  launch_main(a, decode_kernel<KV, QT, D, BS, G>,
-                     dim3((unsigned)a.max_parts, (unsigned)a.num_kv_heads, (unsigned)a.num_seqs),
-                     dim3(nw * kWave), a.out, a.part_o, a.part_ml, a.query,
-                     a.k_cache, a.v_cache, a.block_tables, a.seq_lens, a.max_blocks_per_seq,
-                     a.num_kv_heads, tiles_per_part, a.max_parts, qk, v_scale, kSubShift,
-                     a.read_once);
+  // Fixed partitions on the matrix cores where that engine is built and not
+  // pinned away (one wavefront per partition; a whole sequence in one
+  // partition stays on the vector engine, whose wavefronts share it).
+  bool mfma_parts = false;
+  if constexpr (kHasMfma<KV, QT, D, G>) {
+    mfma_parts = a.engine == kEngineMfma && a.partition_blocks > 0;
+    if (mfma_parts) {
+      const int units = a.partition_blocks * PBS / MfmaAttn<KV, PBS, G>::UBS;
+      launch_main(a, decode_partitioned_mfma_kernel<KV, QT, PBS, G>,
+                  dim3((unsigned)((a.max_parts + kMaxDecodeWaves - 1) / kMaxDecodeWaves),
+                       (unsigned)a.num_kv_heads, (unsigned)a.num_seqs),
+                  dim3(kMaxDecodeWaves * kWave), a.out, a.part_o, a.part_ml, a.query, a.k_cache,
+                  a.v_cache, a.block_tables, a.seq_lens, a.max_blocks_per_seq, a.num_kv_heads,
+                  units, a.max_parts, qk, v_scale, a.read_once);
+    }
+  }
+  if (!mfma_parts) {
+    const int nw = a.num_waves > 0 ? a.num_waves : decode_waves(tiles_per_part, a.max_seq_len, BS);
+    launch_main(a, decode_kernel<KV, QT, D, BS, G>,
+                dim3((unsigned)a.max_parts, (unsigned)a.num_kv_heads, (unsigned)a.num_seqs),
+                dim3(nw * kWave), a.out, a.part_o, a.part_ml, a.query, a.k_cache, a.v_cache,
+                a.block_tables, a.seq_lens, a.max_blocks_per_seq, a.num_kv_heads, tiles_per_part,
+                a.max_parts, qk, v_scale, kSubShift, a.read_once);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.max_parts <= 1) return e;
-  hipLaunchKernelGGL((lse_reduce_kernel<QT, D, G>),
-                     dim3((unsigned)G, (unsigned)a.num_kv_heads, (unsigned)a.num_seqs), dim3(D), 0,
-                     a.stream,
-                     a.out, a.part_o, a.part_ml, a.seq_lens, a.num_kv_heads, a.block_size,
-                     a.partition_blocks, a.max_parts);
+  if constexpr (D * G >= 4 * kWave)
+    hipLaunchKernelGGL((lse_reduce_wg_kernel<QT, D, G>),
+                       dim3((unsigned)((int64_t)a.num_seqs * a.num_kv_heads *
+                                       ReduceShape<D, G>::kGroups)),
+                       dim3(kLseWaves * kWave), 0, a.stream, a.out, a.part_o, a.part_ml,
+                       a.seq_lens, a.num_kv_heads, a.block_size, a.partition_blocks, a.max_parts);
+  else
+    hipLaunchKernelGGL((lse_reduce_kernel<QT, D, G>),
+                       dim3((unsigned)G, (unsigned)a.num_kv_heads, (unsigned)a.num_seqs), dim3(D),
+                       0, a.stream, a.out, a.part_o, a.part_ml, a.seq_lens, a.num_kv_heads,
+                       a.block_size, a.partition_blocks, a.max_parts);
   return hipGetLastError();
 }
 

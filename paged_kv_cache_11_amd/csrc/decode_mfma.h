@@ -603,4 +603,72 @@ __global__ __launch_bounds__(kMaxDecodeWaves * kWave, 2) void decode_balanced_mf
   }
 }
 
+// Fixed partitions on the matrix-core engine (the split-K decode with a
+// separate log-sum-exp reduce): workgroup (x, g, s) takes partitions
+// 4x .. 4x+3 of sequence s for KV head g, one per wavefront, each a run of
+// partition_units units of the sequence streamed as the balanced split
+// streams a run.  Its outputs are decode_kernel's: the output itself when
+// the sequence has one partition, else per partition the output normalised
+// by its own sum, times v_scale, and its (reference, sum) for
+// lse_reduce_kernel.
+template <typename KV, typename QT, int BS, int G>
+__global__ __launch_bounds__(kMaxDecodeWaves * kWave, 2) void decode_partitioned_mfma_kernel(
+    void* __restrict__ out, float* __restrict__ part_o, float* __restrict__ part_ml,
+    const void* __restrict__ query, const void* __restrict__ k_cache,
+    const void* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
+    const int32_t* __restrict__ seq_lens, int max_blocks_per_seq, int num_kv_heads,
+    int partition_units, int max_parts, float qk_scale_log2, float v_scale, int read_once_hint) {
+  static_assert(std::is_same<QT, BF16>::value, "bf16 queries");
+  using MA = MfmaAttn<KV, BS, G>;
+  constexpr int D = kMD;
+  __shared__ __attribute__((aligned(16))) __bf16 vt_lds[kMaxDecodeWaves][MA::kLdsElems];
+  __shared__ int win_lds[kMaxDecodeWaves][kWave];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wv = threadIdx.x / kWave;
+  const int part = blockIdx.x * (blockDim.x / kWave) + wv, g = blockIdx.y, s = blockIdx.z;
+  const int num_heads = num_kv_heads * G;
+  const int L = seq_lens[s];
+  const int nunits = nblocks_of(L, MA::UBS);
+  const int nparts = nunits > partition_units ? (nunits + partition_units - 1) / partition_units : 1;
+  if (part >= nparts) return;
+  const int u0 = part * partition_units;
+  const int u1 = u0 + partition_units < nunits ? u0 + partition_units : nunits;
+  const int64_t hq0 = (int64_t)s * num_heads + (int64_t)g * G;
+  MA A;
+  A.init(lane, qk_scale_log2, vt_lds[wv]);
+  A.reset();
+  A.load_q(query, hq0);
+  const int32_t* row = block_tables + (int64_t)s * max_blocks_per_seq;
+  const int nxt_v = row[0];  // no run follows: a harmless table read, parked and unused
+  if (read_once_hint)
+    A.template stream<true>(k_cache, v_cache, row, g, num_kv_heads, u0, u1 - u0, L, -1, nxt_v,
+                            win_lds[wv], 0, false);
+  else
+    A.template stream<false>(k_cache, v_cache, row, g, num_kv_heads, u0, u1 - u0, L, -1, nxt_v,
+                             win_lds[wv], 0, false);
+  const float l_tot = A.l_total();
+  if (A.n < G) {
+    const int64_t hq = hq0 + A.n;
+    const float inv = l_tot > 0.f ? v_scale / l_tot : 0.f;
+    if (nparts == 1) {
+#pragma unroll
+      for (int mb = 0; mb < D / 16; ++mb) {
+        const int d0 = 16 * mb + 4 * A.g4;
+        const uint32_t w0 = pack_bf16(A.acc[mb][0] * inv, A.acc[mb][1] * inv);
+        const uint32_t w1 = pack_bf16(A.acc[mb][2] * inv, A.acc[mb][3] * inv);
+        *(u32x2*)((uint16_t*)out + hq * D + d0) = u32x2{w0, w1};
+      }
+    } else {
+      const int64_t st = hq * max_parts + part;
+#pragma unroll
+      for (int mb = 0; mb < D / 16; ++mb)
+        *(f32x4*)(part_o + st * D + 16 * mb + 4 * A.g4) = A.acc[mb] * inv;
+      if (A.g4 == 0) {
+        part_ml[st * 2 + 0] = A.m_ref;
+        part_ml[st * 2 + 1] = l_tot;
+      }
+    }
+  }
+}
+
 }  // namespace pa
