@@ -1067,8 +1067,10 @@ __global__ __launch_bounds__(kReduceWaves * kWave) void balanced_reduce_wave_ker
 // The last step of a shared-prefix decode: the log-sum-exp merge of each
 // sequence's suffix (its pieces when the balanced split cut it, else the
 // whole-sequence state the suffix mode kept) with the prefix's splits.
-// Every state is unnormalised with its own reference maximum (log2
-// domain); a state with no keys has m = -inf and is skipped.
+// Every state has its own reference maximum (log2 domain) and exponent sum;
+// the suffix's are unnormalised fp32 accumulators, the prefix splits'
+// outputs normalised by their sums, in bf16.  A state with no keys has
+// m = -inf and is skipped.
 // Workgroups of kMergeThreads, grid (sequence, element block of
 // 4 kMergeThreads outputs); a thread owns 4 consecutive output elements of
 // one head (16-byte loads).  The prefix
@@ -1082,7 +1084,7 @@ __global__ __launch_bounds__(kMergeThreads) void prefix_merge_kernel(
     void* __restrict__ out, const float* __restrict__ part_acc,
     const float* __restrict__ part_ml, const int32_t* __restrict__ cuts,
     const int32_t* __restrict__ seq_lens, int num_seqs, int num_kv_heads, float v_scale,
-    SuffixStates sx, const float* __restrict__ prefix_acc, const float* __restrict__ prefix_ml,
+    SuffixStates sx, const uint16_t* __restrict__ prefix_o, const float* __restrict__ prefix_ml,
     int prefix_splits) {
   constexpr int kMaxSplits = kMaxPrefixSplits;
   const int s = blockIdx.x;
@@ -1095,7 +1097,9 @@ __global__ __launch_bounds__(kMergeThreads) void prefix_merge_kernel(
     const int64_t hq = (int64_t)s * num_heads + h;
     float M = -INFINITY, den = 0.f;
     f32x4 num = {0.f, 0.f, 0.f, 0.f};
-    auto add = [&](float m, float l, f32x4 a) {
+    // A state with its own sum l: an unnormalised accumulator a enters with
+    // weight 2^(m - M), a normalised output (norm) with 2^(m - M) l.
+    auto add = [&](float m, float l, f32x4 a, bool norm) {
       if (m == -INFINITY) return;
       if (m > M) {
         const float f = M == -INFINITY ? 0.f : fast_exp2(M - m);
@@ -1104,7 +1108,7 @@ __global__ __launch_bounds__(kMergeThreads) void prefix_merge_kernel(
         M = m;
       }
       const float e = fast_exp2(m - M);
-      num += e * a;
+      num += (norm ? e * l : e) * a;
       den = __builtin_fmaf(e, l, den);
     };
     // Every load that does not depend on another is issued up front (the
@@ -1124,21 +1128,21 @@ __global__ __launch_bounds__(kMergeThreads) void prefix_merge_kernel(
         const int64_t st = (int64_t)c * num_seqs * num_heads + hq;
         pm[c] = prefix_ml[2 * st];
         pl[c] = prefix_ml[2 * st + 1];
-        pa[c] = *(const f32x4*)(prefix_acc + st * D + d);
+        pa[c] = bf16x4_to_f32x4(*(const u32x2*)(prefix_o + st * D + d));
       }
     }
 #pragma unroll
     for (int c = 0; c < kMaxSplits; ++c)
-      if (c < prefix_splits) add(pm[c], pl[c], pa[c]);
+      if (c < prefix_splits) add(pm[c], pl[c], pa[c], true);
     if (has_suffix) {
       const int np = code >> 1, slot0 = code & 1;
       if (np <= 1) {
-        add(wm, wl, wa);
+        add(wm, wl, wa, false);
       } else {
         for (int p = 0; p < np; ++p) {
           const int64_t st =
               ((int64_t)((va + p) * num_kv_heads + g) * 2 + (p == 0 ? slot0 : 0)) * G + hg;
-          add(part_ml[2 * st], part_ml[2 * st + 1], *(const f32x4*)(part_acc + st * D + d));
+          add(part_ml[2 * st], part_ml[2 * st + 1], *(const f32x4*)(part_acc + st * D + d), false);
         }
       }
     }
@@ -1161,15 +1165,18 @@ __global__ __launch_bounds__(kMergeThreads) void prefix_merge_kernel(
 // state, or the pieces of a cut suffix, which wait for the cut record only)
 // are requested four at a time, the prefix's and the suffix's first four
 // together, before any is used.
-template <int D, int G>
+// kNorm: the states are outputs normalised by their own sum, in bf16 (the
+// prefix splits); else unnormalised fp32 accumulators (the suffix pieces).
+template <int D, int G, bool kNorm>
 struct MergeBatch {
   static constexpr int kLanesPerHead = kWave / G, kDims = D / kLanesPerHead, kVecs = kDims / 4;
   static constexpr int kN = 4;
+  using Acc = typename std::conditional<kNorm, uint16_t, float>::type;
   float m[kN], l[kN];
   f32x4 a[kN][kVecs];
   // States idx(0 .. n-1) from q0 on (at most kN; the rest repeat the last).
   template <typename IndexFn>
-  __device__ __forceinline__ void load(const float* ml, const float* acc, int q0, int n, int d0,
+  __device__ __forceinline__ void load(const float* ml, const Acc* acc, int q0, int n, int d0,
                                        IndexFn idx) {
 #pragma unroll
     for (int q = 0; q < kN; ++q) {
@@ -1177,7 +1184,12 @@ struct MergeBatch {
       m[q] = ml[2 * st];
       l[q] = ml[2 * st + 1];
 #pragma unroll
-      for (int v = 0; v < kVecs; ++v) a[q][v] = *(const f32x4*)(acc + st * D + d0 + 4 * v);
+      for (int v = 0; v < kVecs; ++v) {
+        if constexpr (kNorm)
+          a[q][v] = bf16x4_to_f32x4(*(const u32x2*)(acc + st * D + d0 + 4 * v));
+        else
+          a[q][v] = *(const f32x4*)(acc + st * D + d0 + 4 * v);
+      }
     }
   }
   // Adds states q0 .. min(n, q0 + kN) - 1 (states with m = -inf hold no
@@ -1199,10 +1211,11 @@ struct MergeBatch {
 #pragma unroll
     for (int q = 0; q < kN; ++q) {
       const float e = (q0 + q >= n || m[q] == -INFINITY) ? 0.f : fast_exp2(m[q] - M);
+      const float w = kNorm ? e * l[q] : e;
 #pragma unroll
       for (int v = 0; v < kVecs; ++v)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) num[v][i] = __builtin_fmaf(e, a[q][v][i], num[v][i]);
+        for (int i = 0; i < 4; ++i) num[v][i] = __builtin_fmaf(w, a[q][v][i], num[v][i]);
       den = __builtin_fmaf(e, l[q], den);
     }
   }
@@ -1213,9 +1226,10 @@ __global__ __launch_bounds__(kReduceWaves * kWave) void prefix_merge_wave_kernel
     void* __restrict__ out, const float* __restrict__ part_acc,
     const float* __restrict__ part_ml, const int32_t* __restrict__ cuts,
     const int32_t* __restrict__ seq_lens, int num_seqs, int num_kv_heads, float v_scale,
-    SuffixStates sx, const float* __restrict__ prefix_acc, const float* __restrict__ prefix_ml,
+    SuffixStates sx, const uint16_t* __restrict__ prefix_o, const float* __restrict__ prefix_ml,
     int prefix_splits) {
-  using MB = MergeBatch<D, G>;
+  using MB = MergeBatch<D, G, false>;
+  using PB = MergeBatch<D, G, true>;
   constexpr int kVecs = MB::kVecs;
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t item = (int64_t)blockIdx.x * kReduceWaves +
@@ -1243,12 +1257,13 @@ __global__ __launch_bounds__(kReduceWaves * kWave) void prefix_merge_wave_kernel
   for (int v = 0; v < kVecs; ++v)
 #pragma unroll
     for (int i = 0; i < 4; ++i) num[v][i] = 0.f;
-  MB pb, sb;
-  if (prefix_splits > 0) pb.load(prefix_ml, prefix_acc, 0, prefix_splits, d0, prefix_idx);
+  PB pb;
+  MB sb;
+  if (prefix_splits > 0) pb.load(prefix_ml, prefix_o, 0, prefix_splits, d0, prefix_idx);
   if (ns > 0) sb.load(s_ml, s_acc, 0, ns, d0, suffix_idx);
   if (prefix_splits > 0) pb.absorb(0, prefix_splits, M, den, num);
   for (int c0 = MB::kN; c0 < prefix_splits; c0 += MB::kN) {
-    pb.load(prefix_ml, prefix_acc, c0, prefix_splits, d0, prefix_idx);
+    pb.load(prefix_ml, prefix_o, c0, prefix_splits, d0, prefix_idx);
     pb.absorb(c0, prefix_splits, M, den, num);
   }
   if (ns > 0) sb.absorb(0, ns, M, den, num);
@@ -1464,14 +1479,14 @@ hipError_t launch_decode(const DecodeArgs& a) {
                          kSubShift, a.read_once, a.suffix);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (a.prefix_acc) {
+    if (a.prefix_o) {
       if constexpr (D * G >= 4 * kWave)
         hipLaunchKernelGGL((prefix_merge_wave_kernel<QT, D, G>),
                          dim3((unsigned)(((int64_t)a.num_seqs * a.num_kv_heads + kReduceWaves - 1) /
                                          kReduceWaves)),
                          dim3(kReduceWaves * kWave), 0, a.stream, a.out, a.part_o, a.part_ml,
                          a.cuts, a.seq_lens, a.num_seqs, a.num_kv_heads, v_scale, a.suffix,
-                         a.prefix_acc, a.prefix_ml, a.prefix_splits);
+                         a.prefix_o, a.prefix_ml, a.prefix_splits);
       else
         hipLaunchKernelGGL((prefix_merge_kernel<QT, D, G>),
                          dim3((unsigned)a.num_seqs,
@@ -1479,7 +1494,7 @@ hipError_t launch_decode(const DecodeArgs& a) {
                                          (4 * kMergeThreads))),
                          dim3(kMergeThreads),
                          0, a.stream, a.out, a.part_o, a.part_ml, a.cuts, a.seq_lens, a.num_seqs,
-                         a.num_kv_heads, v_scale, a.suffix, a.prefix_acc, a.prefix_ml,
+                         a.num_kv_heads, v_scale, a.suffix, a.prefix_o, a.prefix_ml,
                          a.prefix_splits);
     } else if constexpr (D * G >= 4 * kWave)
       hipLaunchKernelGGL((balanced_reduce_wave_kernel<QT, D, G>),

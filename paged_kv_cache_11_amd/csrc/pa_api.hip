@@ -310,7 +310,7 @@ int32_t pa::decode_call(void* out, const void* query, int32_t q_dtype, int32_t n
       a.append.v_scale = v_scale;
     }
     a.suffix = extra->suffix;
-    a.prefix_acc = extra->prefix_acc;
+    a.prefix_o = extra->prefix_o;
     a.prefix_ml = extra->prefix_ml;
     a.prefix_splits = extra->prefix_splits;
     if (extra->before_launch) {
@@ -517,7 +517,7 @@ size_t pa_decode_shared_prefix_workspace_size(int32_t num_seqs, int32_t num_head
   int64_t splits = ceil_div(prefix_len, kPrefixSplitQuantum);
   if (splits > kMaxPrefixSplits) splits = kMaxPrefixSplits;
   return bal + align256(rows * head_size * 4) + align256(rows * 2 * 4) +
-         align256((size_t)splits * rows * head_size * 4) + align256((size_t)splits * rows * 2 * 4);
+         align256((size_t)splits * rows * head_size * 2) + align256((size_t)splits * rows * 2 * 4);
 }
 
 int32_t pa_decode_shared_prefix(void* out, const void* query, int32_t q_dtype, int32_t num_seqs,
@@ -569,16 +569,16 @@ int32_t pa_decode_shared_prefix(void* out, const void* query, int32_t q_dtype, i
   p += align256(rows * head_size * 4);
   ex.suffix.ml = (float*)p;
   p += align256(rows * 2 * 4);
-  float* pre_acc = (float*)p;
+  uint16_t* pre_o = (uint16_t*)p;
   int32_t splits = 0;
   int32_t split_len = 0;
   if (prefix_len > 0) {
     split_len = prefix_split_len(prefix_len, num_seqs, group, num_kv_heads, device_cus());
     splits = (int32_t)ceil_div(prefix_len, split_len);
   }
-  p += align256((size_t)splits * rows * head_size * 4);
+  p += align256((size_t)splits * rows * head_size * 2);
   float* pre_ml = (float*)p;
-  ex.prefix_acc = pre_acc;
+  ex.prefix_o = pre_o;
   ex.prefix_ml = pre_ml;
   ex.prefix_splits = splits;
   // The prefix: every sequence's query against the shared blocks of row 0,
@@ -591,7 +591,7 @@ int32_t pa_decode_shared_prefix(void* out, const void* query, int32_t q_dtype, i
     a.num_blocks = num_blocks; a.block_size = block_size; a.num_kv_heads = num_kv_heads;
     a.block_tables = block_tables; a.max_blocks_per_seq = max_blocks_per_seq;
     a.scale = scale; a.k_scale = k_scale; a.v_scale = v_scale;
-    a.prefix.acc = pre_acc;
+    a.prefix.o = pre_o;
     a.prefix.ml = pre_ml;
     a.prefix.split_len = split_len;
     a.prefix.prefix_len = prefix_len;

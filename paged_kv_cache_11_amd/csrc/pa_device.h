@@ -69,6 +69,11 @@ template <> struct Vec<FP8> {
   }
 };
 
+// Four bf16 values (two packed words, low half first) widened to fp32.
+__device__ __forceinline__ f32x4 bf16x4_to_f32x4(u32x2 w) {
+  return f32x4{bf16lo(w.x), bf16hi(w.x), bf16lo(w.y), bf16hi(w.y)};
+}
+
 // float -> bfloat16 bits, round to nearest even; NaN stays a quiet NaN.
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
   uint32_t u = f2u(x);

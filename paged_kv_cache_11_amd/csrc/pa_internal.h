@@ -102,11 +102,12 @@ struct DecodeArgs {
   int32_t read_once;         // 1: no block is read twice in the call (evict-first loads)
   // Shared-prefix decode: the balanced split runs in suffix mode, and a
   // merge kernel joins each sequence's suffix state with prefix_splits
-  // prefix states ([(split * num_seqs + s) * num_heads + h][head_size] and
-  // [...][2]) into the output.
+  // prefix states into the output: each split's output normalised by its
+  // own sum, bf16 ([(split * num_seqs + s) * num_heads + h][head_size]),
+  // and its (reference, sum), fp32 ([...][2]).
   SuffixStates suffix;
   AppendTokens append;
-  const float* prefix_acc;
+  const uint16_t* prefix_o;
   const float* prefix_ml;
   int32_t prefix_splits;
   // Measurement (pa_profile_next_decode): events recorded right before and
@@ -147,11 +148,11 @@ struct PrefillArgs {
   int32_t max_blocks_per_seq;
   const int32_t* seq_lens;
   float scale, k_scale, v_scale;
-  // Prefix mode (acc != nullptr): num_tokens decode queries against the
+  // Prefix mode (o != nullptr): num_tokens decode queries against the
   // first prefix_len keys of block_tables row 0, non-causal, in splits of
-  // split_len keys; the splits' states go to acc / ml (see prefill_kernels).
+  // split_len keys; the splits' states go to o / ml (see prefill_kernels).
   struct {
-    float* acc;
+    uint16_t* o;
     float* ml;
     int32_t split_len, prefix_len;
   } prefix;
@@ -194,7 +195,7 @@ int32_t decode_call(void* out, const void* query, int32_t q_dtype, int32_t num_s
 struct DecodeExtras {
   SuffixStates suffix;
   AppendTokens append;
-  const float* prefix_acc;
+  const uint16_t* prefix_o;
   const float* prefix_ml;
   int32_t prefix_splits;
   // Called after every host check passed, before the decode kernels are

@@ -57,10 +57,10 @@ constexpr int kVBytes = kStep * kVStride * 2;
 constexpr int kBufBytes = kKBytes + kVBytes;
 // After the key walk: the two key halves trade half of their accumulators
 // (kMergeFloats), then the finished tile goes through LDS row by row
-// (kTileStride bytes per row: bf16 outputs, or fp32 states in prefix mode)
-// so that global stores cover whole rows.
+// (kTileStride bytes per row of bf16 outputs) so that global stores cover
+// whole rows.
 constexpr int kMergeFloats = 2 * kRowGroups * (kPD / 4) * kWave + 4 * kRowGroups * kWave;
-constexpr int kTileStride = kPD * 4 + 16;
+constexpr int kTileStride = kPD * 2 + 16;
 constexpr int kTileOff = kMergeFloats * 4;
 constexpr int kQStride = kPD * 2 + 16;  // LDS row stride of the query tile (bytes)
 constexpr int kLdsBytes = kBufs * kBufBytes;
@@ -105,11 +105,12 @@ template <int N> struct Buf { static constexpr int value = N; };
 // sees every key of the prefix (no causal mask), and the keys are cut into
 // splits of split_len (grid z): split c covers keys c * split_len ..
 // min(prefix_len, (c + 1) * split_len) - 1 of table row 0.  Each split
-// leaves, per (query, head), its unnormalised accumulator and (reference
-// maximum, exponent sum), log2 domain, for a log-sum-exp merge:
-// acc[(c * num_q + q) * num_heads + h][head dim], ml[...][2].
+// leaves, per (query, head), its output normalised by its own exponent sum
+// (no value scale), rounded to bf16 like any output, and its (reference
+// maximum, exponent sum), log2 domain, in fp32, for a log-sum-exp merge:
+// o[(c * num_q + q) * num_heads + h][head dim], ml[...][2].
 struct PrefixStates {
-  float* acc;
+  uint16_t* o;
   float* ml;
   int num_q;
   int split_len;   // a multiple of 128 keys: whole blocks and whole steps
@@ -460,8 +461,10 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(
 
   // The finished tile goes to LDS as rows (row-major, kTileStride bytes per
   // row), then every thread stores whole 16-byte pieces of rows.
+  // An output is scaled by v_scale / sum; a prefix split's state by
+  // 1 / sum (the merge applies v_scale once, to the merged output).
   uint8_t* tile_lds = lds + kTileOff;
-  const float inv = kPrefix ? 1.f : (l_tot > 0.f ? v_scale / l_tot : 0.f);
+  const float inv = l_tot > 0.f ? (kPrefix ? 1.f : v_scale) / l_tot : 0.f;
 #pragma unroll
   for (int u = 0; u < 2; ++u)
 #pragma unroll
@@ -469,12 +472,8 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(
       const int d0 = 64 * kh + 32 * u + q4 * 8 + 4 * half;
       const float x0 = keep[u][4 * q4 + 0], x1 = keep[u][4 * q4 + 1];
       const float x2 = keep[u][4 * q4 + 2], x3 = keep[u][4 * q4 + 3];
-      if constexpr (kPrefix) {
-        *(f32x4*)(tile_lds + row * kTileStride + d0 * 4) = f32x4{x0, x1, x2, x3};
-      } else {
-        *(u32x2*)(tile_lds + row * kTileStride + d0 * 2) =
-            u32x2{pk_bf16(x0 * inv, x1 * inv), pk_bf16(x2 * inv, x3 * inv)};
-      }
+      *(u32x2*)(tile_lds + row * kTileStride + d0 * 2) =
+          u32x2{pk_bf16(x0 * inv, x1 * inv), pk_bf16(x2 * inv, x3 * inv)};
     }
   if constexpr (kPrefix) {
     if (kh == 0 && half == 0 && row_ok) {
@@ -484,18 +483,16 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(
     }
   }
   __syncthreads();
-  constexpr int kRowPieces = kPD * (kPrefix ? 4 : 2) / 16;  // 16-byte pieces per row
+  constexpr int kRowPieces = kPD * 2 / 16;  // 16-byte pieces per row
+  uint16_t* const dst = kPrefix ? ps.o + (int64_t)c * n * num_heads * kPD : (uint16_t*)out;
 #pragma unroll
   for (int k = 0; k < kRows * kRowPieces / kPThreads; ++k) {
     const int f = t + k * kPThreads, r = f / kRowPieces, piece = f % kRowPieces;
     const int rq = q_first + r / G;
     if (rq >= n) continue;
     const int64_t grow = (int64_t)(qs + rq) * num_heads + g * G + r % G;
-    const u32x4 v = *(const u32x4*)(tile_lds + r * kTileStride + piece * 16);
-    if constexpr (kPrefix)
-      *(u32x4*)(ps.acc + ((int64_t)c * n * num_heads + grow) * kPD + 4 * piece) = v;
-    else
-      *(u32x4*)((uint16_t*)out + grow * kPD + 8 * piece) = v;
+    *(u32x4*)(dst + grow * kPD + 8 * piece) =
+        *(const u32x4*)(tile_lds + r * kTileStride + piece * 16);
   }
 }
 
@@ -514,14 +511,14 @@ static hipError_t launch_prefix(const PrefillArgs& a) {
                      a.k_cache, a.v_cache, a.block_tables, a.max_blocks_per_seq, a.seq_lens,
                      a.num_kv_heads, qk == 0.f ? 1.f : fabsf(qk),
                      qk == 0.f ? kQZero : (qk < 0.f ? kQNegate : kQAsIs), 1.0f,
-                     PrefixStates{a.prefix.acc, a.prefix.ml, a.num_tokens, a.prefix.split_len,
+                     PrefixStates{a.prefix.o, a.prefix.ml, a.num_tokens, a.prefix.split_len,
                                   a.prefix.prefix_len});
   return hipGetLastError();
 }
 
 template <typename KV, int BS, int G>
 static hipError_t launch_prefill(const PrefillArgs& a) {
-  if (a.prefix.acc) return launch_prefix<KV, BS, G>(a);
+  if (a.prefix.o) return launch_prefix<KV, BS, G>(a);
   const float k_scale = std::is_same<KV, FP8>::value ? a.k_scale : 1.0f;
   const float v_scale = std::is_same<KV, FP8>::value ? a.v_scale : 1.0f;
   // The kernel takes a positive score scale (see kQNegate, kQZero).
